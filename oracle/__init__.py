@@ -1,0 +1,26 @@
+"""CPU oracle for the memory-efficient linear GRPO loss — TEST INFRASTRUCTURE.
+
+A plain, slow, fp64 NumPy statement of what the loss computes, written from the
+pages and checked against closed forms, brute force and finite differences in
+``tests/``.  It materialises every row's full vocabulary of logits and shares
+no code with the HIP path.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path never calls it.
+
+Parity status: every function here is pinned (see the tests named in each
+docstring); none is "parity unpinned".
+"""
+
+from .grpo_oracle import (  # noqa: F401
+    backward,
+    forward,
+    found_inf,
+    group_advantages,
+    log_softmax_rows,
+    logit_grad,
+    policy_grad,
+    reverse_kl_k3,
+    surrogate_objective,
+    token_loss,
+)

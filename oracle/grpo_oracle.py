@@ -1,0 +1,292 @@
+"""fp64 NumPy oracle for the memory-efficient linear GRPO loss (test infrastructure).
+
+What the pages fix, restated (the formulas on the pages were images and did not
+survive; the prose and the one surviving code fragment carry the method):
+
+* GRPO scores each sampled response of a group and compares it with the group
+  mean; better-than-average responses are reinforced [Train your own R1
+  reasoning model with Unsloth, §3 "GRPO + aha moment"].  The advantage A
+  takes every reward function into account [Long-context GRPO, §4].
+* The KL term is the reverse KL between the trained policy Q and the frozen
+  reference P, estimated per token without an extra Q factor, scaled by
+  beta = 0.04 [Long-context GRPO, §3 and §4].
+* The advantage is multiplied by exp(q - stopgrad(q)): a factor whose value is 1
+  but whose gradient flows through the policy log-prob q [Long-context GRPO, §4].
+* Log-probs come from the logsumexp trick [Long-context GRPO, §4], and the
+  memory-efficient algorithm never stores the (G, L, V) logits
+  [Long-context GRPO, §2 and §3].  Chunking and an online logsumexp reach the
+  same numbers as the dense definition, so this oracle is the dense definition:
+  it materialises each row's full vocabulary of logits in fp64.
+
+Readings where the pages are silent (each one is pinned by a test):
+* loss = sum_t m_t * l_t / N_tok, a masked mean over all completion tokens,
+  with N_tok = sum_t m_t clamped to at least 1;
+* l_t = beta * KL_t - A_s (the value of -(ratio * A - beta * KL), ratio = 1);
+* KL_t = exp(ref - q) - (ref - q) - 1, written expm1(d) - d with d = ref - q;
+* A_s = (r_s - mean) / (std + eps) with the unbiased std and eps = 1e-4, rewards
+  of the K reward functions summed first, in the fixed fp32 order below;
+* one lm_head W serves policy and reference; only the policy path is
+  differentiated, so X_p and the reference log-probs get no gradient;
+* rows with mask 0 are never read; their outputs are 0.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+F32 = np.float32
+
+
+# --------------------------------------------------------------------------------------
+# Advantages
+# --------------------------------------------------------------------------------------
+
+def group_advantages(rewards, eps: float = 1e-4, unbiased: bool = True) -> np.ndarray:
+    """Group-relative advantages in fp32, in one fixed order of operations.
+
+    For each prompt b: each response's score is the sum of its K reward-function
+    scores (k ascending); mean = (sum over g ascending) / G; the squared
+    deviations are summed g ascending with no fused multiply-add; std is the
+    correctly rounded sqrt of that sum / (G - 1) (G with ``unbiased=False``);
+    A = (r - mean) / (std + eps).  Every step rounds to fp32 nearest-even, so a
+    GPU that performs the same operations in the same order matches bit for bit.
+    [Train your own R1 reasoning model with Unsloth, §3; Long-context GRPO, §4]
+
+    Pinned by tests/test_oracle_pins.py::test_advantages_* (closed forms, torch.std,
+    exact zero for equal rewards, K-sum).
+    """
+    r = np.asarray(rewards, dtype=F32)
+    if r.ndim == 2:
+        r = r[:, :, None]
+    B, G, K = r.shape
+    if G < 1 or K < 1 or (unbiased and G < 2):
+        raise ValueError("need G >= 2 for the unbiased std and K >= 1")
+    e = F32(eps)
+    out = np.empty(B * G, dtype=F32)
+    for b in range(B):
+        score = []
+        for g in range(G):
+            acc = r[b, g, 0]
+            for k in range(1, K):
+                acc = F32(acc + r[b, g, k])
+            score.append(acc)
+        total = F32(0.0)
+        for g in range(G):
+            total = F32(total + score[g])
+        mean = F32(total / F32(G))
+        sq = F32(0.0)
+        for g in range(G):
+            d = F32(score[g] - mean)
+            sq = F32(sq + F32(d * d))
+        var = F32(sq / F32(G - 1 if unbiased else G))
+        std = F32(np.sqrt(var))
+        den = F32(std + e)
+        for g in range(G):
+            out[b * G + g] = F32(F32(score[g] - mean) / den)
+    return out
+
+
+# --------------------------------------------------------------------------------------
+# Per-token pieces
+# --------------------------------------------------------------------------------------
+
+def log_softmax_rows(z: np.ndarray):
+    """Row-wise log-softmax of fp64 logits by the logsumexp trick: subtract the
+    row max before exponentiating [Long-context GRPO, §4].  Returns
+    (log-probs, lse).  Pinned by test_logsoftmax_normalised and the brute force."""
+    z = np.asarray(z, dtype=np.float64)
+    m = z.max(axis=1, keepdims=True)
+    lse = m[:, 0] + np.log(np.exp(z - m).sum(axis=1))
+    return z - lse[:, None], lse
+
+
+def reverse_kl_k3(q: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per-token estimator of KL(Q || P) from the sampled token's log-probs under
+    the policy (q) and the reference (ref): exp(ref - q) - (ref - q) - 1, with no
+    extra Q factor [Long-context GRPO, §3 and §4].  Its expectation under y ~ Q is
+    the reverse KL.  Pinned by test_kl_direction_exact_expectation."""
+    d = np.asarray(ref, dtype=np.float64) - np.asarray(q, dtype=np.float64)
+    return np.expm1(d) - d
+
+
+def token_loss(kl: np.ndarray, adv_tok: np.ndarray, beta: float) -> np.ndarray:
+    """Per-token loss value beta * KL - A: the value of -(exp(q - sg(q)) * A - beta * KL)
+    with the ratio equal to 1 [Long-context GRPO, §4].  Pinned by
+    test_policy_equals_reference and the brute force."""
+    return beta * kl - adv_tok
+
+
+def policy_grad(adv_tok: np.ndarray, q: np.ndarray, ref: np.ndarray, beta: float,
+                n_tok: float) -> np.ndarray:
+    """d loss / d q per loss token: (-A - beta * (exp(ref - q) - 1)) / N_tok.  The
+    ratio contributes A * dq (its value is 1, its gradient is not zero) and the
+    estimator contributes beta * (1 - exp(ref - q)) [Long-context GRPO, §4].
+    Pinned by test_g_matches_surrogate_fd and the brute force."""
+    return (-adv_tok - beta * np.expm1(ref - q)) / n_tok
+
+
+def logit_grad(logp: np.ndarray, y: np.ndarray) -> np.ndarray:
+    """d q / d z for the sampled token y of each row: onehot(y) - softmax(z).
+    Pinned by test_dx_dw_finite_differences and test_cross_entropy_reduction."""
+    T = -np.exp(logp)
+    T[np.arange(len(y)), y] += 1.0
+    return T
+
+
+def surrogate_objective(q, q0, ref, adv_tok, mask, beta: float) -> float:
+    """The GRPO objective as autograd sees it: sum over loss tokens of
+    -A * exp(q - q0) + beta * KL(q, ref), divided by N_tok, where q0 is a frozen
+    copy of q.  At q = q0 its value is the loss; its gradient in q is the policy
+    gradient.  [Long-context GRPO, §4]  Used by the finite-difference pins."""
+    q = np.asarray(q, dtype=np.float64)
+    m = np.asarray(mask, dtype=np.float64)
+    n_tok = max(1.0, float(m.sum()))
+    ratio = np.exp(q - np.asarray(q0, dtype=np.float64))
+    terms = -np.asarray(adv_tok, dtype=np.float64) * ratio + beta * reverse_kl_k3(q, ref)
+    return float((m * terms).sum() / n_tok)
+
+
+# --------------------------------------------------------------------------------------
+# Forward and backward, materialising full rows of logits
+# --------------------------------------------------------------------------------------
+
+def _f64(x) -> np.ndarray:
+    if hasattr(x, "detach"):  # a torch tensor: promote exactly via float64
+        import torch
+        return x.detach().to(torch.float64).cpu().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _finite(a) -> bool:
+    return bool(np.all(np.isfinite(a)))
+
+
+def forward(xq, xp, W, targets, mask, adv, L: int, beta: float = 0.04, rows=None,
+            block: int = 256) -> dict:
+    """Loss and per-token terms.
+
+    Arguments: xq, xp hidden states [N, H] (or only the rows listed in ``rows``,
+    in that order); W [V, H]; targets int [N]; mask {0,1} [N]; adv fp32 [S] (one
+    per sequence, broadcast over its L tokens); L positions per sequence.
+
+    Returns per-row arrays of length N (zero for masked rows and, in sampled
+    mode, for rows not listed): ``lse_q``, ``logp`` (q), ``ref_logp``, ``kl``,
+    ``ell`` (beta*KL - A), ``g`` (d loss / d q); plus ``n_tok``, ``loss`` (None in
+    sampled mode), ``rows`` (the rows computed) and ``inputs_finite``.
+    """
+    targets = np.asarray(targets).reshape(-1)
+    mask = np.asarray(mask).reshape(-1).astype(np.int64)
+    N = mask.shape[0]
+    adv = np.asarray(adv, dtype=F32).reshape(-1)
+    Wd = _f64(W)
+    V = Wd.shape[0]
+    n_tok = int(mask.sum())
+    denom = float(max(1, n_tok))
+    loss_rows = np.nonzero(mask)[0]
+    if rows is None:
+        rows = loss_rows
+        xq_rows = _f64(xq)[rows]
+        xp_rows = _f64(xp)[rows]
+        full = True
+    else:
+        rows = np.asarray(rows, dtype=np.int64)
+        xq_rows, xp_rows = _f64(xq), _f64(xp)
+        assert xq_rows.shape[0] == len(rows)
+        full = False
+    out = {k: np.zeros(N) for k in ("lse_q", "logp", "ref_logp", "kl", "ell", "g")}
+    finite = _finite(Wd) and _finite(adv)
+    for i0 in range(0, len(rows), block):
+        sel = slice(i0, i0 + block)
+        r = rows[sel]
+        keep = mask[r] == 1                     # masked rows are not read
+        r = r[keep]
+        if len(r) == 0:
+            continue
+        y = targets[r]
+        if np.any((y < 0) | (y >= V)):
+            raise ValueError("target id outside [0, V) on a loss token")
+        xq_b = xq_rows[sel][keep]
+        xp_b = xp_rows[sel][keep]
+        finite = finite and _finite(xq_b) and _finite(xp_b)
+        lp_q, lse_q = log_softmax_rows(xq_b @ Wd.T)
+        lp_p, _ = log_softmax_rows(xp_b @ Wd.T)
+        q = lp_q[np.arange(len(r)), y]
+        ref = lp_p[np.arange(len(r)), y]
+        kl = reverse_kl_k3(q, ref)
+        a = adv[r // L].astype(np.float64)
+        out["lse_q"][r] = lse_q
+        out["logp"][r] = q
+        out["ref_logp"][r] = ref
+        out["kl"][r] = kl
+        out["ell"][r] = token_loss(kl, a, beta)
+        out["g"][r] = policy_grad(a, q, ref, beta, denom)
+    out["n_tok"] = n_tok
+    out["rows"] = rows
+    out["loss"] = float(out["ell"][loss_rows].sum() / denom) if full else None
+    out["inputs_finite"] = finite
+    return out
+
+
+def backward(xq, W, targets, mask, fwd: dict, grad_loss: float = 1.0,
+             loss_scale: float = 1.0, need_dW: bool = False, rows=None,
+             block: int = 256) -> dict:
+    """Gradients of the loss with respect to X_q (and W), from ``forward``'s g.
+
+    dX_q[t] = c * g_t * (onehot(y_t) - P_t) @ W and dW = sum_t c * g_t *
+    (onehot(y_t) - P_t)^T x_q[t], where P_t is the softmax of row t's policy
+    logits and c = grad_loss / loss_scale (an fp16 caller back-propagates the
+    loss scaled by S and passes S for both, so the gradients come back
+    unscaled).  Rows with mask 0 get zero.  ``rows``/``xq`` follow ``forward``'s
+    convention; dW needs every loss row.
+
+    Also reports ``naive_fp16_overflow``: whether a path that formed the scaled
+    logit gradient grad_loss * g_t * (onehot - P) in fp16 would overflow (any
+    magnitude >= 65520) — the mixed-precision hazard [Long-context GRPO, §3].
+    """
+    targets = np.asarray(targets).reshape(-1)
+    mask = np.asarray(mask).reshape(-1).astype(np.int64)
+    Wd = _f64(W)
+    V, H = Wd.shape
+    c = float(grad_loss) / float(loss_scale)
+    if rows is None:
+        rows = np.nonzero(mask)[0]
+        xq_rows = _f64(xq)[rows]
+        full = True
+    else:
+        rows = np.asarray(rows, dtype=np.int64)
+        xq_rows = _f64(xq)
+        full = False
+    if need_dW and not full:
+        raise ValueError("dW needs every loss row")
+    dX = np.zeros((len(rows), H))
+    dW = np.zeros((V, H)) if need_dW else None
+    worst = 0.0
+    for i0 in range(0, len(rows), block):
+        sel = slice(i0, i0 + block)
+        r = rows[sel]
+        keep = np.nonzero(mask[r] == 1)[0]
+        if len(keep) == 0:
+            continue
+        rk = r[keep]
+        x = xq_rows[sel][keep]
+        lp, _ = log_softmax_rows(x @ Wd.T)
+        T = logit_grad(lp, targets[rk])
+        gt = fwd["g"][rk]
+        worst = max(worst, float(np.max(np.abs(gt * float(grad_loss))[:, None] * np.abs(T))))
+        dX[i0 + keep] = (c * gt)[:, None] * (T @ Wd)
+        if need_dW:
+            dW += ((c * gt)[:, None] * T).T @ x
+    finite = _finite(dX) and (dW is None or _finite(dW))
+    return {"dX": dX, "dW": dW, "rows": rows, "outputs_finite": finite,
+            "naive_fp16_overflow": worst >= 65520.0, "naive_max_abs": worst}
+
+
+def found_inf(fwd: dict, bwd: dict | None = None) -> bool:
+    """The non-finite predicate a mixed-precision caller needs: anything read on a
+    loss row, the loss, g, dX or dW is inf/NaN."""
+    ok = fwd["inputs_finite"] and _finite(fwd["g"])
+    if fwd["loss"] is not None:
+        ok = ok and np.isfinite(fwd["loss"])
+    if bwd is not None:
+        ok = ok and bwd["outputs_finite"]
+    return not ok
