@@ -1,0 +1,218 @@
+"""ctypes marshalling for libgrpo.so.  No arithmetic of the loss happens here."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+_DTYPE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
+
+_c_i64 = ctypes.c_int64
+_c_p = ctypes.c_void_p
+
+
+class GRPOError(RuntimeError):
+    """A negative grpo_status returned by the library."""
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libgrpo.so")
+
+
+def load_library():
+    """Load libgrpo.so (once) and declare the exported signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m grpo_loss_amd.build` first")
+    lib = ctypes.CDLL(path)
+    lib.grpo_status_string.restype = ctypes.c_char_p
+    lib.grpo_status_string.argtypes = [ctypes.c_int]
+    lib.grpo_workspace_bytes.restype = ctypes.c_size_t
+    lib.grpo_workspace_bytes.argtypes = [_c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_int, ctypes.c_int]
+    lib.grpo_advantages.restype = ctypes.c_int
+    lib.grpo_advantages.argtypes = [_c_p, _c_i64, _c_i64, _c_i64, ctypes.c_float, ctypes.c_int,
+                                    _c_p, _c_p]
+    lib.grpo_loss_fwd.restype = ctypes.c_int
+    lib.grpo_loss_fwd.argtypes = [_c_p, _c_p, _c_p, ctypes.c_int, _c_p, _c_p, _c_p, _c_i64,
+                                  _c_i64, _c_i64, _c_i64, ctypes.c_float, _c_p, _c_p, _c_p, _c_p,
+                                  _c_p, _c_p, _c_p, ctypes.c_size_t, _c_p]
+    lib.grpo_loss_bwd.restype = ctypes.c_int
+    lib.grpo_loss_bwd.argtypes = [_c_p, _c_p, ctypes.c_int, _c_p, _c_p, _c_p, _c_i64, _c_i64,
+                                  _c_i64, _c_i64, _c_p, ctypes.c_float, _c_p, _c_p, ctypes.c_int,
+                                  _c_p, _c_p, ctypes.c_size_t, _c_p]
+    _LIB = lib
+    return lib
+
+
+load_library()
+
+
+def _check(rc: int):
+    if rc != 0:
+        msg = _LIB.grpo_status_string(rc).decode()
+        raise GRPOError(f"libgrpo returned {rc}: {msg}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPE:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DTYPE[t.dtype]
+
+
+def _need(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def grpo_workspace_bytes(S: int, L: int, H: int, V: int, dtype: torch.dtype,
+                         need_dW: bool = False) -> int:
+    return int(_LIB.grpo_workspace_bytes(S, L, H, V, _DTYPE[dtype], int(bool(need_dW))))
+
+
+def grpo_advantages(rewards: torch.Tensor, eps: float = 1e-4, unbiased: bool = True,
+                    out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """rewards fp32 [B, G] or [B, G, K] on the device -> advantages fp32 [B*G]."""
+    _need(rewards, "rewards")
+    if rewards.dtype != torch.float32:
+        raise TypeError("rewards must be float32")
+    r = rewards if rewards.dim() == 3 else rewards.unsqueeze(-1)
+    B, G, K = r.shape
+    if out is None:
+        out = torch.empty(B * G, dtype=torch.float32, device=rewards.device)
+    _check(_LIB.grpo_advantages(_ptr(r), B, G, K, eps, int(bool(unbiased)), _ptr(out),
+                                _stream(stream)))
+    return out
+
+
+def _shape(xq: torch.Tensor, L: int | None):
+    if xq.dim() == 3:
+        S, L2, H = xq.shape
+        if L is not None and L != L2:
+            raise ValueError("L does not match X's shape")
+        return S, L2, H
+    if xq.dim() != 2 or L is None or xq.shape[0] % L:
+        raise ValueError("X must be [S, L, H], or [S*L, H] with L given")
+    return xq.shape[0] // L, L, xq.shape[1]
+
+
+def grpo_loss_fwd(xq, xp, W, targets, mask, adv, beta: float = 0.04, L: int | None = None,
+                  workspace: torch.Tensor | None = None, want_terms: bool = True, stream=None):
+    """Forward.  Returns dict(loss [1], saved [N, 4], logp, ref_logp, kl [N] (or None),
+    status int32 [1], workspace)."""
+    for t, n in ((xq, "xq"), (xp, "xp"), (W, "W"), (targets, "targets"), (mask, "mask"),
+                 (adv, "adv")):
+        _need(t, n)
+    S, L, H = _shape(xq, L)
+    V = W.shape[0]
+    dt = _dt(xq)
+    if xp.dtype != xq.dtype or W.dtype != xq.dtype:
+        raise TypeError("xq, xp and W must share one dtype")
+    if targets.dtype != torch.int64 or mask.dtype != torch.uint8 or adv.dtype != torch.float32:
+        raise TypeError("targets int64, mask uint8, adv float32 expected")
+    dev = xq.device
+    N = S * L
+    need = grpo_workspace_bytes(S, L, H, V, xq.dtype, False)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    loss = torch.empty(1, **f32)
+    saved = torch.empty(N, 4, **f32)
+    terms = [torch.empty(N, **f32) for _ in range(3)] if want_terms else [None] * 3
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(_LIB.grpo_loss_fwd(_ptr(xq), _ptr(xp), _ptr(W), dt, _ptr(targets), _ptr(mask),
+                              _ptr(adv), S, L, H, V, beta, _ptr(loss), _ptr(saved),
+                              _ptr(terms[0]), _ptr(terms[1]), _ptr(terms[2]), _ptr(status),
+                              _ptr(workspace), workspace.numel(), _stream(stream)))
+    return {"loss": loss, "saved": saved, "logp": terms[0], "ref_logp": terms[1],
+            "kl": terms[2], "status": status, "workspace": workspace}
+
+
+def grpo_loss_bwd(xq, W, targets, mask, saved, L: int | None = None, grad_loss=None,
+                  loss_scale: float = 1.0, need_dW: bool = False, dW: torch.Tensor | None = None,
+                  accumulate_dW: bool = False, found_inf: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None, dXq: torch.Tensor | None = None,
+                  stream=None):
+    """Backward.  Returns dict(dXq, dW (or None), found_inf, workspace)."""
+    for t, n in ((xq, "xq"), (W, "W"), (targets, "targets"), (mask, "mask"), (saved, "saved")):
+        _need(t, n)
+    S, L, H = _shape(xq, L)
+    V = W.shape[0]
+    dev = xq.device
+    need_dW = need_dW or dW is not None
+    need = grpo_workspace_bytes(S, L, H, V, xq.dtype, need_dW)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if dXq is None:
+        dXq = torch.empty_like(xq)
+    if need_dW and dW is None:
+        dW = torch.empty(V, H, dtype=torch.float32, device=dev)
+    if found_inf is None:
+        found_inf = torch.zeros(1, dtype=torch.int32, device=dev)
+    if grad_loss is not None:
+        _need(grad_loss, "grad_loss")
+    _check(_LIB.grpo_loss_bwd(_ptr(xq), _ptr(W), _dt(xq), _ptr(targets), _ptr(mask),
+                              _ptr(saved), S, L, H, V, _ptr(grad_loss), float(loss_scale),
+                              _ptr(dXq), _ptr(dW) if need_dW else None, int(bool(accumulate_dW)),
+                              _ptr(found_inf), _ptr(workspace), workspace.numel(),
+                              _stream(stream)))
+    return {"dXq": dXq, "dW": dW if need_dW else None, "found_inf": found_inf,
+            "workspace": workspace}
+
+
+class _GRPOLoss(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, xq, xp, W, targets, mask, adv, beta, L, loss_scale, need_dW):
+        out = grpo_loss_fwd(xq, xp, W, targets, mask, adv, beta, L, want_terms=False)
+        ctx.save_for_backward(xq, W, targets, mask, out["saved"])
+        ctx.L, ctx.loss_scale, ctx.need_dW = L, loss_scale, need_dW
+        ctx.workspace = out["workspace"]
+        ctx.mark_non_differentiable(out["status"])
+        return out["loss"][0], out["status"]
+
+    @staticmethod
+    def backward(ctx, grad_loss, _grad_status):
+        xq, W, targets, mask, saved = ctx.saved_tensors
+        g = grad_loss.reshape(1).to(torch.float32).contiguous()
+        out = grpo_loss_bwd(xq, W, targets, mask, saved, ctx.L, g, ctx.loss_scale,
+                            need_dW=ctx.need_dW and W.requires_grad, workspace=None)
+        dW = out["dW"].to(W.dtype) if out["dW"] is not None else None
+        ctx.found_inf = out["found_inf"]
+        return out["dXq"], None, dW, None, None, None, None, None, None, None
+
+
+def grpo_loss(xq, xp, W, targets, mask, rewards, beta: float = 0.04, eps: float = 1e-4,
+              loss_scale: float = 1.0, need_dW: bool = False, L: int | None = None):
+    """The GRPO loss with autograd.  xq, xp [S, L, H] (or [S*L, H] with L), W [V, H],
+    targets int64 and mask (bool/uint8) of S*L elements, rewards fp32 [S] or [B, G(, K)].
+
+    Returns (loss, status).  Gradients flow to xq (and W when need_dW); xp and the
+    reference path get none.  With loss scaling, back-propagate loss * loss_scale and pass
+    the same loss_scale here: the returned gradients are unscaled."""
+    r = rewards.float()
+    if r.dim() == 1:
+        r = r.unsqueeze(0)
+    adv = grpo_advantages(r.contiguous(), eps)
+    m = mask.reshape(-1).to(torch.uint8).contiguous()
+    y = targets.reshape(-1).contiguous()
+    return _GRPOLoss.apply(xq.contiguous(), xp.contiguous(), W.contiguous(), y, m, adv,
+                           float(beta), L if xq.dim() == 2 else xq.shape[1], float(loss_scale),
+                           bool(need_dW))

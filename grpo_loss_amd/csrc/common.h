@@ -1,0 +1,110 @@
+// Internal declarations shared by the HIP translation units of libgrpo.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "grpo.h"
+
+namespace grpo {
+
+typedef uint16_t u16;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ------------------------------------------------------------------------ element types
+// Storage types of X, W, dX and of the staged (onehot - softmax) chunk.  Values are
+// widened to fp32 for arithmetic; narrowing rounds to nearest-even.
+struct F32T {
+  typedef float T;
+  static constexpr int kBytes = 4;
+  __device__ static inline float to_f32(T v) { return v; }
+  __device__ static inline T from_f32(float f) { return f; }
+};
+
+struct BF16T {
+  typedef u16 T;
+  static constexpr int kBytes = 2;
+  __device__ static inline float to_f32(T v) { return __uint_as_float((uint32_t)v << 16); }
+  __device__ static inline T from_f32(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (T)((u >> 16) | 0x40u);  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (T)(u >> 16);
+  }
+};
+
+struct F16T {
+  typedef u16 T;
+  static constexpr int kBytes = 2;
+  __device__ static inline float to_f32(T v) {
+    _Float16 h;
+    __builtin_memcpy(&h, &v, 2);
+    return (float)h;
+  }
+  __device__ static inline T from_f32(float f) {
+    _Float16 h = (_Float16)f;  // v_cvt_f16_f32: round to nearest even
+    T v;
+    __builtin_memcpy(&v, &h, 2);
+    return v;
+  }
+};
+
+// ------------------------------------------------------------------------ workspace plan
+// One plan describes every buffer carved out of the caller's workspace.  The host fills
+// it from the sizes alone (the number of loss tokens lives on the device).
+struct Plan {
+  int64_t N;        // rows = S * L
+  int64_t L, H, V;
+  int64_t Vpad;     // V rounded up to the vocabulary tile (256)
+  int dtype;        // grpo_dtype
+  int esize;        // bytes per element of X / W / T
+  int need_dW;
+  int phases;       // forward: vocabulary phases per token block (partials per row)
+  int64_t R;        // backward: rows per recompute chunk (multiple of 256)
+  int ksplit;       // backward: split of the dX reduction over the vocabulary
+  // byte offsets into the workspace
+  size_t off_ntok, off_idx, off_rank, off_part, off_lsum, off_T, off_WT, off_TT, off_XgT,
+      off_dxp, total;
+};
+
+constexpr int kTokTile = 256;    // rows per token tile of the MFMA kernels
+constexpr int kVocTile = 256;    // vocabulary entries per tile
+constexpr int kMergeBlock = 256; // rows per block of the merge kernel
+
+bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_dW, Plan* p);
+
+template <typename P>
+inline P* ws_ptr(void* ws, size_t off) {
+  return reinterpret_cast<P*>(reinterpret_cast<char*>(ws) + off);
+}
+
+// ------------------------------------------------------------------------ launchers
+// Each returns hipSuccess or the launch error.  All run on `st` and read the number of
+// loss tokens from device memory (ntok), so no host synchronisation is needed.
+hipError_t launch_advantages(const float* rewards, int64_t B, int64_t G, int64_t K, float eps,
+                             int unbiased, float* adv, hipStream_t st);
+hipError_t launch_compact(const uint8_t* mask, int64_t N, int32_t* ntok, int32_t* idx,
+                          int32_t* rank, hipStream_t st);
+// Same, and clears the forward's status word first.
+hipError_t launch_compact_status(const uint8_t* mask, int64_t N, int32_t* ntok, int32_t* idx,
+                                 int32_t* rank, int32_t* status, hipStream_t st);
+hipError_t launch_merge(const Plan& p, const void* ws, const int64_t* targets,
+                        const uint8_t* mask, const float* adv, float beta, float* saved,
+                        float* logp, float* ref_logp, float* kl, int32_t* status, float* loss,
+                        hipStream_t st);
+hipError_t launch_zero_masked_rows(const Plan& p, const uint8_t* mask, void* dX,
+                                   hipStream_t st);
+
+// Forward partials (online max / sum-exp / target logit per row and vocabulary phase).
+hipError_t launch_fwd_partials(const Plan& p, void* ws, const void* Xq, const void* Xp,
+                               const void* W, const int64_t* targets, hipStream_t st);
+// Backward over all row chunks: recompute, dX (and dW).
+hipError_t launch_bwd(const Plan& p, void* ws, const void* Xq, const void* W,
+                      const int64_t* targets, const float* saved, const float* grad_loss,
+                      float loss_scale, void* dX, float* dW, int accumulate_dW,
+                      int32_t* found_inf, hipStream_t st);
+
+}  // namespace grpo

@@ -1,0 +1,182 @@
+// Host side of the C ABI declared in include/grpo.h: argument validation, the workspace
+// plan and the launch sequence.  Nothing here allocates, synchronises or prints.
+#include <math.h>
+#include <string.h>
+
+#include "common.h"
+
+namespace grpo {
+
+hipError_t simple_fwd_partials(const Plan& p, void* ws, const void* Xq, const void* Xp,
+                               const void* W, const int64_t* targets, hipStream_t st);
+hipError_t simple_backward(const Plan& p, void* ws, const void* Xq, const void* W,
+                           const int64_t* targets, const float* saved, const float* grad_loss,
+                           float loss_scale, void* dX, float* dW, int accumulate_dW,
+                           int32_t* found_inf, hipStream_t st);
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxDevices = 64;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool valid_dtype(int dt) { return dt == GRPO_F32 || dt == GRPO_BF16 || dt == GRPO_F16; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// 1 = gfx950, 0 = another device, cached per device ordinal.
+int device_ok() {
+  static int cache[kMaxDevices] = {0};  // 0 unknown, 1 ok, 2 not ok
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDevices && cache[dev]) return cache[dev] == 1;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+  const int ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) cache[dev] = ok ? 1 : 2;
+  return ok;
+}
+
+bool sizes_ok(int64_t S, int64_t L, int64_t H, int64_t V) {
+  if (S < 1 || L < 1 || H < 64 || V < 1) return false;
+  if (H % 64 != 0) return false;
+  if (S > INT32_MAX / L) return false;            // row indices are int32
+  if (V > (int64_t)1 << 30 || H > (int64_t)1 << 20) return false;
+  return true;
+}
+
+}  // namespace
+
+bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_dW, Plan* p) {
+  if (!sizes_ok(S, L, H, V) || !valid_dtype(dtype)) return false;
+  memset(p, 0, sizeof(*p));
+  p->N = S * L;
+  p->L = L;
+  p->H = H;
+  p->V = V;
+  p->Vpad = (V + kVocTile - 1) / kVocTile * kVocTile;
+  p->dtype = dtype;
+  p->esize = dtype == GRPO_F32 ? 4 : 2;
+  p->need_dW = need_dW ? 1 : 0;
+  p->phases = 8;
+  const int64_t Npad = (p->N + kTokTile - 1) / kTokTile * kTokTile;
+  p->R = Npad < 4096 ? Npad : 4096;
+  p->ksplit = 1;
+  size_t o = 0;
+  p->off_ntok = o;
+  o = align_up(o + 16);
+  p->off_idx = o;
+  o = align_up(o + (size_t)p->N * 4);
+  p->off_rank = o;
+  o = align_up(o + (size_t)p->N * 4);
+  p->off_part = o;
+  o = align_up(o + (size_t)6 * p->phases * p->N * 4);
+  p->off_lsum = o;
+  o = align_up(o + (size_t)((p->N + kMergeBlock - 1) / kMergeBlock) * 8);
+  p->off_T = o;
+  o = align_up(o + (size_t)p->R * p->Vpad * p->esize);
+  p->off_WT = p->off_TT = p->off_XgT = p->off_dxp = o;
+  p->total = o;
+  return true;
+}
+
+}  // namespace grpo
+
+using namespace grpo;
+
+extern "C" {
+
+const char* grpo_status_string(int status) {
+  switch (status) {
+    case GRPO_OK: return "ok";
+    case GRPO_ERR_NULL: return "a required pointer is NULL";
+    case GRPO_ERR_SHAPE: return "a size is out of range";
+    case GRPO_ERR_DTYPE: return "unknown dtype";
+    case GRPO_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case GRPO_ERR_WORKSPACE: return "workspace too small";
+    case GRPO_ERR_HIP: return "HIP runtime error while enqueuing";
+    case GRPO_ERR_DEVICE: return "current device is not gfx950";
+    default: return "unknown status";
+  }
+}
+
+size_t grpo_workspace_bytes(int64_t S, int64_t L, int64_t H, int64_t V, grpo_dtype dtype,
+                            int need_dW) {
+  Plan p;
+  if (!make_plan(S, L, H, V, dtype, need_dW, &p)) return 0;
+  return p.total;
+}
+
+int grpo_advantages(const float* rewards, int64_t B, int64_t G, int64_t K, float eps,
+                    int unbiased, float* adv, grpo_stream_t stream) {
+  if (!rewards || !adv) return GRPO_ERR_NULL;
+  if (B < 1 || G < 1 || K < 1 || (unbiased && G < 2)) return GRPO_ERR_SHAPE;
+  if (G > INT32_MAX / K || B > INT64_MAX / (G * K)) return GRPO_ERR_SHAPE;
+  if (!(eps >= 0.0f) || !isfinite(eps)) return GRPO_ERR_SHAPE;
+  if (!device_ok()) return GRPO_ERR_DEVICE;
+  if (launch_advantages(rewards, B, G, K, eps, unbiased, adv, (hipStream_t)stream) !=
+      hipSuccess)
+    return GRPO_ERR_HIP;
+  return GRPO_OK;
+}
+
+int grpo_loss_fwd(const void* Xq, const void* Xp, const void* W, grpo_dtype dtype,
+                  const int64_t* targets, const uint8_t* mask, const float* adv, int64_t S,
+                  int64_t L, int64_t H, int64_t V, float beta, float* loss, float* saved,
+                  float* logp_out, float* ref_logp_out, float* kl_out, int32_t* status,
+                  void* workspace, size_t workspace_bytes, grpo_stream_t stream) {
+  if (!Xq || !Xp || !W || !targets || !mask || !adv || !loss || !saved || !status || !workspace)
+    return GRPO_ERR_NULL;
+  if (!valid_dtype(dtype)) return GRPO_ERR_DTYPE;
+  if (!sizes_ok(S, L, H, V) || !isfinite(beta)) return GRPO_ERR_SHAPE;
+  if (!aligned16(Xq) || !aligned16(Xp) || !aligned16(W) || !aligned16(saved) ||
+      !aligned16(workspace))
+    return GRPO_ERR_ALIGN;
+  Plan p;
+  if (!make_plan(S, L, H, V, dtype, 0, &p)) return GRPO_ERR_SHAPE;
+  if (workspace_bytes < p.total) return GRPO_ERR_WORKSPACE;
+  if (!device_ok()) return GRPO_ERR_DEVICE;
+  hipStream_t st = (hipStream_t)stream;
+  void* ws = workspace;
+  if (launch_compact_status(mask, p.N, ws_ptr<int32_t>(ws, p.off_ntok),
+                            ws_ptr<int32_t>(ws, p.off_idx), ws_ptr<int32_t>(ws, p.off_rank),
+                            status, st) != hipSuccess)
+    return GRPO_ERR_HIP;
+  if (simple_fwd_partials(p, ws, Xq, Xp, W, targets, st) != hipSuccess) return GRPO_ERR_HIP;
+  if (launch_merge(p, ws, targets, mask, adv, beta, saved, logp_out, ref_logp_out, kl_out,
+                   status, loss, st) != hipSuccess)
+    return GRPO_ERR_HIP;
+  return GRPO_OK;
+}
+
+int grpo_loss_bwd(const void* Xq, const void* W, grpo_dtype dtype, const int64_t* targets,
+                  const uint8_t* mask, const float* saved, int64_t S, int64_t L, int64_t H,
+                  int64_t V, const float* grad_loss, float loss_scale, void* dXq, float* dW,
+                  int accumulate_dW, int32_t* found_inf, void* workspace,
+                  size_t workspace_bytes, grpo_stream_t stream) {
+  if (!Xq || !W || !targets || !mask || !saved || !dXq || !found_inf || !workspace)
+    return GRPO_ERR_NULL;
+  if (!valid_dtype(dtype)) return GRPO_ERR_DTYPE;
+  if (!sizes_ok(S, L, H, V) || !(loss_scale > 0.0f) || !isfinite(loss_scale))
+    return GRPO_ERR_SHAPE;
+  if (!aligned16(Xq) || !aligned16(W) || !aligned16(saved) || !aligned16(dXq) ||
+      (dW && !aligned16(dW)) || !aligned16(workspace))
+    return GRPO_ERR_ALIGN;
+  Plan p;
+  if (!make_plan(S, L, H, V, dtype, dW != nullptr, &p)) return GRPO_ERR_SHAPE;
+  if (workspace_bytes < p.total) return GRPO_ERR_WORKSPACE;
+  if (!device_ok()) return GRPO_ERR_DEVICE;
+  hipStream_t st = (hipStream_t)stream;
+  void* ws = workspace;
+  if (launch_compact(mask, p.N, ws_ptr<int32_t>(ws, p.off_ntok), ws_ptr<int32_t>(ws, p.off_idx),
+                     ws_ptr<int32_t>(ws, p.off_rank), st) != hipSuccess)
+    return GRPO_ERR_HIP;
+  if (launch_zero_masked_rows(p, mask, dXq, st) != hipSuccess) return GRPO_ERR_HIP;
+  if (simple_backward(p, ws, Xq, W, targets, saved, grad_loss, loss_scale, dXq, dW,
+                      accumulate_dW, found_inf, st) != hipSuccess)
+    return GRPO_ERR_HIP;
+  return GRPO_OK;
+}
+
+}  // extern "C"

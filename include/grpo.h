@@ -1,0 +1,139 @@
+/*
+ * grpo.h — C ABI of libgrpo, the memory-efficient linear GRPO loss on MI355X (gfx950).
+ *
+ * The loss, as the pages define it [Long-context GRPO (note.com), §2-§4; Train your own
+ * R1 reasoning model with Unsloth, §3]:
+ *
+ *   For G sampled completions of one prompt, the policy's and the reference model's final
+ *   hidden states X_q, X_p [S*L, H] are projected through one lm_head W [V, H] to
+ *   per-token log-probs of the sampled tokens, q and ref, by a logsumexp over the
+ *   vocabulary.  The (G, L, V) logits are never stored: the vocabulary is swept in
+ *   chunks with an online max / sum-of-exponentials.  Per loss token t of sequence s
+ *
+ *       KL_t = exp(ref_t - q_t) - (ref_t - q_t) - 1          (reverse-KL estimator)
+ *       l_t  = beta * KL_t - A_s                              (value of -(ratio*A - beta*KL),
+ *                                                              ratio = exp(q - sg(q)) = 1)
+ *       loss = sum_t m_t * l_t / max(1, sum_t m_t)            (mean over completion tokens)
+ *
+ *   The gradient flows through q only: dloss/dq_t = m_t * (-A_s - beta*(exp(ref_t-q_t)-1))
+ *   / N_tok, and dq_t/dz_t = onehot(y_t) - softmax(z_t) with z_t = W x_q[t].  The backward
+ *   recomputes the same vocabulary chunks instead of storing softmax.
+ *
+ *   Advantages are group-relative: A_s = (r_s - mean_g r) / (std_g r + eps), where r_s is
+ *   the sum of the K reward-function scores of completion s and std is the unbiased
+ *   (G - 1) standard deviation.
+ *
+ * Conventions common to every entry point
+ *   - Every pointer argument except scalars is DEVICE memory, owned by the caller.  The
+ *     library never allocates, never synchronises the host with the device, never prints
+ *     and never aborts.  All work is enqueued on `stream` (a hipStream_t; NULL = the
+ *     default stream) in order, and may still be running when the call returns.
+ *   - Matrices are row-major and dense: X_q, X_p, dX_q are [S*L, H] with row t = position
+ *     t % L of sequence t / L; W is [V, H].  H must be a positive multiple of 64; V is
+ *     arbitrary (ragged vocabulary tails are handled).  S * L must fit in int32.
+ *   - `targets[t]` is the token that row t's hidden state predicts (the caller has already
+ *     shifted ids by one position).  Rows with mask 0 are never read and their outputs are 0;
+ *     a NaN in a masked-out row therefore sets no flag.
+ *   - Invalid arguments return a negative grpo_status before anything is enqueued.  Launch
+ *     failures return GRPO_ERR_HIP.  Data-dependent problems (non-finite values, a target
+ *     outside [0, V) on a loss row) are reported through device-side flag words.
+ *   - Calls that share a workspace must not overlap in time (same stream, or synchronised).
+ */
+#ifndef GRPO_H_
+#define GRPO_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* grpo_stream_t; /* hipStream_t */
+
+typedef enum grpo_dtype {
+  GRPO_F32 = 0,  /* fp32 operands, fp32 FMA products (parity workloads) */
+  GRPO_BF16 = 1, /* bfloat16 operands, MFMA with fp32 accumulation      */
+  GRPO_F16 = 2   /* IEEE half operands, MFMA with fp32 accumulation     */
+} grpo_dtype;
+
+typedef enum grpo_status {
+  GRPO_OK = 0,
+  GRPO_ERR_NULL = -1,      /* a required pointer is NULL                                  */
+  GRPO_ERR_SHAPE = -2,     /* a size is out of range (G < 2, H not a multiple of 64, ...) */
+  GRPO_ERR_DTYPE = -3,     /* unknown grpo_dtype                                          */
+  GRPO_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned                            */
+  GRPO_ERR_WORKSPACE = -5, /* workspace smaller than grpo_workspace_bytes()               */
+  GRPO_ERR_HIP = -6,       /* the HIP runtime reported an error when enqueuing           */
+  GRPO_ERR_DEVICE = -7     /* the current device is not a gfx950 GPU                      */
+} grpo_status;
+
+/* Bits of the forward's status word. */
+#define GRPO_FLAG_NONFINITE 1   /* loss, a log-prob, KL or g of a loss row is inf/NaN */
+#define GRPO_FLAG_BAD_TARGET 2  /* a loss row's target lies outside [0, V)             */
+
+/* Human-readable name of a grpo_status value (static storage). */
+const char* grpo_status_string(int status);
+
+/* Bytes of device workspace that grpo_loss_fwd and grpo_loss_bwd need for these sizes
+ * (S = sequences, L = positions per sequence).  The same workspace can serve both calls.
+ * It grows with one chunk of rows times V and with V*H (a transposed copy of W for the
+ * backward), never with S*L*V.  Returns 0 if the sizes are invalid. */
+size_t grpo_workspace_bytes(int64_t S, int64_t L, int64_t H, int64_t V, grpo_dtype dtype,
+                            int need_dW);
+
+/* Group-relative advantages [Train your own R1 reasoning model with Unsloth, §3;
+ * Long-context GRPO, §4].
+ *   rewards  fp32 [B, G, K]: score of completion g of prompt b under reward function k.
+ *   adv      fp32 [B*G] out: A = (r - mean) / (std + eps), r summed over k first.
+ *   unbiased 1: std divides by G - 1 (needs G >= 2); 0: divides by G.
+ * Operations run in one fixed fp32 order (k ascending, then g ascending sums, no fused
+ * multiply-add, correctly rounded division and square root), so results are
+ * reproducible bit for bit. */
+int grpo_advantages(const float* rewards, int64_t B, int64_t G, int64_t K, float eps,
+                    int unbiased, float* adv, grpo_stream_t stream);
+
+/* Forward: loss and per-token terms, without materialising logits
+ * [Long-context GRPO, §2 (memory figures), §3 (the linear algorithm), §4 (KL, ratio,
+ * logsumexp)].
+ *   Xq, Xp   [S*L, H] in `dtype`: policy and reference final hidden states.
+ *   W        [V, H] in `dtype`: the lm_head shared by policy and reference.
+ *   targets  int64 [S*L]; mask uint8 [S*L] (1 = completion token counted in the loss);
+ *   adv      fp32 [S]: one advantage per sequence (see grpo_advantages).
+ *   loss     fp32 [1] out.
+ *   saved    fp32 [S*L, 4] out: (lse_q, q, ref, dloss/dq) per row; the backward reads it.
+ *   logp_out, ref_logp_out, kl_out: fp32 [S*L] out, each may be NULL.
+ *   status   int32 [1] out: GRPO_FLAG_* bits of this call (overwritten, not accumulated).
+ *   workspace, workspace_bytes: at least grpo_workspace_bytes(..., need_dW = 0).
+ * Xq, Xp, W, saved, workspace must be 16-byte aligned. */
+int grpo_loss_fwd(const void* Xq, const void* Xp, const void* W, grpo_dtype dtype,
+                  const int64_t* targets, const uint8_t* mask, const float* adv, int64_t S,
+                  int64_t L, int64_t H, int64_t V, float beta, float* loss, float* saved,
+                  float* logp_out, float* ref_logp_out, float* kl_out, int32_t* status,
+                  void* workspace, size_t workspace_bytes, grpo_stream_t stream);
+
+/* Backward: dloss/dXq (and dloss/dW) by recomputing the vocabulary chunks.
+ *   Xq, W, targets, mask, saved: as given to / produced by grpo_loss_fwd.
+ *   grad_loss  fp32 [1] device, or NULL for 1.0: the upstream gradient of the loss.
+ *   loss_scale the factor the caller scaled the loss by (1.0 without loss scaling).  The
+ *              outputs are multiplied by grad_loss / loss_scale, so an fp16 caller that
+ *              back-propagates S * loss passes S twice and gets unscaled gradients.  The
+ *              per-token factors stay in fp32; 16-bit GEMM operands only ever hold
+ *              onehot - softmax, which lies in [-1, 1], so loss scaling cannot overflow
+ *              them (the mixed-precision hazard of [Long-context GRPO, §3]).
+ *   dXq        [S*L, H] in `dtype`, out (masked rows are written as 0).
+ *   dW         fp32 [V, H] out, or NULL to skip; accumulate_dW = 1 adds into it.
+ *   found_inf  int32 [1] device: set to 1 if any element of dXq or dW is inf/NaN; never
+ *              cleared by the library.
+ *   workspace  at least grpo_workspace_bytes(..., need_dW = (dW != NULL)). */
+int grpo_loss_bwd(const void* Xq, const void* W, grpo_dtype dtype, const int64_t* targets,
+                  const uint8_t* mask, const float* saved, int64_t S, int64_t L, int64_t H,
+                  int64_t V, const float* grad_loss, float loss_scale, void* dXq, float* dW,
+                  int accumulate_dW, int32_t* found_inf, void* workspace,
+                  size_t workspace_bytes, grpo_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GRPO_H_ */

@@ -1,0 +1,82 @@
+"""The C ABI without a GPU: the library loads, exports every function the header
+declares, rejects bad arguments before touching the device, and its workspace grows
+with one chunk of rows and with V*H, never with S*L*V."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "grpo.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(grpo_[a-z_]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import grpo_loss_amd
+    return grpo_loss_amd.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert {"grpo_advantages", "grpo_loss_fwd", "grpo_loss_bwd",
+            "grpo_workspace_bytes", "grpo_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(0, -8, -1):
+        s = lib.grpo_status_string(code)
+        assert s and s != b"unknown status"
+    assert lib.grpo_status_string(-99) == b"unknown status"
+
+
+def test_workspace_bytes(lib):
+    f = lib.grpo_workspace_bytes
+    assert f(8, 20480, 4096, 128256, 1, 0) > 0
+    assert f(8, 20480, 4096, 128256, 1, 0) == f(8, 20480, 4096, 128256, 1, 0)
+    assert f(0, 10, 64, 10, 1, 0) == 0          # S < 1
+    assert f(2, 10, 100, 10, 1, 0) == 0         # H not a multiple of 64
+    assert f(2, 10, 64, 10, 7, 0) == 0          # bad dtype
+    # O(chunk): doubling L doubles only per-row bookkeeping, far below 2*L*V*2 bytes
+    a = f(8, 20480, 4096, 128256, 1, 0)
+    b = f(8, 40960, 4096, 128256, 1, 0)
+    assert b - a < 8 * 20480 * 256
+    materialised = 2 * 2 * 8 * 20480 * 128256
+    assert a < materialised / 20
+
+
+def test_bad_arguments_rejected_before_launch(lib):
+    p = ctypes.c_void_p(16)   # never dereferenced: validation fails first
+    nul = None
+    rc = lib.grpo_loss_fwd(nul, p, p, 1, p, p, p, 2, 3, 64, 5, ctypes.c_float(0.04), p, p,
+                           nul, nul, nul, p, p, ctypes.c_size_t(1 << 40), nul)
+    assert rc == -1
+    rc = lib.grpo_loss_fwd(p, p, p, 9, p, p, p, 2, 3, 64, 5, ctypes.c_float(0.04), p, p,
+                           nul, nul, nul, p, p, ctypes.c_size_t(1 << 40), nul)
+    assert rc == -3
+    rc = lib.grpo_loss_fwd(p, p, p, 1, p, p, p, 2, 3, 96, 5, ctypes.c_float(0.04), p, p,
+                           nul, nul, nul, p, p, ctypes.c_size_t(1 << 40), nul)
+    assert rc == -2
+    odd = ctypes.c_void_p(18)
+    rc = lib.grpo_loss_fwd(odd, p, p, 1, p, p, p, 2, 3, 64, 5, ctypes.c_float(0.04), p, p,
+                           nul, nul, nul, p, p, ctypes.c_size_t(1 << 40), nul)
+    assert rc == -4
+    rc = lib.grpo_loss_fwd(p, p, p, 1, p, p, p, 2, 3, 64, 5, ctypes.c_float(0.04), p, p,
+                           nul, nul, nul, p, p, ctypes.c_size_t(8), nul)
+    assert rc == -5
+    rc = lib.grpo_loss_bwd(p, p, 1, p, p, p, 2, 3, 64, 5, nul, ctypes.c_float(0.0), p, nul, 0,
+                           p, p, ctypes.c_size_t(1 << 40), nul)
+    assert rc == -2                              # loss_scale must be > 0
+    rc = lib.grpo_advantages(p, 1, 1, 1, ctypes.c_float(1e-4), 1, p, nul)
+    assert rc == -2                              # unbiased std needs G >= 2
+    rc = lib.grpo_advantages(nul, 1, 8, 1, ctypes.c_float(1e-4), 1, p, nul)
+    assert rc == -1

@@ -1,0 +1,229 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Small cases use each workload's dtype, hidden size and vocabulary with fewer rows, so
+the fp64 oracle finishes in seconds while the GPU still sweeps many tiles and ragged
+tails.  Full-size cases run the exact workloads on the GPU and check sampled rows
+against the oracle row by row, plus properties that hold at any size.
+
+Tolerances: fp32 loss rel <= 1e-5 and dX rel-L2 <= 1e-5; bf16/fp16 log-prob abs <= 2e-2,
+loss rel <= 1e-3, dX / dW rel-L2 <= 1e-2; advantages bit-exact.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import generate, workload_by_name
+from synth.device import to_device
+from synth.generate import hidden_rows
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": dict(loss=1e-5, dx=1e-5, logp=1e-5, dw=1e-5),
+       "bf16": dict(loss=1e-3, dx=1e-2, logp=2e-2, dw=1e-2),
+       "f16": dict(loss=1e-3, dx=1e-2, logp=2e-2, dw=1e-2)}
+
+
+def _lib():
+    import grpo_loss_amd
+    return grpo_loss_amd
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def run_gpu(wl, inp, need_dW=None, grad_scale=True):
+    """advantages -> forward -> backward on the device; host copies of every output."""
+    g = _lib()
+    d = to_device(inp)
+    need_dW = wl.need_dW if need_dW is None else need_dW
+    adv = g.grpo_advantages(d["rewards"], wl.eps)
+    f = g.grpo_loss_fwd(d["xq"], d["xp"], d["W"], d["targets"], d["mask"], adv, wl.beta, wl.L)
+    S = wl.loss_scale
+    grad = torch.full((1,), S, dtype=torch.float32, device="cuda")
+    b = g.grpo_loss_bwd(d["xq"], d["W"], d["targets"], d["mask"], f["saved"], wl.L, grad, S,
+                        need_dW=need_dW, workspace=f["workspace"])
+    torch.cuda.synchronize()
+    out = {"adv": adv.cpu().numpy(), "loss": float(f["loss"].item()),
+           "saved": f["saved"].cpu().numpy(), "logp": f["logp"].cpu().numpy(),
+           "ref_logp": f["ref_logp"].cpu().numpy(), "kl": f["kl"].cpu().numpy(),
+           "status": int(f["status"].item()), "dX": b["dXq"].float().cpu().numpy(),
+           "found_inf": int(b["found_inf"].item()),
+           "dW": b["dW"].cpu().numpy() if b["dW"] is not None else None}
+    return out
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+SMALL = {
+    "tiny-f32": dict(),
+    "qwen2.5-1.5b-bf16": dict(G=8, L=64, prefix=16, comp_min=8, comp_max=48),
+    "llama3.1-8b-train-bf16": dict(G=4, L=96, H=1024, prefix=16, comp_min=20, comp_max=80),
+    "llama3.1-8b-long-bf16": dict(G=2, L=160, prefix=16, comp_min=144, comp_max=144),
+    "phi4-f16": dict(G=4, L=96, prefix=16, comp_min=16, comp_max=80),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_parity_small(name):
+    wl = dataclasses.replace(workload_by_name(name), **SMALL[name])
+    _say(f"[parity small] {name} S={wl.S} L={wl.L} H={wl.H} V={wl.V} dtype={wl.dtype}")
+    inp = generate(wl)
+    gpu = run_gpu(wl, inp)
+    adv = oracle.group_advantages(inp.rewards.numpy(), wl.eps)
+    assert np.array_equal(gpu["adv"].view(np.uint32), adv.view(np.uint32)), (gpu["adv"], adv)
+    f = oracle.forward(inp.xq, inp.xp, inp.W, inp.targets.numpy(), inp.mask.numpy(), adv, wl.L,
+                       wl.beta)
+    b = oracle.backward(inp.xq, inp.W, inp.targets.numpy(), inp.mask.numpy(), f,
+                        grad_loss=wl.loss_scale, loss_scale=wl.loss_scale, need_dW=wl.need_dW)
+    tol = TOL[wl.dtype]
+    m = inp.mask.numpy() == 1
+    assert gpu["status"] == 0 and gpu["found_inf"] == 0
+    rel = abs(gpu["loss"] - f["loss"]) / abs(f["loss"])
+    _say(f"  loss gpu={gpu['loss']:.8g} oracle={f['loss']:.8g} rel={rel:.2e}")
+    assert rel <= tol["loss"]
+    for k in ("logp", "ref_logp"):
+        err = np.abs(gpu[k][m] - f[k][m]).max()
+        _say(f"  {k} max abs err {err:.2e}")
+        assert err <= tol["logp"]
+        assert np.all(gpu[k][~m] == 0.0)
+    dX = np.zeros((wl.N, wl.H))
+    dX[b["rows"]] = b["dX"]
+    e = rel_l2(gpu["dX"], dX)
+    _say(f"  dX rel-L2 {e:.2e}")
+    assert e <= tol["dx"]
+    assert np.all(gpu["dX"][~m] == 0.0)
+    if wl.need_dW:
+        e = rel_l2(gpu["dW"], b["dW"])
+        _say(f"  dW rel-L2 {e:.2e}")
+        assert e <= tol["dw"]
+
+
+@pytest.mark.parametrize("B,G,K", [(1, 8, 1), (3, 4, 2), (37, 8, 3), (300, 16, 1), (1, 2, 1)])
+def test_advantages_bitexact(B, G, K):
+    g = _lib()
+    rng = np.random.default_rng(B * 100 + G * 10 + K)
+    r = (rng.normal(0, 1, size=(B, G, K)) * rng.choice([1e-3, 1.0, 1e4], size=(B, 1, 1)))
+    r = r.astype(np.float32)
+    A = g.grpo_advantages(torch.from_numpy(r).cuda(), 1e-4).cpu().numpy()
+    ref = oracle.group_advantages(r, 1e-4)
+    assert np.array_equal(A.view(np.uint32), ref.view(np.uint32))
+
+
+def test_advantages_order_sensitive_case():
+    g = _lib()
+    r = np.array([[[1e8], [1.0], [-1e8], [1.0]]], np.float32)
+    A = g.grpo_advantages(torch.from_numpy(r).cuda(), 1e-4).cpu().numpy()
+    assert np.array_equal(A.view(np.uint32), oracle.group_advantages(r, 1e-4).view(np.uint32))
+
+
+def test_no_loss_tokens_and_bad_target():
+    """N_tok = 0 gives loss 0 and zero gradients; a loss row whose target is out of range
+    raises the status bit (forced from the host by the input, no kernel misbehaves)."""
+    g = _lib()
+    wl = dataclasses.replace(workload_by_name("tiny-f32"))
+    inp = generate(wl)
+    inp.mask[:] = 0
+    out = run_gpu(wl, inp, need_dW=True)
+    assert out["loss"] == 0.0 and out["status"] == 0
+    assert np.all(out["dX"] == 0.0) and np.all(out["dW"] == 0.0)
+    inp = generate(wl)
+    t = int(np.nonzero(inp.mask.numpy())[0][3])
+    inp.targets[t] = wl.V + 5
+    out = run_gpu(wl, inp)
+    assert out["status"] & 2
+
+
+def test_nonfinite_flags():
+    """inf in a loss row of X_q sets the forward's non-finite bit and found_inf; NaN in a
+    masked-out row sets neither."""
+    wl = workload_by_name("tiny-f32")
+    inp = generate(wl)
+    mrow = int(np.nonzero(inp.mask.numpy() == 0)[0][0])
+    inp.xq[mrow, 3] = float("nan")
+    inp.xp[mrow, 5] = float("nan")
+    out = run_gpu(wl, inp)
+    assert out["status"] == 0 and out["found_inf"] == 0 and np.isfinite(out["loss"])
+    lrow = int(np.nonzero(inp.mask.numpy())[0][0])
+    inp.xq[lrow, 7] = float("inf")
+    out = run_gpu(wl, inp)
+    assert out["status"] & 1 and out["found_inf"] == 1
+
+
+def test_repeat_is_bit_identical():
+    """Two runs on the same inputs agree bit for bit (fixed-order reductions, no atomics
+    on values)."""
+    wl = dataclasses.replace(workload_by_name("qwen2.5-1.5b-bf16"), **SMALL["qwen2.5-1.5b-bf16"])
+    inp = generate(wl)
+    a = run_gpu(wl, inp)
+    b = run_gpu(wl, inp)
+    assert a["loss"] == b["loss"]
+    assert np.array_equal(a["dX"], b["dX"]) and np.array_equal(a["saved"], b["saved"])
+
+
+# ------------------------------------------------------------------ full sizes, sampled rows
+
+FULL = ["qwen2.5-1.5b-bf16", "llama3.1-8b-train-bf16", "llama3.1-8b-long-bf16", "phi4-f16"]
+
+
+def _sample_rows(mask, L, per_seq=6, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = []
+    S = len(mask) // L
+    for s in range(S):
+        nz = np.nonzero(mask[s * L:(s + 1) * L])[0] + s * L
+        if len(nz) == 0:
+            continue
+        pick = {nz[0], nz[-1]} | set(rng.choice(nz, size=min(per_seq, len(nz)), replace=False))
+        rows += sorted(int(x) for x in pick)
+    return np.array(rows, dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_parity_full_sampled(name):
+    wl = workload_by_name(name)
+    _say(f"[parity full] {name} S={wl.S} L={wl.L} H={wl.H} V={wl.V}")
+    inp = generate(wl)
+    gpu = run_gpu(wl, inp)
+    assert gpu["status"] == 0 and gpu["found_inf"] == 0
+    mask = inp.mask.numpy()
+    m = mask == 1
+    adv = oracle.group_advantages(inp.rewards.numpy(), wl.eps)
+    assert np.array_equal(gpu["adv"].view(np.uint32), adv.view(np.uint32))
+    # the loss is the mean of beta*KL - A over loss rows; recompute it from the GPU's
+    # per-row KL in fp64 (a property at any size) ...
+    a_tok = adv[np.arange(wl.N) // wl.L].astype(np.float64)
+    loss_from_rows = float(((wl.beta * gpu["kl"].astype(np.float64) - a_tok)[m]).sum() / m.sum())
+    assert abs(gpu["loss"] - loss_from_rows) <= 1e-5 * abs(loss_from_rows)
+    # ... and check sampled rows against the oracle one by one
+    rows = _sample_rows(mask, wl.L)
+    xq = hidden_rows(wl, "q", rows)
+    xp = hidden_rows(wl, "p", rows)
+    W = inp.W
+    f = oracle.forward(xq, xp, W, inp.targets.numpy(), mask, adv, wl.L, wl.beta, rows=rows)
+    b = oracle.backward(xq, W, inp.targets.numpy(), mask, f, grad_loss=wl.loss_scale,
+                        loss_scale=wl.loss_scale, rows=rows)
+    tol = TOL[wl.dtype]
+    for k in ("logp", "ref_logp"):
+        err = np.abs(gpu[k][rows] - f[k][rows]).max()
+        _say(f"  {k} max abs err {err:.2e} over {len(rows)} rows")
+        assert err <= tol["logp"]
+    ell_gpu = wl.beta * gpu["kl"][rows].astype(np.float64) - a_tok[rows]
+    e = np.abs(ell_gpu - f["ell"][rows]).max()
+    _say(f"  per-token loss max abs err {e:.2e}")
+    assert e <= tol["loss"] * max(1.0, np.abs(f["ell"][rows]).max())
+    e = rel_l2(gpu["dX"][rows], b["dX"])
+    _say(f"  dX rel-L2 (sampled rows) {e:.2e}")
+    assert e <= tol["dx"]
+    if wl.need_dW:
+        # every row of onehot - softmax sums to 0, so the columns of dW sum to ~0
+        colsum = np.abs(gpu["dW"].astype(np.float64).sum(0)).max()
+        assert colsum <= 1e-3 * np.abs(gpu["dW"]).max() * np.sqrt(wl.V)
