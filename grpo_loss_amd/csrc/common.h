@@ -65,6 +65,7 @@ struct Plan {
   int phases;       // forward: vocabulary phases per token block (partials per row)
   int64_t R;        // backward: rows per recompute chunk (multiple of 256)
   int ksplit;       // backward: split of the dX reduction over the vocabulary
+  int mfma;         // 1: 16-bit MFMA kernels, 0: fp32 FMA kernels
   // byte offsets into the workspace
   size_t off_ntok, off_idx, off_rank, off_part, off_lsum, off_T, off_WT, off_TT, off_XgT,
       off_dxp, total;

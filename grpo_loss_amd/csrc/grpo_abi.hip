@@ -13,6 +13,12 @@ hipError_t simple_backward(const Plan& p, void* ws, const void* Xq, const void* 
                            const int64_t* targets, const float* saved, const float* grad_loss,
                            float loss_scale, void* dX, float* dW, int accumulate_dW,
                            int32_t* found_inf, hipStream_t st);
+hipError_t mfma_fwd_partials(const Plan& p, void* ws, const void* Xq, const void* Xp,
+                             const void* W, const int64_t* targets, hipStream_t st);
+hipError_t mfma_backward(const Plan& p, void* ws, const void* Xq, const void* W,
+                         const int64_t* targets, const float* saved, const float* grad_loss,
+                         float loss_scale, void* dX, float* dW, int accumulate_dW,
+                         int32_t* found_inf, hipStream_t st);
 
 namespace {
 
@@ -60,9 +66,21 @@ bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_d
   p->esize = dtype == GRPO_F32 ? 4 : 2;
   p->need_dW = need_dW ? 1 : 0;
   p->phases = 8;
+  // 16-bit operands with H a multiple of 256 take the MFMA kernels (256-wide tiles over H;
+  // hidden-state rows addressed by 32-bit byte offsets, so S*L*H*2 must stay below 4 GiB);
+  // everything else takes the fp32-accumulating FMA kernels.
+  p->mfma = dtype != GRPO_F32 && H % 256 == 0 && (uint64_t)p->N * H * 2 < ((uint64_t)1 << 32);
   const int64_t Npad = (p->N + kTokTile - 1) / kTokTile * kTokTile;
   p->R = Npad < 4096 ? Npad : 4096;
   p->ksplit = 1;
+  if (p->mfma) {
+    // split the dX reduction over the vocabulary when one chunk has too few output tiles
+    const int64_t tiles = (H / 256) * (p->R / 256);
+    if (tiles < 192) {
+      int64_t ks = (256 + tiles - 1) / tiles;
+      p->ksplit = (int)(ks > 8 ? 8 : ks);
+    }
+  }
   size_t o = 0;
   p->off_ntok = o;
   o = align_up(o + 16);
@@ -76,7 +94,14 @@ bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_d
   o = align_up(o + (size_t)((p->N + kMergeBlock - 1) / kMergeBlock) * 8);
   p->off_T = o;
   o = align_up(o + (size_t)p->R * p->Vpad * p->esize);
-  p->off_WT = p->off_TT = p->off_XgT = p->off_dxp = o;
+  p->off_WT = o;
+  if (p->mfma) o = align_up(o + (size_t)H * p->Vpad * p->esize);
+  p->off_TT = o;
+  if (p->mfma && need_dW) o = align_up(o + (size_t)p->Vpad * p->R * p->esize);
+  p->off_XgT = o;
+  if (p->mfma && need_dW) o = align_up(o + (size_t)H * p->R * p->esize);
+  p->off_dxp = o;
+  if (p->mfma && p->ksplit > 1) o = align_up(o + (size_t)p->ksplit * p->R * H * 4);
   p->total = o;
   return true;
 }
@@ -143,7 +168,9 @@ int grpo_loss_fwd(const void* Xq, const void* Xp, const void* W, grpo_dtype dtyp
                             ws_ptr<int32_t>(ws, p.off_idx), ws_ptr<int32_t>(ws, p.off_rank),
                             status, st) != hipSuccess)
     return GRPO_ERR_HIP;
-  if (simple_fwd_partials(p, ws, Xq, Xp, W, targets, st) != hipSuccess) return GRPO_ERR_HIP;
+  const hipError_t fe = p.mfma ? mfma_fwd_partials(p, ws, Xq, Xp, W, targets, st)
+                               : simple_fwd_partials(p, ws, Xq, Xp, W, targets, st);
+  if (fe != hipSuccess) return GRPO_ERR_HIP;
   if (launch_merge(p, ws, targets, mask, adv, beta, saved, logp_out, ref_logp_out, kl_out,
                    status, loss, st) != hipSuccess)
     return GRPO_ERR_HIP;
@@ -173,9 +200,12 @@ int grpo_loss_bwd(const void* Xq, const void* W, grpo_dtype dtype, const int64_t
                      ws_ptr<int32_t>(ws, p.off_rank), st) != hipSuccess)
     return GRPO_ERR_HIP;
   if (launch_zero_masked_rows(p, mask, dXq, st) != hipSuccess) return GRPO_ERR_HIP;
-  if (simple_backward(p, ws, Xq, W, targets, saved, grad_loss, loss_scale, dXq, dW,
-                      accumulate_dW, found_inf, st) != hipSuccess)
-    return GRPO_ERR_HIP;
+  const hipError_t be =
+      p.mfma ? mfma_backward(p, ws, Xq, W, targets, saved, grad_loss, loss_scale, dXq, dW,
+                             accumulate_dW, found_inf, st)
+             : simple_backward(p, ws, Xq, W, targets, saved, grad_loss, loss_scale, dXq, dW,
+                               accumulate_dW, found_inf, st);
+  if (be != hipSuccess) return GRPO_ERR_HIP;
   return GRPO_OK;
 }
 

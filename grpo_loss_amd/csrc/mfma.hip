@@ -1,0 +1,708 @@
+// The 16-bit path: MFMA kernels for gfx950 (v_mfma_f32_16x16x32_{bf16,f16}).
+//
+// Every GEMM here is C[m][n] = sum_k A[m][k] * B[n][k] with both operands stored
+// row-major with k contiguous.  Block tile 256 (m) x 256 (n) x 64 (k), 512 threads =
+// 8 waves in a 2 (m) x 4 (n) grid, each wave owning a 128 x 64 sub-tile as 8 x 4 MFMA
+// blocks of 16 x 16 (128 fp32 accumulators per lane).  Two waves share each SIMD, so the
+// accumulators fit in the architectural VGPRs with room to spare (a 128 x 128 wave tile
+// needs all 256 AGPRs and the register allocator then shuffles accumulators between
+// MFMAs), and one wave's LDS and barrier latency is covered by its neighbour's MFMAs.
+// Operand tiles go straight from global memory
+// into a double-buffered LDS ring (2 x 64 KB) with global_load_lds_dwordx4, so no
+// registers are spent on staging; each 128-byte row's eight 16-byte chunks are
+// XOR-swizzled so fragment reads are free of bank conflicts.
+//
+// In the 16 x 16 accumulator layout, lane l holds C[4*(l/16) + j][l % 16], j = 0..3.
+// All kernels put the vocabulary (or the hidden dimension) on m and tokens on n, so a
+// lane owns whole token columns: the forward's online max / sum-exp runs per lane with
+// no cross-lane traffic until a token block is finished.
+#include "common.h"
+
+namespace grpo {
+
+hipError_t mfma_fwd_partials(const Plan& p, void* ws, const void* Xq, const void* Xp,
+                             const void* W, const int64_t* targets, hipStream_t st);
+hipError_t mfma_backward(const Plan& p, void* ws, const void* Xq, const void* W,
+                         const int64_t* targets, const float* saved, const float* grad_loss,
+                         float loss_scale, void* dX, float* dW, int accumulate_dW,
+                         int32_t* found_inf, hipStream_t st);
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <class E>
+struct Mma;
+template <>
+struct Mma<BF16T> {
+  __device__ static inline f32x4 op(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+template <>
+struct Mma<F16T> {
+  __device__ static inline f32x4 op(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+};
+
+constexpr int kThreads = 512;
+constexpr int kWN = 4;                        // waves along n
+constexpr int kMB = 8, kNB = 4;               // 16 x 16 blocks per wave along m, n
+constexpr int kWaveN = 16 * kNB;              // 64 columns per wave
+constexpr int kTileBytes = 256 * 64 * 2;      // one operand, one stage: 256 rows x 128 B
+constexpr int kNumWG = 256;                   // persistent grid: one workgroup per CU
+constexpr int kXcds = 8;
+constexpr int kPhases = 8;                    // forward vocabulary phases
+
+// LDS layout of one operand tile: 256 rows x 128 B; the 16-byte chunk c of row r sits at
+// position c ^ f(r) of its row, f(r) = (r & 7) ^ ((r >> 3) & 1).  A fragment read has 16
+// consecutive rows at one chunk: rows 0-7 and 8-15 each land on 8 distinct positions
+// (conflict free when the LDS serves 8 lanes x 16 B per pass over 32 banks), and the 16
+// (row parity, position) pairs are distinct (conflict free for 16 lanes over 64 banks).
+//
+// Tiles are filled with global_load_lds_dwordx4: one wave instruction writes 1 KB of LDS
+// (8 rows) with lane l landing at byte 16 l.  Wave w's instruction i covers rows
+// 32 w + 8 i .. + 7, so lane l lands in row r = 32 w + 8 i + l / 8 at position l % 8 and
+// therefore loads chunk (l % 8) ^ f(r) of that row: the swizzle is applied to the source
+// address.  Every thread stages the same 8 rows of each operand for every k, addressed as
+// a wave-uniform base plus a 32-bit per-row offset.
+//
+// The two ring stages are four distinct LDS arrays and the k loop is unrolled by two,
+// so every LDS read names the array it reads and the compiler can see that the loads in
+// flight target the other stage: it then waits for them only at the barrier that hands
+// the stage over, and the loads overlap the MFMAs of the current stage.
+__shared__ __attribute__((aligned(16))) char g_sA0[kTileBytes];
+__shared__ __attribute__((aligned(16))) char g_sB0[kTileBytes];
+__shared__ __attribute__((aligned(16))) char g_sA1[kTileBytes];
+__shared__ __attribute__((aligned(16))) char g_sB1[kTileBytes];
+
+__device__ inline int stage_row(int i) {
+  return 32 * (int)(threadIdx.x >> 6) + 8 * i + (int)((threadIdx.x & 63) >> 3);
+}
+__device__ inline int swz_f(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ inline uint32_t stage_chunk_bytes(int r) {
+  return (uint32_t)((((int)threadIdx.x & 7) ^ swz_f(r)) << 4);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+
+typedef f32x4 Acc[kMB][kNB];
+typedef uint32_t Offs[4];
+
+__device__ inline void zero_acc(Acc& acc) {
+#pragma unroll
+  for (int i = 0; i < kMB; ++i)
+#pragma unroll
+    for (int j = 0; j < kNB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Enqueue the direct-to-LDS loads of k-step kt (byte 128 kt of every row) into stage S.
+template <int S>
+__device__ inline void stage_tiles(const char* abase, const char* bbase, const Offs& ao,
+                                   const Offs& bo, int kt, int w) {
+  char* sa = (S ? g_sA1 : g_sA0) + w * 4 * 1024;
+  char* sb = (S ? g_sB1 : g_sB0) + w * 4 * 1024;
+  const char* ab = abase + (int64_t)kt * 128;
+  const char* bb = bbase + (int64_t)kt * 128;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(ab + ao[i]), (lds_void_t*)(sa + i * 1024), 16,
+                                     0, 0);
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(bb + bo[i]), (lds_void_t*)(sb + i * 1024), 16,
+                                     0, 0);
+  }
+}
+
+// acc += (64-wide k slab of stage S).  Fragment rows wm*128 + mb*16 + (lane & 15) of A and
+// wn*64 + nb*16 + (lane & 15) of B,
+// chunk ks*4 + (lane >> 4).  Both 32-wide halves' fragments are requested up front so the
+// second half's LDS reads are in flight while the first half's 64 MFMAs run.
+template <class E, int S>
+__device__ inline void mma_stage(Acc& acc, int fa, int fb, int fs, int lane) {
+  const char* As = S ? g_sA1 : g_sA0;
+  const char* Bs = S ? g_sB1 : g_sB0;
+  const int c0 = ((lane >> 4) ^ fs) << 4;
+  const int c1 = ((4 + (lane >> 4)) ^ fs) << 4;
+  uint4 a0[kMB], b0[kNB], a1[kMB], b1[kNB];
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb) a0[mb] = *reinterpret_cast<const uint4*>(As + fa + mb * 2048 + c0);
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) b0[nb] = *reinterpret_cast<const uint4*>(Bs + fb + nb * 2048 + c0);
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb) a1[mb] = *reinterpret_cast<const uint4*>(As + fa + mb * 2048 + c1);
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) b1[nb] = *reinterpret_cast<const uint4*>(Bs + fb + nb * 2048 + c1);
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = Mma<E>::op(a0[mb], b0[nb], acc[mb][nb]);
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = Mma<E>::op(a1[mb], b1[nb], acc[mb][nb]);
+}
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima)
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// acc += A . B^T over nk k-steps of 64 (nk even and > 0).  Row i of this thread's
+// staging set is at abase + ao[i] (A) and bbase + bo[i] (B) for k-step 0.
+template <class E>
+__device__ inline void gemm_core(const char* abase, const char* bbase, const Offs& ao,
+                                 const Offs& bo, int nk, Acc& acc) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int wm = w / kWN, wn = w % kWN;
+  const int fr = lane & 15;
+  const int fs = swz_f(fr);
+  const int fa = (wm * 128 + fr) * 128;
+  const int fb = (wn * kWaveN + fr) * 128;
+  stage_tiles<0>(abase, bbase, ao, bo, 0, w);
+  for (int kt = 0; kt < nk; kt += 2) {
+    wait_vmem();
+    __syncthreads();  // stage 0 holds k-step kt; every wave is done reading stage 1
+    stage_tiles<1>(abase, bbase, ao, bo, kt + 1, w);
+    mma_stage<E, 0>(acc, fa, fb, fs, lane);
+    wait_vmem();
+    __syncthreads();  // stage 1 holds k-step kt + 1; every wave is done reading stage 0
+    if (kt + 2 < nk) stage_tiles<0>(abase, bbase, ao, bo, kt + 2, w);
+    mma_stage<E, 1>(acc, fa, fb, fs, lane);
+  }
+  __syncthreads();  // the caller may refill stage 0 for its next tile
+}
+
+// ------------------------------------------------------------------------------ forward
+struct FwdArgs {
+  int64_t N, H, V;
+  const int32_t* ntok;
+  const int32_t* idx;
+  const char* Xq;
+  const char* Xp;
+  const char* W;
+  const int64_t* targets;
+  float* part;  // [3][2 sides][kPhases][N]: running max (log2 units), sum, target logit
+};
+
+// Persistent.  Workgroup w runs on XCD w % 8; its slot s = w / 8 picks a token block of
+// the current round and a vocabulary phase: the 32 workgroups of one XCD cover 4 token
+// blocks x 8 phases, so each W tile in flight on an XCD is shared by 4 workgroups and
+// each X block by 8, and all XCDs sweep the same W tiles together.  A workgroup keeps
+// its token block for a whole round and walks the vocabulary tiles of its phase
+// (vt = phase, phase + 8, ...), folding each 256 x 256 logit tile into per-lane running
+// (max, sum of exp2, target logit) without storing it.
+template <class E>
+__global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
+  __shared__ float mrg[2][3][256];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / kWN, wn = w % kWN;
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int slots = gridDim.x / kXcds;           // workgroups per XCD
+  const int tb_per_xcd = slots / kPhases;
+  const int phase = slot % kPhases;
+  const int tbg = kXcds * tb_per_xcd;            // token blocks per round
+  const int ntok = *a.ntok;
+  const int64_t ntb1 = (ntok + 255) / 256;
+  const int64_t TB = 2 * ntb1;
+  const int64_t nvt = (a.V + 255) / 256;
+  const int64_t rowb = a.H * 2;                  // bytes per row
+  const int nk = (int)(a.H / 64);
+
+  for (int64_t tb = xcd * tb_per_xcd + slot / kPhases; tb < TB; tb += tbg) {
+    const int side = tb >= ntb1 ? 1 : 0;
+    const int64_t tok0 = (tb - side * ntb1) * 256;
+    const char* X = side ? a.Xp : a.Xq;
+    Offs bo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sr = stage_row(i);
+      int64_t r = tok0 + sr;
+      if (r >= ntok) r = ntok - 1;
+      bo[i] = (uint32_t)(a.idx[r] * rowb) + stage_chunk_bytes(sr);
+    }
+    int y[kNB];
+    float rm[kNB], rs[kNB], rz[kNB];
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      const int64_t r = tok0 + wn * kWaveN + nb * 16 + (lane & 15);
+      int yy = -1;
+      if (r < ntok) {
+        const int64_t t = a.targets[a.idx[r]];
+        yy = (t >= 0 && t < a.V) ? (int)t : -1;
+      }
+      y[nb] = yy;
+      rm[nb] = -INFINITY;
+      rs[nb] = 0.f;
+      rz[nb] = 0.f;
+    }
+    for (int64_t vt = phase; vt < nvt; vt += kPhases) {
+      const int64_t v0 = vt * 256;
+      Offs ao;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int sr = stage_row(i);
+        int64_t v = v0 + sr;
+        if (v >= a.V) v = a.V - 1;
+        ao[i] = (uint32_t)((v - v0) * rowb) + stage_chunk_bytes(sr);
+      }
+      Acc acc;
+      zero_acc(acc);
+      gemm_core<E>(a.W + v0 * rowb, X, ao, bo, nk, acc);
+      const int vb = (int)(v0 + wm * 128 + 4 * (lane >> 4));  // vocab of acc[mb][.][j] = vb + 16 mb + j
+      const bool full = v0 + 256 <= a.V;
+      const int vlim = (int)(a.V - vb);                         // valid iff 16 mb + j < vlim
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) {
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (full || mb * 16 + j < vlim) tmax = fmaxf(tmax, acc[mb][nb][j]);
+        const float nm = fmaxf(rm[nb], tmax * kLog2e);
+        float s = rm[nb] == -INFINITY ? 0.f : rs[nb] * exp2f(rm[nb] - nm);
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (full || mb * 16 + j < vlim) s += exp2f(acc[mb][nb][j] * kLog2e - nm);
+        rm[nb] = nm;
+        rs[nb] = s;
+        const int loc = y[nb] - vb;
+        if ((unsigned)loc < 128u && (loc & 12) == 0) {
+          float z = 0.f;
+#pragma unroll
+          for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) z = (loc == mb * 16 + j) ? acc[mb][nb][j] : z;
+          rz[nb] += z;
+        }
+      }
+    }
+    // merge the four lane groups holding each token column, then the two m-waves
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      float m = rm[nb], s = rs[nb], z = rz[nb];
+#pragma unroll
+      for (int off = 16; off <= 32; off <<= 1) {
+        const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off), z2 = __shfl_xor(z, off);
+        const float M = fmaxf(m, m2);
+        s = M == -INFINITY ? 0.f
+                           : (m == -INFINITY ? 0.f : s * exp2f(m - M)) +
+                                 (m2 == -INFINITY ? 0.f : s2 * exp2f(m2 - M));
+        m = M;
+        z += z2;
+      }
+      if (lane < 16) {
+        const int n = wn * kWaveN + nb * 16 + lane;
+        mrg[wm][0][n] = m;
+        mrg[wm][1][n] = s;
+        mrg[wm][2][n] = z;
+      }
+    }
+    __syncthreads();
+    if (tid < 256) {  // one thread per token column of the block
+      const int n = tid;
+      const int64_t r = tok0 + n;
+      if (r < ntok) {
+        const float m0 = mrg[0][0][n], m1 = mrg[1][0][n];
+        const float M = fmaxf(m0, m1);
+        const float s = M == -INFINITY ? 0.f
+                                       : (m0 == -INFINITY ? 0.f : mrg[0][1][n] * exp2f(m0 - M)) +
+                                             (m1 == -INFINITY ? 0.f : mrg[1][1][n] * exp2f(m1 - M));
+        const int64_t PN = (int64_t)kPhases * a.N;
+        const int64_t o = (int64_t)(side * kPhases + phase) * a.N + r;
+        a.part[o] = M;
+        a.part[2 * PN + o] = s;
+        a.part[4 * PN + o] = mrg[0][2][n] + mrg[1][2][n];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------- recompute
+// T[r - c0][v] = onehot(y_r)[v] - exp(z_rv - lse_r) for one 256-token x 256-vocabulary
+// tile of the chunk; zero for v >= V and for rows past the last loss token.
+template <class E>
+__global__ void __launch_bounds__(kThreads, 1)
+recompute_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t c0, int ntt,
+                 const int32_t* __restrict__ ntok_p, const int32_t* __restrict__ idx,
+                 const char* __restrict__ Xq, const char* __restrict__ W,
+                 const int64_t* __restrict__ targets, const float* __restrict__ saved,
+                 typename E::T* __restrict__ T) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / kWN, wn = w % kWN;
+  // token tiles vary fastest so consecutive workgroups share a W tile
+  const int64_t tt = blockIdx.x % ntt, vt = blockIdx.x / ntt;
+  const int ntok = *ntok_p;
+  const int64_t tok0 = c0 + tt * 256;
+  if (tok0 >= ntok) return;
+  const int64_t v0 = vt * 256;
+  const int64_t rowb = H * 2;
+  Offs ao, bo;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int sr = stage_row(i);
+    const uint32_t cb = stage_chunk_bytes(sr);
+    int64_t v = v0 + sr;
+    if (v >= V) v = V - 1;
+    ao[i] = (uint32_t)((v - v0) * rowb) + cb;
+    int64_t r = tok0 + sr;
+    if (r >= ntok) r = ntok - 1;
+    bo[i] = (uint32_t)(idx[r] * rowb) + cb;
+  }
+  Acc acc;
+  zero_acc(acc);
+  gemm_core<E>(W + v0 * rowb, Xq, ao, bo, (int)(H / 64), acc);
+  const int64_t vb = v0 + wm * 128 + 4 * (lane >> 4);
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    const int64_t r = tok0 + wn * kWaveN + nb * 16 + (lane & 15);
+    const bool ok = r < ntok;
+    float lse2 = 0.f;
+    int64_t y = -1;
+    if (ok) {
+      const int64_t t = idx[r];
+      lse2 = saved[t * 4] * kLog2e;
+      y = targets[t];
+    }
+    typename E::T* trow = T + (r - c0) * Vpad;
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) {
+      const int64_t v = vb + mb * 16;
+      uint16_t o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float val = 0.f;
+        if (ok && v + j < V) val = (v + j == y ? 1.f : 0.f) - exp2f(acc[mb][nb][j] * kLog2e - lse2);
+        o[j] = E::from_f32(val);
+      }
+      uint2 pk;
+      pk.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+      pk.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+      *reinterpret_cast<uint2*>(trow + v) = pk;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------- dX
+// C[h][r] = sum_v W^T[h][v] T[r][v] over the padded vocabulary (or one split of it).
+// ksplit == 1: dX[idx[r]][h] = c * g_r * C, in the storage type.  ksplit > 1: fp32
+// partials to dxp[ks][r - c0][h], reduced by dx_reduce_kernel.
+template <class E>
+__global__ void __launch_bounds__(kThreads, 1)
+dx_kernel(int64_t H, int64_t Vpad, int64_t R, int64_t c0, int nht, int ntt, int ksplit,
+          const int32_t* __restrict__ ntok_p, const int32_t* __restrict__ idx,
+          const char* __restrict__ WT, const char* __restrict__ T,
+          const float* __restrict__ saved, const float* __restrict__ grad_loss, float loss_scale,
+          typename E::T* __restrict__ dX, float* __restrict__ dxp,
+          int32_t* __restrict__ found_inf) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / kWN, wn = w % kWN;
+  const int tiles = nht * ntt;
+  const int ks = blockIdx.x / tiles;
+  const int rem = blockIdx.x % tiles;
+  const int64_t ht = rem % nht, tt = rem / nht;
+  const int ntok = *ntok_p;
+  const int64_t tok0 = c0 + tt * 256;
+  if (tok0 >= ntok) return;
+  const int64_t h0 = ht * 256;
+  // k-steps of 64 split into ksplit ranges with even boundaries (Vpad / 64 is a multiple of 4)
+  const int64_t npair = Vpad / 128;
+  const int64_t kbeg = 2 * (npair * ks / ksplit), kend = 2 * (npair * (ks + 1) / ksplit);
+  const int64_t rowb = Vpad * 2;
+  Offs ao, bo;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int sr = stage_row(i);
+    ao[i] = (uint32_t)(sr * rowb) + stage_chunk_bytes(sr);
+    bo[i] = ao[i];
+  }
+  Acc acc;
+  zero_acc(acc);
+  if (kend > kbeg)
+    gemm_core<E>(WT + h0 * rowb + kbeg * 128, T + tt * 256 * rowb + kbeg * 128, ao, bo,
+                 (int)(kend - kbeg), acc);
+  const int64_t hb = h0 + wm * 128 + 4 * (lane >> 4);
+  if (ksplit == 1) {
+    const float c = (grad_loss ? *grad_loss : 1.f) / loss_scale;
+    bool bad = false;
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      const int64_t r = tok0 + wn * kWaveN + nb * 16 + (lane & 15);
+      if (r >= ntok) continue;
+      const int64_t t = idx[r];
+      const float gs = saved[t * 4 + 3] * c;
+      typename E::T* drow = dX + t * H;
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) {
+        uint16_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          o[j] = E::from_f32(acc[mb][nb][j] * gs);
+          bad |= !isfinite(E::to_f32(o[j]));
+        }
+        uint2 pk;
+        pk.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+        pk.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+        *reinterpret_cast<uint2*>(drow + hb + mb * 16) = pk;
+      }
+    }
+    if (bad) atomicOr(found_inf, 1);
+  } else {
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      const int64_t rl = tt * 256 + wn * kWaveN + nb * 16 + (lane & 15);
+      float* prow = dxp + ((int64_t)ks * R + rl) * H;
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb)
+        *reinterpret_cast<f32x4*>(prow + hb + mb * 16) = acc[mb][nb];
+    }
+  }
+}
+
+// dX[idx[r]][h] = c * g_r * sum_ks dxp[ks][r - c0][h], ks ascending.
+template <class E>
+__global__ void __launch_bounds__(256)
+dx_reduce_kernel(int64_t H, int64_t R, int64_t c0, int ksplit, const int32_t* __restrict__ ntok_p,
+                 const int32_t* __restrict__ idx, const float* __restrict__ dxp,
+                 const float* __restrict__ saved, const float* __restrict__ grad_loss,
+                 float loss_scale, typename E::T* __restrict__ dX,
+                 int32_t* __restrict__ found_inf) {
+  const int64_t rl = blockIdx.x;
+  const int ntok = *ntok_p;
+  const int64_t r = c0 + rl;
+  if (r >= ntok) return;
+  const int64_t t = idx[r];
+  const float gs = saved[t * 4 + 3] * ((grad_loss ? *grad_loss : 1.f) / loss_scale);
+  bool bad = false;
+  for (int64_t h = threadIdx.x * 4; h < H; h += 256 * 4) {
+    f32x4 s = *reinterpret_cast<const f32x4*>(dxp + rl * H + h);
+    for (int k = 1; k < ksplit; ++k) s += *reinterpret_cast<const f32x4*>(dxp + (k * R + rl) * H + h);
+    uint16_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o[j] = E::from_f32(s[j] * gs);
+      bad |= !isfinite(E::to_f32(o[j]));
+    }
+    uint2 pk;
+    pk.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+    pk.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+    *reinterpret_cast<uint2*>(dX + t * H + h) = pk;
+  }
+  if (bad) atomicOr(found_inf, 1);
+}
+
+// ------------------------------------------------------------------------------- dW
+// C[h][v] = sum_r XgT[h][r] TT[v][r] over the chunk's rows; dW[v][h] (+)= C.
+template <class E>
+__global__ void __launch_bounds__(kThreads, 1)
+dw_kernel(int64_t H, int64_t V, int64_t R, int64_t c0, int nht, int accumulate,
+          const int32_t* __restrict__ ntok_p, const char* __restrict__ XgT,
+          const char* __restrict__ TT, float* __restrict__ dW, int32_t* __restrict__ found_inf) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / kWN, wn = w % kWN;
+  const int64_t ht = blockIdx.x % nht, vt = blockIdx.x / nht;
+  const int ntok = *ntok_p;
+  int64_t nrows = (int64_t)ntok - c0;
+  if (nrows > R) nrows = R;
+  if (nrows <= 0 && accumulate) return;
+  if (nrows < 0) nrows = 0;
+  // rows padded to a multiple of 128 (an even number of k-steps); the padding rows of
+  // T^T and (g X)^T are zero
+  const int64_t nk = 2 * ((nrows + 127) / 128);
+  const int64_t h0 = ht * 256, v0 = vt * 256;
+  const int64_t rowb = R * 2;
+  Offs ao, bo;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int sr = stage_row(i);
+    ao[i] = (uint32_t)(sr * rowb) + stage_chunk_bytes(sr);
+    bo[i] = ao[i];
+  }
+  Acc acc;
+  zero_acc(acc);
+  if (nk > 0) gemm_core<E>(XgT + h0 * rowb, TT + v0 * rowb, ao, bo, (int)nk, acc);
+  const int64_t hb = h0 + wm * 128 + 4 * (lane >> 4);
+  bool bad = false;
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    const int64_t v = v0 + wn * kWaveN + nb * 16 + (lane & 15);
+    if (v >= V) continue;
+    float* drow = dW + v * H;
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) {
+      f32x4* p = reinterpret_cast<f32x4*>(drow + hb + mb * 16);
+      f32x4 val = acc[mb][nb];
+      if (accumulate) val += *p;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bad |= !isfinite(val[j]);
+      *p = val;
+    }
+  }
+  if (bad) atomicOr(found_inf, 1);
+}
+
+// --------------------------------------------------------------------------- transposes
+// out[j][i] = scale_i * in[row(i)][j] for 16-bit data, through a 64 x 64 LDS tile.
+//   mode 0: row(i) = i, scale 1, rows i >= nvalid_i are written as 0 (W -> W^T padded, T -> T^T)
+//   mode 1: row(i) = idx[c0 + i], scale = c * g, rows past the last loss token are 0
+//           (X_q chunk -> (g X_q)^T)
+template <class E, int kMode>
+__global__ void __launch_bounds__(256)
+transpose_kernel(const typename E::T* __restrict__ in, int64_t ld_in, int64_t nvalid_i,
+                 int64_t ncols_j, typename E::T* __restrict__ out, int64_t ld_out, int64_t c0,
+                 const int32_t* __restrict__ ntok_p, const int32_t* __restrict__ idx,
+                 const float* __restrict__ saved, const float* __restrict__ grad_loss,
+                 float loss_scale) {
+  __shared__ uint16_t tile[64][66];
+  const int64_t i0 = (int64_t)blockIdx.x * 64, j0 = (int64_t)blockIdx.y * 64;
+  const int tid = threadIdx.x;
+  int64_t ni = nvalid_i;
+  if (kMode == 1) {
+    int64_t nr = (int64_t)(*ntok_p) - c0;
+    if (nr < ni) ni = nr;
+  }
+  // load: thread -> row i0 + tid / 4, 16 consecutive j
+  {
+    const int li = tid >> 2, lj = (tid & 3) * 16;
+    const int64_t i = i0 + li;
+    uint16_t v[16];
+    if (i < ni && j0 + lj < ncols_j) {
+      int64_t row = i;
+      float sc = 1.f;
+      if (kMode == 1) {
+        row = idx[c0 + i];
+        sc = saved[row * 4 + 3] * ((grad_loss ? *grad_loss : 1.f) / loss_scale);
+      }
+      const uint4* src = reinterpret_cast<const uint4*>(in + row * ld_in + j0 + lj);
+      uint4 q0 = src[0], q1 = src[1];
+      const uint16_t* h0 = reinterpret_cast<const uint16_t*>(&q0);
+      const uint16_t* h1 = reinterpret_cast<const uint16_t*>(&q1);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        v[k] = h0[k];
+        v[8 + k] = h1[k];
+      }
+      if (kMode == 1) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = E::from_f32(sc * E::to_f32(v[k]));
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[k] = 0;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) tile[li][lj + k] = v[k];
+  }
+  __syncthreads();
+  {
+    const int lj = tid >> 2, li = (tid & 3) * 16;
+    const int64_t j = j0 + lj;
+    if (j < ncols_j) {
+      uint16_t v[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[k] = tile[li + k][lj];
+      uint4 q0, q1;
+      __builtin_memcpy(&q0, v, 16);
+      __builtin_memcpy(&q1, v + 8, 16);
+      uint4* dst = reinterpret_cast<uint4*>(out + j * ld_out + i0 + li);
+      dst[0] = q0;
+      dst[1] = q1;
+    }
+  }
+}
+
+template <class E>
+hipError_t fwd_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, const void* W,
+                    const int64_t* targets, hipStream_t st) {
+  FwdArgs a;
+  a.N = p.N;
+  a.H = p.H;
+  a.V = p.V;
+  a.ntok = ws_ptr<int32_t>(ws, p.off_ntok);
+  a.idx = ws_ptr<int32_t>(ws, p.off_idx);
+  a.Xq = (const char*)Xq;
+  a.Xp = (const char*)Xp;
+  a.W = (const char*)W;
+  a.targets = targets;
+  a.part = ws_ptr<float>(ws, p.off_part);
+  hipLaunchKernelGGL(fwd_kernel<E>, dim3(kNumWG), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+template <class E>
+hipError_t bwd_impl(const Plan& p, void* ws, const void* Xq, const void* W,
+                    const int64_t* targets, const float* saved, const float* grad_loss,
+                    float loss_scale, void* dX, float* dW, int accumulate_dW, int32_t* found_inf,
+                    hipStream_t st) {
+  typedef typename E::T T;
+  const int32_t* ntok = ws_ptr<int32_t>(ws, p.off_ntok);
+  const int32_t* idx = ws_ptr<int32_t>(ws, p.off_idx);
+  T* Tb = ws_ptr<T>(ws, p.off_T);
+  T* WT = ws_ptr<T>(ws, p.off_WT);
+  // W^T [H][Vpad], zero-padded past V
+  hipLaunchKernelGGL((transpose_kernel<E, 0>), dim3((unsigned)(p.Vpad / 64), (unsigned)(p.H / 64)),
+                     dim3(256), 0, st, (const T*)W, p.H, p.V, p.H, WT, p.Vpad, (int64_t)0, ntok,
+                     idx, saved, grad_loss, loss_scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int ntt = (int)(p.R / 256), nvt = (int)(p.Vpad / 256), nht = (int)(p.H / 256);
+  for (int64_t c0 = 0; c0 < p.N; c0 += p.R) {
+    hipLaunchKernelGGL(recompute_kernel<E>, dim3((unsigned)(ntt * nvt)), dim3(kThreads), 0, st,
+                       p.H, p.V, p.Vpad, c0, ntt, ntok, idx, (const char*)Xq, (const char*)W,
+                       targets, saved, Tb);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(dx_kernel<E>, dim3((unsigned)(nht * ntt * p.ksplit)), dim3(kThreads), 0, st,
+                       p.H, p.Vpad, p.R, c0, nht, ntt, p.ksplit, ntok, idx, (const char*)WT,
+                       (const char*)Tb, saved, grad_loss, loss_scale, (T*)dX,
+                       ws_ptr<float>(ws, p.off_dxp), found_inf);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (p.ksplit > 1) {
+      hipLaunchKernelGGL(dx_reduce_kernel<E>, dim3((unsigned)p.R), dim3(256), 0, st, p.H, p.R, c0,
+                         p.ksplit, ntok, idx, (const float*)ws_ptr<float>(ws, p.off_dxp), saved,
+                         grad_loss, loss_scale, (T*)dX, found_inf);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (dW) {
+      T* TT = ws_ptr<T>(ws, p.off_TT);
+      T* XgT = ws_ptr<T>(ws, p.off_XgT);
+      hipLaunchKernelGGL((transpose_kernel<E, 0>), dim3((unsigned)(p.R / 64), (unsigned)(p.Vpad / 64)),
+                         dim3(256), 0, st, (const T*)Tb, p.Vpad, p.R, p.Vpad, TT, p.R, c0, ntok,
+                         idx, saved, grad_loss, loss_scale);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      hipLaunchKernelGGL((transpose_kernel<E, 1>), dim3((unsigned)(p.R / 64), (unsigned)(p.H / 64)),
+                         dim3(256), 0, st, (const T*)Xq, p.H, p.R, p.H, XgT, p.R, c0, ntok, idx,
+                         saved, grad_loss, loss_scale);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      hipLaunchKernelGGL(dw_kernel<E>, dim3((unsigned)(nht * nvt)), dim3(kThreads), 0, st, p.H,
+                         p.V, p.R, c0, nht, c0 == 0 ? accumulate_dW : 1, ntok, (const char*)XgT,
+                         (const char*)TT, dW, found_inf);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t mfma_fwd_partials(const Plan& p, void* ws, const void* Xq, const void* Xp,
+                             const void* W, const int64_t* targets, hipStream_t st) {
+  if (p.dtype == GRPO_BF16) return fwd_impl<BF16T>(p, ws, Xq, Xp, W, targets, st);
+  return fwd_impl<F16T>(p, ws, Xq, Xp, W, targets, st);
+}
+
+hipError_t mfma_backward(const Plan& p, void* ws, const void* Xq, const void* W,
+                         const int64_t* targets, const float* saved, const float* grad_loss,
+                         float loss_scale, void* dX, float* dW, int accumulate_dW,
+                         int32_t* found_inf, hipStream_t st) {
+  if (p.dtype == GRPO_BF16)
+    return bwd_impl<BF16T>(p, ws, Xq, W, targets, saved, grad_loss, loss_scale, dX, dW,
+                           accumulate_dW, found_inf, st);
+  return bwd_impl<F16T>(p, ws, Xq, W, targets, saved, grad_loss, loss_scale, dX, dW,
+                        accumulate_dW, found_inf, st);
+}
+
+}  // namespace grpo
