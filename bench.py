@@ -9,7 +9,7 @@ Prints ONE JSON line.  Default workload: the long-context Llama-3.1-8B shape
 (G = 8, L = 20480, H = 4096, V = 128256, bf16, frozen head).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--no-cpu-baseline] [--cpu-rows R]
+                  [--no-cpu-baseline] [--cpu-rows R] [--calibrate-copy-gib X]
 """
 
 import argparse
@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--workload", default="llama3.1-8b-long-bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=256, help="oracle rows per sequence")
+    ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
+                    help="run one device-to-device copy of this many GiB first, so a "
+                         "counter run can scale FETCH_SIZE / WRITE_SIZE by a known size")
     return ap.parse_args()
 
 
@@ -100,6 +103,14 @@ def main():
     torch.cuda.reset_peak_memory_stats()
     ws_bytes = g.grpo_workspace_bytes(wl.S, wl.L, wl.H, wl.V, dt, need_dW)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+
+    if args.calibrate_copy_gib > 0:
+        nb = int(args.calibrate_copy_gib * 2 ** 30)
+        src = torch.ones(nb, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     ev = []
 

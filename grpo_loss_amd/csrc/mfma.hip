@@ -202,7 +202,10 @@ struct FwdArgs {
 // (max, sum of exp2, target logit) without storing it.
 template <class E>
 __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
-  __shared__ float mrg[2][3][256];
+  __shared__ float mrg[2][2][256];
+  __shared__ float s_run[2][kNB][kThreads];
+  __shared__ int s_y[256];
+  __shared__ float s_zt[256];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / kWN, wn = w % kWN;
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
   const int slots = gridDim.x / kXcds;           // workgroups per XCD
@@ -220,38 +223,36 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
     const int side = tb >= ntb1 ? 1 : 0;
     const int64_t tok0 = (tb - side * ntb1) * 256;
     const char* X = side ? a.Xp : a.Xq;
-    Offs bo;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int sr = stage_row(i);
-      int64_t r = tok0 + sr;
-      if (r >= ntok) r = ntok - 1;
-      bo[i] = (uint32_t)(a.idx[r] * rowb) + stage_chunk_bytes(sr);
-    }
-    int y[kNB];
-    float rm[kNB], rs[kNB], rz[kNB];
-#pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-      const int64_t r = tok0 + wn * kWaveN + nb * 16 + (lane & 15);
+    // per-block state lives in LDS so the GEMM loop keeps its registers: target id and
+    // target logit per token column, running (max, sum) per lane and column block
+    if (tid < 256) {
+      const int64_t r = tok0 + tid;
       int yy = -1;
       if (r < ntok) {
         const int64_t t = a.targets[a.idx[r]];
         yy = (t >= 0 && t < a.V) ? (int)t : -1;
       }
-      y[nb] = yy;
-      rm[nb] = -INFINITY;
-      rs[nb] = 0.f;
-      rz[nb] = 0.f;
+      s_y[tid] = yy;
+      s_zt[tid] = 0.f;
+    }
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      s_run[0][nb][tid] = -INFINITY;
+      s_run[1][nb][tid] = 0.f;
     }
     for (int64_t vt = phase; vt < nvt; vt += kPhases) {
       const int64_t v0 = vt * 256;
-      Offs ao;
+      Offs ao, bo;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int sr = stage_row(i);
+        const uint32_t cb = stage_chunk_bytes(sr);
         int64_t v = v0 + sr;
         if (v >= a.V) v = a.V - 1;
-        ao[i] = (uint32_t)((v - v0) * rowb) + stage_chunk_bytes(sr);
+        ao[i] = (uint32_t)((v - v0) * rowb) + cb;
+        int64_t r = tok0 + sr;
+        if (r >= ntok) r = ntok - 1;
+        bo[i] = (uint32_t)(a.idx[r] * rowb) + cb;
       }
       Acc acc;
       zero_acc(acc);
@@ -261,51 +262,51 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
       const int vlim = (int)(a.V - vb);                         // valid iff 16 mb + j < vlim
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) {
+        const int n = wn * kWaveN + nb * 16 + (lane & 15);
         float tmax = -INFINITY;
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             if (full || mb * 16 + j < vlim) tmax = fmaxf(tmax, acc[mb][nb][j]);
-        const float nm = fmaxf(rm[nb], tmax * kLog2e);
-        float s = rm[nb] == -INFINITY ? 0.f : rs[nb] * exp2f(rm[nb] - nm);
+        const float rm = s_run[0][nb][tid];
+        const float nm = fmaxf(rm, tmax * kLog2e);
+        float sum = rm == -INFINITY ? 0.f : s_run[1][nb][tid] * exp2f(rm - nm);
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            if (full || mb * 16 + j < vlim) s += exp2f(acc[mb][nb][j] * kLog2e - nm);
-        rm[nb] = nm;
-        rs[nb] = s;
-        const int loc = y[nb] - vb;
-        if ((unsigned)loc < 128u && (loc & 12) == 0) {
+            if (full || mb * 16 + j < vlim) sum += exp2f(acc[mb][nb][j] * kLog2e - nm);
+        s_run[0][nb][tid] = nm;
+        s_run[1][nb][tid] = sum;
+        const int loc = s_y[n] - vb;
+        if ((unsigned)loc < 128u && (loc & 12) == 0) {  // this lane holds the target logit
           float z = 0.f;
 #pragma unroll
           for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
             for (int j = 0; j < 4; ++j) z = (loc == mb * 16 + j) ? acc[mb][nb][j] : z;
-          rz[nb] += z;
+          s_zt[n] = z;
         }
       }
     }
     // merge the four lane groups holding each token column, then the two m-waves
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
-      float m = rm[nb], s = rs[nb], z = rz[nb];
+      float m = s_run[0][nb][tid], sum = s_run[1][nb][tid];
 #pragma unroll
       for (int off = 16; off <= 32; off <<= 1) {
-        const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off), z2 = __shfl_xor(z, off);
+        const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(sum, off);
         const float M = fmaxf(m, m2);
-        s = M == -INFINITY ? 0.f
-                           : (m == -INFINITY ? 0.f : s * exp2f(m - M)) +
-                                 (m2 == -INFINITY ? 0.f : s2 * exp2f(m2 - M));
+        sum = M == -INFINITY ? 0.f
+                             : (m == -INFINITY ? 0.f : sum * exp2f(m - M)) +
+                                   (m2 == -INFINITY ? 0.f : s2 * exp2f(m2 - M));
         m = M;
-        z += z2;
       }
       if (lane < 16) {
         const int n = wn * kWaveN + nb * 16 + lane;
         mrg[wm][0][n] = m;
-        mrg[wm][1][n] = s;
-        mrg[wm][2][n] = z;
+        mrg[wm][1][n] = sum;
       }
     }
     __syncthreads();
@@ -315,14 +316,15 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
       if (r < ntok) {
         const float m0 = mrg[0][0][n], m1 = mrg[1][0][n];
         const float M = fmaxf(m0, m1);
-        const float s = M == -INFINITY ? 0.f
-                                       : (m0 == -INFINITY ? 0.f : mrg[0][1][n] * exp2f(m0 - M)) +
-                                             (m1 == -INFINITY ? 0.f : mrg[1][1][n] * exp2f(m1 - M));
+        const float sum = M == -INFINITY
+                              ? 0.f
+                              : (m0 == -INFINITY ? 0.f : mrg[0][1][n] * exp2f(m0 - M)) +
+                                    (m1 == -INFINITY ? 0.f : mrg[1][1][n] * exp2f(m1 - M));
         const int64_t PN = (int64_t)kPhases * a.N;
         const int64_t o = (int64_t)(side * kPhases + phase) * a.N + r;
         a.part[o] = M;
-        a.part[2 * PN + o] = s;
-        a.part[4 * PN + o] = mrg[0][2][n] + mrg[1][2][n];
+        a.part[2 * PN + o] = sum;
+        a.part[4 * PN + o] = s_zt[n];
       }
     }
     __syncthreads();

@@ -227,3 +227,76 @@ def test_parity_full_sampled(name):
         # every row of onehot - softmax sums to 0, so the columns of dW sum to ~0
         colsum = np.abs(gpu["dW"].astype(np.float64).sum(0)).max()
         assert colsum <= 1e-3 * np.abs(gpu["dW"]).max() * np.sqrt(wl.V)
+
+
+# ------------------------------------------------------------------ degenerate and API cases
+
+def test_policy_equals_reference_gpu():
+    """X_p = X_q: both sides run the same arithmetic, so KL is exactly 0 and the loss is
+    -sum(m A) / N_tok (to fp32 rounding of A)."""
+    g = _lib()
+    wl = dataclasses.replace(workload_by_name("llama3.1-8b-long-bf16"), **SMALL["llama3.1-8b-long-bf16"])
+    inp = generate(wl)
+    inp.xp = inp.xq.clone()
+    out = run_gpu(wl, inp)
+    m = inp.mask.numpy() == 1
+    assert np.all(out["kl"][m] == 0.0)
+    adv = oracle.group_advantages(inp.rewards.numpy(), wl.eps).astype(np.float64)
+    expect = -(adv[np.arange(wl.N) // wl.L][m]).sum() / m.sum()
+    assert abs(out["loss"] - expect) <= 1e-6 * max(1.0, abs(expect))
+
+
+def test_vocab_boundary_targets():
+    """Targets 0 and V - 1 (the ragged last vocabulary tile) on every loss row."""
+    wl = dataclasses.replace(workload_by_name("qwen2.5-1.5b-bf16"), **SMALL["qwen2.5-1.5b-bf16"])
+    inp = generate(wl)
+    t = inp.targets.numpy().copy()
+    t[::2] = 0
+    t[1::2] = wl.V - 1
+    inp.targets[:] = torch.from_numpy(t)
+    gpu = run_gpu(wl, inp)
+    adv = oracle.group_advantages(inp.rewards.numpy(), wl.eps)
+    f = oracle.forward(inp.xq, inp.xp, inp.W, t, inp.mask.numpy(), adv, wl.L, wl.beta)
+    m = inp.mask.numpy() == 1
+    assert np.abs(gpu["logp"][m] - f["logp"][m]).max() <= 2e-2
+    assert abs(gpu["loss"] - f["loss"]) <= 1e-3 * abs(f["loss"])
+
+
+def test_dw_accumulates():
+    """accumulate_dW = 1 adds into dW: two backward calls give twice one call."""
+    g = _lib()
+    wl = dataclasses.replace(workload_by_name("llama3.1-8b-train-bf16"), **SMALL["llama3.1-8b-train-bf16"])
+    inp = generate(wl)
+    d = to_device(inp)
+    adv = g.grpo_advantages(d["rewards"], wl.eps)
+    f = g.grpo_loss_fwd(d["xq"], d["xp"], d["W"], d["targets"], d["mask"], adv, wl.beta, wl.L)
+    b1 = g.grpo_loss_bwd(d["xq"], d["W"], d["targets"], d["mask"], f["saved"], wl.L, need_dW=True)
+    dW = b1["dW"].clone()
+    g.grpo_loss_bwd(d["xq"], d["W"], d["targets"], d["mask"], f["saved"], wl.L, dW=dW,
+                    accumulate_dW=True)
+    torch.cuda.synchronize()
+    assert torch.allclose(dW, 2 * b1["dW"], rtol=1e-6, atol=0)
+
+
+def test_autograd_wrapper():
+    """grpo_loss as an autograd function: loss value and X_q gradient match the oracle,
+    X_p gets no gradient."""
+    g = _lib()
+    wl = dataclasses.replace(workload_by_name("phi4-f16"), **SMALL["phi4-f16"])
+    inp = generate(wl)
+    d = to_device(inp)
+    xq = d["xq"].view(wl.S, wl.L, wl.H).clone().requires_grad_(True)
+    xp = d["xp"].view(wl.S, wl.L, wl.H)
+    loss, status = g.grpo_loss(xq, xp, d["W"], d["targets"], d["mask"], d["rewards"],
+                               beta=wl.beta, eps=wl.eps)
+    loss.backward()
+    torch.cuda.synchronize()
+    adv = oracle.group_advantages(inp.rewards.numpy(), wl.eps)
+    f = oracle.forward(inp.xq, inp.xp, inp.W, inp.targets.numpy(), inp.mask.numpy(), adv,
+                       wl.L, wl.beta)
+    b = oracle.backward(inp.xq, inp.W, inp.targets.numpy(), inp.mask.numpy(), f)
+    assert int(status.item()) == 0
+    assert abs(float(loss.item()) - f["loss"]) <= 1e-3 * abs(f["loss"])
+    dX = np.zeros((wl.N, wl.H))
+    dX[b["rows"]] = b["dX"]
+    assert rel_l2(xq.grad.float().reshape(wl.N, wl.H).cpu().numpy(), dX) <= 1e-2
