@@ -105,12 +105,16 @@ def main():
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
 
     if args.calibrate_copy_gib > 0:
+        # a known-size copy whose source is not cache resident: fill it, stream an
+        # unrelated 2 GiB buffer through the caches, then copy
         nb = int(args.calibrate_copy_gib * 2 ** 30)
         src = torch.ones(nb, dtype=torch.uint8, device="cuda")
+        flush = torch.zeros(2 * 2 ** 30, dtype=torch.uint8, device="cuda")
+        flush.add_(1)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
-        del src, dst
+        del src, dst, flush
 
     ev = []
 

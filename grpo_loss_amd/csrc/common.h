@@ -62,7 +62,7 @@ struct Plan {
   int dtype;        // grpo_dtype
   int esize;        // bytes per element of X / W / T
   int need_dW;
-  int phases;       // forward: vocabulary phases per token block (partials per row)
+  int phases;       // forward partial slots per row and side (phases actually used may be fewer)
   int64_t R;        // backward: rows per recompute chunk (multiple of 256)
   int ksplit;       // backward: split of the dX reduction over the vocabulary
   int mfma;         // 1: 16-bit MFMA kernels, 0: fp32 FMA kernels
@@ -74,6 +74,25 @@ struct Plan {
 constexpr int kTokTile = 256;    // rows per token tile of the MFMA kernels
 constexpr int kVocTile = 256;    // vocabulary entries per tile
 constexpr int kMergeBlock = 256; // rows per block of the merge kernel
+constexpr int kMaxPhases = 32;   // forward partials per row and side (layout stride)
+
+// Vocabulary phases of the MFMA forward.  Its persistent grid (8 XCDs x 32 workgroups)
+// covers 32 / P token blocks per XCD x P phases per round; pick P in {8, 16, 32} that
+// minimises the tiles per workgroup, ceil(blocks / (8 * 32 / P)) * ceil(tiles / P),
+// preferring fewer phases (each W tile then feeds more workgroups of an XCD).
+__host__ __device__ inline int fwd_phases(int64_t token_blocks, int64_t vocab_tiles) {
+  int best = 8;
+  int64_t best_cost = -1;
+  for (int P = 8; P <= kMaxPhases; P *= 2) {
+    const int64_t per_round = 8 * (32 / P);
+    const int64_t cost = ((token_blocks + per_round - 1) / per_round) * ((vocab_tiles + P - 1) / P);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = P;
+    }
+  }
+  return best;
+}
 
 bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_dW, Plan* p);
 

@@ -51,12 +51,12 @@ compact_kernel(const uint8_t* __restrict__ mask, int64_t N, int32_t* __restrict_
 // log-sum-exp in natural units and the target logit.  Partial maxima are kept in log2
 // units (logit * log2 e); sums are of exp2(logit*log2e - max).
 __device__ inline void merge_side(const float* __restrict__ pm, const float* __restrict__ ps,
-                                  const float* __restrict__ pz, int phases, int64_t N,
+                                  const float* __restrict__ pz, int used, int64_t N,
                                   int64_t r, float* lse, float* zt) {
   float M = -INFINITY;
-  for (int p = 0; p < phases; ++p) M = fmaxf(M, pm[p * N + r]);
+  for (int p = 0; p < used; ++p) M = fmaxf(M, pm[p * N + r]);
   float s = 0.0f, z = 0.0f;
-  for (int p = 0; p < phases; ++p) {
+  for (int p = 0; p < used; ++p) {
     const float sp = ps[p * N + r];
     if (sp != 0.0f) s += sp * exp2f(pm[p * N + r] - M);
     z += pz[p * N + r];
@@ -73,7 +73,8 @@ __device__ inline void merge_side(const float* __restrict__ pm, const float* __r
 // [Long-context GRPO, §4].  Each block reduces m_t * l_t in fp64 by a fixed tree into
 // lsum[block]; the final kernel adds the block sums in index order.
 __global__ void __launch_bounds__(kMergeBlock)
-merge_kernel(int64_t N, int64_t L, int64_t V, int phases, const int32_t* __restrict__ ntok_p,
+merge_kernel(int64_t N, int64_t L, int64_t V, int phases, int adaptive,
+             const int32_t* __restrict__ ntok_p,
              const int32_t* __restrict__ rank, const float* __restrict__ part,
              const int64_t* __restrict__ targets, const uint8_t* __restrict__ mask,
              const float* __restrict__ adv, float beta, float* __restrict__ saved,
@@ -83,6 +84,9 @@ merge_kernel(int64_t N, int64_t L, int64_t V, int phases, const int32_t* __restr
   const int64_t t = (int64_t)blockIdx.x * kMergeBlock + threadIdx.x;
   const int32_t ntok = *ntok_p;
   const float denom = (float)(ntok > 1 ? ntok : 1);
+  // partial slots written by the forward: all of them, or the adaptive phase count
+  const int used = adaptive ? fwd_phases(2 * (((int64_t)ntok + 255) / 256), (V + 255) / 256)
+                            : phases;
   double ell_d = 0.0;
   int flags = 0;
   if (t < N) {
@@ -95,8 +99,8 @@ merge_kernel(int64_t N, int64_t L, int64_t V, int phases, const int32_t* __restr
       const float* ps = part + 2 * PN;
       const float* pz = part + 4 * PN;
       float lse_q, zq, lse_p, zp;
-      merge_side(pm, ps, pz, phases, N, r, &lse_q, &zq);
-      merge_side(pm + PN, ps + PN, pz + PN, phases, N, r, &lse_p, &zp);
+      merge_side(pm, ps, pz, used, N, r, &lse_q, &zq);
+      merge_side(pm + PN, ps + PN, pz + PN, used, N, r, &lse_p, &zp);
       const int64_t y = targets[t];
       if (y < 0 || y >= V) flags |= GRPO_FLAG_BAD_TARGET;
       q = zq - lse_q;
@@ -184,7 +188,7 @@ hipError_t launch_merge(const Plan& p, const void* ws, const int64_t* targets,
   double* lsum = ws_ptr<double>(w, p.off_lsum);
   const int32_t* ntok = ws_ptr<int32_t>(w, p.off_ntok);
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)nblocks), dim3(kMergeBlock), 0, st, p.N, p.L,
-                     p.V, p.phases, ntok, ws_ptr<int32_t>(w, p.off_rank),
+                     p.V, p.phases, p.mfma, ntok, ws_ptr<int32_t>(w, p.off_rank),
                      ws_ptr<float>(w, p.off_part), targets, mask, adv, beta, saved, logp,
                      ref_logp, kl, status, lsum);
   hipError_t e = hipGetLastError();

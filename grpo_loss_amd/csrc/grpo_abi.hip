@@ -65,7 +65,7 @@ bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_d
   p->dtype = dtype;
   p->esize = dtype == GRPO_F32 ? 4 : 2;
   p->need_dW = need_dW ? 1 : 0;
-  p->phases = 8;
+  p->phases = kMaxPhases;
   // 16-bit operands with H a multiple of 256 take the MFMA kernels (256-wide tiles over H;
   // hidden-state rows addressed by 32-bit byte offsets, so S*L*H*2 must stay below 4 GiB);
   // everything else takes the fp32-accumulating FMA kernels.

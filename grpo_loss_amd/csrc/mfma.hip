@@ -57,7 +57,6 @@ constexpr int kWaveN = 16 * kNB;              // 64 columns per wave
 constexpr int kTileBytes = 256 * 64 * 2;      // one operand, one stage: 256 rows x 128 B
 constexpr int kNumWG = 256;                   // persistent grid: one workgroup per CU
 constexpr int kXcds = 8;
-constexpr int kPhases = 8;                    // forward vocabulary phases
 
 // LDS layout of one operand tile: 256 rows x 128 B; the 16-byte chunk c of row r sits at
 // position c ^ f(r) of its row, f(r) = (r & 7) ^ ((r >> 3) & 1).  A fragment read has 16
@@ -190,16 +189,17 @@ struct FwdArgs {
   const char* Xp;
   const char* W;
   const int64_t* targets;
-  float* part;  // [3][2 sides][kPhases][N]: running max (log2 units), sum, target logit
+  float* part;  // [3][2 sides][kMaxPhases][N]: running max (log2 units), sum, target logit
 };
 
 // Persistent.  Workgroup w runs on XCD w % 8; its slot s = w / 8 picks a token block of
-// the current round and a vocabulary phase: the 32 workgroups of one XCD cover 4 token
-// blocks x 8 phases, so each W tile in flight on an XCD is shared by 4 workgroups and
-// each X block by 8, and all XCDs sweep the same W tiles together.  A workgroup keeps
-// its token block for a whole round and walks the vocabulary tiles of its phase
-// (vt = phase, phase + 8, ...), folding each 256 x 256 logit tile into per-lane running
-// (max, sum of exp2, target logit) without storing it.
+// the current round and a vocabulary phase: the 32 workgroups of one XCD cover 32 / P
+// token blocks x P phases (P = fwd_phases(...), 8 for the long-context shape), so each W
+// tile in flight on an XCD is shared by 32 / P workgroups and each X block by P, and all
+// XCDs sweep the same W tiles together.  A workgroup keeps its token block for a whole
+// round and walks the vocabulary tiles of its phase (vt = phase, phase + P, ...), folding
+// each 256 x 256 logit tile into per-lane running (max, sum of exp2, target logit)
+// without storing it.
 template <class E>
 __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
   __shared__ float mrg[2][2][256];
@@ -209,17 +209,18 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / kWN, wn = w % kWN;
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
   const int slots = gridDim.x / kXcds;           // workgroups per XCD
-  const int tb_per_xcd = slots / kPhases;
-  const int phase = slot % kPhases;
-  const int tbg = kXcds * tb_per_xcd;            // token blocks per round
   const int ntok = *a.ntok;
   const int64_t ntb1 = (ntok + 255) / 256;
   const int64_t TB = 2 * ntb1;
   const int64_t nvt = (a.V + 255) / 256;
+  const int P = fwd_phases(TB, nvt);
+  const int tb_per_xcd = slots / P;
+  const int phase = slot % P;
+  const int tbg = kXcds * tb_per_xcd;            // token blocks per round
   const int64_t rowb = a.H * 2;                  // bytes per row
   const int nk = (int)(a.H / 64);
 
-  for (int64_t tb = xcd * tb_per_xcd + slot / kPhases; tb < TB; tb += tbg) {
+  for (int64_t tb = xcd * tb_per_xcd + slot / P; tb < TB; tb += tbg) {
     const int side = tb >= ntb1 ? 1 : 0;
     const int64_t tok0 = (tb - side * ntb1) * 256;
     const char* X = side ? a.Xp : a.Xq;
@@ -240,7 +241,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
       s_run[0][nb][tid] = -INFINITY;
       s_run[1][nb][tid] = 0.f;
     }
-    for (int64_t vt = phase; vt < nvt; vt += kPhases) {
+    for (int64_t vt = phase; vt < nvt; vt += P) {
       const int64_t v0 = vt * 256;
       Offs ao, bo;
 #pragma unroll
@@ -320,8 +321,8 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
                               ? 0.f
                               : (m0 == -INFINITY ? 0.f : mrg[0][1][n] * exp2f(m0 - M)) +
                                     (m1 == -INFINITY ? 0.f : mrg[1][1][n] * exp2f(m1 - M));
-        const int64_t PN = (int64_t)kPhases * a.N;
-        const int64_t o = (int64_t)(side * kPhases + phase) * a.N + r;
+        const int64_t PN = (int64_t)kMaxPhases * a.N;
+        const int64_t o = (int64_t)(side * kMaxPhases + phase) * a.N + r;
         a.part[o] = M;
         a.part[2 * PN + o] = sum;
         a.part[4 * PN + o] = s_zt[n];

@@ -46,10 +46,11 @@ def test_workspace_bytes(lib):
     assert f(0, 10, 64, 10, 1, 0) == 0          # S < 1
     assert f(2, 10, 100, 10, 1, 0) == 0         # H not a multiple of 64
     assert f(2, 10, 64, 10, 7, 0) == 0          # bad dtype
-    # O(chunk): doubling L doubles only per-row bookkeeping, far below 2*L*V*2 bytes
+    # O(chunk): doubling L adds only per-row bookkeeping (indices, partials: about 1 KB a
+    # row), against 2 * 2 * V bytes a row for materialised policy and reference logits
     a = f(8, 20480, 4096, 128256, 1, 0)
     b = f(8, 40960, 4096, 128256, 1, 0)
-    assert b - a < 8 * 20480 * 256
+    assert (b - a) / (8 * 20480) < 1024 < 2 * 2 * 128256
     materialised = 2 * 2 * 8 * 20480 * 128256
     assert a < materialised / 20
 
