@@ -13,6 +13,16 @@ docstring); none is "parity unpinned".
 """
 
 from .grpo_oracle import (  # noqa: F401
+    DEFAULT,
+    advantage_term,
+    grad_factor,
+    logits,
+    Variant,
+    forward_kl_k3,
+    kl_grad_q,
+    kl_value,
+    reverse_kl_q,
+    token_weights,
     backward,
     forward,
     found_inf,

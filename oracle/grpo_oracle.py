@@ -28,9 +28,16 @@ Readings where the pages are silent (each one is pinned by a test):
 * one lm_head W serves policy and reference; only the policy path is
   differentiated, so X_p and the reference log-probs get no gradient;
 * rows with mask 0 are never read; their outputs are 0.
+
+Loss variants (the experiments of [Long-context GRPO, §4], see Variant): the KL
+estimator with the roles of P and Q swapped (forward KL), the reverse estimator
+with the extra Q(y) factor, the ratio without its stop-gradient, a mean over
+sequences instead of tokens, and a softmax temperature.
 """
 
 from __future__ import annotations
+
+from dataclasses import dataclass
 
 import numpy as np
 
@@ -109,6 +116,88 @@ def reverse_kl_k3(q: np.ndarray, ref: np.ndarray) -> np.ndarray:
     return np.expm1(d) - d
 
 
+def forward_kl_k3(q: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """The same estimator with the roles of policy and reference swapped,
+    exp(q - ref) - (q - ref) - 1: its expectation under y ~ P is the forward KL(P || Q)
+    (the "forward KL instead" experiment of [Long-context GRPO, §4]).  Pinned by
+    test_forward_kl_exact_expectation."""
+    d = np.asarray(q, dtype=np.float64) - np.asarray(ref, dtype=np.float64)
+    return np.expm1(d) - d
+
+
+def reverse_kl_q(q: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """The reverse estimator multiplied by the policy probability of the sampled token,
+    Q(y) * (exp(ref - q) - (ref - q) - 1): the reading implemented for the "full reverse KL
+    with the extra Q term" experiment of [Long-context GRPO, §4], whose formula did not
+    survive.  Its gradient is pinned by finite differences."""
+    return np.exp(np.asarray(q, dtype=np.float64)) * reverse_kl_k3(q, ref)
+
+
+def logits(x, W, tau: float = 1.0) -> np.ndarray:
+    """Softmax argument of the rows x: x W^T / tau."""
+    return np.asarray(x, dtype=np.float64) @ np.asarray(W, dtype=np.float64).T / tau
+
+
+def advantage_term(a, detach: bool):
+    """The advantage's contribution to d loss / d q: -A through exp(q - sg(q)), whose
+    gradient is the ratio times dq; nothing through exp(q - q), which is constant."""
+    return -np.asarray(a, dtype=np.float64) if detach else np.zeros_like(a, dtype=np.float64)
+
+
+def grad_factor(grad_loss: float, loss_scale: float, tau: float) -> float:
+    """Per-row factor of the backward: grad_loss / loss_scale times the 1 / tau that
+    d(z / tau)/dz contributes."""
+    return float(grad_loss) / float(loss_scale) / float(tau)
+
+
+@dataclass(frozen=True)
+class Variant:
+    """Loss variant: KL estimator ("reverse", "forward", "reverse_q"), whether the ratio's
+    stop-gradient is kept, normalisation ("tokens" or "sequences") and the temperature the
+    logits are divided by.  The default is the loss of [Long-context GRPO, §4]."""
+    kl: str = "reverse"
+    detach: bool = True
+    norm: str = "tokens"
+    temperature: float = 1.0
+
+
+DEFAULT = Variant()
+
+
+def kl_value(v: Variant, q, ref):
+    return {"reverse": reverse_kl_k3, "forward": forward_kl_k3, "reverse_q": reverse_kl_q}[v.kl](q, ref)
+
+
+def kl_grad_q(v: Variant, q, ref):
+    """d KL / d q of the chosen estimator (written out from its definition)."""
+    q = np.asarray(q, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if v.kl == "reverse":
+        return -np.expm1(ref - q)
+    if v.kl == "forward":
+        return np.expm1(q - ref)
+    if v.kl == "reverse_q":     # d/dq [e^q (e^(ref-q) - (ref-q) - 1)] = (q - ref) e^q
+        return (q - ref) * np.exp(q)
+    raise ValueError(v.kl)
+
+
+def token_weights(mask, L: int, norm: str) -> np.ndarray:
+    """Weight of each loss token in the loss: 1 / N_tok for the token mean; for the
+    sequence mean 1 / (n_s * S'), n_s the loss tokens of the row's sequence and S' the
+    sequences that have any.  Zero for masked rows."""
+    m = np.asarray(mask).reshape(-1).astype(np.float64)
+    if norm == "tokens":
+        return m / max(1.0, m.sum())
+    if norm == "sequences":
+        per = m.reshape(-1, L).sum(1)
+        nseq = max(1.0, float((per > 0).sum()))
+        w = np.zeros_like(m)
+        rows = np.nonzero(m)[0]
+        w[rows] = 1.0 / (per[rows // L] * nseq)
+        return w
+    raise ValueError(norm)
+
+
 def token_loss(kl: np.ndarray, adv_tok: np.ndarray, beta: float) -> np.ndarray:
     """Per-token loss value beta * KL - A: the value of -(exp(q - sg(q)) * A - beta * KL)
     with the ratio equal to 1 [Long-context GRPO, §4].  Pinned by
@@ -133,17 +222,22 @@ def logit_grad(logp: np.ndarray, y: np.ndarray) -> np.ndarray:
     return T
 
 
-def surrogate_objective(q, q0, ref, adv_tok, mask, beta: float) -> float:
+def surrogate_objective(q, q0, ref, adv_tok, mask, beta: float, variant: Variant = DEFAULT,
+                        L: int | None = None) -> float:
     """The GRPO objective as autograd sees it: sum over loss tokens of
-    -A * exp(q - q0) + beta * KL(q, ref), divided by N_tok, where q0 is a frozen
-    copy of q.  At q = q0 its value is the loss; its gradient in q is the policy
-    gradient.  [Long-context GRPO, §4]  Used by the finite-difference pins."""
+    w_t * (-A * ratio + beta * KL(q, ref)), with ratio = exp(q - q0) and q0 a frozen copy of
+    q (or exp(q - q) = 1 without the stop-gradient), w_t the token weights.  At q = q0 its
+    value is the loss; its gradient in q is the policy gradient.  [Long-context GRPO, §4]
+    Used by the finite-difference pins."""
     q = np.asarray(q, dtype=np.float64)
     m = np.asarray(mask, dtype=np.float64)
-    n_tok = max(1.0, float(m.sum()))
-    ratio = np.exp(q - np.asarray(q0, dtype=np.float64))
-    terms = -np.asarray(adv_tok, dtype=np.float64) * ratio + beta * reverse_kl_k3(q, ref)
-    return float((m * terms).sum() / n_tok)
+    if variant.norm == "tokens":
+        w = m / max(1.0, float(m.sum()))
+    else:
+        w = token_weights(m, L, variant.norm)
+    ratio = np.exp(q - np.asarray(q0, dtype=np.float64)) if variant.detach else np.ones_like(q)
+    terms = -np.asarray(adv_tok, dtype=np.float64) * ratio + beta * kl_value(variant, q, ref)
+    return float((w * terms).sum())
 
 
 # --------------------------------------------------------------------------------------
@@ -162,12 +256,13 @@ def _finite(a) -> bool:
 
 
 def forward(xq, xp, W, targets, mask, adv, L: int, beta: float = 0.04, rows=None,
-            block: int = 256) -> dict:
+            block: int = 256, variant: Variant = DEFAULT) -> dict:
     """Loss and per-token terms.
 
     Arguments: xq, xp hidden states [N, H] (or only the rows listed in ``rows``,
     in that order); W [V, H]; targets int [N]; mask {0,1} [N]; adv fp32 [S] (one
-    per sequence, broadcast over its L tokens); L positions per sequence.
+    per sequence, broadcast over its L tokens); L positions per sequence;
+    ``variant`` the loss variant (default: the loss of [Long-context GRPO, §4]).
 
     Returns per-row arrays of length N (zero for masked rows and, in sampled
     mode, for rows not listed): ``lse_q``, ``logp`` (q), ``ref_logp``, ``kl``,
@@ -181,7 +276,8 @@ def forward(xq, xp, W, targets, mask, adv, L: int, beta: float = 0.04, rows=None
     Wd = _f64(W)
     V = Wd.shape[0]
     n_tok = int(mask.sum())
-    denom = float(max(1, n_tok))
+    wts = token_weights(mask, L, variant.norm)
+    tau = float(variant.temperature)
     loss_rows = np.nonzero(mask)[0]
     if rows is None:
         rows = loss_rows
@@ -208,21 +304,31 @@ def forward(xq, xp, W, targets, mask, adv, L: int, beta: float = 0.04, rows=None
         xq_b = xq_rows[sel][keep]
         xp_b = xp_rows[sel][keep]
         finite = finite and _finite(xq_b) and _finite(xp_b)
-        lp_q, lse_q = log_softmax_rows(xq_b @ Wd.T)
-        lp_p, _ = log_softmax_rows(xp_b @ Wd.T)
+        lp_q, lse_q = log_softmax_rows(logits(xq_b, Wd, tau))
+        lp_p, _ = log_softmax_rows(logits(xp_b, Wd, tau))
         q = lp_q[np.arange(len(r)), y]
         ref = lp_p[np.arange(len(r)), y]
-        kl = reverse_kl_k3(q, ref)
+        kl = kl_value(variant, q, ref)
         a = adv[r // L].astype(np.float64)
         out["lse_q"][r] = lse_q
         out["logp"][r] = q
         out["ref_logp"][r] = ref
         out["kl"][r] = kl
         out["ell"][r] = token_loss(kl, a, beta)
-        out["g"][r] = policy_grad(a, q, ref, beta, denom)
+        if variant == DEFAULT:
+            out["g"][r] = policy_grad(a, q, ref, beta, float(max(1, n_tok)))
+        else:
+            out["g"][r] = wts[r] * (advantage_term(a, variant.detach)
+                                    + beta * kl_grad_q(variant, q, ref))
     out["n_tok"] = n_tok
     out["rows"] = rows
-    out["loss"] = float(out["ell"][loss_rows].sum() / denom) if full else None
+    if not full:
+        out["loss"] = None
+    elif variant.norm == "tokens":
+        out["loss"] = float(out["ell"][loss_rows].sum() / max(1, n_tok))
+    else:
+        out["loss"] = float((wts[loss_rows] * out["ell"][loss_rows]).sum())
+    out["variant"] = variant
     out["inputs_finite"] = finite
     return out
 
@@ -247,7 +353,9 @@ def backward(xq, W, targets, mask, fwd: dict, grad_loss: float = 1.0,
     mask = np.asarray(mask).reshape(-1).astype(np.int64)
     Wd = _f64(W)
     V, H = Wd.shape
-    c = float(grad_loss) / float(loss_scale)
+    tau = float(fwd.get("variant", DEFAULT).temperature)
+    # dq/dz = (onehot - softmax(z / tau)) / tau: the 1/tau joins the per-row factor
+    c = grad_factor(grad_loss, loss_scale, tau)
     if rows is None:
         rows = np.nonzero(mask)[0]
         xq_rows = _f64(xq)[rows]
@@ -269,10 +377,10 @@ def backward(xq, W, targets, mask, fwd: dict, grad_loss: float = 1.0,
             continue
         rk = r[keep]
         x = xq_rows[sel][keep]
-        lp, _ = log_softmax_rows(x @ Wd.T)
+        lp, _ = log_softmax_rows(logits(x, Wd, tau))
         T = logit_grad(lp, targets[rk])
         gt = fwd["g"][rk]
-        worst = max(worst, float(np.max(np.abs(gt * float(grad_loss))[:, None] * np.abs(T))))
+        worst = max(worst, float(np.max(np.abs(gt * float(grad_loss) / tau)[:, None] * np.abs(T))))
         dX[i0 + keep] = (c * gt)[:, None] * (T @ Wd)
         if need_dW:
             dW += ((c * gt)[:, None] * T).T @ x
