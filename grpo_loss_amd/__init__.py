@@ -8,11 +8,12 @@ memory and the current stream.  ``grpo_loss`` wraps the three calls in an
 autograd function.
 
 Importing this package loads the library and fails loudly if it is not built
-(``python -m grpo_loss_amd.build``); there is no fallback.
+(``python grpo_loss_amd/build.py``); there is no fallback.
 """
 
 from ._binding import (  # noqa: F401
     GRPOError,
+    GRPOOptions,
     grpo_advantages,
     grpo_loss,
     grpo_loss_bwd,
@@ -20,4 +21,5 @@ from ._binding import (  # noqa: F401
     grpo_workspace_bytes,
     library_path,
     load_library,
+    options,
 )

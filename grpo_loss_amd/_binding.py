@@ -20,6 +20,31 @@ class GRPOError(RuntimeError):
     """A negative grpo_status returned by the library."""
 
 
+class GRPOOptions(ctypes.Structure):
+    """Mirror of struct grpo_options."""
+    _fields_ = [("kl_estimator", ctypes.c_int), ("detach_ratio", ctypes.c_int),
+                ("normalization", ctypes.c_int), ("temperature", ctypes.c_float)]
+
+
+KL_ESTIMATORS = {"reverse": 0, "forward": 1, "reverse_q": 2}
+NORMALIZATIONS = {"tokens": 0, "sequences": 1}
+
+
+def options(kl: str = "reverse", detach: bool = True, norm: str = "tokens",
+            temperature: float = 1.0) -> GRPOOptions:
+    """A grpo_options value from names (the library validates the ranges)."""
+    return GRPOOptions(KL_ESTIMATORS[kl], int(bool(detach)), NORMALIZATIONS[norm],
+                       float(temperature))
+
+
+def _opts(o):
+    if o is None:
+        return None
+    if isinstance(o, dict):
+        o = options(**o)
+    return ctypes.byref(o)
+
+
 def library_path() -> str:
     return os.path.join(_HERE, "libgrpo.so")
 
@@ -31,7 +56,7 @@ def load_library():
         return _LIB
     path = library_path()
     if not os.path.exists(path):
-        raise ImportError(f"{path} is not built; run `python -m grpo_loss_amd.build` first")
+        raise ImportError(f"{path} is not built; run `python grpo_loss_amd/build.py` first")
     lib = ctypes.CDLL(path)
     lib.grpo_status_string.restype = ctypes.c_char_p
     lib.grpo_status_string.argtypes = [ctypes.c_int]
@@ -41,13 +66,16 @@ def load_library():
     lib.grpo_advantages.argtypes = [_c_p, _c_i64, _c_i64, _c_i64, ctypes.c_float, ctypes.c_int,
                                     _c_p, _c_p]
     lib.grpo_loss_fwd.restype = ctypes.c_int
+    opt_p = ctypes.POINTER(GRPOOptions)
+    lib.grpo_default_options.restype = None
+    lib.grpo_default_options.argtypes = [opt_p]
     lib.grpo_loss_fwd.argtypes = [_c_p, _c_p, _c_p, ctypes.c_int, _c_p, _c_p, _c_p, _c_i64,
                                   _c_i64, _c_i64, _c_i64, ctypes.c_float, _c_p, _c_p, _c_p, _c_p,
-                                  _c_p, _c_p, _c_p, ctypes.c_size_t, _c_p]
+                                  _c_p, _c_p, opt_p, _c_p, ctypes.c_size_t, _c_p]
     lib.grpo_loss_bwd.restype = ctypes.c_int
     lib.grpo_loss_bwd.argtypes = [_c_p, _c_p, ctypes.c_int, _c_p, _c_p, _c_p, _c_i64, _c_i64,
                                   _c_i64, _c_i64, _c_p, ctypes.c_float, _c_p, _c_p, ctypes.c_int,
-                                  _c_p, _c_p, ctypes.c_size_t, _c_p]
+                                  _c_p, opt_p, _c_p, ctypes.c_size_t, _c_p]
     _LIB = lib
     return lib
 
@@ -115,9 +143,11 @@ def _shape(xq: torch.Tensor, L: int | None):
 
 
 def grpo_loss_fwd(xq, xp, W, targets, mask, adv, beta: float = 0.04, L: int | None = None,
-                  workspace: torch.Tensor | None = None, want_terms: bool = True, stream=None):
+                  workspace: torch.Tensor | None = None, want_terms: bool = True, stream=None,
+                  opts=None):
     """Forward.  Returns dict(loss [1], saved [N, 4], logp, ref_logp, kl [N] (or None),
-    status int32 [1], workspace)."""
+    status int32 [1], workspace).  opts: a GRPOOptions, a dict of options(...) keywords,
+    or None for the defaults."""
     for t, n in ((xq, "xq"), (xp, "xp"), (W, "W"), (targets, "targets"), (mask, "mask"),
                  (adv, "adv")):
         _need(t, n)
@@ -141,7 +171,7 @@ def grpo_loss_fwd(xq, xp, W, targets, mask, adv, beta: float = 0.04, L: int | No
     _check(_LIB.grpo_loss_fwd(_ptr(xq), _ptr(xp), _ptr(W), dt, _ptr(targets), _ptr(mask),
                               _ptr(adv), S, L, H, V, beta, _ptr(loss), _ptr(saved),
                               _ptr(terms[0]), _ptr(terms[1]), _ptr(terms[2]), _ptr(status),
-                              _ptr(workspace), workspace.numel(), _stream(stream)))
+                              _opts(opts), _ptr(workspace), workspace.numel(), _stream(stream)))
     return {"loss": loss, "saved": saved, "logp": terms[0], "ref_logp": terms[1],
             "kl": terms[2], "status": status, "workspace": workspace}
 
@@ -150,8 +180,9 @@ def grpo_loss_bwd(xq, W, targets, mask, saved, L: int | None = None, grad_loss=N
                   loss_scale: float = 1.0, need_dW: bool = False, dW: torch.Tensor | None = None,
                   accumulate_dW: bool = False, found_inf: torch.Tensor | None = None,
                   workspace: torch.Tensor | None = None, dXq: torch.Tensor | None = None,
-                  stream=None):
-    """Backward.  Returns dict(dXq, dW (or None), found_inf, workspace)."""
+                  stream=None, opts=None):
+    """Backward.  Returns dict(dXq, dW (or None), found_inf, workspace).  opts: the
+    options given to the forward."""
     for t, n in ((xq, "xq"), (W, "W"), (targets, "targets"), (mask, "mask"), (saved, "saved")):
         _need(t, n)
     S, L, H = _shape(xq, L)
@@ -172,7 +203,7 @@ def grpo_loss_bwd(xq, W, targets, mask, saved, L: int | None = None, grad_loss=N
     _check(_LIB.grpo_loss_bwd(_ptr(xq), _ptr(W), _dt(xq), _ptr(targets), _ptr(mask),
                               _ptr(saved), S, L, H, V, _ptr(grad_loss), float(loss_scale),
                               _ptr(dXq), _ptr(dW) if need_dW else None, int(bool(accumulate_dW)),
-                              _ptr(found_inf), _ptr(workspace), workspace.numel(),
+                              _ptr(found_inf), _opts(opts), _ptr(workspace), workspace.numel(),
                               _stream(stream)))
     return {"dXq": dXq, "dW": dW if need_dW else None, "found_inf": found_inf,
             "workspace": workspace}
@@ -180,10 +211,11 @@ def grpo_loss_bwd(xq, W, targets, mask, saved, L: int | None = None, grad_loss=N
 
 class _GRPOLoss(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, xq, xp, W, targets, mask, adv, beta, L, loss_scale, need_dW):
-        out = grpo_loss_fwd(xq, xp, W, targets, mask, adv, beta, L, want_terms=False)
+    def forward(ctx, xq, xp, W, targets, mask, adv, beta, L, loss_scale, need_dW, opts):
+        out = grpo_loss_fwd(xq, xp, W, targets, mask, adv, beta, L, want_terms=False,
+                            opts=opts)
         ctx.save_for_backward(xq, W, targets, mask, out["saved"])
-        ctx.L, ctx.loss_scale, ctx.need_dW = L, loss_scale, need_dW
+        ctx.L, ctx.loss_scale, ctx.need_dW, ctx.opts = L, loss_scale, need_dW, opts
         ctx.workspace = out["workspace"]
         ctx.mark_non_differentiable(out["status"])
         return out["loss"][0], out["status"]
@@ -193,20 +225,23 @@ class _GRPOLoss(torch.autograd.Function):
         xq, W, targets, mask, saved = ctx.saved_tensors
         g = grad_loss.reshape(1).to(torch.float32).contiguous()
         out = grpo_loss_bwd(xq, W, targets, mask, saved, ctx.L, g, ctx.loss_scale,
-                            need_dW=ctx.need_dW and W.requires_grad, workspace=None)
+                            need_dW=ctx.need_dW and W.requires_grad, workspace=None,
+                            opts=ctx.opts)
         dW = out["dW"].to(W.dtype) if out["dW"] is not None else None
         ctx.found_inf = out["found_inf"]
-        return out["dXq"], None, dW, None, None, None, None, None, None, None
+        return out["dXq"], None, dW, None, None, None, None, None, None, None, None
 
 
 def grpo_loss(xq, xp, W, targets, mask, rewards, beta: float = 0.04, eps: float = 1e-4,
-              loss_scale: float = 1.0, need_dW: bool = False, L: int | None = None):
+              loss_scale: float = 1.0, need_dW: bool = False, L: int | None = None,
+              opts=None):
     """The GRPO loss with autograd.  xq, xp [S, L, H] (or [S*L, H] with L), W [V, H],
     targets int64 and mask (bool/uint8) of S*L elements, rewards fp32 [S] or [B, G(, K)].
 
     Returns (loss, status).  Gradients flow to xq (and W when need_dW); xp and the
     reference path get none.  With loss scaling, back-propagate loss * loss_scale and pass
-    the same loss_scale here: the returned gradients are unscaled."""
+    the same loss_scale here: the returned gradients are unscaled.  opts selects the loss
+    variant (see options())."""
     r = rewards.float()
     if r.dim() == 1:
         r = r.unsqueeze(0)
@@ -215,4 +250,4 @@ def grpo_loss(xq, xp, W, targets, mask, rewards, beta: float = 0.04, eps: float 
     y = targets.reshape(-1).contiguous()
     return _GRPOLoss.apply(xq.contiguous(), xp.contiguous(), W.contiguous(), y, m, adv,
                            float(beta), L if xq.dim() == 2 else xq.shape[1], float(loss_scale),
-                           bool(need_dW))
+                           bool(need_dW), opts)

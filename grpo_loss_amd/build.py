@@ -1,6 +1,7 @@
 """Build libgrpo.so for gfx950 from the HIP sources in csrc/ (in-tree, no JIT cache).
 
-Usage: python -m grpo_loss_amd.build   (or call build()).  Each translation unit is
+Usage: python grpo_loss_amd/build.py   (or call build()).  Run as a script, not with
+-m: importing the package loads the library that is being rebuilt.  Each translation unit is
 compiled with hipcc to an object, in parallel, then linked into a shared library
 next to this file.
 """

@@ -66,9 +66,15 @@ struct Plan {
   int64_t R;        // backward: rows per recompute chunk (multiple of 256)
   int ksplit;       // backward: split of the dX reduction over the vocabulary
   int mfma;         // 1: 16-bit MFMA kernels, 0: fp32 FMA kernels
+  // loss variant (grpo_options)
+  int kl;           // grpo_kl_estimator
+  int detach;       // 1: ratio exp(q - sg(q)), 0: exp(q - q)
+  int norm;         // grpo_normalization
+  float inv_tau;    // 1 / temperature
+  float scale2;     // log2(e) / temperature: logits -> log2 units of the softmax argument
   // byte offsets into the workspace
-  size_t off_ntok, off_idx, off_rank, off_part, off_lsum, off_T, off_WT, off_TT, off_XgT,
-      off_dxp, total;
+  size_t off_ntok, off_idx, off_rank, off_part, off_lsum, off_seq, off_T, off_WT, off_TT,
+      off_XgT, off_dxp, total;
 };
 
 constexpr int kTokTile = 256;    // rows per token tile of the MFMA kernels
@@ -95,6 +101,8 @@ __host__ __device__ inline int fwd_phases(int64_t token_blocks, int64_t vocab_ti
 }
 
 bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_dW, Plan* p);
+// Copies a validated grpo_options (NULL = defaults) into the plan.
+void plan_options(const grpo_options* o, Plan* p);
 
 template <typename P>
 inline P* ws_ptr(void* ws, size_t off) {
@@ -115,6 +123,9 @@ hipError_t launch_merge(const Plan& p, const void* ws, const int64_t* targets,
                         const uint8_t* mask, const float* adv, float beta, float* saved,
                         float* logp, float* ref_logp, float* kl, int32_t* status, float* loss,
                         hipStream_t st);
+// Loss rows per sequence and the number of sequences that have any (sequence-mean
+// normalisation only).
+hipError_t launch_seq_counts(const Plan& p, const uint8_t* mask, void* ws, hipStream_t st);
 hipError_t launch_zero_masked_rows(const Plan& p, const uint8_t* mask, void* dX,
                                    hipStream_t st);
 

@@ -44,6 +44,16 @@ int device_ok() {
   return ok;
 }
 
+bool options_ok(const grpo_options* o) {
+  if (!o) return true;
+  if (o->kl_estimator < GRPO_KL_REVERSE || o->kl_estimator > GRPO_KL_REVERSE_Q) return false;
+  if (o->detach_ratio != 0 && o->detach_ratio != 1) return false;
+  if (o->normalization != GRPO_NORM_TOKENS && o->normalization != GRPO_NORM_SEQUENCES)
+    return false;
+  // the softmax argument z / tau must stay finite for finite logits
+  return isfinite(o->temperature) && o->temperature >= 1e-3f && o->temperature <= 1e3f;
+}
+
 bool sizes_ok(int64_t S, int64_t L, int64_t H, int64_t V) {
   if (S < 1 || L < 1 || H < 64 || V < 1) return false;
   if (H % 64 != 0) return false;
@@ -66,6 +76,7 @@ bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_d
   p->esize = dtype == GRPO_F32 ? 4 : 2;
   p->need_dW = need_dW ? 1 : 0;
   p->phases = kMaxPhases;
+  plan_options(nullptr, p);
   // 16-bit operands with H a multiple of 256 take the MFMA kernels (256-wide tiles over H;
   // hidden-state rows addressed by 32-bit byte offsets, so S*L*H*2 must stay below 4 GiB);
   // everything else takes the fp32-accumulating FMA kernels.
@@ -92,6 +103,8 @@ bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_d
   o = align_up(o + (size_t)6 * p->phases * p->N * 4);
   p->off_lsum = o;
   o = align_up(o + (size_t)((p->N + kMergeBlock - 1) / kMergeBlock) * 8);
+  p->off_seq = o;
+  o = align_up(o + (size_t)(S + 1) * 4);
   p->off_T = o;
   o = align_up(o + (size_t)p->R * p->Vpad * p->esize);
   p->off_WT = o;
@@ -104,6 +117,17 @@ bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_d
   if (p->mfma && p->ksplit > 1) o = align_up(o + (size_t)p->ksplit * p->R * H * 4);
   p->total = o;
   return true;
+}
+
+void plan_options(const grpo_options* o, Plan* p) {
+  grpo_options d;
+  grpo_default_options(&d);
+  if (!o) o = &d;
+  p->kl = o->kl_estimator;
+  p->detach = o->detach_ratio;
+  p->norm = o->normalization;
+  p->inv_tau = 1.0f / o->temperature;
+  p->scale2 = kLog2e / o->temperature;
 }
 
 }  // namespace grpo
@@ -122,8 +146,17 @@ const char* grpo_status_string(int status) {
     case GRPO_ERR_WORKSPACE: return "workspace too small";
     case GRPO_ERR_HIP: return "HIP runtime error while enqueuing";
     case GRPO_ERR_DEVICE: return "current device is not gfx950";
+    case GRPO_ERR_OPTIONS: return "a loss option is out of range";
     default: return "unknown status";
   }
+}
+
+void grpo_default_options(grpo_options* opts) {
+  if (!opts) return;
+  opts->kl_estimator = GRPO_KL_REVERSE;
+  opts->detach_ratio = 1;
+  opts->normalization = GRPO_NORM_TOKENS;
+  opts->temperature = 1.0f;
 }
 
 size_t grpo_workspace_bytes(int64_t S, int64_t L, int64_t H, int64_t V, grpo_dtype dtype,
@@ -150,7 +183,8 @@ int grpo_loss_fwd(const void* Xq, const void* Xp, const void* W, grpo_dtype dtyp
                   const int64_t* targets, const uint8_t* mask, const float* adv, int64_t S,
                   int64_t L, int64_t H, int64_t V, float beta, float* loss, float* saved,
                   float* logp_out, float* ref_logp_out, float* kl_out, int32_t* status,
-                  void* workspace, size_t workspace_bytes, grpo_stream_t stream) {
+                  const grpo_options* opts, void* workspace, size_t workspace_bytes,
+                  grpo_stream_t stream) {
   if (!Xq || !Xp || !W || !targets || !mask || !adv || !loss || !saved || !status || !workspace)
     return GRPO_ERR_NULL;
   if (!valid_dtype(dtype)) return GRPO_ERR_DTYPE;
@@ -159,7 +193,9 @@ int grpo_loss_fwd(const void* Xq, const void* Xp, const void* W, grpo_dtype dtyp
       !aligned16(workspace))
     return GRPO_ERR_ALIGN;
   Plan p;
+  if (!options_ok(opts)) return GRPO_ERR_OPTIONS;
   if (!make_plan(S, L, H, V, dtype, 0, &p)) return GRPO_ERR_SHAPE;
+  plan_options(opts, &p);
   if (workspace_bytes < p.total) return GRPO_ERR_WORKSPACE;
   if (!device_ok()) return GRPO_ERR_DEVICE;
   hipStream_t st = (hipStream_t)stream;
@@ -167,6 +203,8 @@ int grpo_loss_fwd(const void* Xq, const void* Xp, const void* W, grpo_dtype dtyp
   if (launch_compact_status(mask, p.N, ws_ptr<int32_t>(ws, p.off_ntok),
                             ws_ptr<int32_t>(ws, p.off_idx), ws_ptr<int32_t>(ws, p.off_rank),
                             status, st) != hipSuccess)
+    return GRPO_ERR_HIP;
+  if (p.norm == GRPO_NORM_SEQUENCES && launch_seq_counts(p, mask, ws, st) != hipSuccess)
     return GRPO_ERR_HIP;
   const hipError_t fe = p.mfma ? mfma_fwd_partials(p, ws, Xq, Xp, W, targets, st)
                                : simple_fwd_partials(p, ws, Xq, Xp, W, targets, st);
@@ -180,8 +218,8 @@ int grpo_loss_fwd(const void* Xq, const void* Xp, const void* W, grpo_dtype dtyp
 int grpo_loss_bwd(const void* Xq, const void* W, grpo_dtype dtype, const int64_t* targets,
                   const uint8_t* mask, const float* saved, int64_t S, int64_t L, int64_t H,
                   int64_t V, const float* grad_loss, float loss_scale, void* dXq, float* dW,
-                  int accumulate_dW, int32_t* found_inf, void* workspace,
-                  size_t workspace_bytes, grpo_stream_t stream) {
+                  int accumulate_dW, int32_t* found_inf, const grpo_options* opts,
+                  void* workspace, size_t workspace_bytes, grpo_stream_t stream) {
   if (!Xq || !W || !targets || !mask || !saved || !dXq || !found_inf || !workspace)
     return GRPO_ERR_NULL;
   if (!valid_dtype(dtype)) return GRPO_ERR_DTYPE;
@@ -190,8 +228,14 @@ int grpo_loss_bwd(const void* Xq, const void* W, grpo_dtype dtype, const int64_t
   if (!aligned16(Xq) || !aligned16(W) || !aligned16(saved) || !aligned16(dXq) ||
       (dW && !aligned16(dW)) || !aligned16(workspace))
     return GRPO_ERR_ALIGN;
+  if (!options_ok(opts)) return GRPO_ERR_OPTIONS;
   Plan p;
   if (!make_plan(S, L, H, V, dtype, dW != nullptr, &p)) return GRPO_ERR_SHAPE;
+  plan_options(opts, &p);
+  // dq/dz = (onehot - softmax(z / tau)) / tau: the 1 / tau joins the per-row factor
+  // grad_loss / loss_scale as a larger divisor (exactly loss_scale at tau = 1)
+  const float ls_eff = opts ? loss_scale * opts->temperature : loss_scale;
+  if (!(ls_eff > 0.0f) || !isfinite(ls_eff)) return GRPO_ERR_SHAPE;
   if (workspace_bytes < p.total) return GRPO_ERR_WORKSPACE;
   if (!device_ok()) return GRPO_ERR_DEVICE;
   hipStream_t st = (hipStream_t)stream;
@@ -201,9 +245,9 @@ int grpo_loss_bwd(const void* Xq, const void* W, grpo_dtype dtype, const int64_t
     return GRPO_ERR_HIP;
   if (launch_zero_masked_rows(p, mask, dXq, st) != hipSuccess) return GRPO_ERR_HIP;
   const hipError_t be =
-      p.mfma ? mfma_backward(p, ws, Xq, W, targets, saved, grad_loss, loss_scale, dXq, dW,
+      p.mfma ? mfma_backward(p, ws, Xq, W, targets, saved, grad_loss, ls_eff, dXq, dW,
                              accumulate_dW, found_inf, st)
-             : simple_backward(p, ws, Xq, W, targets, saved, grad_loss, loss_scale, dXq, dW,
+             : simple_backward(p, ws, Xq, W, targets, saved, grad_loss, ls_eff, dXq, dW,
                                accumulate_dW, found_inf, st);
   if (be != hipSuccess) return GRPO_ERR_HIP;
   return GRPO_OK;

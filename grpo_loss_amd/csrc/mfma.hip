@@ -190,6 +190,7 @@ struct FwdArgs {
   const char* W;
   const int64_t* targets;
   float* part;  // [3][2 sides][kMaxPhases][N]: running max (log2 units), sum, target logit
+  float scale2; // log2(e) / temperature
 };
 
 // Persistent.  Workgroup w runs on XCD w % 8; its slot s = w / 8 picks a token block of
@@ -271,13 +272,13 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
           for (int j = 0; j < 4; ++j)
             if (full || mb * 16 + j < vlim) tmax = fmaxf(tmax, acc[mb][nb][j]);
         const float rm = s_run[0][nb][tid];
-        const float nm = fmaxf(rm, tmax * kLog2e);
+        const float nm = fmaxf(rm, tmax * a.scale2);
         float sum = rm == -INFINITY ? 0.f : s_run[1][nb][tid] * exp2f(rm - nm);
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            if (full || mb * 16 + j < vlim) sum += exp2f(acc[mb][nb][j] * kLog2e - nm);
+            if (full || mb * 16 + j < vlim) sum += exp2f(acc[mb][nb][j] * a.scale2 - nm);
         s_run[0][nb][tid] = nm;
         s_run[1][nb][tid] = sum;
         const int loc = s_y[n] - vb;
@@ -333,11 +334,12 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------- recompute
-// T[r - c0][v] = onehot(y_r)[v] - exp(z_rv - lse_r) for one 256-token x 256-vocabulary
-// tile of the chunk; zero for v >= V and for rows past the last loss token.
+// T[r - c0][v] = onehot(y_r)[v] - exp(z_rv / tau - lse_r) for one 256-token x
+// 256-vocabulary tile of the chunk (scale2 = log2(e) / tau); zero for v >= V and for rows
+// past the last loss token.
 template <class E>
 __global__ void __launch_bounds__(kThreads, 1)
-recompute_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t c0, int ntt,
+recompute_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t c0, int ntt, float scale2,
                  const int32_t* __restrict__ ntok_p, const int32_t* __restrict__ idx,
                  const char* __restrict__ Xq, const char* __restrict__ W,
                  const int64_t* __restrict__ targets, const float* __restrict__ saved,
@@ -385,7 +387,7 @@ recompute_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t c0, int ntt,
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float val = 0.f;
-        if (ok && v + j < V) val = (v + j == y ? 1.f : 0.f) - exp2f(acc[mb][nb][j] * kLog2e - lse2);
+        if (ok && v + j < V) val = (v + j == y ? 1.f : 0.f) - exp2f(acc[mb][nb][j] * scale2 - lse2);
         o[j] = E::from_f32(val);
       }
       uint2 pk;
@@ -636,6 +638,7 @@ hipError_t fwd_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, con
   a.W = (const char*)W;
   a.targets = targets;
   a.part = ws_ptr<float>(ws, p.off_part);
+  a.scale2 = p.scale2;
   hipLaunchKernelGGL(fwd_kernel<E>, dim3(kNumWG), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
@@ -659,7 +662,7 @@ hipError_t bwd_impl(const Plan& p, void* ws, const void* Xq, const void* W,
   const int ntt = (int)(p.R / 256), nvt = (int)(p.Vpad / 256), nht = (int)(p.H / 256);
   for (int64_t c0 = 0; c0 < p.N; c0 += p.R) {
     hipLaunchKernelGGL(recompute_kernel<E>, dim3((unsigned)(ntt * nvt)), dim3(kThreads), 0, st,
-                       p.H, p.V, p.Vpad, c0, ntt, ntok, idx, (const char*)Xq, (const char*)W,
+                       p.H, p.V, p.Vpad, c0, ntt, p.scale2, ntok, idx, (const char*)Xq, (const char*)W,
                        targets, saved, Tb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(dx_kernel<E>, dim3((unsigned)(nht * ntt * p.ksplit)), dim3(kThreads), 0, st,

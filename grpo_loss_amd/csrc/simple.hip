@@ -54,7 +54,8 @@ __device__ inline void logits_tile(const typename E::T* __restrict__ xrow,
 
 template <class E>
 __global__ void __launch_bounds__(256)
-simple_fwd_kernel(int64_t N, int64_t H, int64_t V, int phases, const int32_t* __restrict__ ntok_p,
+simple_fwd_kernel(int64_t N, int64_t H, int64_t V, int phases, float scale2,
+                  const int32_t* __restrict__ ntok_p,
                   const int32_t* __restrict__ idx, const typename E::T* __restrict__ Xq,
                   const typename E::T* __restrict__ Xp, const typename E::T* __restrict__ W,
                   const int64_t* __restrict__ targets, float* __restrict__ part) {
@@ -97,13 +98,13 @@ simple_fwd_kernel(int64_t N, int64_t H, int64_t V, int phases, const int32_t* __
         if (vt * kT + tx * 4 + j < V) tmax = fmaxf(tmax, acc[i][j]);
 #pragma unroll
       for (int off = 8; off > 0; off >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, off, 16));
-      const float nm = fmaxf(rm[i], tmax * kLog2e);
+      const float nm = fmaxf(rm[i], tmax * scale2);
       float s = rs[i] * exp2f(rm[i] - nm);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t v = vt * kT + tx * 4 + j;
         if (v < V) {
-          s += exp2f(acc[i][j] * kLog2e - nm);
+          s += exp2f(acc[i][j] * scale2 - nm);
           if (v == y[i]) rz[i] += acc[i][j];
         }
       }
@@ -129,10 +130,11 @@ simple_fwd_kernel(int64_t N, int64_t H, int64_t V, int phases, const int32_t* __
   }
 }
 
-// T[r - c0][v] = onehot(y_r)[v] - exp(z_rv - lse_r); zero for v >= V.
+// T[r - c0][v] = onehot(y_r)[v] - exp(z_rv / tau - lse_r) (scale2 = log2(e) / tau);
+// zero for v >= V.
 template <class E>
 __global__ void __launch_bounds__(256)
-simple_recompute_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t c0,
+simple_recompute_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t c0, float scale2,
                         const int32_t* __restrict__ ntok_p, const int32_t* __restrict__ idx,
                         const typename E::T* __restrict__ Xq, const typename E::T* __restrict__ W,
                         const int64_t* __restrict__ targets, const float* __restrict__ saved,
@@ -163,7 +165,7 @@ simple_recompute_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t c0,
     for (int j = 0; j < 4; ++j) {
       const int64_t v = v0 + tx * 4 + j;
       float val = 0.0f;
-      if (v < V) val = (v == y ? 1.0f : 0.0f) - exp2f(acc[i][j] * kLog2e - lse2);
+      if (v < V) val = (v == y ? 1.0f : 0.0f) - exp2f(acc[i][j] * scale2 - lse2);
       T[(r - c0) * Vpad + v] = E::from_f32(val);
     }
   }
@@ -282,7 +284,7 @@ hipError_t simple_fwd(const Plan& p, void* ws, const void* Xq, const void* Xp, c
   typedef typename E::T T;
   const int64_t tiles = (p.N + kT - 1) / kT;
   hipLaunchKernelGGL(simple_fwd_kernel<E>, dim3((unsigned)tiles, p.phases, 2), dim3(256), 0, st,
-                     p.N, p.H, p.V, p.phases, ws_ptr<int32_t>(ws, p.off_ntok),
+                     p.N, p.H, p.V, p.phases, p.scale2, ws_ptr<int32_t>(ws, p.off_ntok),
                      ws_ptr<int32_t>(ws, p.off_idx), (const T*)Xq, (const T*)Xp, (const T*)W,
                      targets, ws_ptr<float>(ws, p.off_part));
   return hipGetLastError();
@@ -299,7 +301,7 @@ hipError_t simple_bwd(const Plan& p, void* ws, const void* Xq, const void* W,
   T* Tbuf = ws_ptr<T>(ws, p.off_T);
   for (int64_t c0 = 0; c0 < p.N; c0 += p.R) {
     hipLaunchKernelGGL(simple_recompute_kernel<E>, dim3((unsigned)(p.R / kT), (unsigned)(p.Vpad / kT)),
-                       dim3(256), 0, st, p.H, p.V, p.Vpad, c0, ntok, idx, (const T*)Xq,
+                       dim3(256), 0, st, p.H, p.V, p.Vpad, c0, p.scale2, ntok, idx, (const T*)Xq,
                        (const T*)W, targets, saved, Tbuf);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -65,8 +65,32 @@ typedef enum grpo_status {
   GRPO_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned                            */
   GRPO_ERR_WORKSPACE = -5, /* workspace smaller than grpo_workspace_bytes()               */
   GRPO_ERR_HIP = -6,       /* the HIP runtime reported an error when enqueuing           */
-  GRPO_ERR_DEVICE = -7     /* the current device is not a gfx950 GPU                      */
+  GRPO_ERR_DEVICE = -7,    /* the current device is not a gfx950 GPU                      */
+  GRPO_ERR_OPTIONS = -8    /* a grpo_options field is out of range                        */
 } grpo_status;
+
+/* Loss variants: the four experiments of [Long-context GRPO, §4] and two readings the
+ * pages leave open.  A NULL options pointer selects the defaults (first value of each). */
+typedef enum grpo_kl_estimator {
+  GRPO_KL_REVERSE = 0,    /* exp(ref - q) - (ref - q) - 1: reverse KL(Q||P), no Q factor    */
+  GRPO_KL_FORWARD = 1,    /* exp(q - ref) - (q - ref) - 1: the same estimator, roles swapped */
+  GRPO_KL_REVERSE_Q = 2   /* exp(q) * (exp(ref - q) - (ref - q) - 1): the reverse estimator
+                             with the extra Q(y) factor the pages discuss (their formula was
+                             lost; this is the reading implemented)                          */
+} grpo_kl_estimator;
+
+typedef enum grpo_normalization {
+  GRPO_NORM_TOKENS = 0,   /* loss = sum_t m_t l_t / N_tok (mean over all completion tokens) */
+  GRPO_NORM_SEQUENCES = 1 /* loss = mean over sequences with tokens of their token means     */
+} grpo_normalization;
+
+typedef struct grpo_options {
+  int kl_estimator;       /* grpo_kl_estimator                                             */
+  int detach_ratio;       /* 1: advantage times exp(q - sg(q)) (value 1, gradient A dq);
+                             0: exp(q - q), whose gradient vanishes (the no-detach experiment) */
+  int normalization;      /* grpo_normalization                                            */
+  float temperature;      /* logits are divided by it before the log-softmax; in [1e-3, 1e3] */
+} grpo_options;
 
 /* Bits of the forward's status word. */
 #define GRPO_FLAG_NONFINITE 1   /* loss, a log-prob, KL or g of a loss row is inf/NaN */
@@ -93,6 +117,9 @@ size_t grpo_workspace_bytes(int64_t S, int64_t L, int64_t H, int64_t V, grpo_dty
 int grpo_advantages(const float* rewards, int64_t B, int64_t G, int64_t K, float eps,
                     int unbiased, float* adv, grpo_stream_t stream);
 
+/* Defaults: reverse estimator, detached ratio, token mean, temperature 1. */
+void grpo_default_options(grpo_options* opts);
+
 /* Forward: loss and per-token terms, without materialising logits
  * [Long-context GRPO, §2 (memory figures), §3 (the linear algorithm), §4 (KL, ratio,
  * logsumexp)].
@@ -104,13 +131,15 @@ int grpo_advantages(const float* rewards, int64_t B, int64_t G, int64_t K, float
  *   saved    fp32 [S*L, 4] out: (lse_q, q, ref, dloss/dq) per row; the backward reads it.
  *   logp_out, ref_logp_out, kl_out: fp32 [S*L] out, each may be NULL.
  *   status   int32 [1] out: GRPO_FLAG_* bits of this call (overwritten, not accumulated).
+ *   opts     loss variant, or NULL for the defaults; the backward must get the same one.
  *   workspace, workspace_bytes: at least grpo_workspace_bytes(..., need_dW = 0).
  * Xq, Xp, W, saved, workspace must be 16-byte aligned. */
 int grpo_loss_fwd(const void* Xq, const void* Xp, const void* W, grpo_dtype dtype,
                   const int64_t* targets, const uint8_t* mask, const float* adv, int64_t S,
                   int64_t L, int64_t H, int64_t V, float beta, float* loss, float* saved,
                   float* logp_out, float* ref_logp_out, float* kl_out, int32_t* status,
-                  void* workspace, size_t workspace_bytes, grpo_stream_t stream);
+                  const grpo_options* opts, void* workspace, size_t workspace_bytes,
+                  grpo_stream_t stream);
 
 /* Backward: dloss/dXq (and dloss/dW) by recomputing the vocabulary chunks.
  *   Xq, W, targets, mask, saved: as given to / produced by grpo_loss_fwd.
@@ -125,12 +154,14 @@ int grpo_loss_fwd(const void* Xq, const void* Xp, const void* W, grpo_dtype dtyp
  *   dW         fp32 [V, H] out, or NULL to skip; accumulate_dW = 1 adds into it.
  *   found_inf  int32 [1] device: set to 1 if any element of dXq or dW is inf/NaN; never
  *              cleared by the library.
+ *   opts       the options given to the forward (only the temperature is read here: the
+ *              variant's dloss/dq is already in `saved`).
  *   workspace  at least grpo_workspace_bytes(..., need_dW = (dW != NULL)). */
 int grpo_loss_bwd(const void* Xq, const void* W, grpo_dtype dtype, const int64_t* targets,
                   const uint8_t* mask, const float* saved, int64_t S, int64_t L, int64_t H,
                   int64_t V, const float* grad_loss, float loss_scale, void* dXq, float* dW,
-                  int accumulate_dW, int32_t* found_inf, void* workspace,
-                  size_t workspace_bytes, grpo_stream_t stream);
+                  int accumulate_dW, int32_t* found_inf, const grpo_options* opts,
+                  void* workspace, size_t workspace_bytes, grpo_stream_t stream);
 
 #ifdef __cplusplus
 }

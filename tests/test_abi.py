@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         s = lib.grpo_status_string(code)
         assert s and s != b"unknown status"
     assert lib.grpo_status_string(-99) == b"unknown status"
@@ -59,25 +59,46 @@ def test_bad_arguments_rejected_before_launch(lib):
     p = ctypes.c_void_p(16)   # never dereferenced: validation fails first
     nul = None
     rc = lib.grpo_loss_fwd(nul, p, p, 1, p, p, p, 2, 3, 64, 5, ctypes.c_float(0.04), p, p,
-                           nul, nul, nul, p, p, ctypes.c_size_t(1 << 40), nul)
+                           nul, nul, nul, p, nul, p, ctypes.c_size_t(1 << 40), nul)
     assert rc == -1
     rc = lib.grpo_loss_fwd(p, p, p, 9, p, p, p, 2, 3, 64, 5, ctypes.c_float(0.04), p, p,
-                           nul, nul, nul, p, p, ctypes.c_size_t(1 << 40), nul)
+                           nul, nul, nul, p, nul, p, ctypes.c_size_t(1 << 40), nul)
     assert rc == -3
     rc = lib.grpo_loss_fwd(p, p, p, 1, p, p, p, 2, 3, 96, 5, ctypes.c_float(0.04), p, p,
-                           nul, nul, nul, p, p, ctypes.c_size_t(1 << 40), nul)
+                           nul, nul, nul, p, nul, p, ctypes.c_size_t(1 << 40), nul)
     assert rc == -2
     odd = ctypes.c_void_p(18)
     rc = lib.grpo_loss_fwd(odd, p, p, 1, p, p, p, 2, 3, 64, 5, ctypes.c_float(0.04), p, p,
-                           nul, nul, nul, p, p, ctypes.c_size_t(1 << 40), nul)
+                           nul, nul, nul, p, nul, p, ctypes.c_size_t(1 << 40), nul)
     assert rc == -4
     rc = lib.grpo_loss_fwd(p, p, p, 1, p, p, p, 2, 3, 64, 5, ctypes.c_float(0.04), p, p,
-                           nul, nul, nul, p, p, ctypes.c_size_t(8), nul)
+                           nul, nul, nul, p, nul, p, ctypes.c_size_t(8), nul)
     assert rc == -5
     rc = lib.grpo_loss_bwd(p, p, 1, p, p, p, 2, 3, 64, 5, nul, ctypes.c_float(0.0), p, nul, 0,
-                           p, p, ctypes.c_size_t(1 << 40), nul)
+                           p, nul, p, ctypes.c_size_t(1 << 40), nul)
     assert rc == -2                              # loss_scale must be > 0
     rc = lib.grpo_advantages(p, 1, 1, 1, ctypes.c_float(1e-4), 1, p, nul)
     assert rc == -2                              # unbiased std needs G >= 2
     rc = lib.grpo_advantages(nul, 1, 8, 1, ctypes.c_float(1e-4), 1, p, nul)
     assert rc == -1
+
+
+def test_options(lib):
+    import grpo_loss_amd as g
+    d = g.GRPOOptions()
+    lib.grpo_default_options(ctypes.byref(d))
+    assert (d.kl_estimator, d.detach_ratio, d.normalization, d.temperature) == (0, 1, 0, 1.0)
+    lib.grpo_default_options(None)               # tolerated
+    p = ctypes.c_void_p(16)
+    nul = None
+    bad = [g.options(temperature=0.0), g.options(temperature=float("nan")),
+           g.options(temperature=1e4), g.GRPOOptions(3, 1, 0, 1.0), g.GRPOOptions(0, 2, 0, 1.0),
+           g.GRPOOptions(0, 1, 2, 1.0)]
+    for o in bad:
+        rc = lib.grpo_loss_fwd(p, p, p, 1, p, p, p, 2, 3, 64, 5, ctypes.c_float(0.04), p, p,
+                               nul, nul, nul, p, ctypes.byref(o), p, ctypes.c_size_t(1 << 40),
+                               nul)
+        assert rc == -8
+        rc = lib.grpo_loss_bwd(p, p, 1, p, p, p, 2, 3, 64, 5, nul, ctypes.c_float(1.0), p, nul,
+                               0, p, ctypes.byref(o), p, ctypes.c_size_t(1 << 40), nul)
+        assert rc == -8

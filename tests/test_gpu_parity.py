@@ -36,17 +36,20 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def run_gpu(wl, inp, need_dW=None, grad_scale=True):
-    """advantages -> forward -> backward on the device; host copies of every output."""
+def run_gpu(wl, inp, need_dW=None, grad_scale=True, variant=None):
+    """advantages -> forward -> backward on the device; host copies of every output.
+    variant: an oracle.Variant whose fields name the same options for the library."""
     g = _lib()
     d = to_device(inp)
     need_dW = wl.need_dW if need_dW is None else need_dW
+    opts = None if variant is None else g.options(**dataclasses.asdict(variant))
     adv = g.grpo_advantages(d["rewards"], wl.eps)
-    f = g.grpo_loss_fwd(d["xq"], d["xp"], d["W"], d["targets"], d["mask"], adv, wl.beta, wl.L)
+    f = g.grpo_loss_fwd(d["xq"], d["xp"], d["W"], d["targets"], d["mask"], adv, wl.beta, wl.L,
+                        opts=opts)
     S = wl.loss_scale
     grad = torch.full((1,), S, dtype=torch.float32, device="cuda")
     b = g.grpo_loss_bwd(d["xq"], d["W"], d["targets"], d["mask"], f["saved"], wl.L, grad, S,
-                        need_dW=need_dW, workspace=f["workspace"])
+                        need_dW=need_dW, workspace=f["workspace"], opts=opts)
     torch.cuda.synchronize()
     out = {"adv": adv.cpu().numpy(), "loss": float(f["loss"].item()),
            "saved": f["saved"].cpu().numpy(), "logp": f["logp"].cpu().numpy(),
@@ -72,16 +75,13 @@ SMALL = {
 }
 
 
-@pytest.mark.parametrize("name", list(SMALL))
-def test_parity_small(name):
-    wl = dataclasses.replace(workload_by_name(name), **SMALL[name])
-    _say(f"[parity small] {name} S={wl.S} L={wl.L} H={wl.H} V={wl.V} dtype={wl.dtype}")
-    inp = generate(wl)
-    gpu = run_gpu(wl, inp)
+def check_small(wl, inp, variant=None):
+    gpu = run_gpu(wl, inp, variant=variant)
+    variant = oracle.DEFAULT if variant is None else variant
     adv = oracle.group_advantages(inp.rewards.numpy(), wl.eps)
     assert np.array_equal(gpu["adv"].view(np.uint32), adv.view(np.uint32)), (gpu["adv"], adv)
     f = oracle.forward(inp.xq, inp.xp, inp.W, inp.targets.numpy(), inp.mask.numpy(), adv, wl.L,
-                       wl.beta)
+                       wl.beta, variant=variant)
     b = oracle.backward(inp.xq, inp.W, inp.targets.numpy(), inp.mask.numpy(), f,
                         grad_loss=wl.loss_scale, loss_scale=wl.loss_scale, need_dW=wl.need_dW)
     tol = TOL[wl.dtype]
@@ -105,6 +105,35 @@ def test_parity_small(name):
         e = rel_l2(gpu["dW"], b["dW"])
         _say(f"  dW rel-L2 {e:.2e}")
         assert e <= tol["dw"]
+    # KL per token: an error e in q and in ref moves it by at most about 2 e |dKL/dq|
+    slope = np.abs(oracle.kl_grad_q(variant, f["logp"][m], f["ref_logp"][m]))
+    excess = np.abs(gpu["kl"][m] - f["kl"][m]) - 2 * tol["logp"] * (1 + slope)
+    _say(f"  kl max excess over bound {excess.max():.2e}")
+    assert np.all(excess <= 0)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_parity_small(name):
+    wl = dataclasses.replace(workload_by_name(name), **SMALL[name])
+    _say(f"[parity small] {name} S={wl.S} L={wl.L} H={wl.H} V={wl.V} dtype={wl.dtype}")
+    check_small(wl, generate(wl))
+
+
+VARIANTS = [oracle.Variant(kl="forward"), oracle.Variant(kl="reverse_q"),
+            oracle.Variant(detach=False), oracle.Variant(norm="sequences"),
+            oracle.Variant(temperature=0.7),
+            oracle.Variant(kl="forward", detach=False, norm="sequences", temperature=1.6)]
+
+
+@pytest.mark.parametrize("name", ["tiny-f32", "qwen2.5-1.5b-bf16", "llama3.1-8b-train-bf16",
+                                  "phi4-f16"])
+@pytest.mark.parametrize("vi", range(len(VARIANTS)))
+def test_parity_variants(name, vi):
+    """The loss variants of [Long-context GRPO, §4] on the fp32 and both MFMA paths."""
+    v = VARIANTS[vi]
+    wl = dataclasses.replace(workload_by_name(name), **SMALL[name])
+    _say(f"[parity variant] {name} {v}")
+    check_small(wl, generate(wl), variant=v)
 
 
 @pytest.mark.parametrize("B,G,K", [(1, 8, 1), (3, 4, 2), (37, 8, 3), (300, 16, 1), (1, 2, 1)])
