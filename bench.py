@@ -1,14 +1,23 @@
 """Benchmark of the GRPO loss hot path on one MI355X.
 
-One step = grpo_advantages + grpo_loss_fwd + grpo_loss_bwd over one batch of synthetic
-inputs already resident in HBM: advantages, row compaction, the fused forward GEMM with
-its online logsumexp for policy and reference, the KL / advantage epilogue and loss,
-the backward recompute of onehot - softmax, dX (and dW for the trainable-head workload).
+One step = the whole loss with its gradients over one batch of synthetic inputs already
+resident in HBM: advantages, row compaction, the forward GEMMs with their online
+logsumexp for policy and reference, the KL / advantage epilogue and loss, onehot - softmax
+and dX (and dW for the trainable-head workload).
+
+  single-pass (timed for `value`): grpo_advantages + grpo_loss_fwd_bwd, which keeps the
+      policy forward's softmax terms per chunk of rows instead of recomputing the logits;
+  two-pass (reported as `two_pass`): grpo_advantages + grpo_loss_fwd + grpo_loss_bwd, the
+      backward recomputing each chunk's logits.
+
+The roofline is that of the forward kernel, timed with HIP events around each two-pass
+grpo_loss_fwd call (one fwd_kernel launch covering both sides, plus the row compaction
+and merge, which take well under 0.1% of it).
 
 Prints ONE JSON line.  Default workload: the long-context Llama-3.1-8B shape
 (G = 8, L = 20480, H = 4096, V = 128256, bf16, frozen head).
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--path P]
                   [--no-cpu-baseline] [--cpu-rows R] [--calibrate-copy-gib X]
 """
 
@@ -34,12 +43,35 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama3.1-8b-long-bf16")
+    ap.add_argument("--path", choices=["single", "two"], default="single",
+                    help="path timed for value; the other one is reported beside it")
+    ap.add_argument("--no-two-pass", action="store_true",
+                    help="time only the path given by --path")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=256, help="oracle rows per sequence")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                     help="run one device-to-device copy of this many GiB first, so a "
                          "counter run can scale FETCH_SIZE / WRITE_SIZE by a known size")
     return ap.parse_args()
+
+
+def measured_traffic(workload):
+    """HBM-side bytes per launch of fwd_kernel from the committed counter summary, or None
+    when there is none for this workload or the kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_fwd_kernel_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.split(":")[0] in ("kernel_source_sha256", "traffic_bytes_per_launch"):
+            k, v = line.split(":", 1)
+            fields[k] = v.strip()
+    src = b"".join(open(os.path.join(ROOT, "grpo_loss_amd", "csrc", f), "rb").read()
+                   for f in ("mfma.hip", "common.h"))
+    if fields.get("kernel_source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(wl, inp, adv_host, rows_per_seq):
@@ -115,10 +147,12 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst, flush
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
 
     ev = []
 
-    def step(record):
+    def step_two(record):
         g.grpo_advantages(d["rewards"], wl.eps, out=adv)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -132,49 +166,77 @@ def main():
             ev.append((e0, e1))
         return f
 
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        f = step(True)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    peak_extra = torch.cuda.max_memory_allocated() - base_mem
-    fwd_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    ms = elapsed / args.steps * 1e3
+    def step_single(record):
+        g.grpo_advantages(d["rewards"], wl.eps, out=adv)
+        return g.grpo_loss_fwd_bwd(d["xq"], d["xp"], d["W"], d["targets"], d["mask"], adv,
+                                   wl.beta, wl.L, grad, wl.loss_scale, dW=dW, found_inf=found,
+                                   workspace=ws, dXq=dX, want_terms=False)
+
+    def timed(step):
+        for _ in range(args.warmup):
+            step(False)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            f = step(True)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / args.steps * 1e3, f
+
     gemm_eq = 2.0 * n_tok * wl.H * wl.V
-    method_flops = (5 if need_dW else 4) * gemm_eq
     dtn = wl.dtype
     peak = PEAK_TFLOPS[dtn]
-    fwd_tflops = 2 * gemm_eq / (fwd_ms * 1e-3) / 1e12
+    # GEMM-equivalents executed per step: policy and reference forward, dX, dW if trainable,
+    # plus the recompute in the two-pass path; the survey's method count always includes it
+    n_exec = {"single": 3 + need_dW, "two": 4 + need_dW}
+    n_method = 4 + need_dW
+    legs = {}
+    order = [args.path]
+    if not args.no_two_pass:
+        order.append("two" if args.path == "single" else "single")
+    for path in order:
+        ms, f = timed(step_single if path == "single" else step_two)
+        legs[path] = {"value": n_tok / (ms * 1e-3), "ms_per_step": ms,
+                      "mfma_peak_frac": n_exec[path] * gemm_eq / (ms * 1e-3) / (peak * 1e12),
+                      "method_flops_frac": n_method * gemm_eq / (ms * 1e-3) / (peak * 1e12),
+                      "status": int(f["status"].item()), "found_inf": int(found.item())}
+    peak_extra = torch.cuda.max_memory_allocated() - base_mem
+    main_leg = legs[args.path]
     out = {
         "metric": METRIC,
-        "value": n_tok / (ms * 1e-3),
+        "value": main_leg["value"],
         "unit": "completion tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": main_leg["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": dtn,
         "data": "synthetic",
         "config": {"workload": wl.name, "G": wl.G, "L": wl.L, "H": wl.H, "V": wl.V,
-                   "completion_tokens": n_tok, "trainable_head": need_dW},
-        "mfma_peak_frac": method_flops / (ms * 1e-3) / (peak * 1e12),
+                   "completion_tokens": n_tok, "trainable_head": need_dW,
+                   "path": "single-pass" if args.path == "single" else "two-pass"},
+        "mfma_peak_frac": main_leg["mfma_peak_frac"],
+        "method_flops_frac": main_leg["method_flops_frac"],
         "extra_gib": peak_extra / 2 ** 30,
         "workspace_gib": ws_bytes / 2 ** 30,
         "materialized_logits_gib": 2 * 2 * wl.S * wl.L * wl.V / 2 ** 30,
-        "roofline": {"bound": "mfma", "kernel": "fwd_kernel (policy + reference logits, "
-                                                  "online logsumexp)",
-                     "achieved": fwd_tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": fwd_tflops / peak, "traffic": None,
-                     "fwd_call_ms": fwd_ms},
-        "status": int(f["status"].item()),
-        "found_inf": int(found.item()),
     }
+    if ev:
+        fwd_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        fwd_tflops = 2 * gemm_eq / (fwd_ms * 1e-3) / 1e12
+        out["roofline"] = {"bound": "mfma",
+                           "kernel": "fwd_kernel mode 0 (policy + reference logits, online "
+                                     "logsumexp; one launch per two-pass forward)",
+                           "achieved": fwd_tflops, "peak": peak, "unit": "TFLOP/s",
+                           "frac": fwd_tflops / peak, "traffic": measured_traffic(wl.name),
+                           "launch_ms": fwd_ms, "flop_per_launch": 2 * gemm_eq}
+    other = [p for p in legs if p != args.path]
+    if other:
+        out["two_pass" if other[0] == "two" else "single_pass"] = legs[other[0]]
+    out["status"] = main_leg["status"]
+    out["found_inf"] = main_leg["found_inf"]
     if not args.no_cpu_baseline:
         import oracle
         adv_host = oracle.group_advantages(inp.rewards.numpy(), wl.eps)

@@ -18,6 +18,8 @@ from ._binding import (  # noqa: F401
     grpo_loss,
     grpo_loss_bwd,
     grpo_loss_fwd,
+    grpo_loss_fwd_bwd,
+    grpo_scale_grad,
     grpo_workspace_bytes,
     library_path,
     load_library,

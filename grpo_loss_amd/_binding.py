@@ -76,6 +76,15 @@ def load_library():
     lib.grpo_loss_bwd.argtypes = [_c_p, _c_p, ctypes.c_int, _c_p, _c_p, _c_p, _c_i64, _c_i64,
                                   _c_i64, _c_i64, _c_p, ctypes.c_float, _c_p, _c_p, ctypes.c_int,
                                   _c_p, opt_p, _c_p, ctypes.c_size_t, _c_p]
+    lib.grpo_loss_fwd_bwd.restype = ctypes.c_int
+    lib.grpo_loss_fwd_bwd.argtypes = [_c_p, _c_p, _c_p, ctypes.c_int, _c_p, _c_p, _c_p, _c_i64,
+                                      _c_i64, _c_i64, _c_i64, ctypes.c_float, _c_p,
+                                      ctypes.c_float, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                      _c_p, ctypes.c_int, _c_p, opt_p, _c_p, ctypes.c_size_t,
+                                      _c_p]
+    lib.grpo_scale_grad.restype = ctypes.c_int
+    lib.grpo_scale_grad.argtypes = [_c_p, ctypes.c_int, _c_i64, _c_i64, _c_p, _c_i64, _c_p,
+                                    ctypes.c_float, _c_p, _c_p]
     _LIB = lib
     return lib
 
@@ -209,39 +218,129 @@ def grpo_loss_bwd(xq, W, targets, mask, saved, L: int | None = None, grad_loss=N
             "workspace": workspace}
 
 
+def grpo_loss_fwd_bwd(xq, xp, W, targets, mask, adv, beta: float = 0.04, L: int | None = None,
+                      grad_loss=None, loss_scale: float = 1.0, need_dW: bool = False,
+                      dW: torch.Tensor | None = None, accumulate_dW: bool = False,
+                      found_inf: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None, dXq: torch.Tensor | None = None,
+                      want_terms: bool = True, stream=None, opts=None):
+    """Forward and backward in one call (the policy logits are computed once).  Returns
+    dict(loss, saved, logp, ref_logp, kl, status, dXq, dW (or None), found_inf,
+    workspace)."""
+    for t, n in ((xq, "xq"), (xp, "xp"), (W, "W"), (targets, "targets"), (mask, "mask"),
+                 (adv, "adv")):
+        _need(t, n)
+    S, L, H = _shape(xq, L)
+    V = W.shape[0]
+    dt = _dt(xq)
+    if xp.dtype != xq.dtype or W.dtype != xq.dtype:
+        raise TypeError("xq, xp and W must share one dtype")
+    if targets.dtype != torch.int64 or mask.dtype != torch.uint8 or adv.dtype != torch.float32:
+        raise TypeError("targets int64, mask uint8, adv float32 expected")
+    dev = xq.device
+    N = S * L
+    need_dW = need_dW or dW is not None
+    need = grpo_workspace_bytes(S, L, H, V, xq.dtype, need_dW)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    loss = torch.empty(1, **f32)
+    saved = torch.empty(N, 4, **f32)
+    terms = [torch.empty(N, **f32) for _ in range(3)] if want_terms else [None] * 3
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    if dXq is None:
+        dXq = torch.empty_like(xq)
+    if need_dW and dW is None:
+        dW = torch.empty(V, H, **f32)
+    if found_inf is None:
+        found_inf = torch.zeros(1, dtype=torch.int32, device=dev)
+    if grad_loss is not None:
+        _need(grad_loss, "grad_loss")
+    _check(_LIB.grpo_loss_fwd_bwd(_ptr(xq), _ptr(xp), _ptr(W), dt, _ptr(targets), _ptr(mask),
+                                  _ptr(adv), S, L, H, V, beta, _ptr(grad_loss),
+                                  float(loss_scale), _ptr(loss), _ptr(saved), _ptr(terms[0]),
+                                  _ptr(terms[1]), _ptr(terms[2]), _ptr(status), _ptr(dXq),
+                                  _ptr(dW) if need_dW else None, int(bool(accumulate_dW)),
+                                  _ptr(found_inf), _opts(opts), _ptr(workspace),
+                                  workspace.numel(), _stream(stream)))
+    return {"loss": loss, "saved": saved, "logp": terms[0], "ref_logp": terms[1],
+            "kl": terms[2], "status": status, "dXq": dXq, "dW": dW if need_dW else None,
+            "found_inf": found_inf, "workspace": workspace}
+
+
+def grpo_scale_grad(dXq, grad_loss, loss_scale: float = 1.0, dW=None, found_inf=None,
+                    stream=None):
+    """dXq (and dW) *= grad_loss / loss_scale in place; returns found_inf."""
+    _need(dXq, "dXq")
+    _need(grad_loss, "grad_loss")
+    H = dXq.shape[-1]
+    rows = dXq.numel() // H
+    if found_inf is None:
+        found_inf = torch.zeros(1, dtype=torch.int32, device=dXq.device)
+    V = 0
+    if dW is not None:
+        _need(dW, "dW")
+        if dW.dtype != torch.float32 or dW.shape[-1] != H:
+            raise TypeError("dW must be float32 [V, H]")
+        V = dW.shape[0]
+    _check(_LIB.grpo_scale_grad(_ptr(dXq), _dt(dXq), rows, H, _ptr(dW), V, _ptr(grad_loss),
+                                float(loss_scale), _ptr(found_inf), _stream(stream)))
+    return found_inf
+
+
 class _GRPOLoss(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, xq, xp, W, targets, mask, adv, beta, L, loss_scale, need_dW, opts):
+    def forward(ctx, xq, xp, W, targets, mask, adv, beta, L, loss_scale, need_dW, opts,
+                single_pass):
+        ctx.L, ctx.loss_scale, ctx.need_dW, ctx.opts = L, loss_scale, need_dW, opts
+        ctx.single_pass = single_pass
+        ctx.w_dtype = W.dtype
+        if single_pass:
+            # gradients for an upstream gradient of 1 now; backward only rescales them
+            out = grpo_loss_fwd_bwd(xq, xp, W, targets, mask, adv, beta, L, None, 1.0,
+                                    need_dW=need_dW and ctx.needs_input_grad[2],
+                                    want_terms=False, opts=opts)
+            ctx.grads = (out["dXq"], out["dW"], out["found_inf"])
+            ctx.mark_non_differentiable(out["status"])
+            return out["loss"][0], out["status"]
         out = grpo_loss_fwd(xq, xp, W, targets, mask, adv, beta, L, want_terms=False,
                             opts=opts)
         ctx.save_for_backward(xq, W, targets, mask, out["saved"])
-        ctx.L, ctx.loss_scale, ctx.need_dW, ctx.opts = L, loss_scale, need_dW, opts
         ctx.workspace = out["workspace"]
         ctx.mark_non_differentiable(out["status"])
         return out["loss"][0], out["status"]
 
     @staticmethod
     def backward(ctx, grad_loss, _grad_status):
-        xq, W, targets, mask, saved = ctx.saved_tensors
         g = grad_loss.reshape(1).to(torch.float32).contiguous()
+        if ctx.single_pass:
+            dX, dW32, found = ctx.grads
+            ctx.grads = None
+            grpo_scale_grad(dX, g, ctx.loss_scale, dW=dW32, found_inf=found)
+            ctx.found_inf = found
+            dW = dW32.to(ctx.w_dtype) if dW32 is not None else None
+            return dX, None, dW, None, None, None, None, None, None, None, None, None
+        xq, W, targets, mask, saved = ctx.saved_tensors
         out = grpo_loss_bwd(xq, W, targets, mask, saved, ctx.L, g, ctx.loss_scale,
                             need_dW=ctx.need_dW and W.requires_grad, workspace=None,
                             opts=ctx.opts)
         dW = out["dW"].to(W.dtype) if out["dW"] is not None else None
         ctx.found_inf = out["found_inf"]
-        return out["dXq"], None, dW, None, None, None, None, None, None, None, None
+        return out["dXq"], None, dW, None, None, None, None, None, None, None, None, None
 
 
 def grpo_loss(xq, xp, W, targets, mask, rewards, beta: float = 0.04, eps: float = 1e-4,
               loss_scale: float = 1.0, need_dW: bool = False, L: int | None = None,
-              opts=None):
+              opts=None, single_pass: bool = False):
     """The GRPO loss with autograd.  xq, xp [S, L, H] (or [S*L, H] with L), W [V, H],
     targets int64 and mask (bool/uint8) of S*L elements, rewards fp32 [S] or [B, G(, K)].
 
     Returns (loss, status).  Gradients flow to xq (and W when need_dW); xp and the
     reference path get none.  With loss scaling, back-propagate loss * loss_scale and pass
     the same loss_scale here: the returned gradients are unscaled.  opts selects the loss
-    variant (see options())."""
+    variant (see options()).  single_pass computes the gradients during the forward
+    (grpo_loss_fwd_bwd) and keeps them, X_q-sized (plus dW), until the backward, which then
+    only applies the upstream gradient."""
     r = rewards.float()
     if r.dim() == 1:
         r = r.unsqueeze(0)
@@ -250,4 +349,4 @@ def grpo_loss(xq, xp, W, targets, mask, rewards, beta: float = 0.04, eps: float 
     y = targets.reshape(-1).contiguous()
     return _GRPOLoss.apply(xq.contiguous(), xp.contiguous(), W.contiguous(), y, m, adv,
                            float(beta), L if xq.dim() == 2 else xq.shape[1], float(loss_scale),
-                           bool(need_dW), opts)
+                           bool(need_dW), opts, bool(single_pass))

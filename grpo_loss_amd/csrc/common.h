@@ -73,8 +73,8 @@ struct Plan {
   float inv_tau;    // 1 / temperature
   float scale2;     // log2(e) / temperature: logits -> log2 units of the softmax argument
   // byte offsets into the workspace
-  size_t off_ntok, off_idx, off_rank, off_part, off_lsum, off_seq, off_T, off_WT, off_TT,
-      off_XgT, off_dxp, total;
+  size_t off_ntok, off_idx, off_rank, off_part, off_lsum, off_seq, off_T, off_pm, off_WT,
+      off_TT, off_XgT, off_dxp, total;
 };
 
 constexpr int kTokTile = 256;    // rows per token tile of the MFMA kernels
@@ -123,6 +123,21 @@ hipError_t launch_merge(const Plan& p, const void* ws, const int64_t* targets,
                         const uint8_t* mask, const float* adv, float beta, float* saved,
                         float* logp, float* ref_logp, float* kl, int32_t* status, float* loss,
                         hipStream_t st);
+// Single-pass forward: merge of compact rows [c0, c0 + R) (R = Plan::R), the zeroing of
+// masked rows' outputs, and the loss reduction (compact = 1: block sums over loss rows).
+hipError_t launch_merge_rows(const Plan& p, const void* ws, int64_t c0, const int64_t* targets,
+                             const uint8_t* mask, const float* adv, float beta, float* saved,
+                             float* logp, float* ref_logp, float* kl, int32_t* status,
+                             hipStream_t st);
+hipError_t launch_zero_masked_outputs(const Plan& p, const uint8_t* mask, float* saved,
+                                      float* logp, float* ref_logp, float* kl, hipStream_t st);
+hipError_t launch_loss_final(const Plan& p, const void* ws, int compact, int32_t* status,
+                             float* loss, hipStream_t st);
+// x *= grad_loss / loss_scale over n16 elements of the storage type and nW fp32 elements;
+// found_inf on a non-finite result.  Nothing happens when the factor is exactly 1.
+hipError_t launch_scale_grad(void* dX, int dtype, int64_t nX, float* dW, int64_t nW,
+                             const float* grad_loss, float loss_scale, int32_t* found_inf,
+                             hipStream_t st);
 // Loss rows per sequence and the number of sequences that have any (sequence-mean
 // normalisation only).
 hipError_t launch_seq_counts(const Plan& p, const uint8_t* mask, void* ws, hipStream_t st);

@@ -72,6 +72,7 @@ struct MergeArgs {
   float beta, inv_tau;
   const int32_t* ntok;
   const int32_t* rank;
+  const int32_t* idx;
   const float* part;
   const int32_t* seq;   // [S] loss rows per sequence, then the count of non-empty sequences
   int64_t S;
@@ -84,9 +85,10 @@ struct MergeArgs {
   float* kl_out;
   int32_t* status;
   double* lsum;
+  int64_t c0, R;        // chunked merge: compact rows [c0, c0 + R)
 };
 
-// Per row t (grid over all rows, masked rows included so their outputs are zeroed):
+// Per loss row t (compact index r):
 //   q = z_q[y] / tau - lse_q, ref = z_p[y] / tau - lse_p, d = ref - q,
 //   KL and dKL/dq of the chosen estimator:
 //     reverse    expm1(d) - d               -expm1(d)
@@ -95,81 +97,128 @@ struct MergeArgs {
 //   l = beta * KL - A_s                      (loss value; the ratio is 1 at q = sg(q))
 //   g = w_t (-A_s [if detached] + beta dKL/dq)   (dloss/dq)
 // with w_t = 1 / N_tok (token mean) or 1 / (n_s S') (sequence mean: n_s loss rows of the
-// row's sequence, S' sequences with any) [Long-context GRPO, §4].  Each block reduces
-// m_t * l_t (token mean) or m_t * l_t / n_s (sequence mean) in fp64 by a fixed tree into
-// lsum[block]; the final kernel adds the block sums in index order.
-__global__ void __launch_bounds__(kMergeBlock) merge_kernel(MergeArgs a) {
-  __shared__ double red[kMergeBlock];
-  const int64_t t = (int64_t)blockIdx.x * kMergeBlock + threadIdx.x;
+// row's sequence, S' sequences with any) [Long-context GRPO, §4].  used0 / used1: the
+// vocabulary phases the forward wrote for the policy and the reference side.  Returns
+// the row's contribution to the loss sum (l, or l / n_s for the sequence mean) and ORs
+// status bits into *flags.
+__device__ inline double merge_row(const MergeArgs& a, int64_t t, int64_t r, int used0,
+                                   int used1, int32_t ntok, int* flags) {
   const int64_t N = a.N;
-  const int32_t ntok = *a.ntok;
-  const float denom = (float)(ntok > 1 ? ntok : 1);
-  // partial slots written by the forward: all of them, or the adaptive phase count
-  const int used = a.adaptive ? fwd_phases(2 * (((int64_t)ntok + 255) / 256), (a.V + 255) / 256)
-                              : a.phases;
-  double ell_d = 0.0;
-  int flags = 0;
-  if (t < N) {
-    float4 sv = make_float4(0.f, 0.f, 0.f, 0.f);
-    float q = 0.f, ref = 0.f, klv = 0.f;
-    if (a.mask[t]) {
-      const int64_t r = a.rank[t];
-      const int64_t PN = (int64_t)a.phases * N;
-      const float* pm = a.part;
-      const float* ps = a.part + 2 * PN;
-      const float* pz = a.part + 4 * PN;
-      float lse_q, zq, lse_p, zp;
-      merge_side(pm, ps, pz, used, N, r, &lse_q, &zq);
-      merge_side(pm + PN, ps + PN, pz + PN, used, N, r, &lse_p, &zp);
-      const int64_t y = a.targets[t];
-      if (y < 0 || y >= a.V) flags |= GRPO_FLAG_BAD_TARGET;
-      q = zq * a.inv_tau - lse_q;
-      ref = zp * a.inv_tau - lse_p;
-      const float d = ref - q;
-      float dkl;
-      if (a.kl == GRPO_KL_FORWARD) {
-        const float em1 = expm1f(-d);
-        klv = em1 + d;
-        dkl = em1;
-      } else {
-        const float em1 = expm1f(d);
-        klv = em1 - d;
-        dkl = -em1;
-        if (a.kl == GRPO_KL_REVERSE_Q) {
-          const float eq = expf(q);
-          klv = eq * klv;
-          dkl = -d * eq;
-        }
-      }
-      const float av = a.adv[t / a.L];
-      const float num = (a.detach ? -av : 0.f) + a.beta * dkl;
-      float g;
-      ell_d = (double)a.beta * (double)klv - (double)av;
-      if (a.norm == GRPO_NORM_SEQUENCES) {
-        const int32_t ns = a.seq[t / a.L], nseq = a.seq[a.S];
-        g = num / (float)((double)ns * (double)nseq);
-        ell_d /= (double)ns;
-      } else {
-        g = num / denom;
-      }
-      sv = make_float4(lse_q, q, ref, g);
-      if (!isfinite(lse_q) || !isfinite(q) || !isfinite(ref) || !isfinite(klv) ||
-          !isfinite(g))
-        flags |= GRPO_FLAG_NONFINITE;
+  const int64_t PN = (int64_t)a.phases * N;
+  const float* pm = a.part;
+  const float* ps = a.part + 2 * PN;
+  const float* pz = a.part + 4 * PN;
+  float lse_q, zq, lse_p, zp;
+  merge_side(pm, ps, pz, used0, N, r, &lse_q, &zq);
+  merge_side(pm + PN, ps + PN, pz + PN, used1, N, r, &lse_p, &zp);
+  const int64_t y = a.targets[t];
+  if (y < 0 || y >= a.V) *flags |= GRPO_FLAG_BAD_TARGET;
+  const float q = zq * a.inv_tau - lse_q;
+  const float ref = zp * a.inv_tau - lse_p;
+  const float d = ref - q;
+  float klv, dkl;
+  if (a.kl == GRPO_KL_FORWARD) {
+    const float em1 = expm1f(-d);
+    klv = em1 + d;
+    dkl = em1;
+  } else {
+    const float em1 = expm1f(d);
+    klv = em1 - d;
+    dkl = -em1;
+    if (a.kl == GRPO_KL_REVERSE_Q) {
+      const float eq = expf(q);
+      klv = eq * klv;
+      dkl = -d * eq;
     }
-    reinterpret_cast<float4*>(a.saved)[t] = sv;
-    if (a.logp) a.logp[t] = q;
-    if (a.ref_logp) a.ref_logp[t] = ref;
-    if (a.kl_out) a.kl_out[t] = klv;
   }
-  if (flags) atomicOr(a.status, flags);
-  red[threadIdx.x] = ell_d;
+  const float av = a.adv[t / a.L];
+  const float num = (a.detach ? -av : 0.f) + a.beta * dkl;
+  float g;
+  double ell_d = (double)a.beta * (double)klv - (double)av;
+  if (a.norm == GRPO_NORM_SEQUENCES) {
+    const int32_t ns = a.seq[t / a.L], nseq = a.seq[a.S];
+    g = num / (float)((double)ns * (double)nseq);
+    ell_d /= (double)ns;
+  } else {
+    g = num / (float)(ntok > 1 ? ntok : 1);
+  }
+  reinterpret_cast<float4*>(a.saved)[t] = make_float4(lse_q, q, ref, g);
+  if (a.logp) a.logp[t] = q;
+  if (a.ref_logp) a.ref_logp[t] = ref;
+  if (a.kl_out) a.kl_out[t] = klv;
+  if (!isfinite(lse_q) || !isfinite(q) || !isfinite(ref) || !isfinite(klv) || !isfinite(g))
+    *flags |= GRPO_FLAG_NONFINITE;
+  return ell_d;
+}
+
+__device__ inline void block_sum_store(double v, double* out) {
+  __shared__ double red[kMergeBlock];
+  red[threadIdx.x] = v;
   __syncthreads();
   for (int off = kMergeBlock / 2; off > 0; off >>= 1) {
     if (threadIdx.x < (unsigned)off) red[threadIdx.x] += red[threadIdx.x + off];
     __syncthreads();
   }
-  if (threadIdx.x == 0) a.lsum[blockIdx.x] = red[0];
+  if (threadIdx.x == 0) *out = red[0];
+}
+
+// Two-pass forward: grid over all rows (masked rows included so their outputs are
+// zeroed), both sides' partials from one launch.  Each block reduces its rows' loss terms
+// in fp64 by a fixed tree into lsum[block]; the final kernel adds the block sums in index
+// order.
+__global__ void __launch_bounds__(kMergeBlock) merge_kernel(MergeArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * kMergeBlock + threadIdx.x;
+  const int32_t ntok = *a.ntok;
+  // partial slots written by the forward: all of them, or the adaptive phase count
+  const int used = a.adaptive ? fwd_phases(2 * (((int64_t)ntok + 255) / 256), (a.V + 255) / 256)
+                              : a.phases;
+  double ell_d = 0.0;
+  int flags = 0;
+  if (t < a.N) {
+    if (a.mask[t]) {
+      ell_d = merge_row(a, t, a.rank[t], used, used, ntok, &flags);
+    } else {
+      reinterpret_cast<float4*>(a.saved)[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (a.logp) a.logp[t] = 0.f;
+      if (a.ref_logp) a.ref_logp[t] = 0.f;
+      if (a.kl_out) a.kl_out[t] = 0.f;
+    }
+  }
+  if (flags) atomicOr(a.status, flags);
+  block_sum_store(ell_d, a.lsum + blockIdx.x);
+}
+
+// Single-pass forward: compact rows [c0, min(c0 + R, ntok)) after the chunk's policy
+// partials; the reference partials come from one launch over all rows.  Blocks are
+// aligned to 256 compact rows, so lsum[r / 256] sums the same rows in the same order
+// whatever the chunking.
+__global__ void __launch_bounds__(kMergeBlock) merge_rows_kernel(MergeArgs a) {
+  const int32_t ntok = *a.ntok;
+  const int64_t r = a.c0 + (int64_t)blockIdx.x * kMergeBlock + threadIdx.x;
+  const int64_t blk0 = a.c0 / kMergeBlock + blockIdx.x;
+  if ((int64_t)blk0 * kMergeBlock >= ntok) return;   // whole block past the last row
+  const int64_t nvt = (a.V + 255) / 256;
+  const int64_t crow = (ntok - a.c0 < a.R ? ntok - a.c0 : a.R);
+  const int used0 = fwd_phases((crow + 255) / 256, nvt);
+  const int used1 = fwd_phases(((int64_t)ntok + 255) / 256, nvt);
+  double ell_d = 0.0;
+  int flags = 0;
+  if (r < ntok && r < a.c0 + a.R) ell_d = merge_row(a, a.idx[r], r, used0, used1, ntok, &flags);
+  if (flags) atomicOr(a.status, flags);
+  block_sum_store(ell_d, a.lsum + blk0);
+}
+
+// Outputs of masked rows for the single-pass forward (its merge visits loss rows only).
+__global__ void __launch_bounds__(256)
+zero_masked_outputs_kernel(int64_t N, const uint8_t* __restrict__ mask, float* __restrict__ saved,
+                           float* __restrict__ logp, float* __restrict__ ref_logp,
+                           float* __restrict__ kl) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= N || mask[t]) return;
+  reinterpret_cast<float4*>(saved)[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (logp) logp[t] = 0.f;
+  if (ref_logp) ref_logp[t] = 0.f;
+  if (kl) kl[t] = 0.f;
 }
 
 // Loss rows of each sequence: one block per sequence.
@@ -205,10 +254,12 @@ __global__ void __launch_bounds__(1024) seq_nonempty_kernel(int64_t S, int32_t* 
 constexpr int kFinalThreads = 256;
 
 __global__ void __launch_bounds__(kFinalThreads)
-loss_final_kernel(const double* __restrict__ lsum, int64_t nblocks,
-                  const int32_t* __restrict__ count_p, float* __restrict__ loss,
-                  int32_t* __restrict__ status) {
+loss_final_kernel(const double* __restrict__ lsum, int64_t nblocks, int compact,
+                  const int32_t* __restrict__ ntok_p, const int32_t* __restrict__ count_p,
+                  float* __restrict__ loss, int32_t* __restrict__ status) {
   __shared__ double red[kFinalThreads];
+  // compact: the block sums are over 256 loss rows each (single-pass forward)
+  if (compact) nblocks = ((int64_t)*ntok_p + kMergeBlock - 1) / kMergeBlock;
   double s = 0.0;
   for (int64_t i = threadIdx.x; i < nblocks; i += kFinalThreads) s += lsum[i];
   red[threadIdx.x] = s;
@@ -236,7 +287,61 @@ zero_rows_kernel(const uint8_t* __restrict__ mask, int64_t N, int64_t row_bytes,
   for (int64_t i = threadIdx.x % 64; i < n16; i += 64) row[i] = make_uint4(0, 0, 0, 0);
 }
 
+// In-place scaling of a gradient by grad_loss / loss_scale, 8 elements per thread
+// (16 bytes of 16-bit data, or two 16-byte fp32 vectors), grid-stride.
+template <class E>
+__global__ void __launch_bounds__(256)
+scale_kernel(typename E::T* __restrict__ x, int64_t n, const float* __restrict__ grad_loss,
+             float loss_scale, int32_t* __restrict__ found_inf) {
+  const float c = *grad_loss / loss_scale;
+  if (c == 1.0f) return;
+  bool bad = false;
+  const int64_t stride = (int64_t)gridDim.x * 256 * 8;
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; i < n; i += stride) {
+    if (i + 8 <= n) {
+      typename E::T h[8];
+      __builtin_memcpy(h, x + i, sizeof(h));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        h[j] = E::from_f32(E::to_f32(h[j]) * c);
+        bad |= !isfinite(E::to_f32(h[j]));
+      }
+      __builtin_memcpy(x + i, h, sizeof(h));
+    } else {
+      for (int64_t k = i; k < n; ++k) {
+        x[k] = E::from_f32(E::to_f32(x[k]) * c);
+        bad |= !isfinite(E::to_f32(x[k]));
+      }
+    }
+  }
+  if (bad) atomicOr(found_inf, 1);
+}
+
+template <class E>
+hipError_t scale_one(void* x, int64_t n, const float* grad_loss, float loss_scale,
+                     int32_t* found_inf, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 2047) / 2048;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(scale_kernel<E>, dim3((unsigned)blocks), dim3(256), 0, st,
+                     reinterpret_cast<typename E::T*>(x), n, grad_loss, loss_scale, found_inf);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_scale_grad(void* dX, int dtype, int64_t nX, float* dW, int64_t nW,
+                             const float* grad_loss, float loss_scale, int32_t* found_inf,
+                             hipStream_t st) {
+  hipError_t e;
+  switch (dtype) {
+    case GRPO_F32: e = scale_one<F32T>(dX, nX, grad_loss, loss_scale, found_inf, st); break;
+    case GRPO_BF16: e = scale_one<BF16T>(dX, nX, grad_loss, loss_scale, found_inf, st); break;
+    default: e = scale_one<F16T>(dX, nX, grad_loss, loss_scale, found_inf, st); break;
+  }
+  if (e != hipSuccess || !dW) return e;
+  return scale_one<F32T>(dW, nW, grad_loss, loss_scale, found_inf, st);
+}
 
 hipError_t launch_compact(const uint8_t* mask, int64_t N, int32_t* ntok, int32_t* idx,
                           int32_t* rank, hipStream_t st) {
@@ -269,6 +374,7 @@ hipError_t launch_merge(const Plan& p, const void* ws, const int64_t* targets,
   a.inv_tau = p.inv_tau;
   a.ntok = ws_ptr<int32_t>(w, p.off_ntok);
   a.rank = ws_ptr<int32_t>(w, p.off_rank);
+  a.idx = ws_ptr<int32_t>(w, p.off_idx);
   a.part = ws_ptr<float>(w, p.off_part);
   a.seq = ws_ptr<int32_t>(w, p.off_seq);
   a.S = p.N / p.L;
@@ -281,12 +387,68 @@ hipError_t launch_merge(const Plan& p, const void* ws, const int64_t* targets,
   a.kl_out = kl;
   a.status = status;
   a.lsum = ws_ptr<double>(w, p.off_lsum);
+  a.c0 = 0;
+  a.R = p.N;
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)nblocks), dim3(kMergeBlock), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int32_t* count = p.norm == GRPO_NORM_SEQUENCES ? a.seq + a.S : a.ntok;
-  hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(kFinalThreads), 0, st, a.lsum, nblocks,
-                     count, loss, status);
+  return launch_loss_final(p, ws, 0, status, loss, st);
+}
+
+hipError_t launch_loss_final(const Plan& p, const void* ws, int compact, int32_t* status,
+                             float* loss, hipStream_t st) {
+  void* w = const_cast<void*>(ws);
+  const int64_t nblocks = (p.N + kMergeBlock - 1) / kMergeBlock;
+  const int32_t* ntok = ws_ptr<int32_t>(w, p.off_ntok);
+  const int32_t* seq = ws_ptr<int32_t>(w, p.off_seq);
+  const int32_t* count = p.norm == GRPO_NORM_SEQUENCES ? seq + p.N / p.L : ntok;
+  hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(kFinalThreads), 0, st,
+                     ws_ptr<double>(w, p.off_lsum), nblocks, compact, ntok, count, loss, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_rows(const Plan& p, const void* ws, int64_t c0, const int64_t* targets,
+                             const uint8_t* mask, const float* adv, float beta, float* saved,
+                             float* logp, float* ref_logp, float* kl, int32_t* status,
+                             hipStream_t st) {
+  void* w = const_cast<void*>(ws);
+  MergeArgs a;
+  a.N = p.N;
+  a.L = p.L;
+  a.V = p.V;
+  a.phases = p.phases;
+  a.adaptive = 1;
+  a.kl = p.kl;
+  a.detach = p.detach;
+  a.norm = p.norm;
+  a.beta = beta;
+  a.inv_tau = p.inv_tau;
+  a.ntok = ws_ptr<int32_t>(w, p.off_ntok);
+  a.rank = ws_ptr<int32_t>(w, p.off_rank);
+  a.idx = ws_ptr<int32_t>(w, p.off_idx);
+  a.part = ws_ptr<float>(w, p.off_part);
+  a.seq = ws_ptr<int32_t>(w, p.off_seq);
+  a.S = p.N / p.L;
+  a.targets = targets;
+  a.mask = mask;
+  a.adv = adv;
+  a.saved = saved;
+  a.logp = logp;
+  a.ref_logp = ref_logp;
+  a.kl_out = kl;
+  a.status = status;
+  a.lsum = ws_ptr<double>(w, p.off_lsum);
+  a.c0 = c0;
+  a.R = p.R;
+  hipLaunchKernelGGL(merge_rows_kernel, dim3((unsigned)(p.R / kMergeBlock)), dim3(kMergeBlock),
+                     0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_masked_outputs(const Plan& p, const uint8_t* mask, float* saved,
+                                      float* logp, float* ref_logp, float* kl, hipStream_t st) {
+  hipLaunchKernelGGL(zero_masked_outputs_kernel, dim3((unsigned)((p.N + 255) / 256)), dim3(256),
+                     0, st, p.N, mask, saved, logp, ref_logp, kl);
   return hipGetLastError();
 }
 

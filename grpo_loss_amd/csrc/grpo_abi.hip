@@ -19,6 +19,11 @@ hipError_t mfma_backward(const Plan& p, void* ws, const void* Xq, const void* W,
                          const int64_t* targets, const float* saved, const float* grad_loss,
                          float loss_scale, void* dX, float* dW, int accumulate_dW,
                          int32_t* found_inf, hipStream_t st);
+hipError_t mfma_fused(const Plan& p, void* ws, const void* Xq, const void* Xp, const void* W,
+                      const int64_t* targets, const uint8_t* mask, const float* adv, float beta,
+                      float* saved, float* logp, float* ref_logp, float* kl, int32_t* status,
+                      float* loss, const float* grad_loss, float loss_scale, void* dX, float* dW,
+                      int accumulate_dW, int32_t* found_inf, hipStream_t st);
 
 namespace {
 
@@ -107,6 +112,8 @@ bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_d
   o = align_up(o + (size_t)(S + 1) * 4);
   p->off_T = o;
   o = align_up(o + (size_t)p->R * p->Vpad * p->esize);
+  p->off_pm = o;
+  if (p->mfma) o = align_up(o + (size_t)p->R * (p->Vpad / kVocTile) * 4);
   p->off_WT = o;
   if (p->mfma) o = align_up(o + (size_t)H * p->Vpad * p->esize);
   p->off_TT = o;
@@ -250,6 +257,73 @@ int grpo_loss_bwd(const void* Xq, const void* W, grpo_dtype dtype, const int64_t
              : simple_backward(p, ws, Xq, W, targets, saved, grad_loss, ls_eff, dXq, dW,
                                accumulate_dW, found_inf, st);
   if (be != hipSuccess) return GRPO_ERR_HIP;
+  return GRPO_OK;
+}
+
+int grpo_loss_fwd_bwd(const void* Xq, const void* Xp, const void* W, grpo_dtype dtype,
+                      const int64_t* targets, const uint8_t* mask, const float* adv, int64_t S,
+                      int64_t L, int64_t H, int64_t V, float beta, const float* grad_loss,
+                      float loss_scale, float* loss, float* saved, float* logp_out,
+                      float* ref_logp_out, float* kl_out, int32_t* status, void* dXq, float* dW,
+                      int accumulate_dW, int32_t* found_inf, const grpo_options* opts,
+                      void* workspace, size_t workspace_bytes, grpo_stream_t stream) {
+  if (!Xq || !Xp || !W || !targets || !mask || !adv || !loss || !saved || !status || !dXq ||
+      !found_inf || !workspace)
+    return GRPO_ERR_NULL;
+  if (!valid_dtype(dtype)) return GRPO_ERR_DTYPE;
+  if (!sizes_ok(S, L, H, V) || !isfinite(beta) || !(loss_scale > 0.0f) || !isfinite(loss_scale))
+    return GRPO_ERR_SHAPE;
+  if (!aligned16(Xq) || !aligned16(Xp) || !aligned16(W) || !aligned16(saved) ||
+      !aligned16(dXq) || (dW && !aligned16(dW)) || !aligned16(workspace))
+    return GRPO_ERR_ALIGN;
+  if (!options_ok(opts)) return GRPO_ERR_OPTIONS;
+  Plan p;
+  if (!make_plan(S, L, H, V, dtype, dW != nullptr, &p)) return GRPO_ERR_SHAPE;
+  plan_options(opts, &p);
+  const float ls_eff = opts ? loss_scale * opts->temperature : loss_scale;
+  if (!(ls_eff > 0.0f) || !isfinite(ls_eff)) return GRPO_ERR_SHAPE;
+  if (workspace_bytes < p.total) return GRPO_ERR_WORKSPACE;
+  if (!device_ok()) return GRPO_ERR_DEVICE;
+  hipStream_t st = (hipStream_t)stream;
+  void* ws = workspace;
+  if (launch_compact_status(mask, p.N, ws_ptr<int32_t>(ws, p.off_ntok),
+                            ws_ptr<int32_t>(ws, p.off_idx), ws_ptr<int32_t>(ws, p.off_rank),
+                            status, st) != hipSuccess)
+    return GRPO_ERR_HIP;
+  if (p.norm == GRPO_NORM_SEQUENCES && launch_seq_counts(p, mask, ws, st) != hipSuccess)
+    return GRPO_ERR_HIP;
+  if (launch_zero_masked_rows(p, mask, dXq, st) != hipSuccess) return GRPO_ERR_HIP;
+  if (p.mfma) {
+    if (mfma_fused(p, ws, Xq, Xp, W, targets, mask, adv, beta, saved, logp_out, ref_logp_out,
+                   kl_out, status, loss, grad_loss, ls_eff, dXq, dW, accumulate_dW, found_inf,
+                   st) != hipSuccess)
+      return GRPO_ERR_HIP;
+    return GRPO_OK;
+  }
+  // fp32 (or H not a multiple of 256): the two passes back to back
+  if (simple_fwd_partials(p, ws, Xq, Xp, W, targets, st) != hipSuccess) return GRPO_ERR_HIP;
+  if (launch_merge(p, ws, targets, mask, adv, beta, saved, logp_out, ref_logp_out, kl_out,
+                   status, loss, st) != hipSuccess)
+    return GRPO_ERR_HIP;
+  if (simple_backward(p, ws, Xq, W, targets, saved, grad_loss, ls_eff, dXq, dW, accumulate_dW,
+                      found_inf, st) != hipSuccess)
+    return GRPO_ERR_HIP;
+  return GRPO_OK;
+}
+
+int grpo_scale_grad(void* dXq, grpo_dtype dtype, int64_t rows, int64_t H, float* dW, int64_t V,
+                    const float* grad_loss, float loss_scale, int32_t* found_inf,
+                    grpo_stream_t stream) {
+  if (!dXq || !grad_loss || !found_inf) return GRPO_ERR_NULL;
+  if (!valid_dtype(dtype)) return GRPO_ERR_DTYPE;
+  if (rows < 0 || H < 1 || H % 8 != 0 || (dW && V < 1) || !(loss_scale > 0.0f) ||
+      !isfinite(loss_scale))
+    return GRPO_ERR_SHAPE;
+  if (!aligned16(dXq) || (dW && !aligned16(dW))) return GRPO_ERR_ALIGN;
+  if (!device_ok()) return GRPO_ERR_DEVICE;
+  if (launch_scale_grad(dXq, dtype, rows * H, dW, dW ? V * H : 0, grad_loss, loss_scale,
+                        found_inf, (hipStream_t)stream) != hipSuccess)
+    return GRPO_ERR_HIP;
   return GRPO_OK;
 }
 

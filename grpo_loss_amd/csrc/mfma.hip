@@ -26,6 +26,11 @@ hipError_t mfma_backward(const Plan& p, void* ws, const void* Xq, const void* W,
                          const int64_t* targets, const float* saved, const float* grad_loss,
                          float loss_scale, void* dX, float* dW, int accumulate_dW,
                          int32_t* found_inf, hipStream_t st);
+hipError_t mfma_fused(const Plan& p, void* ws, const void* Xq, const void* Xp, const void* W,
+                      const int64_t* targets, const uint8_t* mask, const float* adv, float beta,
+                      float* saved, float* logp, float* ref_logp, float* kl, int32_t* status,
+                      float* loss, const float* grad_loss, float loss_scale, void* dX, float* dW,
+                      int accumulate_dW, int32_t* found_inf, hipStream_t st);
 
 namespace {
 
@@ -154,10 +159,28 @@ __device__ inline void mma_stage(Acc& acc, int fa, int fb, int fs, int lane) {
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima)
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// acc += A . B^T over nk k-steps of 64 (nk even and > 0).  Row i of this thread's
-// staging set is at abase + ao[i] (A) and bbase + bo[i] (B) for k-step 0.
+// 2^x with the bare v_exp_f32: results below 2^-126 come back as 0 instead of a
+// subnormal.  Used only for softmax terms exp2(z - m) with m at least the running
+// maximum, where a term that small cannot change an fp32 sum that already holds a
+// term of 1.
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// First half of the k-loop prologue: enqueue k-step 0 into stage 0.  Stage 0 is free
+// once the previous gemm_main on this workgroup has returned, so a persistent kernel
+// issues its next tile's loads before working on the previous tile's accumulators.
+__device__ inline void gemm_pre(const char* abase, const char* bbase, const Offs& ao,
+                                const Offs& bo) {
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  stage_tiles<0>(abase, bbase, ao, bo, 0, w);
+}
+
+// acc += A . B^T over nk k-steps of 64 (nk even and > 0), k-step 0 already enqueued by
+// gemm_pre.  Row i of this thread's staging set is at abase + ao[i] (A) and bbase + bo[i]
+// (B) for k-step 0.  On return every wave has finished reading stage 0 (the last barrier
+// of the loop follows its last reads), so stage 0 may be refilled at once; stage 1 is
+// refilled only after the first barrier of the next call.
 template <class E>
-__device__ inline void gemm_core(const char* abase, const char* bbase, const Offs& ao,
+__device__ inline void gemm_main(const char* abase, const char* bbase, const Offs& ao,
                                  const Offs& bo, int nk, Acc& acc) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -166,7 +189,6 @@ __device__ inline void gemm_core(const char* abase, const char* bbase, const Off
   const int fs = swz_f(fr);
   const int fa = (wm * 128 + fr) * 128;
   const int fb = (wn * kWaveN + fr) * 128;
-  stage_tiles<0>(abase, bbase, ao, bo, 0, w);
   for (int kt = 0; kt < nk; kt += 2) {
     wait_vmem();
     __syncthreads();  // stage 0 holds k-step kt; every wave is done reading stage 1
@@ -177,7 +199,13 @@ __device__ inline void gemm_core(const char* abase, const char* bbase, const Off
     if (kt + 2 < nk) stage_tiles<0>(abase, bbase, ao, bo, kt + 2, w);
     mma_stage<E, 1>(acc, fa, fb, fs, lane);
   }
-  __syncthreads();  // the caller may refill stage 0 for its next tile
+}
+
+template <class E>
+__device__ inline void gemm_core(const char* abase, const char* bbase, const Offs& ao,
+                                 const Offs& bo, int nk, Acc& acc) {
+  gemm_pre(abase, bbase, ao, bo);
+  gemm_main<E>(abase, bbase, ao, bo, nk, acc);
 }
 
 // ------------------------------------------------------------------------------ forward
@@ -191,7 +219,150 @@ struct FwdArgs {
   const int64_t* targets;
   float* part;  // [3][2 sides][kMaxPhases][N]: running max (log2 units), sum, target logit
   float scale2; // log2(e) / temperature
+  // This launch covers the loss rows [row_lo, min(row_hi, ntok)) of sides side0 ..
+  // side0 + nsides - 1 (side 0: policy X_q, side 1: reference X_p).
+  int64_t row_lo, row_hi;
+  int side0, nsides;
+  // Single-pass mode (pt != nullptr; policy rows of one chunk): every softmax term
+  // exp2(z s2 - m_vt) is also stored, in the storage type, at pt[(r - row_lo) Vpad + v]
+  // (0 for v >= V and for rows past the last loss row), with m_vt the running maximum of
+  // row r after vocabulary tile vt, identical for all lanes of the row, stored at
+  // pm[(r - row_lo) nvt + vt].  The backward's logit gradient is then
+  // onehot - pt * exp2(m_vt - lse2) without recomputing the logits.
+  char* pt;
+  float* pm;
+  int64_t Vpad;
 };
+
+// Rows and token blocks of one launch.
+struct FwdRange {
+  int64_t rhi;   // one past the last row
+  int64_t ntbs;  // token blocks per side
+  int64_t TB;    // token blocks in all
+};
+__device__ inline FwdRange fwd_range(const FwdArgs& a, int ntok) {
+  FwdRange f;
+  f.rhi = a.row_hi < ntok ? a.row_hi : ntok;
+  const int64_t nrows = f.rhi > a.row_lo ? f.rhi - a.row_lo : 0;
+  f.ntbs = (nrows + 255) / 256;
+  f.TB = a.nsides * f.ntbs;
+  return f;
+}
+
+// Staging offsets of vocabulary tile v0 (rows past V clamped to the last one).
+__device__ inline void w_offsets(int64_t v0, int64_t V, int64_t rowb, Offs& ao) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int sr = stage_row(i);
+    int64_t v = v0 + sr;
+    if (v >= V) v = V - 1;
+    ao[i] = (uint32_t)((v - v0) * rowb) + stage_chunk_bytes(sr);
+  }
+}
+
+// Staging offsets of the loss rows tok0 .. tok0 + 255 (rows from rhi on clamped to the
+// last valid one).
+__device__ inline void x_offsets(int64_t tok0, int64_t rhi, const int32_t* __restrict__ idx,
+                                 int64_t rowb, Offs& bo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int sr = stage_row(i);
+    int64_t r = tok0 + sr;
+    if (r >= rhi) r = rhi - 1;
+    bo[i] = (uint32_t)(idx[r] * rowb) + stage_chunk_bytes(sr);
+  }
+}
+
+// Where a fold stores the softmax terms of its tile (single-pass mode).
+template <class E>
+struct FoldOut {
+  typename E::T* rows;  // pt row of token column 0 of this block
+  float* pm;            // pm row of token column 0 of this block, at tile vt
+  int64_t Vpad, nvt;
+  int nvalid;           // token columns of this block that are loss rows
+};
+
+// Fold one 256 x 256 logit tile into this lane's running (max, sum of exp2) per token
+// column, kept in LDS, and catch the target logit.  kFull: every vocabulary row of the
+// tile is below V, so no row masks are evaluated.  kStore: single-pass mode; the running
+// maximum is first made common to the eight lanes (four lane groups, two m-waves) that
+// hold a token column, so the stored terms of a row share one reference per tile.
+template <class E, bool kFull, bool kStore>
+__device__ inline void fwd_fold(const Acc& acc, float s2, int vlim, int vb, int wm, int wn,
+                                int lane, int tid, float (*s_run)[kNB][kThreads],
+                                const int* s_y, float* s_zt, float (*s_cm)[256],
+                                const FoldOut<E>& fo) {
+  float cmax[kNB];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    float t = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (kFull || mb * 16 + j < vlim) t = fmaxf(t, acc[mb][nb][j]);
+    cmax[nb] = t;
+  }
+  if (kStore) {
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      float t = fmaxf(cmax[nb], __shfl_xor(cmax[nb], 16));
+      t = fmaxf(t, __shfl_xor(t, 32));
+      cmax[nb] = t;
+      if (lane < 16) s_cm[wm][wn * kWaveN + nb * 16 + lane] = t;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      const int n = wn * kWaveN + nb * 16 + (lane & 15);
+      cmax[nb] = fmaxf(s_cm[0][n], s_cm[1][n]);
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    const int n = wn * kWaveN + nb * 16 + (lane & 15);
+    const float rm = s_run[0][nb][tid];
+    const float nm = fmaxf(rm, cmax[nb] * s2);
+    float sum = rm == -INFINITY ? 0.f : s_run[1][nb][tid] * exp2_fast(rm - nm);
+    if (kStore) {
+      const bool ok = n < fo.nvalid;
+      typename E::T* trow = fo.rows + (int64_t)n * fo.Vpad + vb;
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) {
+        uint16_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float e = 0.f;
+          if (kFull || mb * 16 + j < vlim) e = exp2_fast(fmaf(acc[mb][nb][j], s2, -nm));
+          sum += e;
+          o[j] = E::from_f32(ok ? e : 0.f);
+        }
+        uint2 pk;
+        pk.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+        pk.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+        *reinterpret_cast<uint2*>(trow + mb * 16) = pk;
+      }
+      if (wm == 0 && lane < 16 && ok) fo.pm[(int64_t)n * fo.nvt] = nm;
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (kFull || mb * 16 + j < vlim) sum += exp2_fast(fmaf(acc[mb][nb][j], s2, -nm));
+    }
+    s_run[0][nb][tid] = nm;
+    s_run[1][nb][tid] = sum;
+    const int loc = s_y[n] - vb;
+    if ((unsigned)loc < 128u && (loc & 12) == 0) {  // this lane holds the target logit
+      float z = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) z = (loc == mb * 16 + j) ? acc[mb][nb][j] : z;
+      s_zt[n] = z;
+    }
+  }
+}
 
 // Persistent.  Workgroup w runs on XCD w % 8; its slot s = w / 8 picks a token block of
 // the current round and a vocabulary phase: the 32 workgroups of one XCD cover 32 / P
@@ -200,19 +371,26 @@ struct FwdArgs {
 // XCDs sweep the same W tiles together.  A workgroup keeps its token block for a whole
 // round and walks the vocabulary tiles of its phase (vt = phase, phase + P, ...), folding
 // each 256 x 256 logit tile into per-lane running (max, sum of exp2, target logit)
-// without storing it.
-template <class E>
+// without storing it (or, in single-pass mode, storing its softmax terms).  The loads of
+// each next tile are issued before the previous tile is folded, so the fold overlaps the
+// first k-step's memory latency.
+// kMode 0: both sides over all rows (two-pass forward); 1: one side over all rows
+// (single-pass reference); 2: policy rows of one chunk, softmax terms kept (single-pass).
+// Modes 0 and 1 run the same code; distinct instances keep their profiles apart.
+template <class E, int kMode>
 __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
+  constexpr bool kStore = kMode == 2;
   __shared__ float mrg[2][2][256];
   __shared__ float s_run[2][kNB][kThreads];
   __shared__ int s_y[256];
   __shared__ float s_zt[256];
+  __shared__ float s_cm[kStore ? 2 : 1][256];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / kWN, wn = w % kWN;
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
   const int slots = gridDim.x / kXcds;           // workgroups per XCD
   const int ntok = *a.ntok;
-  const int64_t ntb1 = (ntok + 255) / 256;
-  const int64_t TB = 2 * ntb1;
+  const FwdRange fr = fwd_range(a, ntok);
+  const int64_t TB = fr.TB;
   const int64_t nvt = (a.V + 255) / 256;
   const int P = fwd_phases(TB, nvt);
   const int tb_per_xcd = slots / P;
@@ -220,17 +398,30 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
   const int tbg = kXcds * tb_per_xcd;            // token blocks per round
   const int64_t rowb = a.H * 2;                  // bytes per row
   const int nk = (int)(a.H / 64);
+  const float s2 = a.scale2;
 
-  for (int64_t tb = xcd * tb_per_xcd + slot / P; tb < TB; tb += tbg) {
-    const int side = tb >= ntb1 ? 1 : 0;
-    const int64_t tok0 = (tb - side * ntb1) * 256;
+  int64_t tb = xcd * tb_per_xcd + slot / P;
+  if (tb >= TB) return;
+  // loads of the first tile.  A phase with no vocabulary tile (V below P tiles) still
+  // writes its empty partials (max -inf, sum 0) for every token block.
+  Offs ao, bo;
+  if (phase < nvt) {
+    const int sd = (int)(tb / fr.ntbs);
+    x_offsets(a.row_lo + (tb - sd * fr.ntbs) * 256, fr.rhi, a.idx, rowb, bo);
+    w_offsets(phase * 256, a.V, rowb, ao);
+    gemm_pre(a.W + phase * 256 * rowb, (a.side0 + sd) ? a.Xp : a.Xq, ao, bo);
+  }
+  for (; tb < TB; tb += tbg) {
+    const int sd = (int)(tb / fr.ntbs);
+    const int side = a.side0 + sd;
+    const int64_t tok0 = a.row_lo + (tb - sd * fr.ntbs) * 256;
     const char* X = side ? a.Xp : a.Xq;
     // per-block state lives in LDS so the GEMM loop keeps its registers: target id and
     // target logit per token column, running (max, sum) per lane and column block
     if (tid < 256) {
       const int64_t r = tok0 + tid;
       int yy = -1;
-      if (r < ntok) {
+      if (r < fr.rhi) {
         const int64_t t = a.targets[a.idx[r]];
         yy = (t >= 0 && t < a.V) ? (int)t : -1;
       }
@@ -242,55 +433,43 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
       s_run[0][nb][tid] = -INFINITY;
       s_run[1][nb][tid] = 0.f;
     }
+    FoldOut<E> fo;
+    if (kStore) {
+      fo.rows = reinterpret_cast<typename E::T*>(a.pt) + (tok0 - a.row_lo) * a.Vpad;
+      fo.pm = a.pm + (tok0 - a.row_lo) * nvt;
+      fo.Vpad = a.Vpad;
+      fo.nvt = nvt;
+      fo.nvalid = (int)(fr.rhi - tok0 < 256 ? fr.rhi - tok0 : 256);
+    }
     for (int64_t vt = phase; vt < nvt; vt += P) {
       const int64_t v0 = vt * 256;
-      Offs ao, bo;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int sr = stage_row(i);
-        const uint32_t cb = stage_chunk_bytes(sr);
-        int64_t v = v0 + sr;
-        if (v >= a.V) v = a.V - 1;
-        ao[i] = (uint32_t)((v - v0) * rowb) + cb;
-        int64_t r = tok0 + sr;
-        if (r >= ntok) r = ntok - 1;
-        bo[i] = (uint32_t)(a.idx[r] * rowb) + cb;
-      }
       Acc acc;
       zero_acc(acc);
-      gemm_core<E>(a.W + v0 * rowb, X, ao, bo, nk, acc);
-      const int vb = (int)(v0 + wm * 128 + 4 * (lane >> 4));  // vocab of acc[mb][.][j] = vb + 16 mb + j
-      const bool full = v0 + 256 <= a.V;
-      const int vlim = (int)(a.V - vb);                         // valid iff 16 mb + j < vlim
-#pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) {
-        const int n = wn * kWaveN + nb * 16 + (lane & 15);
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (full || mb * 16 + j < vlim) tmax = fmaxf(tmax, acc[mb][nb][j]);
-        const float rm = s_run[0][nb][tid];
-        const float nm = fmaxf(rm, tmax * a.scale2);
-        float sum = rm == -INFINITY ? 0.f : s_run[1][nb][tid] * exp2f(rm - nm);
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (full || mb * 16 + j < vlim) sum += exp2f(acc[mb][nb][j] * a.scale2 - nm);
-        s_run[0][nb][tid] = nm;
-        s_run[1][nb][tid] = sum;
-        const int loc = s_y[n] - vb;
-        if ((unsigned)loc < 128u && (loc & 12) == 0) {  // this lane holds the target logit
-          float z = 0.f;
-#pragma unroll
-          for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) z = (loc == mb * 16 + j) ? acc[mb][nb][j] : z;
-          s_zt[n] = z;
+      gemm_main<E>(a.W + v0 * rowb, X, ao, bo, nk, acc);
+      // enqueue the next tile: the next vocabulary tile of this block, else the first
+      // tile of this workgroup's next token block
+      {
+        int64_t nv = vt + P, ntb = tb;
+        if (nv >= nvt) {
+          nv = phase;
+          ntb = tb + tbg;
+        }
+        if (ntb < TB) {
+          const int nsd = (int)(ntb / fr.ntbs);
+          if (ntb != tb)
+            x_offsets(a.row_lo + (ntb - nsd * fr.ntbs) * 256, fr.rhi, a.idx, rowb, bo);
+          w_offsets(nv * 256, a.V, rowb, ao);
+          gemm_pre(a.W + nv * 256 * rowb, (a.side0 + nsd) ? a.Xp : a.Xq, ao, bo);
         }
       }
+      const int vb = (int)(v0 + wm * 128 + 4 * (lane >> 4));  // vocab of acc[mb][.][j] = vb + 16 mb + j
+      FoldOut<E> ft = fo;
+      if (kStore) ft.pm = fo.pm + vt;
+      if (v0 + 256 <= a.V)
+        fwd_fold<E, true, kStore>(acc, s2, 0, vb, wm, wn, lane, tid, s_run, s_y, s_zt, s_cm, ft);
+      else
+        fwd_fold<E, false, kStore>(acc, s2, (int)(a.V - vb), vb, wm, wn, lane, tid, s_run, s_y,
+                                   s_zt, s_cm, ft);
     }
     // merge the four lane groups holding each token column, then the two m-waves
 #pragma unroll
@@ -298,11 +477,11 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
       float m = s_run[0][nb][tid], sum = s_run[1][nb][tid];
 #pragma unroll
       for (int off = 16; off <= 32; off <<= 1) {
-        const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(sum, off);
+        const float m2 = __shfl_xor(m, off), s2x = __shfl_xor(sum, off);
         const float M = fmaxf(m, m2);
         sum = M == -INFINITY ? 0.f
                              : (m == -INFINITY ? 0.f : sum * exp2f(m - M)) +
-                                   (m2 == -INFINITY ? 0.f : s2 * exp2f(m2 - M));
+                                   (m2 == -INFINITY ? 0.f : s2x * exp2f(m2 - M));
         m = M;
       }
       if (lane < 16) {
@@ -315,7 +494,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
     if (tid < 256) {  // one thread per token column of the block
       const int n = tid;
       const int64_t r = tok0 + n;
-      if (r < ntok) {
+      if (r < fr.rhi) {
         const float m0 = mrg[0][0][n], m1 = mrg[1][0][n];
         const float M = fmaxf(m0, m1);
         const float sum = M == -INFINITY
@@ -331,6 +510,34 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
     }
     __syncthreads();
   }
+}
+
+// Single-pass mode, after the merge of a chunk: T = onehot(y) - pt * exp2(m_vt - lse2) in
+// place, 8 elements (16 bytes) per thread.  Rows past the last loss row stay 0.
+template <class E>
+__global__ void __launch_bounds__(256)
+fixup_kernel(int64_t Vpad, int64_t nvt, int64_t c0, const int32_t* __restrict__ ntok_p,
+             const int32_t* __restrict__ idx, const int64_t* __restrict__ targets,
+             const float* __restrict__ saved, const float* __restrict__ pm,
+             typename E::T* __restrict__ T) {
+  const int64_t row = blockIdx.y;
+  const int64_t r = c0 + row;
+  if (r >= *ntok_p) return;
+  const int64_t v = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (v >= Vpad) return;
+  const int64_t t = idx[r];
+  const float lse2 = saved[t * 4] * kLog2e;
+  const int64_t y = targets[t];
+  const float f = exp2f(pm[row * nvt + v / 256] - lse2);
+  uint4* p = reinterpret_cast<uint4*>(T + row * Vpad + v);
+  uint4 q = *p;
+  uint16_t h[8];
+  __builtin_memcpy(h, &q, 16);
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    h[j] = E::from_f32((v + j == y ? 1.f : 0.f) - E::to_f32(h[j]) * f);
+  __builtin_memcpy(&q, h, 16);
+  *p = q;
 }
 
 // ---------------------------------------------------------------------------- recompute
@@ -387,7 +594,8 @@ recompute_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t c0, int ntt, float 
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float val = 0.f;
-        if (ok && v + j < V) val = (v + j == y ? 1.f : 0.f) - exp2f(acc[mb][nb][j] * scale2 - lse2);
+        if (ok && v + j < V)
+          val = (v + j == y ? 1.f : 0.f) - exp2_fast(fmaf(acc[mb][nb][j], scale2, -lse2));
         o[j] = E::from_f32(val);
       }
       uint2 pk;
@@ -639,8 +847,68 @@ hipError_t fwd_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, con
   a.targets = targets;
   a.part = ws_ptr<float>(ws, p.off_part);
   a.scale2 = p.scale2;
-  hipLaunchKernelGGL(fwd_kernel<E>, dim3(kNumWG), dim3(kThreads), 0, st, a);
+  a.row_lo = 0;
+  a.row_hi = p.N;
+  a.side0 = 0;
+  a.nsides = 2;
+  a.pt = nullptr;
+  a.pm = nullptr;
+  a.Vpad = p.Vpad;
+  hipLaunchKernelGGL((fwd_kernel<E, 0>), dim3(kNumWG), dim3(kThreads), 0, st, a);
   return hipGetLastError();
+}
+
+// W^T [H][Vpad], zero-padded past V.
+template <class E>
+hipError_t transpose_w(const Plan& p, void* ws, const void* W, hipStream_t st) {
+  typedef typename E::T T;
+  hipLaunchKernelGGL((transpose_kernel<E, 0>), dim3((unsigned)(p.Vpad / 64), (unsigned)(p.H / 64)),
+                     dim3(256), 0, st, (const T*)W, p.H, p.V, p.H, ws_ptr<T>(ws, p.off_WT), p.Vpad,
+                     (int64_t)0, ws_ptr<int32_t>(ws, p.off_ntok), ws_ptr<int32_t>(ws, p.off_idx),
+                     (const float*)nullptr, (const float*)nullptr, 1.f);
+  return hipGetLastError();
+}
+
+// dX (and dW) of the loss rows of chunk c0 from the chunk's T = onehot - softmax.
+template <class E>
+hipError_t chunk_grads(const Plan& p, void* ws, int64_t c0, const void* Xq, const float* saved,
+                       const float* grad_loss, float loss_scale, void* dX, float* dW,
+                       int accumulate_dW, int32_t* found_inf, hipStream_t st) {
+  typedef typename E::T T;
+  const int32_t* ntok = ws_ptr<int32_t>(ws, p.off_ntok);
+  const int32_t* idx = ws_ptr<int32_t>(ws, p.off_idx);
+  T* Tb = ws_ptr<T>(ws, p.off_T);
+  T* WT = ws_ptr<T>(ws, p.off_WT);
+  const int ntt = (int)(p.R / 256), nvt = (int)(p.Vpad / 256), nht = (int)(p.H / 256);
+  hipError_t e;
+  hipLaunchKernelGGL(dx_kernel<E>, dim3((unsigned)(nht * ntt * p.ksplit)), dim3(kThreads), 0, st,
+                     p.H, p.Vpad, p.R, c0, nht, ntt, p.ksplit, ntok, idx, (const char*)WT,
+                     (const char*)Tb, saved, grad_loss, loss_scale, (T*)dX,
+                     ws_ptr<float>(ws, p.off_dxp), found_inf);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (p.ksplit > 1) {
+    hipLaunchKernelGGL(dx_reduce_kernel<E>, dim3((unsigned)p.R), dim3(256), 0, st, p.H, p.R, c0,
+                       p.ksplit, ntok, idx, (const float*)ws_ptr<float>(ws, p.off_dxp), saved,
+                       grad_loss, loss_scale, (T*)dX, found_inf);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (dW) {
+    T* TT = ws_ptr<T>(ws, p.off_TT);
+    T* XgT = ws_ptr<T>(ws, p.off_XgT);
+    hipLaunchKernelGGL((transpose_kernel<E, 0>), dim3((unsigned)(p.R / 64), (unsigned)(p.Vpad / 64)),
+                       dim3(256), 0, st, (const T*)Tb, p.Vpad, p.R, p.Vpad, TT, p.R, c0, ntok,
+                       idx, saved, grad_loss, loss_scale);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((transpose_kernel<E, 1>), dim3((unsigned)(p.R / 64), (unsigned)(p.H / 64)),
+                       dim3(256), 0, st, (const T*)Xq, p.H, p.R, p.H, XgT, p.R, c0, ntok, idx,
+                       saved, grad_loss, loss_scale);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(dw_kernel<E>, dim3((unsigned)(nht * nvt)), dim3(kThreads), 0, st, p.H,
+                       p.V, p.R, c0, nht, c0 == 0 ? accumulate_dW : 1, ntok, (const char*)XgT,
+                       (const char*)TT, dW, found_inf);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <class E>
@@ -652,48 +920,81 @@ hipError_t bwd_impl(const Plan& p, void* ws, const void* Xq, const void* W,
   const int32_t* ntok = ws_ptr<int32_t>(ws, p.off_ntok);
   const int32_t* idx = ws_ptr<int32_t>(ws, p.off_idx);
   T* Tb = ws_ptr<T>(ws, p.off_T);
-  T* WT = ws_ptr<T>(ws, p.off_WT);
-  // W^T [H][Vpad], zero-padded past V
-  hipLaunchKernelGGL((transpose_kernel<E, 0>), dim3((unsigned)(p.Vpad / 64), (unsigned)(p.H / 64)),
-                     dim3(256), 0, st, (const T*)W, p.H, p.V, p.H, WT, p.Vpad, (int64_t)0, ntok,
-                     idx, saved, grad_loss, loss_scale);
-  hipError_t e = hipGetLastError();
+  hipError_t e = transpose_w<E>(p, ws, W, st);
   if (e != hipSuccess) return e;
-  const int ntt = (int)(p.R / 256), nvt = (int)(p.Vpad / 256), nht = (int)(p.H / 256);
+  const int ntt = (int)(p.R / 256), nvt = (int)(p.Vpad / 256);
   for (int64_t c0 = 0; c0 < p.N; c0 += p.R) {
     hipLaunchKernelGGL(recompute_kernel<E>, dim3((unsigned)(ntt * nvt)), dim3(kThreads), 0, st,
                        p.H, p.V, p.Vpad, c0, ntt, p.scale2, ntok, idx, (const char*)Xq, (const char*)W,
                        targets, saved, Tb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(dx_kernel<E>, dim3((unsigned)(nht * ntt * p.ksplit)), dim3(kThreads), 0, st,
-                       p.H, p.Vpad, p.R, c0, nht, ntt, p.ksplit, ntok, idx, (const char*)WT,
-                       (const char*)Tb, saved, grad_loss, loss_scale, (T*)dX,
-                       ws_ptr<float>(ws, p.off_dxp), found_inf);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (p.ksplit > 1) {
-      hipLaunchKernelGGL(dx_reduce_kernel<E>, dim3((unsigned)p.R), dim3(256), 0, st, p.H, p.R, c0,
-                         p.ksplit, ntok, idx, (const float*)ws_ptr<float>(ws, p.off_dxp), saved,
-                         grad_loss, loss_scale, (T*)dX, found_inf);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    if (dW) {
-      T* TT = ws_ptr<T>(ws, p.off_TT);
-      T* XgT = ws_ptr<T>(ws, p.off_XgT);
-      hipLaunchKernelGGL((transpose_kernel<E, 0>), dim3((unsigned)(p.R / 64), (unsigned)(p.Vpad / 64)),
-                         dim3(256), 0, st, (const T*)Tb, p.Vpad, p.R, p.Vpad, TT, p.R, c0, ntok,
-                         idx, saved, grad_loss, loss_scale);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-      hipLaunchKernelGGL((transpose_kernel<E, 1>), dim3((unsigned)(p.R / 64), (unsigned)(p.H / 64)),
-                         dim3(256), 0, st, (const T*)Xq, p.H, p.R, p.H, XgT, p.R, c0, ntok, idx,
-                         saved, grad_loss, loss_scale);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-      hipLaunchKernelGGL(dw_kernel<E>, dim3((unsigned)(nht * nvt)), dim3(kThreads), 0, st, p.H,
-                         p.V, p.R, c0, nht, c0 == 0 ? accumulate_dW : 1, ntok, (const char*)XgT,
-                         (const char*)TT, dW, found_inf);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
+    e = chunk_grads<E>(p, ws, c0, Xq, saved, grad_loss, loss_scale, dX, dW, accumulate_dW,
+                       found_inf, st);
+    if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// Single pass: reference forward over all rows, then per chunk of R loss rows the policy
+// forward that also keeps its softmax terms, the chunk's merge, the fixup of the kept
+// terms into T = onehot - softmax, and dX (and dW) from T.  The logits of each row are
+// computed once per side instead of twice for the policy.
+template <class E>
+hipError_t fused_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, const void* W,
+                      const int64_t* targets, const uint8_t* mask, const float* adv, float beta,
+                      float* saved, float* logp, float* ref_logp, float* kl, int32_t* status,
+                      float* loss, const float* grad_loss, float loss_scale, void* dX, float* dW,
+                      int accumulate_dW, int32_t* found_inf, hipStream_t st) {
+  typedef typename E::T T;
+  const int32_t* ntok = ws_ptr<int32_t>(ws, p.off_ntok);
+  const int32_t* idx = ws_ptr<int32_t>(ws, p.off_idx);
+  T* Tb = ws_ptr<T>(ws, p.off_T);
+  float* pm = ws_ptr<float>(ws, p.off_pm);
+  const int64_t nvt = (p.V + 255) / 256;
+  hipError_t e = launch_zero_masked_outputs(p, mask, saved, logp, ref_logp, kl, st);
+  if (e != hipSuccess) return e;
+  if ((e = transpose_w<E>(p, ws, W, st)) != hipSuccess) return e;
+  FwdArgs a;
+  a.N = p.N;
+  a.H = p.H;
+  a.V = p.V;
+  a.ntok = ntok;
+  a.idx = idx;
+  a.Xq = (const char*)Xq;
+  a.Xp = (const char*)Xp;
+  a.W = (const char*)W;
+  a.targets = targets;
+  a.part = ws_ptr<float>(ws, p.off_part);
+  a.scale2 = p.scale2;
+  a.Vpad = p.Vpad;
+  a.row_lo = 0;
+  a.row_hi = p.N;
+  a.side0 = 1;
+  a.nsides = 1;
+  a.pt = nullptr;
+  a.pm = nullptr;
+  hipLaunchKernelGGL((fwd_kernel<E, 1>), dim3(kNumWG), dim3(kThreads), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  for (int64_t c0 = 0; c0 < p.N; c0 += p.R) {
+    a.row_lo = c0;
+    a.row_hi = c0 + p.R;
+    a.side0 = 0;
+    a.pt = reinterpret_cast<char*>(Tb);
+    a.pm = pm;
+    hipLaunchKernelGGL((fwd_kernel<E, 2>), dim3(kNumWG), dim3(kThreads), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    e = launch_merge_rows(p, ws, c0, targets, mask, adv, beta, saved, logp, ref_logp, kl, status,
+                          st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fixup_kernel<E>, dim3((unsigned)((p.Vpad + 2047) / 2048), (unsigned)p.R),
+                       dim3(256), 0, st, p.Vpad, nvt, c0, ntok, idx, targets, saved,
+                       (const float*)pm, Tb);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    e = chunk_grads<E>(p, ws, c0, Xq, saved, grad_loss, loss_scale, dX, dW, accumulate_dW,
+                       found_inf, st);
+    if (e != hipSuccess) return e;
+  }
+  return launch_loss_final(p, ws, 1, status, loss, st);
 }
 
 }  // namespace
@@ -702,6 +1003,20 @@ hipError_t mfma_fwd_partials(const Plan& p, void* ws, const void* Xq, const void
                              const void* W, const int64_t* targets, hipStream_t st) {
   if (p.dtype == GRPO_BF16) return fwd_impl<BF16T>(p, ws, Xq, Xp, W, targets, st);
   return fwd_impl<F16T>(p, ws, Xq, Xp, W, targets, st);
+}
+
+hipError_t mfma_fused(const Plan& p, void* ws, const void* Xq, const void* Xp, const void* W,
+                      const int64_t* targets, const uint8_t* mask, const float* adv, float beta,
+                      float* saved, float* logp, float* ref_logp, float* kl, int32_t* status,
+                      float* loss, const float* grad_loss, float loss_scale, void* dX, float* dW,
+                      int accumulate_dW, int32_t* found_inf, hipStream_t st) {
+  if (p.dtype == GRPO_BF16)
+    return fused_impl<BF16T>(p, ws, Xq, Xp, W, targets, mask, adv, beta, saved, logp, ref_logp,
+                             kl, status, loss, grad_loss, loss_scale, dX, dW, accumulate_dW,
+                             found_inf, st);
+  return fused_impl<F16T>(p, ws, Xq, Xp, W, targets, mask, adv, beta, saved, logp, ref_logp, kl,
+                          status, loss, grad_loss, loss_scale, dX, dW, accumulate_dW, found_inf,
+                          st);
 }
 
 hipError_t mfma_backward(const Plan& p, void* ws, const void* Xq, const void* W,

@@ -163,6 +163,40 @@ int grpo_loss_bwd(const void* Xq, const void* W, grpo_dtype dtype, const int64_t
                   int accumulate_dW, int32_t* found_inf, const grpo_options* opts,
                   void* workspace, size_t workspace_bytes, grpo_stream_t stream);
 
+/* Forward and backward in one call: the loss and per-token terms of grpo_loss_fwd and the
+ * gradients of grpo_loss_bwd, with the policy logits of each row computed once instead of
+ * twice.  The reference side runs over all rows first; then, per chunk of rows, the policy
+ * forward keeps its softmax terms (scaled by a per-row, per-vocabulary-tile running
+ * maximum) in the workspace, the chunk's loss terms are merged, the kept terms are
+ * rescaled into onehot - softmax, and dX (and dW) follow from them.  This is the chunked
+ * algorithm of [Long-context GRPO, §3] with the backward's recomputation of the chunk's
+ * logits replaced by the forward's own; memory stays one chunk of rows times V.
+ *   Arguments: those of grpo_loss_fwd, then grad_loss / loss_scale, dXq, dW,
+ *   accumulate_dW and found_inf as in grpo_loss_bwd.  The upstream gradient must be known
+ *   when the call is enqueued (grad_loss is read on the device; NULL means 1).  An
+ *   autograd caller passes NULL and 1, keeps dXq (and dW), and applies its upstream
+ *   gradient later with grpo_scale_grad.
+ *   workspace: at least grpo_workspace_bytes(..., need_dW = (dW != NULL)).
+ * Results equal grpo_loss_fwd followed by grpo_loss_bwd up to rounding: the kept softmax
+ * terms are rounded to the storage type once more than the recomputed ones.  fp32, and H
+ * not a multiple of 256, run the two passes back to back inside this call. */
+int grpo_loss_fwd_bwd(const void* Xq, const void* Xp, const void* W, grpo_dtype dtype,
+                      const int64_t* targets, const uint8_t* mask, const float* adv, int64_t S,
+                      int64_t L, int64_t H, int64_t V, float beta, const float* grad_loss,
+                      float loss_scale, float* loss, float* saved, float* logp_out,
+                      float* ref_logp_out, float* kl_out, int32_t* status, void* dXq, float* dW,
+                      int accumulate_dW, int32_t* found_inf, const grpo_options* opts,
+                      void* workspace, size_t workspace_bytes, grpo_stream_t stream);
+
+/* Multiplies gradients in place by grad_loss / loss_scale (grad_loss: fp32 [1] on the
+ * device; nothing is done when the factor is exactly 1): dXq [rows, H] in `dtype` and,
+ * if dW is not NULL, dW fp32 [V, H].  found_inf is set to 1 on any non-finite result.
+ * For the upstream gradient of a grpo_loss_fwd_bwd call made with grad_loss = 1.
+ * H must be a multiple of 8; dXq and dW 16-byte aligned. */
+int grpo_scale_grad(void* dXq, grpo_dtype dtype, int64_t rows, int64_t H, float* dW, int64_t V,
+                    const float* grad_loss, float loss_scale, int32_t* found_inf,
+                    grpo_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -102,3 +102,36 @@ def test_options(lib):
         rc = lib.grpo_loss_bwd(p, p, 1, p, p, p, 2, 3, 64, 5, nul, ctypes.c_float(1.0), p, nul,
                                0, p, ctypes.byref(o), p, ctypes.c_size_t(1 << 40), nul)
         assert rc == -8
+
+
+def test_fused_and_scale_bad_arguments(lib):
+    p = ctypes.c_void_p(16)
+    nul = None
+    f = ctypes.c_float
+    # grpo_loss_fwd_bwd: NULL dXq, bad dtype, loss_scale 0, bad option
+    rc = lib.grpo_loss_fwd_bwd(p, p, p, 1, p, p, p, 2, 3, 64, 5, f(0.04), nul, f(1.0), p, p,
+                               nul, nul, nul, p, nul, nul, 0, p, nul, p,
+                               ctypes.c_size_t(1 << 40), nul)
+    assert rc == -1
+    rc = lib.grpo_loss_fwd_bwd(p, p, p, 9, p, p, p, 2, 3, 64, 5, f(0.04), nul, f(1.0), p, p,
+                               nul, nul, nul, p, p, nul, 0, p, nul, p,
+                               ctypes.c_size_t(1 << 40), nul)
+    assert rc == -3
+    rc = lib.grpo_loss_fwd_bwd(p, p, p, 1, p, p, p, 2, 3, 64, 5, f(0.04), nul, f(0.0), p, p,
+                               nul, nul, nul, p, p, nul, 0, p, nul, p,
+                               ctypes.c_size_t(1 << 40), nul)
+    assert rc == -2
+    import grpo_loss_amd as g
+    o = g.options(temperature=-1.0)
+    rc = lib.grpo_loss_fwd_bwd(p, p, p, 1, p, p, p, 2, 3, 64, 5, f(0.04), nul, f(1.0), p, p,
+                               nul, nul, nul, p, p, nul, 0, p, ctypes.byref(o), p,
+                               ctypes.c_size_t(1 << 40), nul)
+    assert rc == -8
+    rc = lib.grpo_loss_fwd_bwd(p, p, p, 1, p, p, p, 2, 3, 64, 5, f(0.04), nul, f(1.0), p, p,
+                               nul, nul, nul, p, p, nul, 0, p, nul, p, ctypes.c_size_t(8), nul)
+    assert rc == -5
+    # grpo_scale_grad: NULL grad, H not a multiple of 8, bad scale
+    assert lib.grpo_scale_grad(p, 1, 4, 64, nul, 0, nul, f(1.0), p, nul) == -1
+    assert lib.grpo_scale_grad(p, 1, 4, 12, nul, 0, p, f(1.0), p, nul) == -2
+    assert lib.grpo_scale_grad(p, 1, 4, 64, nul, 0, p, f(0.0), p, nul) == -2
+    assert lib.grpo_scale_grad(p, 7, 4, 64, nul, 0, p, f(1.0), p, nul) == -3

@@ -36,20 +36,26 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def run_gpu(wl, inp, need_dW=None, grad_scale=True, variant=None):
-    """advantages -> forward -> backward on the device; host copies of every output.
+def run_gpu(wl, inp, need_dW=None, grad_scale=True, variant=None, single_pass=False):
+    """advantages -> forward -> backward on the device (grpo_loss_fwd then grpo_loss_bwd,
+    or grpo_loss_fwd_bwd when single_pass); host copies of every output.
     variant: an oracle.Variant whose fields name the same options for the library."""
     g = _lib()
     d = to_device(inp)
     need_dW = wl.need_dW if need_dW is None else need_dW
     opts = None if variant is None else g.options(**dataclasses.asdict(variant))
     adv = g.grpo_advantages(d["rewards"], wl.eps)
-    f = g.grpo_loss_fwd(d["xq"], d["xp"], d["W"], d["targets"], d["mask"], adv, wl.beta, wl.L,
-                        opts=opts)
     S = wl.loss_scale
     grad = torch.full((1,), S, dtype=torch.float32, device="cuda")
-    b = g.grpo_loss_bwd(d["xq"], d["W"], d["targets"], d["mask"], f["saved"], wl.L, grad, S,
-                        need_dW=need_dW, workspace=f["workspace"], opts=opts)
+    if single_pass:
+        f = g.grpo_loss_fwd_bwd(d["xq"], d["xp"], d["W"], d["targets"], d["mask"], adv,
+                                wl.beta, wl.L, grad, S, need_dW=need_dW, opts=opts)
+        b = f
+    else:
+        f = g.grpo_loss_fwd(d["xq"], d["xp"], d["W"], d["targets"], d["mask"], adv, wl.beta,
+                            wl.L, opts=opts)
+        b = g.grpo_loss_bwd(d["xq"], d["W"], d["targets"], d["mask"], f["saved"], wl.L, grad,
+                            S, need_dW=need_dW, workspace=f["workspace"], opts=opts)
     torch.cuda.synchronize()
     out = {"adv": adv.cpu().numpy(), "loss": float(f["loss"].item()),
            "saved": f["saved"].cpu().numpy(), "logp": f["logp"].cpu().numpy(),
@@ -75,8 +81,8 @@ SMALL = {
 }
 
 
-def check_small(wl, inp, variant=None):
-    gpu = run_gpu(wl, inp, variant=variant)
+def check_small(wl, inp, variant=None, single_pass=False):
+    gpu = run_gpu(wl, inp, variant=variant, single_pass=single_pass)
     variant = oracle.DEFAULT if variant is None else variant
     adv = oracle.group_advantages(inp.rewards.numpy(), wl.eps)
     assert np.array_equal(gpu["adv"].view(np.uint32), adv.view(np.uint32)), (gpu["adv"], adv)
@@ -112,11 +118,13 @@ def check_small(wl, inp, variant=None):
     assert np.all(excess <= 0)
 
 
+@pytest.mark.parametrize("single_pass", [False, True], ids=["two-pass", "single-pass"])
 @pytest.mark.parametrize("name", list(SMALL))
-def test_parity_small(name):
+def test_parity_small(name, single_pass):
     wl = dataclasses.replace(workload_by_name(name), **SMALL[name])
-    _say(f"[parity small] {name} S={wl.S} L={wl.L} H={wl.H} V={wl.V} dtype={wl.dtype}")
-    check_small(wl, generate(wl))
+    _say(f"[parity small] {name} S={wl.S} L={wl.L} H={wl.H} V={wl.V} dtype={wl.dtype} "
+         f"single_pass={single_pass}")
+    check_small(wl, generate(wl), single_pass=single_pass)
 
 
 VARIANTS = [oracle.Variant(kl="forward"), oracle.Variant(kl="reverse_q"),
@@ -134,6 +142,59 @@ def test_parity_variants(name, vi):
     wl = dataclasses.replace(workload_by_name(name), **SMALL[name])
     _say(f"[parity variant] {name} {v}")
     check_small(wl, generate(wl), variant=v)
+
+
+@pytest.mark.parametrize("name", ["llama3.1-8b-train-bf16", "phi4-f16"])
+@pytest.mark.parametrize("vi", [0, 1, 3, 5])
+def test_parity_variants_single_pass(name, vi):
+    v = VARIANTS[vi]
+    wl = dataclasses.replace(workload_by_name(name), **SMALL[name])
+    _say(f"[parity variant single-pass] {name} {v}")
+    check_small(wl, generate(wl), variant=v, single_pass=True)
+
+
+def test_single_pass_matches_two_pass():
+    """Both paths on one input: the forward terms agree to fp32 rounding (only the order of
+    the log-sum-exp partials differs), the gradients to the extra bf16 rounding of the
+    kept softmax terms.  Three chunks of rows with a ragged last one."""
+    wl = dataclasses.replace(workload_by_name("llama3.1-8b-train-bf16"), G=4, L=2600,
+                             H=1024, prefix=100, comp_min=2000, comp_max=2500)
+    inp = generate(wl)
+    _say(f"[single vs two pass] S={wl.S} L={wl.L} loss rows {int(inp.mask.sum())}")
+    a = run_gpu(wl, inp)
+    b = run_gpu(wl, inp, single_pass=True)
+    m = inp.mask.numpy() == 1
+    assert a["status"] == b["status"] == 0 and a["found_inf"] == b["found_inf"] == 0
+    assert abs(a["loss"] - b["loss"]) <= 1e-5 * abs(a["loss"])
+    for k in ("logp", "ref_logp", "kl"):
+        err = np.abs(a[k][m] - b[k][m]).max()
+        _say(f"  {k} max abs diff {err:.2e}")
+        assert err <= 1e-4
+    e = rel_l2(b["dX"], a["dX"])
+    _say(f"  dX rel-L2 between paths {e:.2e}")
+    assert e <= 5e-3
+    assert np.all(b["dX"][~m] == 0.0)
+    e = rel_l2(b["dW"], a["dW"])
+    _say(f"  dW rel-L2 between paths {e:.2e}")
+    assert e <= 5e-3
+
+
+def test_scale_grad():
+    g = _lib()
+    x = torch.randn(37, 64, device="cuda").to(torch.bfloat16)
+    w = torch.randn(5, 64, device="cuda")
+    x0, w0 = x.clone(), w.clone()
+    found = torch.zeros(1, dtype=torch.int32, device="cuda")
+    g.grpo_scale_grad(x, torch.full((1,), 1.0, device="cuda"), 1.0, dW=w, found_inf=found)
+    assert torch.equal(x, x0) and torch.equal(w, w0)          # factor 1: untouched
+    g.grpo_scale_grad(x, torch.full((1,), 6.0, device="cuda"), 2.0, dW=w, found_inf=found)
+    torch.cuda.synchronize()
+    assert torch.equal(x, (x0.float() * 3.0).to(torch.bfloat16))
+    assert torch.equal(w, w0 * 3.0)
+    assert int(found.item()) == 0
+    g.grpo_scale_grad(x, torch.full((1,), float("inf"), device="cuda"), 1.0, found_inf=found)
+    torch.cuda.synchronize()
+    assert int(found.item()) == 1
 
 
 @pytest.mark.parametrize("B,G,K", [(1, 8, 1), (3, 4, 2), (37, 8, 3), (300, 16, 1), (1, 2, 1)])
@@ -168,6 +229,23 @@ def test_no_loss_tokens_and_bad_target():
     t = int(np.nonzero(inp.mask.numpy())[0][3])
     inp.targets[t] = wl.V + 5
     out = run_gpu(wl, inp)
+    assert out["status"] & 2
+
+
+@pytest.mark.parametrize("single_pass", [False, True], ids=["two-pass", "single-pass"])
+def test_no_loss_tokens_and_bad_target_mfma(single_pass):
+    """The same degenerate cases on the bf16 MFMA path, where the single-pass call runs its
+    chunked kernels."""
+    wl = dataclasses.replace(workload_by_name("qwen2.5-1.5b-bf16"), **SMALL["qwen2.5-1.5b-bf16"])
+    inp = generate(wl)
+    inp.mask[:] = 0
+    out = run_gpu(wl, inp, need_dW=True, single_pass=single_pass)
+    assert out["loss"] == 0.0 and out["status"] == 0
+    assert np.all(out["dX"] == 0.0) and np.all(out["dW"] == 0.0)
+    inp = generate(wl)
+    t = int(np.nonzero(inp.mask.numpy())[0][3])
+    inp.targets[t] = wl.V + 5
+    out = run_gpu(wl, inp, single_pass=single_pass)
     assert out["status"] & 2
 
 
@@ -217,11 +295,12 @@ def _sample_rows(mask, L, per_seq=6, seed=0):
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_parity_full_sampled(name):
+@pytest.mark.parametrize("single_pass", [False, True], ids=["two-pass", "single-pass"])
+def test_parity_full_sampled(name, single_pass):
     wl = workload_by_name(name)
-    _say(f"[parity full] {name} S={wl.S} L={wl.L} H={wl.H} V={wl.V}")
+    _say(f"[parity full] {name} S={wl.S} L={wl.L} H={wl.H} V={wl.V} single_pass={single_pass}")
     inp = generate(wl)
-    gpu = run_gpu(wl, inp)
+    gpu = run_gpu(wl, inp, single_pass=single_pass)
     assert gpu["status"] == 0 and gpu["found_inf"] == 0
     mask = inp.mask.numpy()
     m = mask == 1
@@ -329,3 +408,31 @@ def test_autograd_wrapper():
     dX = np.zeros((wl.N, wl.H))
     dX[b["rows"]] = b["dX"]
     assert rel_l2(xq.grad.float().reshape(wl.N, wl.H).cpu().numpy(), dX) <= 1e-2
+
+
+def test_autograd_single_pass():
+    """grpo_loss(single_pass=True): gradients computed in the forward, rescaled by the
+    upstream gradient in the backward (here 3, and a trainable head)."""
+    g = _lib()
+    wl = dataclasses.replace(workload_by_name("llama3.1-8b-train-bf16"),
+                             **SMALL["llama3.1-8b-train-bf16"])
+    inp = generate(wl)
+    d = to_device(inp)
+    xq = d["xq"].view(wl.S, wl.L, wl.H).clone().requires_grad_(True)
+    xp = d["xp"].view(wl.S, wl.L, wl.H)
+    W = d["W"].clone().requires_grad_(True)
+    loss, status = g.grpo_loss(xq, xp, W, d["targets"], d["mask"], d["rewards"], beta=wl.beta,
+                               eps=wl.eps, need_dW=True, single_pass=True)
+    (3.0 * loss).backward()
+    torch.cuda.synchronize()
+    adv = oracle.group_advantages(inp.rewards.numpy(), wl.eps)
+    f = oracle.forward(inp.xq, inp.xp, inp.W, inp.targets.numpy(), inp.mask.numpy(), adv,
+                       wl.L, wl.beta)
+    b = oracle.backward(inp.xq, inp.W, inp.targets.numpy(), inp.mask.numpy(), f, grad_loss=3.0,
+                        need_dW=True)
+    assert int(status.item()) == 0
+    assert abs(float(loss.item()) - f["loss"]) <= 1e-3 * abs(f["loss"])
+    dX = np.zeros((wl.N, wl.H))
+    dX[b["rows"]] = b["dX"]
+    assert rel_l2(xq.grad.float().reshape(wl.N, wl.H).cpu().numpy(), dX) <= 1e-2
+    assert rel_l2(W.grad.float().cpu().numpy(), b["dW"]) <= 1e-2
