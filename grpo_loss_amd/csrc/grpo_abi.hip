@@ -82,12 +82,15 @@ bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_d
   p->need_dW = need_dW ? 1 : 0;
   p->phases = kMaxPhases;
   plan_options(nullptr, p);
-  // 16-bit operands with H a multiple of 256 take the MFMA kernels (256-wide tiles over H;
-  // hidden-state rows addressed by 32-bit byte offsets, so S*L*H*2 must stay below 4 GiB);
+  // 16-bit operands with H a multiple of 256 take the MFMA kernels (256-wide tiles over H);
   // everything else takes the fp32-accumulating FMA kernels.
-  p->mfma = dtype != GRPO_F32 && H % 256 == 0 && (uint64_t)p->N * H * 2 < ((uint64_t)1 << 32);
   const int64_t Npad = (p->N + kTokTile - 1) / kTokTile * kTokTile;
   p->R = Npad < 4096 ? Npad : 4096;
+  // (the MFMA kernels address each operand with 32-bit byte offsets from a buffer base:
+  // X, W, W^T and one chunk of onehot - softmax must each stay below 4 GiB)
+  const uint64_t k4G = (uint64_t)1 << 32;
+  p->mfma = dtype != GRPO_F32 && H % 256 == 0 && (uint64_t)p->N * H * 2 < k4G &&
+            (uint64_t)p->Vpad * H * 2 < k4G && (uint64_t)p->R * p->Vpad * 2 < k4G;
   p->ksplit = 1;
   if (p->mfma) {
     // split the dX reduction over the vocabulary when one chunk has too few output tiles

@@ -8,7 +8,7 @@
 // needs all 256 AGPRs and the register allocator then shuffles accumulators between
 // MFMAs), and one wave's LDS and barrier latency is covered by its neighbour's MFMAs.
 // Operand tiles go straight from global memory
-// into a double-buffered LDS ring (2 x 64 KB) with global_load_lds_dwordx4, so no
+// into a double-buffered LDS ring (2 x 64 KB) with buffer_load_dwordx4 ... lds, so no
 // registers are spent on staging; each 128-byte row's eight 16-byte chunks are
 // XOR-swizzled so fragment reads are free of bank conflicts.
 //
@@ -69,7 +69,7 @@ constexpr int kXcds = 8;
 // (conflict free when the LDS serves 8 lanes x 16 B per pass over 32 banks), and the 16
 // (row parity, position) pairs are distinct (conflict free for 16 lanes over 64 banks).
 //
-// Tiles are filled with global_load_lds_dwordx4: one wave instruction writes 1 KB of LDS
+// Tiles are filled with buffer_load_dwordx4 ... lds: one wave instruction writes 1 KB of LDS
 // (8 rows) with lane l landing at byte 16 l.  Wave w's instruction i covers rows
 // 32 w + 8 i .. + 7, so lane l lands in row r = 32 w + 8 i + l / 8 at position l % 8 and
 // therefore loads chunk (l % 8) ^ f(r) of that row: the swizzle is applied to the source
@@ -94,7 +94,14 @@ __device__ inline uint32_t stage_chunk_bytes(int r) {
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void gbl_void_t;
+// An operand as a buffer resource: base, extent in bytes (loads past it return 0), and the
+// raw-buffer format word of this GPU family.  The tile loads then take one 32-bit VGPR
+// offset per lane and the k-step offset in an SGPR, instead of 64-bit per-lane addresses.
+typedef __amdgpu_buffer_rsrc_t Src;
+__device__ inline Src make_src(const char* base, const char* end) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0,
+                                           (int)(uint32_t)(end - base), 0x00020000);
+}
 
 typedef f32x4 Acc[kMB][kNB];
 typedef uint32_t Offs[4];
@@ -108,18 +115,16 @@ __device__ inline void zero_acc(Acc& acc) {
 
 // Enqueue the direct-to-LDS loads of k-step kt (byte 128 kt of every row) into stage S.
 template <int S>
-__device__ inline void stage_tiles(const char* abase, const char* bbase, const Offs& ao,
-                                   const Offs& bo, int kt, int w) {
+__device__ inline void stage_tiles(Src ra, Src rb, const Offs& ao, const Offs& bo, int kt,
+                                   int w) {
   char* sa = (S ? g_sA1 : g_sA0) + w * 4 * 1024;
   char* sb = (S ? g_sB1 : g_sB0) + w * 4 * 1024;
-  const char* ab = abase + (int64_t)kt * 128;
-  const char* bb = bbase + (int64_t)kt * 128;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)(ab + ao[i]), (lds_void_t*)(sa + i * 1024), 16,
-                                     0, 0);
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)(bb + bo[i]), (lds_void_t*)(sb + i * 1024), 16,
-                                     0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(sa + i * 1024), 16, (int)ao[i],
+                                             kt * 128, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(sb + i * 1024), 16, (int)bo[i],
+                                             kt * 128, 0, 0);
   }
 }
 
@@ -168,20 +173,19 @@ __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 // First half of the k-loop prologue: enqueue k-step 0 into stage 0.  Stage 0 is free
 // once the previous gemm_main on this workgroup has returned, so a persistent kernel
 // issues its next tile's loads before working on the previous tile's accumulators.
-__device__ inline void gemm_pre(const char* abase, const char* bbase, const Offs& ao,
-                                const Offs& bo) {
+__device__ inline void gemm_pre(Src ra, Src rb, const Offs& ao, const Offs& bo) {
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  stage_tiles<0>(abase, bbase, ao, bo, 0, w);
+  stage_tiles<0>(ra, rb, ao, bo, 0, w);
 }
 
 // acc += A . B^T over nk k-steps of 64 (nk even and > 0), k-step 0 already enqueued by
-// gemm_pre.  Row i of this thread's staging set is at abase + ao[i] (A) and bbase + bo[i]
-// (B) for k-step 0.  On return every wave has finished reading stage 0 (the last barrier
+// gemm_pre.  Row i of this thread's staging set is at byte ao[i] of A's buffer and bo[i]
+// of B's for k-step 0.  On return every wave has finished reading stage 0 (the last barrier
 // of the loop follows its last reads), so stage 0 may be refilled at once; stage 1 is
 // refilled only after the first barrier of the next call.
 template <class E>
-__device__ inline void gemm_main(const char* abase, const char* bbase, const Offs& ao,
-                                 const Offs& bo, int nk, Acc& acc) {
+__device__ inline void gemm_main(Src ra, Src rb, const Offs& ao, const Offs& bo, int nk,
+                                 Acc& acc) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int wm = w / kWN, wn = w % kWN;
@@ -192,20 +196,20 @@ __device__ inline void gemm_main(const char* abase, const char* bbase, const Off
   for (int kt = 0; kt < nk; kt += 2) {
     wait_vmem();
     __syncthreads();  // stage 0 holds k-step kt; every wave is done reading stage 1
-    stage_tiles<1>(abase, bbase, ao, bo, kt + 1, w);
+    stage_tiles<1>(ra, rb, ao, bo, kt + 1, w);
     mma_stage<E, 0>(acc, fa, fb, fs, lane);
     wait_vmem();
     __syncthreads();  // stage 1 holds k-step kt + 1; every wave is done reading stage 0
-    if (kt + 2 < nk) stage_tiles<0>(abase, bbase, ao, bo, kt + 2, w);
+    if (kt + 2 < nk) stage_tiles<0>(ra, rb, ao, bo, kt + 2, w);
     mma_stage<E, 1>(acc, fa, fb, fs, lane);
   }
 }
 
 template <class E>
-__device__ inline void gemm_core(const char* abase, const char* bbase, const Offs& ao,
-                                 const Offs& bo, int nk, Acc& acc) {
-  gemm_pre(abase, bbase, ao, bo);
-  gemm_main<E>(abase, bbase, ao, bo, nk, acc);
+__device__ inline void gemm_core(Src ra, Src rb, const Offs& ao, const Offs& bo, int nk,
+                                 Acc& acc) {
+  gemm_pre(ra, rb, ao, bo);
+  gemm_main<E>(ra, rb, ao, bo, nk, acc);
 }
 
 // ------------------------------------------------------------------------------ forward
@@ -399,6 +403,8 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
   const int64_t rowb = a.H * 2;                  // bytes per row
   const int nk = (int)(a.H / 64);
   const float s2 = a.scale2;
+  const char* wend = a.W + a.V * rowb;           // operand extents for the buffer loads
+  const int64_t xbytes = a.N * rowb;
 
   int64_t tb = xcd * tb_per_xcd + slot / P;
   if (tb >= TB) return;
@@ -409,7 +415,8 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
     const int sd = (int)(tb / fr.ntbs);
     x_offsets(a.row_lo + (tb - sd * fr.ntbs) * 256, fr.rhi, a.idx, rowb, bo);
     w_offsets(phase * 256, a.V, rowb, ao);
-    gemm_pre(a.W + phase * 256 * rowb, (a.side0 + sd) ? a.Xp : a.Xq, ao, bo);
+    const char* X0 = (a.side0 + sd) ? a.Xp : a.Xq;
+    gemm_pre(make_src(a.W + phase * 256 * rowb, wend), make_src(X0, X0 + xbytes), ao, bo);
   }
   for (; tb < TB; tb += tbg) {
     const int sd = (int)(tb / fr.ntbs);
@@ -445,7 +452,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
       const int64_t v0 = vt * 256;
       Acc acc;
       zero_acc(acc);
-      gemm_main<E>(a.W + v0 * rowb, X, ao, bo, nk, acc);
+      gemm_main<E>(make_src(a.W + v0 * rowb, wend), make_src(X, X + xbytes), ao, bo, nk, acc);
       // enqueue the next tile: the next vocabulary tile of this block, else the first
       // tile of this workgroup's next token block
       {
@@ -459,7 +466,8 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
           if (ntb != tb)
             x_offsets(a.row_lo + (ntb - nsd * fr.ntbs) * 256, fr.rhi, a.idx, rowb, bo);
           w_offsets(nv * 256, a.V, rowb, ao);
-          gemm_pre(a.W + nv * 256 * rowb, (a.side0 + nsd) ? a.Xp : a.Xq, ao, bo);
+          const char* Xn = (a.side0 + nsd) ? a.Xp : a.Xq;
+          gemm_pre(make_src(a.W + nv * 256 * rowb, wend), make_src(Xn, Xn + xbytes), ao, bo);
         }
       }
       const int vb = (int)(v0 + wm * 128 + 4 * (lane >> 4));  // vocab of acc[mb][.][j] = vb + 16 mb + j
@@ -546,7 +554,7 @@ fixup_kernel(int64_t Vpad, int64_t nvt, int64_t c0, const int32_t* __restrict__ 
 // past the last loss token.
 template <class E>
 __global__ void __launch_bounds__(kThreads, 1)
-recompute_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t c0, int ntt, float scale2,
+recompute_kernel(int64_t N, int64_t H, int64_t V, int64_t Vpad, int64_t c0, int ntt, float scale2,
                  const int32_t* __restrict__ ntok_p, const int32_t* __restrict__ idx,
                  const char* __restrict__ Xq, const char* __restrict__ W,
                  const int64_t* __restrict__ targets, const float* __restrict__ saved,
@@ -573,7 +581,8 @@ recompute_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t c0, int ntt, float 
   }
   Acc acc;
   zero_acc(acc);
-  gemm_core<E>(W + v0 * rowb, Xq, ao, bo, (int)(H / 64), acc);
+  gemm_core<E>(make_src(W + v0 * rowb, W + V * rowb), make_src(Xq, Xq + N * rowb), ao, bo,
+               (int)(H / 64), acc);
   const int64_t vb = v0 + wm * 128 + 4 * (lane >> 4);
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
@@ -641,7 +650,8 @@ dx_kernel(int64_t H, int64_t Vpad, int64_t R, int64_t c0, int nht, int ntt, int 
   Acc acc;
   zero_acc(acc);
   if (kend > kbeg)
-    gemm_core<E>(WT + h0 * rowb + kbeg * 128, T + tt * 256 * rowb + kbeg * 128, ao, bo,
+    gemm_core<E>(make_src(WT + h0 * rowb + kbeg * 128, WT + H * rowb),
+                 make_src(T + tt * 256 * rowb + kbeg * 128, T + R * rowb), ao, bo,
                  (int)(kend - kbeg), acc);
   const int64_t hb = h0 + wm * 128 + 4 * (lane >> 4);
   if (ksplit == 1) {
@@ -741,7 +751,10 @@ dw_kernel(int64_t H, int64_t V, int64_t R, int64_t c0, int nht, int accumulate,
   }
   Acc acc;
   zero_acc(acc);
-  if (nk > 0) gemm_core<E>(XgT + h0 * rowb, TT + v0 * rowb, ao, bo, (int)nk, acc);
+  const int64_t Vpad = (int64_t)(gridDim.x / nht) * 256;  // rows of T^T
+  if (nk > 0)
+    gemm_core<E>(make_src(XgT + h0 * rowb, XgT + H * rowb), make_src(TT + v0 * rowb, TT + Vpad * rowb),
+                 ao, bo, (int)nk, acc);
   const int64_t hb = h0 + wm * 128 + 4 * (lane >> 4);
   bool bad = false;
 #pragma unroll
@@ -925,8 +938,8 @@ hipError_t bwd_impl(const Plan& p, void* ws, const void* Xq, const void* W,
   const int ntt = (int)(p.R / 256), nvt = (int)(p.Vpad / 256);
   for (int64_t c0 = 0; c0 < p.N; c0 += p.R) {
     hipLaunchKernelGGL(recompute_kernel<E>, dim3((unsigned)(ntt * nvt)), dim3(kThreads), 0, st,
-                       p.H, p.V, p.Vpad, c0, ntt, p.scale2, ntok, idx, (const char*)Xq, (const char*)W,
-                       targets, saved, Tb);
+                       p.N, p.H, p.V, p.Vpad, c0, ntt, p.scale2, ntok, idx, (const char*)Xq,
+                       (const char*)W, targets, saved, Tb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     e = chunk_grads<E>(p, ws, c0, Xq, saved, grad_loss, loss_scale, dX, dW, accumulate_dW,
                        found_inf, st);
