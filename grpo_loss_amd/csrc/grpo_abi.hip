@@ -28,6 +28,12 @@ hipError_t mfma_fused(const Plan& p, void* ws, const void* Xq, const void* Xp, c
 namespace {
 
 constexpr size_t kAlign = 256;
+// Rows per backward chunk (a multiple of 256): the workspace holds one chunk of
+// onehot - softmax, chunk rows x V in the storage type.
+#ifndef GRPO_CHUNK_ROWS
+#define GRPO_CHUNK_ROWS 4096
+#endif
+constexpr int64_t kChunkRows = GRPO_CHUNK_ROWS;
 constexpr int kMaxDevices = 64;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -85,7 +91,7 @@ bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_d
   // 16-bit operands with H a multiple of 256 take the MFMA kernels (256-wide tiles over H);
   // everything else takes the fp32-accumulating FMA kernels.
   const int64_t Npad = (p->N + kTokTile - 1) / kTokTile * kTokTile;
-  p->R = Npad < 4096 ? Npad : 4096;
+  p->R = Npad < kChunkRows ? Npad : kChunkRows;
   // (the MFMA kernels address each operand with 32-bit byte offsets from a buffer base:
   // X, W, W^T and one chunk of onehot - softmax must each stay below 4 GiB)
   const uint64_t k4G = (uint64_t)1 << 32;
