@@ -14,6 +14,11 @@ docstring); none is "parity unpinned".
 
 from .grpo_oracle import (  # noqa: F401
     DEFAULT,
+    E4M3_MAX,
+    dequantize_e4m3_rows,
+    e4m3_codes,
+    e4m3_round,
+    quantize_e4m3_rows,
     advantage_term,
     grad_factor,
     logits,

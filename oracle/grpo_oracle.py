@@ -150,15 +150,71 @@ def grad_factor(grad_loss: float, loss_scale: float, tau: float) -> float:
     return float(grad_loss) / float(loss_scale) / float(tau)
 
 
+E4M3_MAX = 448.0
+
+
+def e4m3_round(y) -> np.ndarray:
+    """Round to the nearest fp8 e4m3 (fn) value, ties to even, for |y| <= 448: 3 fraction
+    bits for |y| >= 2^-6, steps of 2^-9 below.  Pinned against torch's float8_e4m3fn cast
+    by test_e4m3_round_matches_torch."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    if np.any(a > E4M3_MAX):
+        raise ValueError("value outside the e4m3 range")
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    quantum = np.where(e < -6, 2.0 ** -9, 2.0 ** (e - 3))
+    return np.sign(y) * np.rint(a / quantum) * quantum
+
+
+def e4m3_codes(v) -> np.ndarray:
+    """Byte codes of e4m3 (fn) values (sign, 4 exponent bits with bias 7, 3 fraction bits;
+    exponent field 0 holds the subnormals k 2^-9; a negative value that rounds to zero is
+    -0, code 0x80)."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    sign = np.where(np.signbit(v), 0x80, 0).astype(np.int64)   # -0 keeps its sign
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0))).astype(np.int64)
+    sub = a < 2.0 ** -6
+    code_sub = np.rint(a * 512.0).astype(np.int64)
+    frac = np.rint((a / 2.0 ** e - 1.0) * 8.0).astype(np.int64)
+    code_norm = ((e + 7) << 3) | frac
+    return (sign | np.where(sub, code_sub, code_norm)).astype(np.uint8)
+
+
+def quantize_e4m3_rows(x):
+    """Per-row fp8 quantisation: amax = max |x| of the row (fp32), inv = 448 / amax and
+    s = amax / 448 (fp32 divisions; 1 and 1 for an all-zero row), q = e4m3_round(x * inv)
+    with the product rounded to fp32.  Returns (q as float64 values, codes uint8 [rows, H],
+    s float32 [rows]); the dequantised row is q * s."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.abs(x).max(axis=1)
+    nz = amax > 0
+    one = np.float32(1.0)
+    inv = np.where(nz, np.float32(E4M3_MAX) / np.where(nz, amax, one), one).astype(np.float32)
+    s = np.where(nz, amax / np.float32(E4M3_MAX), one).astype(np.float32)
+    y = (x * inv[:, None]).astype(np.float32)
+    q = e4m3_round(np.minimum(np.abs(y), np.float32(E4M3_MAX)) * np.sign(y))
+    return q, e4m3_codes(q), s
+
+
+def dequantize_e4m3_rows(x) -> np.ndarray:
+    """x rounded through the per-row fp8 quantisation, as float64."""
+    q, _, s = quantize_e4m3_rows(x)
+    return q * s.astype(np.float64)[:, None]
+
+
 @dataclass(frozen=True)
 class Variant:
     """Loss variant: KL estimator ("reverse", "forward", "reverse_q"), whether the ratio's
-    stop-gradient is kept, normalisation ("tokens" or "sequences") and the temperature the
-    logits are divided by.  The default is the loss of [Long-context GRPO, §4]."""
+    stop-gradient is kept, normalisation ("tokens" or "sequences"), the temperature the
+    logits are divided by, and fp8 logits (both sides' logits from per-row e4m3 copies of
+    X and W; the gradients' products use the original X and W, the straight-through
+    reading).  The default is the loss of [Long-context GRPO, §4]."""
     kl: str = "reverse"
     detach: bool = True
     norm: str = "tokens"
     temperature: float = 1.0
+    fp8_logits: bool = False
 
 
 DEFAULT = Variant()
@@ -278,6 +334,7 @@ def forward(xq, xp, W, targets, mask, adv, L: int, beta: float = 0.04, rows=None
     n_tok = int(mask.sum())
     wts = token_weights(mask, L, variant.norm)
     tau = float(variant.temperature)
+    Wl = dequantize_e4m3_rows(Wd) if variant.fp8_logits else Wd
     loss_rows = np.nonzero(mask)[0]
     if rows is None:
         rows = loss_rows
@@ -304,8 +361,10 @@ def forward(xq, xp, W, targets, mask, adv, L: int, beta: float = 0.04, rows=None
         xq_b = xq_rows[sel][keep]
         xp_b = xp_rows[sel][keep]
         finite = finite and _finite(xq_b) and _finite(xp_b)
-        lp_q, lse_q = log_softmax_rows(logits(xq_b, Wd, tau))
-        lp_p, _ = log_softmax_rows(logits(xp_b, Wd, tau))
+        if variant.fp8_logits:
+            xq_b, xp_b = dequantize_e4m3_rows(xq_b), dequantize_e4m3_rows(xp_b)
+        lp_q, lse_q = log_softmax_rows(logits(xq_b, Wl, tau))
+        lp_p, _ = log_softmax_rows(logits(xp_b, Wl, tau))
         q = lp_q[np.arange(len(r)), y]
         ref = lp_p[np.arange(len(r)), y]
         kl = kl_value(variant, q, ref)
@@ -353,9 +412,11 @@ def backward(xq, W, targets, mask, fwd: dict, grad_loss: float = 1.0,
     mask = np.asarray(mask).reshape(-1).astype(np.int64)
     Wd = _f64(W)
     V, H = Wd.shape
-    tau = float(fwd.get("variant", DEFAULT).temperature)
+    variant = fwd.get("variant", DEFAULT)
+    tau = float(variant.temperature)
     # dq/dz = (onehot - softmax(z / tau)) / tau: the 1/tau joins the per-row factor
     c = grad_factor(grad_loss, loss_scale, tau)
+    Wl = dequantize_e4m3_rows(Wd) if variant.fp8_logits else Wd
     if rows is None:
         rows = np.nonzero(mask)[0]
         xq_rows = _f64(xq)[rows]
@@ -377,7 +438,8 @@ def backward(xq, W, targets, mask, fwd: dict, grad_loss: float = 1.0,
             continue
         rk = r[keep]
         x = xq_rows[sel][keep]
-        lp, _ = log_softmax_rows(logits(x, Wd, tau))
+        xl = dequantize_e4m3_rows(x) if variant.fp8_logits else x
+        lp, _ = log_softmax_rows(logits(xl, Wl, tau))
         T = logit_grad(lp, targets[rk])
         gt = fwd["g"][rk]
         worst = max(worst, float(np.max(np.abs(gt * float(grad_loss) / tau)[:, None] * np.abs(T))))
