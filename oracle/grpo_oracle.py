@@ -163,7 +163,7 @@ def e4m3_round(y) -> np.ndarray:
         raise ValueError("value outside the e4m3 range")
     e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
     quantum = np.where(e < -6, 2.0 ** -9, 2.0 ** (e - 3))
-    return np.sign(y) * np.rint(a / quantum) * quantum
+    return np.copysign(np.rint(a / quantum) * quantum, y)     # the sign of zero is kept
 
 
 def e4m3_codes(v) -> np.ndarray:
@@ -193,7 +193,7 @@ def quantize_e4m3_rows(x):
     inv = np.where(nz, np.float32(E4M3_MAX) / np.where(nz, amax, one), one).astype(np.float32)
     s = np.where(nz, amax / np.float32(E4M3_MAX), one).astype(np.float32)
     y = (x * inv[:, None]).astype(np.float32)
-    q = e4m3_round(np.minimum(np.abs(y), np.float32(E4M3_MAX)) * np.sign(y))
+    q = e4m3_round(np.copysign(np.minimum(np.abs(y), np.float32(E4M3_MAX)), y))
     return q, e4m3_codes(q), s
 
 

@@ -30,7 +30,7 @@ def _values(seed, n=20000):
     v = (mag * g.choice([-1.0, 1.0], size=n)).astype(np.float32)
     # exact ties between neighbours in both ranges, and the range ends
     ties = np.array([1.0 + 1 / 16, 1.0 + 3 / 16, 2 ** -7 + 2 ** -10, 3 * 2 ** -10, 448.0,
-                     -448.0, 2 ** -6, 2 ** -9, 2 ** -10, 0.0], np.float32)
+                     -448.0, 2 ** -6, 2 ** -9, 2 ** -10, 0.0, -0.0, -2 ** -11], np.float32)
     return np.concatenate([v, ties])
 
 
