@@ -157,13 +157,18 @@ def e4m3_round(y) -> np.ndarray:
     """Round to the nearest fp8 e4m3 (fn) value, ties to even, for |y| <= 448: 3 fraction
     bits for |y| >= 2^-6, steps of 2^-9 below.  Pinned against torch's float8_e4m3fn cast
     by test_e4m3_round_matches_torch."""
-    y = np.asarray(y, dtype=np.float64)
+    y = np.asarray(y)
+    if y.dtype != np.float32:
+        y = y.astype(np.float64)
     a = np.abs(y)
     if np.any(a > E4M3_MAX):
         raise ValueError("value outside the e4m3 range")
-    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
-    quantum = np.where(e < -6, 2.0 ** -9, 2.0 ** (e - 3))
-    return np.copysign(np.rint(a / quantum) * quantum, y)     # the sign of zero is kept
+    # a = m 2^e with m in [0.5, 1): the step is 2^(max(e - 1, -6) - 3); every operation
+    # below is exact, the rounding is the one rint
+    _, e = np.frexp(a)
+    step = np.maximum(e - 1, -6) - 3
+    q = np.ldexp(np.rint(np.ldexp(a, -step)), step)
+    return np.copysign(q, y).astype(np.float64)     # the sign of zero is kept
 
 
 def e4m3_codes(v) -> np.ndarray:
@@ -181,11 +186,11 @@ def e4m3_codes(v) -> np.ndarray:
     return (sign | np.where(sub, code_sub, code_norm)).astype(np.uint8)
 
 
-def quantize_e4m3_rows(x):
+def quantize_e4m3_rows(x, codes: bool = True):
     """Per-row fp8 quantisation: amax = max |x| of the row (fp32), inv = 448 / amax and
     s = amax / 448 (fp32 divisions; 1 and 1 for an all-zero row), q = e4m3_round(x * inv)
-    with the product rounded to fp32.  Returns (q as float64 values, codes uint8 [rows, H],
-    s float32 [rows]); the dequantised row is q * s."""
+    with the product rounded to fp32.  Returns (q as float64 values, codes uint8 [rows, H]
+    or None, s float32 [rows]); the dequantised row is q * s."""
     x = np.asarray(x, dtype=np.float32)
     amax = np.abs(x).max(axis=1)
     nz = amax > 0
@@ -194,13 +199,17 @@ def quantize_e4m3_rows(x):
     s = np.where(nz, amax / np.float32(E4M3_MAX), one).astype(np.float32)
     y = (x * inv[:, None]).astype(np.float32)
     q = e4m3_round(np.copysign(np.minimum(np.abs(y), np.float32(E4M3_MAX)), y))
-    return q, e4m3_codes(q), s
+    return q, (e4m3_codes(q) if codes else None), s
 
 
-def dequantize_e4m3_rows(x) -> np.ndarray:
-    """x rounded through the per-row fp8 quantisation, as float64."""
-    q, _, s = quantize_e4m3_rows(x)
-    return q * s.astype(np.float64)[:, None]
+def dequantize_e4m3_rows(x, block: int = 128) -> np.ndarray:
+    """x rounded through the per-row fp8 quantisation, as float64 (rows in blocks)."""
+    x = np.asarray(x)
+    out = np.empty(x.shape, dtype=np.float64)
+    for i in range(0, x.shape[0], block):
+        q, _, s = quantize_e4m3_rows(x[i:i + block], codes=False)
+        out[i:i + block] = q * s.astype(np.float64)[:, None]
+    return out
 
 
 @dataclass(frozen=True)

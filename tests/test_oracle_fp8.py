@@ -171,7 +171,7 @@ def _mut_round_no_subnormals(y):
     return np.sign(y) * np.rint(a / quantum) * quantum
 
 
-def _mut_quantize_240(x):
+def _mut_quantize_240(x, codes=True):
     x = np.asarray(x, dtype=np.float32)
     amax = np.abs(x).max(axis=1)
     inv = (np.float32(240.0) / amax).astype(np.float32)
