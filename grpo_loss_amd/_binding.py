@@ -23,7 +23,8 @@ class GRPOError(RuntimeError):
 class GRPOOptions(ctypes.Structure):
     """Mirror of struct grpo_options."""
     _fields_ = [("kl_estimator", ctypes.c_int), ("detach_ratio", ctypes.c_int),
-                ("normalization", ctypes.c_int), ("temperature", ctypes.c_float)]
+                ("normalization", ctypes.c_int), ("temperature", ctypes.c_float),
+                ("fp8_logits", ctypes.c_int)]
 
 
 KL_ESTIMATORS = {"reverse": 0, "forward": 1, "reverse_q": 2}
@@ -31,18 +32,21 @@ NORMALIZATIONS = {"tokens": 0, "sequences": 1}
 
 
 def options(kl: str = "reverse", detach: bool = True, norm: str = "tokens",
-            temperature: float = 1.0) -> GRPOOptions:
+            temperature: float = 1.0, fp8_logits: bool = False) -> GRPOOptions:
     """A grpo_options value from names (the library validates the ranges)."""
     return GRPOOptions(KL_ESTIMATORS[kl], int(bool(detach)), NORMALIZATIONS[norm],
-                       float(temperature))
+                       float(temperature), int(bool(fp8_logits)))
+
+
+def _as_options(o):
+    if o is None or isinstance(o, GRPOOptions):
+        return o
+    return options(**o)
 
 
 def _opts(o):
-    if o is None:
-        return None
-    if isinstance(o, dict):
-        o = options(**o)
-    return ctypes.byref(o)
+    o = _as_options(o)
+    return None if o is None else ctypes.byref(o)
 
 
 def library_path() -> str:
@@ -62,6 +66,11 @@ def load_library():
     lib.grpo_status_string.argtypes = [ctypes.c_int]
     lib.grpo_workspace_bytes.restype = ctypes.c_size_t
     lib.grpo_workspace_bytes.argtypes = [_c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_int, ctypes.c_int]
+    lib.grpo_workspace_bytes_opts.restype = ctypes.c_size_t
+    lib.grpo_workspace_bytes_opts.argtypes = [_c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_int,
+                                              ctypes.c_int, ctypes.POINTER(GRPOOptions)]
+    lib.grpo_quantize_e4m3.restype = ctypes.c_int
+    lib.grpo_quantize_e4m3.argtypes = [_c_p, ctypes.c_int, _c_i64, _c_i64, _c_p, _c_p, _c_p]
     lib.grpo_advantages.restype = ctypes.c_int
     lib.grpo_advantages.argtypes = [_c_p, _c_i64, _c_i64, _c_i64, ctypes.c_float, ctypes.c_int,
                                     _c_p, _c_p]
@@ -121,8 +130,23 @@ def _need(t: torch.Tensor, name: str):
 
 
 def grpo_workspace_bytes(S: int, L: int, H: int, V: int, dtype: torch.dtype,
-                         need_dW: bool = False) -> int:
-    return int(_LIB.grpo_workspace_bytes(S, L, H, V, _DTYPE[dtype], int(bool(need_dW))))
+                         need_dW: bool = False, opts=None) -> int:
+    if opts is None:
+        return int(_LIB.grpo_workspace_bytes(S, L, H, V, _DTYPE[dtype], int(bool(need_dW))))
+    return int(_LIB.grpo_workspace_bytes_opts(S, L, H, V, _DTYPE[dtype], int(bool(need_dW)),
+                                              _opts(opts)))
+
+
+def grpo_quantize_e4m3(x: torch.Tensor, stream=None):
+    """Per-row e4m3 quantisation of a [rows, H] device matrix: (codes uint8 [rows, H],
+    scales float32 [rows])."""
+    _need(x, "x")
+    rows, H = x.shape
+    codes = torch.empty(rows, H, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _check(_LIB.grpo_quantize_e4m3(_ptr(x), _dt(x), rows, H, _ptr(codes), _ptr(scales),
+                                   _stream(stream)))
+    return codes, scales
 
 
 def grpo_advantages(rewards: torch.Tensor, eps: float = 1e-4, unbiased: bool = True,
@@ -169,7 +193,7 @@ def grpo_loss_fwd(xq, xp, W, targets, mask, adv, beta: float = 0.04, L: int | No
         raise TypeError("targets int64, mask uint8, adv float32 expected")
     dev = xq.device
     N = S * L
-    need = grpo_workspace_bytes(S, L, H, V, xq.dtype, False)
+    need = grpo_workspace_bytes(S, L, H, V, xq.dtype, False, opts)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     f32 = dict(dtype=torch.float32, device=dev)
@@ -198,7 +222,7 @@ def grpo_loss_bwd(xq, W, targets, mask, saved, L: int | None = None, grad_loss=N
     V = W.shape[0]
     dev = xq.device
     need_dW = need_dW or dW is not None
-    need = grpo_workspace_bytes(S, L, H, V, xq.dtype, need_dW)
+    need = grpo_workspace_bytes(S, L, H, V, xq.dtype, need_dW, opts)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if dXq is None:
@@ -240,7 +264,7 @@ def grpo_loss_fwd_bwd(xq, xp, W, targets, mask, adv, beta: float = 0.04, L: int 
     dev = xq.device
     N = S * L
     need_dW = need_dW or dW is not None
-    need = grpo_workspace_bytes(S, L, H, V, xq.dtype, need_dW)
+    need = grpo_workspace_bytes(S, L, H, V, xq.dtype, need_dW, opts)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     f32 = dict(dtype=torch.float32, device=dev)

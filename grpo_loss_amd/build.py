@@ -24,7 +24,8 @@ COMMON = ["-O3", f"--offload-arch={ARCH}", "-fPIC", "-std=c++17",
           # keep the compiler from emitting packed fp32 arithmetic
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # per-unit extra flags
-EXTRA = {"advantages.hip": ["-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt"]}
+EXACT = ["-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt"]
+EXTRA = {"advantages.hip": EXACT, "quant.hip": EXACT}
 
 
 def sources():

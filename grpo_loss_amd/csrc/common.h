@@ -52,6 +52,12 @@ struct F16T {
   }
 };
 
+// fp8 e4m3 GEMM operand (per-row scaled copies of X and W); no arithmetic of its own.
+struct FP8T {
+  typedef uint8_t T;
+  static constexpr int kBytes = 1;
+};
+
 // ------------------------------------------------------------------------ workspace plan
 // One plan describes every buffer carved out of the caller's workspace.  The host fills
 // it from the sizes alone (the number of loss tokens lives on the device).
@@ -72,9 +78,10 @@ struct Plan {
   int norm;         // grpo_normalization
   float inv_tau;    // 1 / temperature
   float scale2;     // log2(e) / temperature: logits -> log2 units of the softmax argument
+  int fp8;          // logits from per-row e4m3 copies of X and W
   // byte offsets into the workspace
   size_t off_ntok, off_idx, off_rank, off_part, off_lsum, off_seq, off_T, off_pm, off_WT,
-      off_TT, off_XgT, off_dxp, total;
+      off_TT, off_XgT, off_dxp, off_xq8, off_xp8, off_w8, off_sxq, off_sxp, off_sw, total;
 };
 
 constexpr int kTokTile = 256;    // rows per token tile of the MFMA kernels
@@ -100,7 +107,8 @@ __host__ __device__ inline int fwd_phases(int64_t token_blocks, int64_t vocab_ti
   return best;
 }
 
-bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_dW, Plan* p);
+bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_dW, Plan* p,
+               const grpo_options* opts = nullptr);
 // Copies a validated grpo_options (NULL = defaults) into the plan.
 void plan_options(const grpo_options* o, Plan* p);
 
@@ -133,6 +141,11 @@ hipError_t launch_zero_masked_outputs(const Plan& p, const uint8_t* mask, float*
                                       float* logp, float* ref_logp, float* kl, hipStream_t st);
 hipError_t launch_loss_final(const Plan& p, const void* ws, int compact, int32_t* status,
                              float* loss, hipStream_t st);
+// Per-row e4m3 quantisation of rows src[idx ? idx[r] : r] for r < (ntok ? *ntok : nmax):
+// scale[r] = amax / 448, dst[r][:] = e4m3(x * (448 / amax)), round to nearest even.
+hipError_t launch_quant_rows(int dtype, const void* src, int64_t H, const int32_t* idx,
+                             const int32_t* ntok, int64_t nmax, uint8_t* dst, float* scale,
+                             hipStream_t st);
 // x *= grad_loss / loss_scale over n16 elements of the storage type and nW fp32 elements;
 // found_inf on a non-finite result.  Nothing happens when the factor is exactly 1.
 hipError_t launch_scale_grad(void* dX, int dtype, int64_t nX, float* dW, int64_t nW,

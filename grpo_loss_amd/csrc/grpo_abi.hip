@@ -61,6 +61,7 @@ bool options_ok(const grpo_options* o) {
   if (o->detach_ratio != 0 && o->detach_ratio != 1) return false;
   if (o->normalization != GRPO_NORM_TOKENS && o->normalization != GRPO_NORM_SEQUENCES)
     return false;
+  if (o->fp8_logits != 0 && o->fp8_logits != 1) return false;
   // the softmax argument z / tau must stay finite for finite logits
   return isfinite(o->temperature) && o->temperature >= 1e-3f && o->temperature <= 1e3f;
 }
@@ -75,7 +76,8 @@ bool sizes_ok(int64_t S, int64_t L, int64_t H, int64_t V) {
 
 }  // namespace
 
-bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_dW, Plan* p) {
+bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_dW, Plan* p,
+               const grpo_options* opts) {
   if (!sizes_ok(S, L, H, V) || !valid_dtype(dtype)) return false;
   memset(p, 0, sizeof(*p));
   p->N = S * L;
@@ -87,7 +89,7 @@ bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_d
   p->esize = dtype == GRPO_F32 ? 4 : 2;
   p->need_dW = need_dW ? 1 : 0;
   p->phases = kMaxPhases;
-  plan_options(nullptr, p);
+  plan_options(opts, p);
   // 16-bit operands with H a multiple of 256 take the MFMA kernels (256-wide tiles over H);
   // everything else takes the fp32-accumulating FMA kernels.
   const int64_t Npad = (p->N + kTokTile - 1) / kTokTile * kTokTile;
@@ -131,6 +133,22 @@ bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_d
   if (p->mfma && need_dW) o = align_up(o + (size_t)H * p->R * p->esize);
   p->off_dxp = o;
   if (p->mfma && p->ksplit > 1) o = align_up(o + (size_t)p->ksplit * p->R * H * 4);
+  if (p->fp8 && !p->mfma) return false;   // fp8 logits run on the MFMA kernels only
+  p->off_xq8 = p->off_xp8 = p->off_w8 = p->off_sxq = p->off_sxp = p->off_sw = o;
+  if (p->fp8) {
+    p->off_xq8 = o;
+    o = align_up(o + (size_t)p->N * H);
+    p->off_xp8 = o;
+    o = align_up(o + (size_t)p->N * H);
+    p->off_w8 = o;
+    o = align_up(o + (size_t)V * H);
+    p->off_sxq = o;
+    o = align_up(o + (size_t)p->N * 4);
+    p->off_sxp = o;
+    o = align_up(o + (size_t)p->N * 4);
+    p->off_sw = o;
+    o = align_up(o + (size_t)V * 4);
+  }
   p->total = o;
   return true;
 }
@@ -144,6 +162,7 @@ void plan_options(const grpo_options* o, Plan* p) {
   p->norm = o->normalization;
   p->inv_tau = 1.0f / o->temperature;
   p->scale2 = kLog2e / o->temperature;
+  p->fp8 = o->fp8_logits;
 }
 
 }  // namespace grpo
@@ -173,13 +192,33 @@ void grpo_default_options(grpo_options* opts) {
   opts->detach_ratio = 1;
   opts->normalization = GRPO_NORM_TOKENS;
   opts->temperature = 1.0f;
+  opts->fp8_logits = 0;
 }
 
 size_t grpo_workspace_bytes(int64_t S, int64_t L, int64_t H, int64_t V, grpo_dtype dtype,
                             int need_dW) {
+  return grpo_workspace_bytes_opts(S, L, H, V, dtype, need_dW, nullptr);
+}
+
+size_t grpo_workspace_bytes_opts(int64_t S, int64_t L, int64_t H, int64_t V, grpo_dtype dtype,
+                                 int need_dW, const grpo_options* opts) {
+  if (!options_ok(opts)) return 0;
   Plan p;
-  if (!make_plan(S, L, H, V, dtype, need_dW, &p)) return 0;
+  if (!make_plan(S, L, H, V, dtype, need_dW, &p, opts)) return 0;
   return p.total;
+}
+
+int grpo_quantize_e4m3(const void* src, grpo_dtype dtype, int64_t rows, int64_t H,
+                       uint8_t* dst, float* scales, grpo_stream_t stream) {
+  if (!src || !dst || !scales) return GRPO_ERR_NULL;
+  if (!valid_dtype(dtype)) return GRPO_ERR_DTYPE;
+  if (rows < 0 || rows > INT32_MAX || H < 4 || H % 4 != 0) return GRPO_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(dst) & 3u) != 0) return GRPO_ERR_ALIGN;
+  if (!device_ok()) return GRPO_ERR_DEVICE;
+  if (launch_quant_rows(dtype, src, H, nullptr, nullptr, rows, dst, scales,
+                        (hipStream_t)stream) != hipSuccess)
+    return GRPO_ERR_HIP;
+  return GRPO_OK;
 }
 
 int grpo_advantages(const float* rewards, int64_t B, int64_t G, int64_t K, float eps,
@@ -211,7 +250,7 @@ int grpo_loss_fwd(const void* Xq, const void* Xp, const void* W, grpo_dtype dtyp
   Plan p;
   if (!options_ok(opts)) return GRPO_ERR_OPTIONS;
   if (!make_plan(S, L, H, V, dtype, 0, &p)) return GRPO_ERR_SHAPE;
-  plan_options(opts, &p);
+  if (!make_plan(S, L, H, V, dtype, 0, &p, opts)) return GRPO_ERR_OPTIONS;
   if (workspace_bytes < p.total) return GRPO_ERR_WORKSPACE;
   if (!device_ok()) return GRPO_ERR_DEVICE;
   hipStream_t st = (hipStream_t)stream;
@@ -247,7 +286,7 @@ int grpo_loss_bwd(const void* Xq, const void* W, grpo_dtype dtype, const int64_t
   if (!options_ok(opts)) return GRPO_ERR_OPTIONS;
   Plan p;
   if (!make_plan(S, L, H, V, dtype, dW != nullptr, &p)) return GRPO_ERR_SHAPE;
-  plan_options(opts, &p);
+  if (!make_plan(S, L, H, V, dtype, dW != nullptr, &p, opts)) return GRPO_ERR_OPTIONS;
   // dq/dz = (onehot - softmax(z / tau)) / tau: the 1 / tau joins the per-row factor
   // grad_loss / loss_scale as a larger divisor (exactly loss_scale at tau = 1)
   const float ls_eff = opts ? loss_scale * opts->temperature : loss_scale;
@@ -288,7 +327,7 @@ int grpo_loss_fwd_bwd(const void* Xq, const void* Xp, const void* W, grpo_dtype 
   if (!options_ok(opts)) return GRPO_ERR_OPTIONS;
   Plan p;
   if (!make_plan(S, L, H, V, dtype, dW != nullptr, &p)) return GRPO_ERR_SHAPE;
-  plan_options(opts, &p);
+  if (!make_plan(S, L, H, V, dtype, dW != nullptr, &p, opts)) return GRPO_ERR_OPTIONS;
   const float ls_eff = opts ? loss_scale * opts->temperature : loss_scale;
   if (!(ls_eff > 0.0f) || !isfinite(ls_eff)) return GRPO_ERR_SHAPE;
   if (workspace_bytes < p.total) return GRPO_ERR_WORKSPACE;

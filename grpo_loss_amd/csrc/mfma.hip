@@ -55,6 +55,21 @@ struct Mma<F16T> {
   }
 };
 
+typedef int v8i __attribute__((ext_vector_type(8)));
+template <>
+struct Mma<FP8T> {
+  // v_mfma_f32_16x16x128_f8f6f4 with both operands e4m3 and unit block scales: 32 bytes
+  // of k per lane and row.  Any k order shared by A and B gives the same dot product, so
+  // lane group g simply takes bytes 32 g .. 32 g + 31 of the 128-byte k-step.
+  __device__ static inline f32x4 op(uint4 a0, uint4 a1, uint4 b0, uint4 b1, f32x4 c) {
+    const v8i a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                   (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+    const v8i b = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                   (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+  }
+};
+
 constexpr int kThreads = 512;
 constexpr int kWN = 4;                        // waves along n
 constexpr int kMB = 8, kNB = 4;               // 16 x 16 blocks per wave along m, n
@@ -132,32 +147,55 @@ __device__ inline void stage_tiles(Src ra, Src rb, const Offs& ao, const Offs& b
 // wn*64 + nb*16 + (lane & 15) of B,
 // chunk ks*4 + (lane >> 4).  Both 32-wide halves' fragments are requested up front so the
 // second half's LDS reads are in flight while the first half's 64 MFMAs run.
-template <class E, int S>
+template <class G, int S>
 __device__ inline void mma_stage(Acc& acc, int fa, int fb, int fs, int lane) {
   const char* As = S ? g_sA1 : g_sA0;
   const char* Bs = S ? g_sB1 : g_sB0;
   // Raised wave priority while this wave feeds the matrix unit: the arbiter then prefers
   // the MFMA-issuing wave over its SIMD neighbour that is between bursts (+10% measured).
   __builtin_amdgcn_s_setprio(1);
-  const int c0 = ((lane >> 4) ^ fs) << 4;
-  const int c1 = ((4 + (lane >> 4)) ^ fs) << 4;
-  uint4 a0[kMB], b0[kNB], a1[kMB], b1[kNB];
+  if constexpr (G::kBytes == 1) {
+    // fp8: one 16 x 16 x 128 MFMA per block and k-step, chunks 2 g and 2 g + 1 per lane
+    const int g2 = 2 * (lane >> 4);
+    const int c0 = (g2 ^ fs) << 4;
+    const int c1 = ((g2 + 1) ^ fs) << 4;
+    uint4 a0[kMB], a1[kMB], b0[kNB], b1[kNB];
 #pragma unroll
-  for (int mb = 0; mb < kMB; ++mb) a0[mb] = *reinterpret_cast<const uint4*>(As + fa + mb * 2048 + c0);
+    for (int mb = 0; mb < kMB; ++mb) {
+      a0[mb] = *reinterpret_cast<const uint4*>(As + fa + mb * 2048 + c0);
+      a1[mb] = *reinterpret_cast<const uint4*>(As + fa + mb * 2048 + c1);
+    }
 #pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) b0[nb] = *reinterpret_cast<const uint4*>(Bs + fb + nb * 2048 + c0);
+    for (int nb = 0; nb < kNB; ++nb) {
+      b0[nb] = *reinterpret_cast<const uint4*>(Bs + fb + nb * 2048 + c0);
+      b1[nb] = *reinterpret_cast<const uint4*>(Bs + fb + nb * 2048 + c1);
+    }
 #pragma unroll
-  for (int mb = 0; mb < kMB; ++mb) a1[mb] = *reinterpret_cast<const uint4*>(As + fa + mb * 2048 + c1);
+    for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) b1[nb] = *reinterpret_cast<const uint4*>(Bs + fb + nb * 2048 + c1);
+      for (int nb = 0; nb < kNB; ++nb)
+        acc[mb][nb] = Mma<FP8T>::op(a0[mb], a1[mb], b0[nb], b1[nb], acc[mb][nb]);
+  } else {
+    const int c0 = ((lane >> 4) ^ fs) << 4;
+    const int c1 = ((4 + (lane >> 4)) ^ fs) << 4;
+    uint4 a0[kMB], b0[kNB], a1[kMB], b1[kNB];
 #pragma unroll
-  for (int mb = 0; mb < kMB; ++mb)
+    for (int mb = 0; mb < kMB; ++mb) a0[mb] = *reinterpret_cast<const uint4*>(As + fa + mb * 2048 + c0);
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = Mma<E>::op(a0[mb], b0[nb], acc[mb][nb]);
+    for (int nb = 0; nb < kNB; ++nb) b0[nb] = *reinterpret_cast<const uint4*>(Bs + fb + nb * 2048 + c0);
 #pragma unroll
-  for (int mb = 0; mb < kMB; ++mb)
+    for (int mb = 0; mb < kMB; ++mb) a1[mb] = *reinterpret_cast<const uint4*>(As + fa + mb * 2048 + c1);
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = Mma<E>::op(a1[mb], b1[nb], acc[mb][nb]);
+    for (int nb = 0; nb < kNB; ++nb) b1[nb] = *reinterpret_cast<const uint4*>(Bs + fb + nb * 2048 + c1);
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = Mma<G>::op(a0[mb], b0[nb], acc[mb][nb]);
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = Mma<G>::op(a1[mb], b1[nb], acc[mb][nb]);
+  }
   __builtin_amdgcn_s_setprio(0);
 }
 
@@ -236,6 +274,14 @@ struct FwdArgs {
   char* pt;
   float* pm;
   int64_t Vpad;
+  // fp8 logits: per-row e4m3 copies of W [V][H] and of the loss rows of X_q and X_p
+  // [compact row][H], with their fp32 scales; the logit is scale_w * scale_x * (W8 . X8)
+  const char* W8;
+  const char* Xq8;
+  const char* Xp8;
+  const float* sw;
+  const float* sxq;
+  const float* sxp;
 };
 
 // Rows and token blocks of one launch.
@@ -275,6 +321,43 @@ __device__ inline void x_offsets(int64_t tok0, int64_t rhi, const int32_t* __res
     if (r >= rhi) r = rhi - 1;
     bo[i] = (uint32_t)(idx[r] * rowb) + stage_chunk_bytes(sr);
   }
+}
+
+// Staging offsets of compact rows tok0 .. tok0 + 255 of a buffer holding one row per loss
+// row (the fp8 copies), rows from rhi on clamped to the last valid one.
+__device__ inline void xc_offsets(int64_t tok0, int64_t rhi, int64_t rowb, Offs& bo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int sr = stage_row(i);
+    int64_t r = tok0 + sr;
+    if (r >= rhi) r = rhi - 1;
+    bo[i] = (uint32_t)(r * rowb) + stage_chunk_bytes(sr);
+  }
+}
+
+// fp8 logits: acc[mb][nb][j] (vocabulary row vb + 16 mb + j, compact token row
+// tok0 + column) times the two rows' scales.  Rows past V or rhi take a valid row's scale;
+// their values are masked later.
+__device__ inline void scale_acc(Acc& acc, const float* __restrict__ sw,
+                                 const float* __restrict__ sx, int vb, int64_t V, int64_t tok0,
+                                 int64_t rhi, int wn, int lane) {
+  float cs[kNB];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    int64_t r = tok0 + wn * kWaveN + nb * 16 + (lane & 15);
+    if (r >= rhi) r = rhi - 1;
+    cs[nb] = sx[r];
+  }
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int64_t v = vb + mb * 16 + j;
+      if (v >= V) v = V - 1;
+      const float rs = sw[v];
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) acc[mb][nb][j] *= rs * cs[nb];
+    }
 }
 
 // Where a fold stores the softmax terms of its tile (single-pass mode).
@@ -381,9 +464,10 @@ __device__ inline void fwd_fold(const Acc& acc, float s2, int vlim, int vb, int 
 // kMode 0: both sides over all rows (two-pass forward); 1: one side over all rows
 // (single-pass reference); 2: policy rows of one chunk, softmax terms kept (single-pass).
 // Modes 0 and 1 run the same code; distinct instances keep their profiles apart.
-template <class E, int kMode>
+template <class E, class G, int kMode>
 __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
   constexpr bool kStore = kMode == 2;
+  constexpr bool kF8 = G::kBytes == 1;   // operands are the fp8 copies
   __shared__ float mrg[2][2][256];
   __shared__ float s_run[2][kNB][kThreads];
   __shared__ int s_y[256];
@@ -400,11 +484,19 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
   const int tb_per_xcd = slots / P;
   const int phase = slot % P;
   const int tbg = kXcds * tb_per_xcd;            // token blocks per round
-  const int64_t rowb = a.H * 2;                  // bytes per row
-  const int nk = (int)(a.H / 64);
+  const int64_t rowb = a.H * G::kBytes;          // bytes per row
+  const int nk = (int)(rowb / 128);              // k-steps of 128 bytes
   const float s2 = a.scale2;
-  const char* wend = a.W + a.V * rowb;           // operand extents for the buffer loads
+  const char* Wop = kF8 ? a.W8 : a.W;
+  const char* wend = Wop + a.V * rowb;           // operand extents for the buffer loads
   const int64_t xbytes = a.N * rowb;
+  auto xop = [&](int side) { return kF8 ? (side ? a.Xp8 : a.Xq8) : (side ? a.Xp : a.Xq); };
+  auto xoffs = [&](int64_t tok0, Offs& bo) {
+    if (kF8)
+      xc_offsets(tok0, fr.rhi, rowb, bo);
+    else
+      x_offsets(tok0, fr.rhi, a.idx, rowb, bo);
+  };
 
   int64_t tb = xcd * tb_per_xcd + slot / P;
   if (tb >= TB) return;
@@ -413,16 +505,16 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
   Offs ao, bo;
   if (phase < nvt) {
     const int sd = (int)(tb / fr.ntbs);
-    x_offsets(a.row_lo + (tb - sd * fr.ntbs) * 256, fr.rhi, a.idx, rowb, bo);
+    xoffs(a.row_lo + (tb - sd * fr.ntbs) * 256, bo);
     w_offsets(phase * 256, a.V, rowb, ao);
-    const char* X0 = (a.side0 + sd) ? a.Xp : a.Xq;
-    gemm_pre(make_src(a.W + phase * 256 * rowb, wend), make_src(X0, X0 + xbytes), ao, bo);
+    const char* X0 = xop(a.side0 + sd);
+    gemm_pre(make_src(Wop + phase * 256 * rowb, wend), make_src(X0, X0 + xbytes), ao, bo);
   }
   for (; tb < TB; tb += tbg) {
     const int sd = (int)(tb / fr.ntbs);
     const int side = a.side0 + sd;
     const int64_t tok0 = a.row_lo + (tb - sd * fr.ntbs) * 256;
-    const char* X = side ? a.Xp : a.Xq;
+    const char* X = xop(side);
     // per-block state lives in LDS so the GEMM loop keeps its registers: target id and
     // target logit per token column, running (max, sum) per lane and column block
     if (tid < 256) {
@@ -452,7 +544,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
       const int64_t v0 = vt * 256;
       Acc acc;
       zero_acc(acc);
-      gemm_main<E>(make_src(a.W + v0 * rowb, wend), make_src(X, X + xbytes), ao, bo, nk, acc);
+      gemm_main<G>(make_src(Wop + v0 * rowb, wend), make_src(X, X + xbytes), ao, bo, nk, acc);
       // enqueue the next tile: the next vocabulary tile of this block, else the first
       // tile of this workgroup's next token block
       {
@@ -463,14 +555,14 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
         }
         if (ntb < TB) {
           const int nsd = (int)(ntb / fr.ntbs);
-          if (ntb != tb)
-            x_offsets(a.row_lo + (ntb - nsd * fr.ntbs) * 256, fr.rhi, a.idx, rowb, bo);
+          if (ntb != tb) xoffs(a.row_lo + (ntb - nsd * fr.ntbs) * 256, bo);
           w_offsets(nv * 256, a.V, rowb, ao);
-          const char* Xn = (a.side0 + nsd) ? a.Xp : a.Xq;
-          gemm_pre(make_src(a.W + nv * 256 * rowb, wend), make_src(Xn, Xn + xbytes), ao, bo);
+          const char* Xn = xop(a.side0 + nsd);
+          gemm_pre(make_src(Wop + nv * 256 * rowb, wend), make_src(Xn, Xn + xbytes), ao, bo);
         }
       }
       const int vb = (int)(v0 + wm * 128 + 4 * (lane >> 4));  // vocab of acc[mb][.][j] = vb + 16 mb + j
+      if (kF8) scale_acc(acc, a.sw, side ? a.sxp : a.sxq, vb, a.V, tok0, fr.rhi, wn, lane);
       FoldOut<E> ft = fo;
       if (kStore) ft.pm = fo.pm + vt;
       if (v0 + 256 <= a.V)
@@ -551,14 +643,17 @@ fixup_kernel(int64_t Vpad, int64_t nvt, int64_t c0, const int32_t* __restrict__ 
 // ---------------------------------------------------------------------------- recompute
 // T[r - c0][v] = onehot(y_r)[v] - exp(z_rv / tau - lse_r) for one 256-token x
 // 256-vocabulary tile of the chunk (scale2 = log2(e) / tau); zero for v >= V and for rows
-// past the last loss token.
-template <class E>
+// past the last loss token.  G = FP8T: Xq and W are the fp8 copies (Xq by compact row)
+// with scales sxq and sw.
+template <class E, class G>
 __global__ void __launch_bounds__(kThreads, 1)
 recompute_kernel(int64_t N, int64_t H, int64_t V, int64_t Vpad, int64_t c0, int ntt, float scale2,
                  const int32_t* __restrict__ ntok_p, const int32_t* __restrict__ idx,
                  const char* __restrict__ Xq, const char* __restrict__ W,
                  const int64_t* __restrict__ targets, const float* __restrict__ saved,
-                 typename E::T* __restrict__ T) {
+                 typename E::T* __restrict__ T, const float* __restrict__ sw,
+                 const float* __restrict__ sxq) {
+  constexpr bool kF8 = G::kBytes == 1;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / kWN, wn = w % kWN;
   // token tiles vary fastest so consecutive workgroups share a W tile
   const int64_t tt = blockIdx.x % ntt, vt = blockIdx.x / ntt;
@@ -566,24 +661,19 @@ recompute_kernel(int64_t N, int64_t H, int64_t V, int64_t Vpad, int64_t c0, int 
   const int64_t tok0 = c0 + tt * 256;
   if (tok0 >= ntok) return;
   const int64_t v0 = vt * 256;
-  const int64_t rowb = H * 2;
+  const int64_t rowb = H * G::kBytes;
   Offs ao, bo;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int sr = stage_row(i);
-    const uint32_t cb = stage_chunk_bytes(sr);
-    int64_t v = v0 + sr;
-    if (v >= V) v = V - 1;
-    ao[i] = (uint32_t)((v - v0) * rowb) + cb;
-    int64_t r = tok0 + sr;
-    if (r >= ntok) r = ntok - 1;
-    bo[i] = (uint32_t)(idx[r] * rowb) + cb;
-  }
+  w_offsets(v0, V, rowb, ao);
+  if (kF8)
+    xc_offsets(tok0, ntok, rowb, bo);
+  else
+    x_offsets(tok0, ntok, idx, rowb, bo);
   Acc acc;
   zero_acc(acc);
-  gemm_core<E>(make_src(W + v0 * rowb, W + V * rowb), make_src(Xq, Xq + N * rowb), ao, bo,
-               (int)(H / 64), acc);
+  gemm_core<G>(make_src(W + v0 * rowb, W + V * rowb), make_src(Xq, Xq + N * rowb), ao, bo,
+               (int)(rowb / 128), acc);
   const int64_t vb = v0 + wm * 128 + 4 * (lane >> 4);
+  if (kF8) scale_acc(acc, sw, sxq, (int)vb, V, tok0, ntok, wn, lane);
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
     const int64_t r = tok0 + wn * kWaveN + nb * 16 + (lane & 15);
@@ -845,9 +935,8 @@ transpose_kernel(const typename E::T* __restrict__ in, int64_t ld_in, int64_t nv
   }
 }
 
-template <class E>
-hipError_t fwd_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, const void* W,
-                    const int64_t* targets, hipStream_t st) {
+FwdArgs fwd_args(const Plan& p, void* ws, const void* Xq, const void* Xp, const void* W,
+                 const int64_t* targets) {
   FwdArgs a;
   a.N = p.N;
   a.H = p.H;
@@ -867,7 +956,39 @@ hipError_t fwd_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, con
   a.pt = nullptr;
   a.pm = nullptr;
   a.Vpad = p.Vpad;
-  hipLaunchKernelGGL((fwd_kernel<E, 0>), dim3(kNumWG), dim3(kThreads), 0, st, a);
+  a.W8 = ws_ptr<char>(ws, p.off_w8);
+  a.Xq8 = ws_ptr<char>(ws, p.off_xq8);
+  a.Xp8 = ws_ptr<char>(ws, p.off_xp8);
+  a.sw = ws_ptr<float>(ws, p.off_sw);
+  a.sxq = ws_ptr<float>(ws, p.off_sxq);
+  a.sxp = ws_ptr<float>(ws, p.off_sxp);
+  return a;
+}
+
+// fp8 logits: e4m3 copies of W and of the loss rows of X_q (and X_p), by compact row.
+hipError_t quantize_operands(const Plan& p, void* ws, const void* Xq, const void* Xp,
+                             const void* W, hipStream_t st) {
+  const int32_t* ntok = ws_ptr<int32_t>(ws, p.off_ntok);
+  const int32_t* idx = ws_ptr<int32_t>(ws, p.off_idx);
+  hipError_t e = launch_quant_rows(p.dtype, W, p.H, nullptr, nullptr, p.V,
+                                   ws_ptr<uint8_t>(ws, p.off_w8), ws_ptr<float>(ws, p.off_sw), st);
+  if (e != hipSuccess) return e;
+  e = launch_quant_rows(p.dtype, Xq, p.H, idx, ntok, p.N, ws_ptr<uint8_t>(ws, p.off_xq8),
+                        ws_ptr<float>(ws, p.off_sxq), st);
+  if (e != hipSuccess || !Xp) return e;
+  return launch_quant_rows(p.dtype, Xp, p.H, idx, ntok, p.N, ws_ptr<uint8_t>(ws, p.off_xp8),
+                           ws_ptr<float>(ws, p.off_sxp), st);
+}
+
+template <class E, class G>
+hipError_t fwd_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, const void* W,
+                    const int64_t* targets, hipStream_t st) {
+  if (G::kBytes == 1) {
+    const hipError_t e = quantize_operands(p, ws, Xq, Xp, W, st);
+    if (e != hipSuccess) return e;
+  }
+  FwdArgs a = fwd_args(p, ws, Xq, Xp, W, targets);
+  hipLaunchKernelGGL((fwd_kernel<E, G, 0>), dim3(kNumWG), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -924,22 +1045,27 @@ hipError_t chunk_grads(const Plan& p, void* ws, int64_t c0, const void* Xq, cons
   return hipSuccess;
 }
 
-template <class E>
+template <class E, class G>
 hipError_t bwd_impl(const Plan& p, void* ws, const void* Xq, const void* W,
                     const int64_t* targets, const float* saved, const float* grad_loss,
                     float loss_scale, void* dX, float* dW, int accumulate_dW, int32_t* found_inf,
                     hipStream_t st) {
   typedef typename E::T T;
+  constexpr bool kF8 = G::kBytes == 1;
   const int32_t* ntok = ws_ptr<int32_t>(ws, p.off_ntok);
   const int32_t* idx = ws_ptr<int32_t>(ws, p.off_idx);
   T* Tb = ws_ptr<T>(ws, p.off_T);
   hipError_t e = transpose_w<E>(p, ws, W, st);
   if (e != hipSuccess) return e;
+  if (kF8 && (e = quantize_operands(p, ws, Xq, nullptr, W, st)) != hipSuccess) return e;
+  const char* Xop = kF8 ? ws_ptr<char>(ws, p.off_xq8) : (const char*)Xq;
+  const char* Wop = kF8 ? ws_ptr<char>(ws, p.off_w8) : (const char*)W;
   const int ntt = (int)(p.R / 256), nvt = (int)(p.Vpad / 256);
   for (int64_t c0 = 0; c0 < p.N; c0 += p.R) {
-    hipLaunchKernelGGL(recompute_kernel<E>, dim3((unsigned)(ntt * nvt)), dim3(kThreads), 0, st,
-                       p.N, p.H, p.V, p.Vpad, c0, ntt, p.scale2, ntok, idx, (const char*)Xq,
-                       (const char*)W, targets, saved, Tb);
+    hipLaunchKernelGGL((recompute_kernel<E, G>), dim3((unsigned)(ntt * nvt)), dim3(kThreads), 0,
+                       st, p.N, p.H, p.V, p.Vpad, c0, ntt, p.scale2, ntok, idx, Xop, Wop, targets,
+                       saved, Tb, (const float*)ws_ptr<float>(ws, p.off_sw),
+                       (const float*)ws_ptr<float>(ws, p.off_sxq));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     e = chunk_grads<E>(p, ws, c0, Xq, saved, grad_loss, loss_scale, dX, dW, accumulate_dW,
                        found_inf, st);
@@ -952,7 +1078,7 @@ hipError_t bwd_impl(const Plan& p, void* ws, const void* Xq, const void* W,
 // forward that also keeps its softmax terms, the chunk's merge, the fixup of the kept
 // terms into T = onehot - softmax, and dX (and dW) from T.  The logits of each row are
 // computed once per side instead of twice for the policy.
-template <class E>
+template <class E, class G>
 hipError_t fused_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, const void* W,
                       const int64_t* targets, const uint8_t* mask, const float* adv, float beta,
                       float* saved, float* logp, float* ref_logp, float* kl, int32_t* status,
@@ -967,26 +1093,11 @@ hipError_t fused_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, c
   hipError_t e = launch_zero_masked_outputs(p, mask, saved, logp, ref_logp, kl, st);
   if (e != hipSuccess) return e;
   if ((e = transpose_w<E>(p, ws, W, st)) != hipSuccess) return e;
-  FwdArgs a;
-  a.N = p.N;
-  a.H = p.H;
-  a.V = p.V;
-  a.ntok = ntok;
-  a.idx = idx;
-  a.Xq = (const char*)Xq;
-  a.Xp = (const char*)Xp;
-  a.W = (const char*)W;
-  a.targets = targets;
-  a.part = ws_ptr<float>(ws, p.off_part);
-  a.scale2 = p.scale2;
-  a.Vpad = p.Vpad;
-  a.row_lo = 0;
-  a.row_hi = p.N;
+  if (G::kBytes == 1 && (e = quantize_operands(p, ws, Xq, Xp, W, st)) != hipSuccess) return e;
+  FwdArgs a = fwd_args(p, ws, Xq, Xp, W, targets);
   a.side0 = 1;
   a.nsides = 1;
-  a.pt = nullptr;
-  a.pm = nullptr;
-  hipLaunchKernelGGL((fwd_kernel<E, 1>), dim3(kNumWG), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((fwd_kernel<E, G, 1>), dim3(kNumWG), dim3(kThreads), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   for (int64_t c0 = 0; c0 < p.N; c0 += p.R) {
     a.row_lo = c0;
@@ -994,7 +1105,7 @@ hipError_t fused_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, c
     a.side0 = 0;
     a.pt = reinterpret_cast<char*>(Tb);
     a.pm = pm;
-    hipLaunchKernelGGL((fwd_kernel<E, 2>), dim3(kNumWG), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((fwd_kernel<E, G, 2>), dim3(kNumWG), dim3(kThreads), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     e = launch_merge_rows(p, ws, c0, targets, mask, adv, beta, saved, logp, ref_logp, kl, status,
                           st);
@@ -1014,8 +1125,11 @@ hipError_t fused_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, c
 
 hipError_t mfma_fwd_partials(const Plan& p, void* ws, const void* Xq, const void* Xp,
                              const void* W, const int64_t* targets, hipStream_t st) {
-  if (p.dtype == GRPO_BF16) return fwd_impl<BF16T>(p, ws, Xq, Xp, W, targets, st);
-  return fwd_impl<F16T>(p, ws, Xq, Xp, W, targets, st);
+  if (p.dtype == GRPO_BF16)
+    return p.fp8 ? fwd_impl<BF16T, FP8T>(p, ws, Xq, Xp, W, targets, st)
+                 : fwd_impl<BF16T, BF16T>(p, ws, Xq, Xp, W, targets, st);
+  return p.fp8 ? fwd_impl<F16T, FP8T>(p, ws, Xq, Xp, W, targets, st)
+               : fwd_impl<F16T, F16T>(p, ws, Xq, Xp, W, targets, st);
 }
 
 hipError_t mfma_fused(const Plan& p, void* ws, const void* Xq, const void* Xp, const void* W,
@@ -1023,24 +1137,24 @@ hipError_t mfma_fused(const Plan& p, void* ws, const void* Xq, const void* Xp, c
                       float* saved, float* logp, float* ref_logp, float* kl, int32_t* status,
                       float* loss, const float* grad_loss, float loss_scale, void* dX, float* dW,
                       int accumulate_dW, int32_t* found_inf, hipStream_t st) {
-  if (p.dtype == GRPO_BF16)
-    return fused_impl<BF16T>(p, ws, Xq, Xp, W, targets, mask, adv, beta, saved, logp, ref_logp,
-                             kl, status, loss, grad_loss, loss_scale, dX, dW, accumulate_dW,
-                             found_inf, st);
-  return fused_impl<F16T>(p, ws, Xq, Xp, W, targets, mask, adv, beta, saved, logp, ref_logp, kl,
-                          status, loss, grad_loss, loss_scale, dX, dW, accumulate_dW, found_inf,
-                          st);
+#define GRPO_FUSED(E, G)                                                                       \
+  fused_impl<E, G>(p, ws, Xq, Xp, W, targets, mask, adv, beta, saved, logp, ref_logp, kl,     \
+                   status, loss, grad_loss, loss_scale, dX, dW, accumulate_dW, found_inf, st)
+  if (p.dtype == GRPO_BF16) return p.fp8 ? GRPO_FUSED(BF16T, FP8T) : GRPO_FUSED(BF16T, BF16T);
+  return p.fp8 ? GRPO_FUSED(F16T, FP8T) : GRPO_FUSED(F16T, F16T);
+#undef GRPO_FUSED
 }
 
 hipError_t mfma_backward(const Plan& p, void* ws, const void* Xq, const void* W,
                          const int64_t* targets, const float* saved, const float* grad_loss,
                          float loss_scale, void* dX, float* dW, int accumulate_dW,
                          int32_t* found_inf, hipStream_t st) {
-  if (p.dtype == GRPO_BF16)
-    return bwd_impl<BF16T>(p, ws, Xq, W, targets, saved, grad_loss, loss_scale, dX, dW,
-                           accumulate_dW, found_inf, st);
-  return bwd_impl<F16T>(p, ws, Xq, W, targets, saved, grad_loss, loss_scale, dX, dW,
-                        accumulate_dW, found_inf, st);
+#define GRPO_BWD(E, G)                                                                         \
+  bwd_impl<E, G>(p, ws, Xq, W, targets, saved, grad_loss, loss_scale, dX, dW, accumulate_dW,  \
+                 found_inf, st)
+  if (p.dtype == GRPO_BF16) return p.fp8 ? GRPO_BWD(BF16T, FP8T) : GRPO_BWD(BF16T, BF16T);
+  return p.fp8 ? GRPO_BWD(F16T, FP8T) : GRPO_BWD(F16T, F16T);
+#undef GRPO_BWD
 }
 
 }  // namespace grpo

@@ -66,7 +66,8 @@ typedef enum grpo_status {
   GRPO_ERR_WORKSPACE = -5, /* workspace smaller than grpo_workspace_bytes()               */
   GRPO_ERR_HIP = -6,       /* the HIP runtime reported an error when enqueuing           */
   GRPO_ERR_DEVICE = -7,    /* the current device is not a gfx950 GPU                      */
-  GRPO_ERR_OPTIONS = -8    /* a grpo_options field is out of range                        */
+  GRPO_ERR_OPTIONS = -8    /* a grpo_options field is out of range, or not supported for  */
+                           /* these inputs (fp8_logits with fp32 data)                     */
 } grpo_status;
 
 /* Loss variants: the four experiments of [Long-context GRPO, §4] and two readings the
@@ -90,6 +91,10 @@ typedef struct grpo_options {
                              0: exp(q - q), whose gradient vanishes (the no-detach experiment) */
   int normalization;      /* grpo_normalization                                            */
   float temperature;      /* logits are divided by it before the log-softmax; in [1e-3, 1e3] */
+  int fp8_logits;         /* 1: both sides' logits from per-row e4m3 copies of X and W
+                             (scale amax / 448 per row, see grpo_quantize_e4m3); gradients
+                             still use the original X and W.  16-bit inputs with H a
+                             multiple of 256 only.  Needs grpo_workspace_bytes_opts.      */
 } grpo_options;
 
 /* Bits of the forward's status word. */
@@ -106,6 +111,20 @@ const char* grpo_status_string(int status);
 size_t grpo_workspace_bytes(int64_t S, int64_t L, int64_t H, int64_t V, grpo_dtype dtype,
                             int need_dW);
 
+/* The same for a loss variant (opts may be NULL): fp8_logits adds the e4m3 copies of W and
+ * of the loss rows of X_q and X_p (N H + V H bytes and their scales). */
+size_t grpo_workspace_bytes_opts(int64_t S, int64_t L, int64_t H, int64_t V, grpo_dtype dtype,
+                                 int need_dW, const grpo_options* opts);
+
+/* Per-row fp8 e4m3 ("fn": maximum 448, no infinities) quantisation of a [rows, H] matrix:
+ * amax = max |x| of the row, scales[r] = amax / 448 and dst[r][h] = e4m3(x * (448 / amax)),
+ * with correctly rounded fp32 division and product and round-to-nearest-even onto the
+ * e4m3 grid (a row of zeros gets scale 1; a row holding inf or NaN gets scale NaN).  This
+ * is the quantisation of the fp8_logits option, exported for callers that keep fp8
+ * weights.  dst: uint8 [rows, H]; scales: fp32 [rows]; H a multiple of 4. */
+int grpo_quantize_e4m3(const void* src, grpo_dtype dtype, int64_t rows, int64_t H,
+                       uint8_t* dst, float* scales, grpo_stream_t stream);
+
 /* Group-relative advantages [Train your own R1 reasoning model with Unsloth, §3;
  * Long-context GRPO, §4].
  *   rewards  fp32 [B, G, K]: score of completion g of prompt b under reward function k.
@@ -117,7 +136,7 @@ size_t grpo_workspace_bytes(int64_t S, int64_t L, int64_t H, int64_t V, grpo_dty
 int grpo_advantages(const float* rewards, int64_t B, int64_t G, int64_t K, float eps,
                     int unbiased, float* adv, grpo_stream_t stream);
 
-/* Defaults: reverse estimator, detached ratio, token mean, temperature 1. */
+/* Defaults: reverse estimator, detached ratio, token mean, temperature 1, 16-bit logits. */
 void grpo_default_options(grpo_options* opts);
 
 /* Forward: loss and per-token terms, without materialising logits

@@ -135,3 +135,34 @@ def test_fused_and_scale_bad_arguments(lib):
     assert lib.grpo_scale_grad(p, 1, 4, 12, nul, 0, p, f(1.0), p, nul) == -2
     assert lib.grpo_scale_grad(p, 1, 4, 64, nul, 0, p, f(0.0), p, nul) == -2
     assert lib.grpo_scale_grad(p, 7, 4, 64, nul, 0, p, f(1.0), p, nul) == -3
+
+
+def test_fp8_options_and_quantizer_arguments(lib):
+    import grpo_loss_amd as g
+    p = ctypes.c_void_p(16)
+    nul = None
+    f = ctypes.c_float
+    o8 = g.options(fp8_logits=True)
+    base = lib.grpo_workspace_bytes(8, 4096, 4096, 128256, 1, 0)
+    with8 = lib.grpo_workspace_bytes_opts(8, 4096, 4096, 128256, 1, 0, ctypes.byref(o8))
+    # the e4m3 copies: N H (two sides) + V H bytes and the scales
+    assert with8 - base >= 2 * 8 * 4096 * 4096 + 128256 * 4096
+    assert lib.grpo_workspace_bytes_opts(8, 4096, 4096, 128256, 1, 0, None) == base
+    assert lib.grpo_workspace_bytes_opts(2, 64, 64, 1000, 0, 0, ctypes.byref(o8)) == 0  # fp32
+    bad = g.GRPOOptions(0, 1, 0, 1.0, 2)
+    assert lib.grpo_workspace_bytes_opts(8, 4096, 4096, 128256, 1, 0, ctypes.byref(bad)) == 0
+    # fp8 logits with fp32 inputs, or H not a multiple of 256: rejected before any launch
+    rc = lib.grpo_loss_fwd(p, p, p, 0, p, p, p, 2, 3, 64, 5, f(0.04), p, p, nul, nul, nul, p,
+                           ctypes.byref(o8), p, ctypes.c_size_t(1 << 40), nul)
+    assert rc == -8
+    rc = lib.grpo_loss_fwd_bwd(p, p, p, 1, p, p, p, 2, 3, 64, 5, f(0.04), nul, f(1.0), p, p,
+                               nul, nul, nul, p, p, nul, 0, p, ctypes.byref(o8), p,
+                               ctypes.c_size_t(1 << 40), nul)
+    assert rc == -8
+    rc = lib.grpo_loss_bwd(p, p, 1, p, p, p, 2, 3, 64, 5, nul, f(1.0), p, nul, 0, p,
+                           ctypes.byref(bad), p, ctypes.c_size_t(1 << 40), nul)
+    assert rc == -8
+    assert lib.grpo_quantize_e4m3(nul, 1, 4, 64, p, p, nul) == -1
+    assert lib.grpo_quantize_e4m3(p, 1, 4, 62, p, p, nul) == -2
+    assert lib.grpo_quantize_e4m3(p, 5, 4, 64, p, p, nul) == -3
+    assert lib.grpo_quantize_e4m3(p, 1, 4, 64, ctypes.c_void_p(17), p, nul) == -4

@@ -436,3 +436,74 @@ def test_autograd_single_pass():
     dX[b["rows"]] = b["dX"]
     assert rel_l2(xq.grad.float().reshape(wl.N, wl.H).cpu().numpy(), dX) <= 1e-2
     assert rel_l2(W.grad.float().cpu().numpy(), b["dW"]) <= 1e-2
+
+
+# ------------------------------------------------------------------ fp8 logits (e4m3)
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_quantize_e4m3_bitexact(dtype):
+    """Codes and scales of the GPU quantiser equal the oracle's, bit for bit (both make
+    every decision in fp32 with correctly rounded division and one product)."""
+    g = _lib()
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((67, 1024)).astype(np.float32)
+    x *= np.exp2(rng.uniform(-20, 12, size=(67, 1)))          # row magnitudes
+    x[3] = 0.0                                                # all-zero row
+    x[5, :] = 1e-3 * rng.standard_normal(1024)
+    x[5, 7] = 30.0                                            # subnormal codes in the row
+    x[9, ::2] = -x[9, ::2]
+    xt = torch.from_numpy(x).to(dtype)
+    codes, scales = g.grpo_quantize_e4m3(xt.cuda())
+    torch.cuda.synchronize()
+    _, ref_codes, ref_s = oracle.quantize_e4m3_rows(xt.float().numpy())
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
+    got = codes.cpu().numpy()
+    bad = np.nonzero(got != ref_codes)
+    assert bad[0].size == 0, (bad[0][:5], bad[1][:5], got[bad][:5], ref_codes[bad][:5])
+
+
+FP8 = oracle.Variant(fp8_logits=True)
+
+
+@pytest.mark.parametrize("single_pass", [False, True], ids=["two-pass", "single-pass"])
+@pytest.mark.parametrize("name", ["qwen2.5-1.5b-bf16", "llama3.1-8b-train-bf16",
+                                  "llama3.1-8b-long-bf16", "phi4-f16"])
+def test_parity_fp8_logits(name, single_pass):
+    """fp8 logits against the oracle's fp8 variant (the same e4m3 codes and scales, so
+    only accumulation order differs), at the 16-bit tolerances."""
+    wl = dataclasses.replace(workload_by_name(name), **SMALL[name])
+    _say(f"[parity fp8] {name} single_pass={single_pass}")
+    check_small(wl, generate(wl), variant=FP8, single_pass=single_pass)
+
+
+def test_parity_fp8_full_sampled():
+    wl = workload_by_name("llama3.1-8b-long-bf16")
+    _say(f"[parity fp8 full] {wl.name}")
+    inp = generate(wl)
+    gpu = run_gpu(wl, inp, single_pass=True, variant=FP8)
+    assert gpu["status"] == 0 and gpu["found_inf"] == 0
+    mask = inp.mask.numpy()
+    adv = oracle.group_advantages(inp.rewards.numpy(), wl.eps)
+    rows = _sample_rows(mask, wl.L)
+    xq = hidden_rows(wl, "q", rows)
+    xp = hidden_rows(wl, "p", rows)
+    f = oracle.forward(xq, xp, inp.W, inp.targets.numpy(), mask, adv, wl.L, wl.beta, rows=rows,
+                       variant=FP8)
+    b = oracle.backward(xq, inp.W, inp.targets.numpy(), mask, f, rows=rows)
+    tol = TOL[wl.dtype]
+    for k in ("logp", "ref_logp"):
+        err = np.abs(gpu[k][rows] - f[k][rows]).max()
+        _say(f"  {k} max abs err {err:.2e} over {len(rows)} rows")
+        assert err <= tol["logp"]
+    e = rel_l2(gpu["dX"][rows], b["dX"])
+    _say(f"  dX rel-L2 (sampled rows) {e:.2e}")
+    assert e <= tol["dx"]
+
+
+def test_fp8_nonfinite_row_flagged():
+    wl = dataclasses.replace(workload_by_name("qwen2.5-1.5b-bf16"), **SMALL["qwen2.5-1.5b-bf16"])
+    inp = generate(wl)
+    lrow = int(np.nonzero(inp.mask.numpy())[0][2])
+    inp.xq[lrow, 11] = float("inf")
+    out = run_gpu(wl, inp, single_pass=True, variant=FP8)
+    assert out["status"] & 1
