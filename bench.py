@@ -47,6 +47,8 @@ def parse():
                     help="path timed for value; the other one is reported beside it")
     ap.add_argument("--no-two-pass", action="store_true",
                     help="time only the path given by --path")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the single-pass leg with fp8 (e4m3) logits")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=256, help="oracle rows per sequence")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
@@ -166,11 +168,13 @@ def main():
             ev.append((e0, e1))
         return f
 
+    opts = {"v": None}
+
     def step_single(record):
         g.grpo_advantages(d["rewards"], wl.eps, out=adv)
         return g.grpo_loss_fwd_bwd(d["xq"], d["xp"], d["W"], d["targets"], d["mask"], adv,
                                    wl.beta, wl.L, grad, wl.loss_scale, dW=dW, found_inf=found,
-                                   workspace=ws, dXq=dX, want_terms=False)
+                                   workspace=ws, dXq=dX, want_terms=False, opts=opts["v"])
 
     def timed(step):
         for _ in range(args.warmup):
@@ -237,6 +241,19 @@ def main():
         out["two_pass" if other[0] == "two" else "single_pass"] = legs[other[0]]
     out["status"] = main_leg["status"]
     out["found_inf"] = main_leg["found_inf"]
+    if not args.no_fp8 and dtn != "f32":
+        # the same single-pass step with both sides' logits from per-row e4m3 copies (a
+        # lower-precision variant, reported beside the 16-bit result, never as `value`)
+        o8 = g.options(fp8_logits=True)
+        del ws
+        torch.cuda.empty_cache()
+        ws8_bytes = g.grpo_workspace_bytes(wl.S, wl.L, wl.H, wl.V, dt, need_dW, o8)
+        ws = torch.empty(ws8_bytes, dtype=torch.uint8, device="cuda")
+        opts["v"] = o8
+        ms, f = timed(step_single)
+        out["fp8_logits"] = {"value": n_tok / (ms * 1e-3), "ms_per_step": ms,
+                             "workspace_gib": ws8_bytes / 2 ** 30,
+                             "status": int(f["status"].item())}
     if not args.no_cpu_baseline:
         import oracle
         adv_host = oracle.group_advantages(inp.rewards.numpy(), wl.eps)
