@@ -101,11 +101,17 @@ bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_d
             (uint64_t)p->Vpad * H * 2 < k4G && (uint64_t)p->R * p->Vpad * 2 < k4G;
   p->ksplit = 1;
   if (p->mfma) {
-    // split the dX reduction over the vocabulary when one chunk has too few output tiles
+    // Split the dX reduction over the vocabulary so that a full chunk's (tile, split)
+    // items fill whole rounds of the 256 persistent workgroups: time goes as
+    // ceil(tiles k / 256) / k, minimised over k <= 8 (the smallest k on ties).
     const int64_t tiles = (H / 256) * (p->R / 256);
-    if (tiles < 192) {
-      int64_t ks = (256 + tiles - 1) / tiles;
-      p->ksplit = (int)(ks > 8 ? 8 : ks);
+    double best = 1e30;
+    for (int k = 1; k <= 8; ++k) {
+      const double cost = (double)((tiles * k + 255) / 256) / k;
+      if (cost < best - 1e-9) {
+        best = cost;
+        p->ksplit = k;
+      }
     }
   }
   size_t o = 0;

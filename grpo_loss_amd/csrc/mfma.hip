@@ -709,26 +709,30 @@ recompute_kernel(int64_t N, int64_t H, int64_t V, int64_t Vpad, int64_t c0, int 
 // C[h][r] = sum_v W^T[h][v] T[r][v] over the padded vocabulary (or one split of it).
 // ksplit == 1: dX[idx[r]][h] = c * g_r * C, in the storage type.  ksplit > 1: fp32
 // partials to dxp[ks][r - c0][h], reduced by dx_reduce_kernel.
+//
+// Persistent over a work list of (k split, token tile, H tile) items, H tile fastest,
+// holding only the token tiles of this chunk that have loss rows, so every workgroup gets
+// the same number of items up to one.  Workgroups are numbered XCD-major (workgroup b
+// runs on XCD b % 8), so the items that share a T tile and k range run on one XCD.
 template <class E>
 __global__ void __launch_bounds__(kThreads, 1)
-dx_kernel(int64_t H, int64_t Vpad, int64_t R, int64_t c0, int nht, int ntt, int ksplit,
+dx_kernel(int64_t H, int64_t Vpad, int64_t R, int64_t c0, int nht, int ksplit,
           const int32_t* __restrict__ ntok_p, const int32_t* __restrict__ idx,
           const char* __restrict__ WT, const char* __restrict__ T,
           const float* __restrict__ saved, const float* __restrict__ grad_loss, float loss_scale,
           typename E::T* __restrict__ dX, float* __restrict__ dxp,
           int32_t* __restrict__ found_inf) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / kWN, wn = w % kWN;
-  const int tiles = nht * ntt;
-  const int ks = blockIdx.x / tiles;
-  const int rem = blockIdx.x % tiles;
-  const int64_t ht = rem % nht, tt = rem / nht;
   const int ntok = *ntok_p;
-  const int64_t tok0 = c0 + tt * 256;
-  if (tok0 >= ntok) return;
-  const int64_t h0 = ht * 256;
+  int64_t rows = (int64_t)ntok - c0;
+  if (rows <= 0) return;
+  if (rows > R) rows = R;
+  const int64_t ntt = (rows + 255) / 256;
+  const int64_t n_items = ntt * nht * ksplit;
+  const int nwg = gridDim.x;                       // a multiple of 8
+  const int64_t first = (int64_t)(blockIdx.x % kXcds) * (nwg / kXcds) + blockIdx.x / kXcds;
   // k-steps of 64 split into ksplit ranges with even boundaries (Vpad / 64 is a multiple of 4)
   const int64_t npair = Vpad / 128;
-  const int64_t kbeg = 2 * (npair * ks / ksplit), kend = 2 * (npair * (ks + 1) / ksplit);
   const int64_t rowb = Vpad * 2;
   Offs ao, bo;
 #pragma unroll
@@ -737,48 +741,55 @@ dx_kernel(int64_t H, int64_t Vpad, int64_t R, int64_t c0, int nht, int ntt, int 
     ao[i] = (uint32_t)(sr * rowb) + stage_chunk_bytes(sr);
     bo[i] = ao[i];
   }
-  Acc acc;
-  zero_acc(acc);
-  if (kend > kbeg)
-    gemm_core<E>(make_src(WT + h0 * rowb + kbeg * 128, WT + H * rowb),
-                 make_src(T + tt * 256 * rowb + kbeg * 128, T + R * rowb), ao, bo,
-                 (int)(kend - kbeg), acc);
-  const int64_t hb = h0 + wm * 128 + 4 * (lane >> 4);
-  if (ksplit == 1) {
-    const float c = (grad_loss ? *grad_loss : 1.f) / loss_scale;
-    bool bad = false;
+  const float c = (grad_loss ? *grad_loss : 1.f) / loss_scale;
+  bool bad = false;
+  for (int64_t item = first; item < n_items; item += nwg) {
+    const int64_t ht = item % nht, rest = item / nht;
+    const int64_t tt = rest % ntt, ks = rest / ntt;
+    const int64_t tok0 = c0 + tt * 256;
+    const int64_t h0 = ht * 256;
+    const int64_t kbeg = 2 * (npair * ks / ksplit), kend = 2 * (npair * (ks + 1) / ksplit);
+    Acc acc;
+    zero_acc(acc);
+    if (kend > kbeg)
+      gemm_core<E>(make_src(WT + h0 * rowb + kbeg * 128, WT + H * rowb),
+                   make_src(T + tt * 256 * rowb + kbeg * 128, T + R * rowb), ao, bo,
+                   (int)(kend - kbeg), acc);
+    const int64_t hb = h0 + wm * 128 + 4 * (lane >> 4);
+    if (ksplit == 1) {
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-      const int64_t r = tok0 + wn * kWaveN + nb * 16 + (lane & 15);
-      if (r >= ntok) continue;
-      const int64_t t = idx[r];
-      const float gs = saved[t * 4 + 3] * c;
-      typename E::T* drow = dX + t * H;
+      for (int nb = 0; nb < kNB; ++nb) {
+        const int64_t r = tok0 + wn * kWaveN + nb * 16 + (lane & 15);
+        if (r >= ntok) continue;
+        const int64_t t = idx[r];
+        const float gs = saved[t * 4 + 3] * c;
+        typename E::T* drow = dX + t * H;
 #pragma unroll
-      for (int mb = 0; mb < kMB; ++mb) {
-        uint16_t o[4];
+        for (int mb = 0; mb < kMB; ++mb) {
+          uint16_t o[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          o[j] = E::from_f32(acc[mb][nb][j] * gs);
-          bad |= !isfinite(E::to_f32(o[j]));
+          for (int j = 0; j < 4; ++j) {
+            o[j] = E::from_f32(acc[mb][nb][j] * gs);
+            bad |= !isfinite(E::to_f32(o[j]));
+          }
+          uint2 pk;
+          pk.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+          pk.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+          *reinterpret_cast<uint2*>(drow + hb + mb * 16) = pk;
         }
-        uint2 pk;
-        pk.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
-        pk.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
-        *reinterpret_cast<uint2*>(drow + hb + mb * 16) = pk;
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) {
+        const int64_t rl = tt * 256 + wn * kWaveN + nb * 16 + (lane & 15);
+        float* prow = dxp + (ks * R + rl) * H;
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+          *reinterpret_cast<f32x4*>(prow + hb + mb * 16) = acc[mb][nb];
       }
     }
-    if (bad) atomicOr(found_inf, 1);
-  } else {
-#pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-      const int64_t rl = tt * 256 + wn * kWaveN + nb * 16 + (lane & 15);
-      float* prow = dxp + ((int64_t)ks * R + rl) * H;
-#pragma unroll
-      for (int mb = 0; mb < kMB; ++mb)
-        *reinterpret_cast<f32x4*>(prow + hb + mb * 16) = acc[mb][nb];
-    }
   }
+  if (bad) atomicOr(found_inf, 1);
 }
 
 // dX[idx[r]][h] = c * g_r * sum_ks dxp[ks][r - c0][h], ks ascending.
@@ -1015,8 +1026,8 @@ hipError_t chunk_grads(const Plan& p, void* ws, int64_t c0, const void* Xq, cons
   T* WT = ws_ptr<T>(ws, p.off_WT);
   const int ntt = (int)(p.R / 256), nvt = (int)(p.Vpad / 256), nht = (int)(p.H / 256);
   hipError_t e;
-  hipLaunchKernelGGL(dx_kernel<E>, dim3((unsigned)(nht * ntt * p.ksplit)), dim3(kThreads), 0, st,
-                     p.H, p.Vpad, p.R, c0, nht, ntt, p.ksplit, ntok, idx, (const char*)WT,
+  hipLaunchKernelGGL(dx_kernel<E>, dim3(kNumWG), dim3(kThreads), 0, st,
+                     p.H, p.Vpad, p.R, c0, nht, p.ksplit, ntok, idx, (const char*)WT,
                      (const char*)Tb, saved, grad_loss, loss_scale, (T*)dX,
                      ws_ptr<float>(ws, p.off_dxp), found_inf);
   if ((e = hipGetLastError()) != hipSuccess) return e;
