@@ -110,7 +110,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(this build measures the single-GPU kernel path)", file=sys.stderr)
+              "(the benchmark measures the kernels of one GPU)", file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -190,7 +190,8 @@ def main():
     dtn = wl.dtype
     peak = PEAK_TFLOPS[dtn]
     # GEMM-equivalents executed per step: policy and reference forward, dX, dW if trainable,
-    # plus the recompute in the two-pass path; the survey's method count always includes it
+    # plus the recompute in the two-pass path; the method's count (4 or 5 GEMM-equivalents)
+    # always includes the recompute
     n_exec = {"single": 3 + need_dW, "two": 4 + need_dW}
     n_method = 4 + need_dW
     legs = {}

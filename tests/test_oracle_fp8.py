@@ -1,5 +1,5 @@
-"""Pins of the oracle's fp8-logits variant (the e4m3 lm_head path of the survey's next
-rows; [Long-context GRPO, §3] notes that naive fp8 breaks, hence the per-row scales).
+"""Pins of the oracle's fp8-logits variant (an e4m3 lm_head path; [Long-context GRPO, §3]
+notes that naive fp8 breaks, hence the per-row scales).
 
 * e4m3 rounding and byte codes against torch's float8_e4m3fn cast;
 * per-row quantisation: the row maximum maps to 448, the error bound of 3 fraction bits;
