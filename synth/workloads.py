@@ -1,7 +1,7 @@
 """The five synthetic workloads, described by shape and value distribution only.
 
 Shapes stand in for the models the pages train with GRPO (Qwen2.5-1.5B,
-Llama-3.1-8B at the headline 20K context with 8 generations per prompt, and
+Llama-3.1-8B at the pages' 20K context with 8 generations per prompt, and
 Phi-4) [Long-context GRPO, §1 and §2; Unsloth R1 reasoning page, §2].  No
 dataset or checkpoint is involved: every tensor is drawn from the recipe below.
 

@@ -284,7 +284,7 @@ def test_sampled_rows_match_full():
 
 
 def test_memory_figures_golden():
-    """The pages' memory arithmetic for the headline shape: two 16-bit (G, L, V) logits
+    """The pages' memory arithmetic for the long-context shape: two 16-bit (G, L, V) logits
     tensors are 78.3 GiB; one generation's share (1/8) is the 9.8 GiB the efficient loss
     still needs; the difference is the 68.5 GiB saved, a factor of more than 8."""
     gold = json.load(open(os.path.join(GOLDEN, "memory_figures.json")))
