@@ -34,6 +34,17 @@ struct BF16T {
     u += 0x7fffu + ((u >> 16) & 1u);
     return (T)(u >> 16);
   }
+  // a and b narrowed together by v_cvt_pk_bf16_f32 (nearest even, NaN stays NaN), a in
+  // the low half: one instruction for what from_f32 does in several
+  __device__ static inline uint32_t pack2(float a, float b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, h2));
+  }
+  // either half of a pack2 result is inf or NaN (all exponent bits set)
+  __device__ static inline bool nonfinite2(uint32_t p) {
+    return (p & 0x7f80u) == 0x7f80u || (p & 0x7f800000u) == 0x7f800000u;
+  }
 };
 
 struct F16T {
@@ -49,6 +60,16 @@ struct F16T {
     T v;
     __builtin_memcpy(&v, &h, 2);
     return v;
+  }
+  // a and b narrowed together by v_cvt_pk_f16_f32 (nearest even), a in the low half
+  __device__ static inline uint32_t pack2(float a, float b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, h2));
+  }
+  // either half of a pack2 result is inf or NaN (all exponent bits set)
+  __device__ static inline bool nonfinite2(uint32_t p) {
+    return (p & 0x7c00u) == 0x7c00u || (p & 0x7c000000u) == 0x7c000000u;
   }
 };
 

@@ -37,6 +37,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <class E>
 struct Mma;
@@ -202,6 +203,13 @@ __device__ inline void mma_stage(Acc& acc, int fa, int fb, int fs, int lane) {
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima)
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Workgroup barrier for data exchanged through ds_write / ds_read only: it waits for this
+// wave's LDS instructions but not for its vector memory operations in flight, which
+// __syncthreads (and an LDS fence, because of the direct-to-LDS loads) would drain as well:
+// the next tile's prefetch and the stored softmax terms.  Callers must not read LDS that a
+// direct-to-LDS load in flight writes.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // 2^x with the bare v_exp_f32: results below 2^-126 come back as 0 instead of a
 // subnormal.  Used only for softmax terms exp2(z - m) with m at least the running
 // maximum, where a term that small cannot change an fp32 sum that already holds a
@@ -286,15 +294,15 @@ struct FwdArgs {
 
 // Rows and token blocks of one launch.
 struct FwdRange {
-  int64_t rhi;   // one past the last row
-  int64_t ntbs;  // token blocks per side
-  int64_t TB;    // token blocks in all
+  int64_t rhi;  // one past the last row
+  int ntbs;     // token blocks per side
+  int TB;       // token blocks in all
 };
 __device__ inline FwdRange fwd_range(const FwdArgs& a, int ntok) {
   FwdRange f;
   f.rhi = a.row_hi < ntok ? a.row_hi : ntok;
   const int64_t nrows = f.rhi > a.row_lo ? f.rhi - a.row_lo : 0;
-  f.ntbs = (nrows + 255) / 256;
+  f.ntbs = (int)((nrows + 255) / 256);
   f.TB = a.nsides * f.ntbs;
   return f;
 }
@@ -360,13 +368,19 @@ __device__ inline void scale_acc(Acc& acc, const float* __restrict__ sw,
     }
 }
 
-// Where a fold stores the softmax terms of its tile (single-pass mode).
-template <class E>
+// Where a fold stores the softmax terms of its tile (single-pass mode).  The stores are
+// buffer stores addressed by one 32-bit per-lane offset plus a wave-uniform offset, so no
+// per-column 64-bit addresses are held across the GEMM loop.
 struct FoldOut {
-  typename E::T* rows;  // pt row of token column 0 of this block
-  float* pm;            // pm row of token column 0 of this block, at tile vt
-  int64_t Vpad, nvt;
-  int nvalid;           // token columns of this block that are loss rows
+  Src pt;            // this block's 256 pt rows (Vpad elements each)
+  Src pm;            // this block's 256 pm rows (nvt floats each)
+  uint32_t lane_t;   // byte offset in pt of column wn*64 + lane%16, vocabulary wm*128 + 4(lane/16)
+  uint32_t lane_m;   // byte offset in pm of column wn*64 + lane%16
+  uint32_t col16_t;  // bytes of 16 pt rows
+  uint32_t col16_m;  // bytes of 16 pm rows
+  uint32_t v0_t;     // byte offset of the tile's first vocabulary entry in a pt row
+  uint32_t vt_m;     // byte offset of the tile's entry in a pm row
+  int nvalid;        // token columns of this block that are loss rows
 };
 
 // Fold one 256 x 256 logit tile into this lane's running (max, sum of exp2) per token
@@ -378,7 +392,7 @@ template <class E, bool kFull, bool kStore>
 __device__ inline void fwd_fold(const Acc& acc, float s2, int vlim, int vb, int wm, int wn,
                                 int lane, int tid, float (*s_run)[kNB][kThreads],
                                 const int* s_y, float* s_zt, float (*s_cm)[256],
-                                const FoldOut<E>& fo) {
+                                const FoldOut& fo) {
   float cmax[kNB];
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
@@ -398,7 +412,7 @@ __device__ inline void fwd_fold(const Acc& acc, float s2, int vlim, int vb, int 
       cmax[nb] = t;
       if (lane < 16) s_cm[wm][wn * kWaveN + nb * 16 + lane] = t;
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
       const int n = wn * kWaveN + nb * 16 + (lane & 15);
@@ -413,23 +427,24 @@ __device__ inline void fwd_fold(const Acc& acc, float s2, int vlim, int vb, int 
     float sum = rm == -INFINITY ? 0.f : s_run[1][nb][tid] * exp2_fast(rm - nm);
     if (kStore) {
       const bool ok = n < fo.nvalid;
-      typename E::T* trow = fo.rows + (int64_t)n * fo.Vpad + vb;
+      // a column past the last loss row takes +inf as its reference, so its terms are
+      // stored as 0 (its sum is never read)
+      const float ns = ok ? nm : INFINITY;
+      const uint32_t so = (uint32_t)nb * fo.col16_t + fo.v0_t;
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb) {
-        uint16_t o[4];
+        float e[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          float e = 0.f;
-          if (kFull || mb * 16 + j < vlim) e = exp2_fast(fmaf(acc[mb][nb][j], s2, -nm));
-          sum += e;
-          o[j] = E::from_f32(ok ? e : 0.f);
+          e[j] = (kFull || mb * 16 + j < vlim) ? exp2_fast(fmaf(acc[mb][nb][j], s2, -ns)) : 0.f;
+          sum += e[j];
         }
-        uint2 pk;
-        pk.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
-        pk.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
-        *reinterpret_cast<uint2*>(trow + mb * 16) = pk;
+        const u32x2 pk = {E::pack2(e[0], e[1]), E::pack2(e[2], e[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(pk, fo.pt, fo.lane_t + mb * 32, so, 0);
       }
-      if (wm == 0 && lane < 16 && ok) fo.pm[(int64_t)n * fo.nvt] = nm;
+      if (wm == 0 && lane < 16 && ok)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(nm), fo.pm, fo.lane_m,
+                                              nb * fo.col16_m + fo.vt_m, 0);
     } else {
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb)
@@ -478,7 +493,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
   const int slots = gridDim.x / kXcds;           // workgroups per XCD
   const int ntok = *a.ntok;
   const FwdRange fr = fwd_range(a, ntok);
-  const int64_t TB = fr.TB;
+  const int TB = fr.TB;
   const int64_t nvt = (a.V + 255) / 256;
   const int P = fwd_phases(TB, nvt);
   const int tb_per_xcd = slots / P;
@@ -498,7 +513,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
       x_offsets(tok0, fr.rhi, a.idx, rowb, bo);
   };
 
-  int64_t tb = xcd * tb_per_xcd + slot / P;
+  int tb = xcd * tb_per_xcd + slot / P;
   if (tb >= TB) return;
   // loads of the first tile.  A phase with no vocabulary tile (V below P tiles) still
   // writes its empty partials (max -inf, sum 0) for every token block.
@@ -532,12 +547,18 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
       s_run[0][nb][tid] = -INFINITY;
       s_run[1][nb][tid] = 0.f;
     }
-    FoldOut<E> fo;
+    FoldOut fo;
     if (kStore) {
-      fo.rows = reinterpret_cast<typename E::T*>(a.pt) + (tok0 - a.row_lo) * a.Vpad;
-      fo.pm = a.pm + (tok0 - a.row_lo) * nvt;
-      fo.Vpad = a.Vpad;
-      fo.nvt = nvt;
+      const int64_t rt = a.Vpad * E::kBytes, rm = nvt * 4;  // bytes per pt, pm row
+      const char* pt0 = a.pt + (tok0 - a.row_lo) * rt;
+      const char* pm0 = reinterpret_cast<const char*>(a.pm + (tok0 - a.row_lo) * nvt);
+      fo.pt = make_src(pt0, pt0 + 256 * rt);
+      fo.pm = make_src(pm0, pm0 + 256 * rm);
+      const int col = wn * kWaveN + (lane & 15);
+      fo.lane_t = (uint32_t)(col * rt + (wm * 128 + 4 * (lane >> 4)) * E::kBytes);
+      fo.lane_m = (uint32_t)(col * rm);
+      fo.col16_t = (uint32_t)(16 * rt);
+      fo.col16_m = (uint32_t)(16 * rm);
       fo.nvalid = (int)(fr.rhi - tok0 < 256 ? fr.rhi - tok0 : 256);
     }
     for (int64_t vt = phase; vt < nvt; vt += P) {
@@ -548,7 +569,8 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
       // enqueue the next tile: the next vocabulary tile of this block, else the first
       // tile of this workgroup's next token block
       {
-        int64_t nv = vt + P, ntb = tb;
+        int64_t nv = vt + P;
+        int ntb = tb;
         if (nv >= nvt) {
           nv = phase;
           ntb = tb + tbg;
@@ -563,8 +585,11 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
       }
       const int vb = (int)(v0 + wm * 128 + 4 * (lane >> 4));  // vocab of acc[mb][.][j] = vb + 16 mb + j
       if (kF8) scale_acc(acc, a.sw, side ? a.sxp : a.sxq, vb, a.V, tok0, fr.rhi, wn, lane);
-      FoldOut<E> ft = fo;
-      if (kStore) ft.pm = fo.pm + vt;
+      FoldOut ft = fo;
+      if (kStore) {
+        ft.v0_t = (uint32_t)(v0 * E::kBytes);
+        ft.vt_m = (uint32_t)(vt * 4);
+      }
       if (v0 + 256 <= a.V)
         fwd_fold<E, true, kStore>(acc, s2, 0, vb, wm, wn, lane, tid, s_run, s_y, s_zt, s_cm, ft);
       else
@@ -766,15 +791,11 @@ dx_kernel(int64_t H, int64_t Vpad, int64_t R, int64_t c0, int nht, int ksplit,
         typename E::T* drow = dX + t * H;
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb) {
-          uint16_t o[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            o[j] = E::from_f32(acc[mb][nb][j] * gs);
-            bad |= !isfinite(E::to_f32(o[j]));
-          }
+          const f32x4 v = acc[mb][nb] * gs;
           uint2 pk;
-          pk.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
-          pk.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+          pk.x = E::pack2(v[0], v[1]);
+          pk.y = E::pack2(v[2], v[3]);
+          bad |= E::nonfinite2(pk.x) | E::nonfinite2(pk.y);
           *reinterpret_cast<uint2*>(drow + hb + mb * 16) = pk;
         }
       }
