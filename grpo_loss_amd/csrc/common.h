@@ -101,8 +101,8 @@ struct Plan {
   float scale2;     // log2(e) / temperature: logits -> log2 units of the softmax argument
   int fp8;          // logits from per-row e4m3 copies of X and W
   // byte offsets into the workspace
-  size_t off_ntok, off_idx, off_rank, off_part, off_lsum, off_seq, off_T, off_pm, off_WT,
-      off_TT, off_XgT, off_dxp, off_xq8, off_xp8, off_w8, off_sxq, off_sxp, off_sw, total;
+  size_t off_ntok, off_idx, off_rank, off_part, off_lsum, off_seq, off_T, off_pm, off_Xg,
+      off_dxp, off_xq8, off_xp8, off_w8, off_sxq, off_sxp, off_sw, total;
 };
 
 constexpr int kTokTile = 256;    // rows per token tile of the MFMA kernels

@@ -95,7 +95,7 @@ bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_d
   const int64_t Npad = (p->N + kTokTile - 1) / kTokTile * kTokTile;
   p->R = Npad < kChunkRows ? Npad : kChunkRows;
   // (the MFMA kernels address each operand with 32-bit byte offsets from a buffer base:
-  // X, W, W^T and one chunk of onehot - softmax must each stay below 4 GiB)
+  // X, W and one chunk of onehot - softmax must each stay below 4 GiB)
   const uint64_t k4G = (uint64_t)1 << 32;
   p->mfma = dtype != GRPO_F32 && H % 256 == 0 && (uint64_t)p->N * H * 2 < k4G &&
             (uint64_t)p->Vpad * H * 2 < k4G && (uint64_t)p->R * p->Vpad * 2 < k4G;
@@ -131,12 +131,8 @@ bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_d
   o = align_up(o + (size_t)p->R * p->Vpad * p->esize);
   p->off_pm = o;
   if (p->mfma) o = align_up(o + (size_t)p->R * (p->Vpad / kVocTile) * 4);
-  p->off_WT = o;
-  if (p->mfma) o = align_up(o + (size_t)H * p->Vpad * p->esize);
-  p->off_TT = o;
-  if (p->mfma && need_dW) o = align_up(o + (size_t)p->Vpad * p->R * p->esize);
-  p->off_XgT = o;
-  if (p->mfma && need_dW) o = align_up(o + (size_t)H * p->R * p->esize);
+  p->off_Xg = o;
+  if (p->mfma && need_dW) o = align_up(o + (size_t)p->R * H * p->esize);
   p->off_dxp = o;
   if (p->mfma && p->ksplit > 1) o = align_up(o + (size_t)p->ksplit * p->R * H * 4);
   if (p->fp8 && !p->mfma) return false;   // fp8 logits run on the MFMA kernels only

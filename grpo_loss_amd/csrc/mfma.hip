@@ -122,6 +122,78 @@ __device__ inline Src make_src(const char* base, const char* end) {
 typedef f32x4 Acc[kMB][kNB];
 typedef uint32_t Offs[4];
 
+// A second tile layout, for an operand stored with m (or n) contiguous and k as the row
+// index, such as W [V][H] as the A operand of dX = T W or a row block of T as the B operand
+// of dW = T^T X: 64 k-rows of 256 entries (512 B).  The 32-byte unit u of k-row r sits at
+// unit u ^ F(r) of its row, F(r) = (r & 3) | ((r >> 3) & 1) << 2.
+//
+// Fragments come from ds_read_b64_tr_b16: in each 16-lane group, source lane s addresses
+// 4 consecutive entries of one k-row, and lane j receives entry j % 4 of the rows read by
+// source lanes 4 i + j / 4, i = 0..3.  With source lane s pointing at k-row k0 + s / 4,
+// entries m0 + 4 (s % 4) .. + 3, lane j therefore holds k0 .. k0 + 3 of entry m0 + j, the
+// layout of half an MFMA operand.  Lane group g reads k-rows 8 g + 4 t + (0..3) for the
+// two halves t, so the 8 k-rows of a two-group read pass have 8 distinct F and their
+// 32-byte units fall on 8 distinct bank windows.
+//
+// Staging: wave w's instruction i writes k-rows 8 w + 2 i and 8 w + 2 i + 1 (1 KB); lane l
+// lands at 16-byte position l % 32 of k-row 8 w + 2 i + l / 32 and loads chunk
+// (l % 32) ^ 2 F(row) of that row.
+__device__ inline int nat_f(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
+
+// Staging offsets of a natural-layout operand with ld bytes per k-row.
+__device__ inline void nat_offsets(int64_t ld, Offs& o) {
+  const int l = (int)threadIdx.x & 63, w = (int)(threadIdx.x >> 6);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * w + 2 * i + (l >> 5);
+    o[i] = (uint32_t)(r * ld) + (uint32_t)(((l & 31) ^ (2 * nat_f(r))) << 4);
+  }
+}
+
+// An operand of the k loop.  kNat = false: rows are m (n) with k contiguous; k-step kt is
+// the byte offset 128 kt of every row.  kNat = true: rows are k; k-step kt starts kstep
+// bytes further, and the resource is rebuilt from there with the bytes left to the
+// operand's end, so that k-rows past it (a vocabulary padded past V) load as 0.
+template <bool kNat>
+struct Op;
+template <>
+struct Op<false> {
+  Src r;
+  __device__ inline Src at(int kt, int& so) const {
+    so = kt * 128;
+    return r;
+  }
+};
+template <>
+struct Op<true> {
+  const char* base;
+  int64_t left;   // bytes from base to the end of the operand
+  int64_t kstep;
+  __device__ inline Src at(int kt, int& so) const {
+    so = 0;
+    const int64_t o = (int64_t)kt * kstep;
+    const int64_t n = left - o;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + o), (short)0,
+                                             n > 0 ? (int)(uint32_t)n : 0, 0x00020000);
+  }
+};
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+// Half an MFMA operand (4 k of one m) from a natural-layout tile: see above.
+__device__ inline uint2 tr_read(const char* p) {
+  const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)(const_cast<char*>(p)));
+  return __builtin_bit_cast(uint2, v);
+}
+// The 8-k operand of fragment unit x (already XORed with F) for k half hf: rows
+// 32 hf + 8 g + 0..7 of this lane's entry.  lb is the lane's base: k-row 8 g + s / 4,
+// byte 8 (s % 4).
+__device__ inline uint4 nat_frag(const char* tile, int lb, int x, int hf) {
+  const char* q = tile + lb + (x << 5) + hf * (32 * 512);
+  const uint2 lo = tr_read(q), hi = tr_read(q + 4 * 512);
+  return uint4{lo.x, lo.y, hi.x, hi.y};
+}
+
 __device__ inline void zero_acc(Acc& acc) {
 #pragma unroll
   for (int i = 0; i < kMB; ++i)
@@ -129,18 +201,20 @@ __device__ inline void zero_acc(Acc& acc) {
     for (int j = 0; j < kNB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-// Enqueue the direct-to-LDS loads of k-step kt (byte 128 kt of every row) into stage S.
-template <int S>
-__device__ inline void stage_tiles(Src ra, Src rb, const Offs& ao, const Offs& bo, int kt,
-                                   int w) {
+// Enqueue the direct-to-LDS loads of k-step kt into stage S.
+template <int S, bool kNatA, bool kNatB>
+__device__ inline void stage_tiles(const Op<kNatA>& A, const Op<kNatB>& B, const Offs& ao,
+                                   const Offs& bo, int kt, int w) {
   char* sa = (S ? g_sA1 : g_sA0) + w * 4 * 1024;
   char* sb = (S ? g_sB1 : g_sB0) + w * 4 * 1024;
+  int soa, sob;
+  const Src ra = A.at(kt, soa), rb = B.at(kt, sob);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(sa + i * 1024), 16, (int)ao[i],
-                                             kt * 128, 0, 0);
+                                             soa, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(sb + i * 1024), 16, (int)bo[i],
-                                             kt * 128, 0, 0);
+                                             sob, 0, 0);
   }
 }
 
@@ -148,14 +222,18 @@ __device__ inline void stage_tiles(Src ra, Src rb, const Offs& ao, const Offs& b
 // wn*64 + nb*16 + (lane & 15) of B,
 // chunk ks*4 + (lane >> 4).  Both 32-wide halves' fragments are requested up front so the
 // second half's LDS reads are in flight while the first half's 64 MFMAs run.
-template <class G, int S>
-__device__ inline void mma_stage(Acc& acc, int fa, int fb, int fs, int lane) {
+// For a natural-layout A (B), fa (fb) is the lane base of nat_frag plus 256 wm (0), F is
+// the lane's F, and fragment mb (nb) is unit wm * 8 + mb (wn * 4 + nb).
+template <class G, int S, bool kNatA = false, bool kNatB = false>
+__device__ inline void mma_stage(Acc& acc, int fa, int fb, int fs, int lane, int F = 0,
+                                 int wn4 = 0, int kt = 0) {
   const char* As = S ? g_sA1 : g_sA0;
   const char* Bs = S ? g_sB1 : g_sB0;
   // Raised wave priority while this wave feeds the matrix unit: the arbiter then prefers
   // the MFMA-issuing wave over its SIMD neighbour that is between bursts (+10% measured).
   __builtin_amdgcn_s_setprio(1);
   if constexpr (G::kBytes == 1) {
+    static_assert(!kNatA && !kNatB, "fp8 operands are k-contiguous copies");
     // fp8: one 16 x 16 x 128 MFMA per block and k-step, chunks 2 g and 2 g + 1 per lane
     const int g2 = 2 * (lane >> 4);
     const int c0 = (g2 ^ fs) << 4;
@@ -180,14 +258,26 @@ __device__ inline void mma_stage(Acc& acc, int fa, int fb, int fs, int lane) {
     const int c0 = ((lane >> 4) ^ fs) << 4;
     const int c1 = ((4 + (lane >> 4)) ^ fs) << 4;
     uint4 a0[kMB], b0[kNB], a1[kMB], b1[kNB];
+    // F passed through an empty asm that depends on the k-step: the per-fragment addresses
+    // of natural-layout tiles are then formed at each read (one v_xad) instead of being
+    // held in registers across the k loop
+    if constexpr (kNatA || kNatB) asm("" : "+v"(F) : "s"(kt));
+    auto fa_ = [&](int mb, int hf) {
+      if constexpr (kNatA) return nat_frag(As, fa, mb ^ F, hf);
+      else return *reinterpret_cast<const uint4*>(As + fa + mb * 2048 + (hf ? c1 : c0));
+    };
+    auto fb_ = [&](int nb, int hf) {
+      if constexpr (kNatB) return nat_frag(Bs, fb, (wn4 + nb) ^ F, hf);
+      else return *reinterpret_cast<const uint4*>(Bs + fb + nb * 2048 + (hf ? c1 : c0));
+    };
 #pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) a0[mb] = *reinterpret_cast<const uint4*>(As + fa + mb * 2048 + c0);
+    for (int mb = 0; mb < kMB; ++mb) a0[mb] = fa_(mb, 0);
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) b0[nb] = *reinterpret_cast<const uint4*>(Bs + fb + nb * 2048 + c0);
+    for (int nb = 0; nb < kNB; ++nb) b0[nb] = fb_(nb, 0);
 #pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) a1[mb] = *reinterpret_cast<const uint4*>(As + fa + mb * 2048 + c1);
+    for (int mb = 0; mb < kMB; ++mb) a1[mb] = fa_(mb, 1);
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) b1[nb] = *reinterpret_cast<const uint4*>(Bs + fb + nb * 2048 + c1);
+    for (int nb = 0; nb < kNB; ++nb) b1[nb] = fb_(nb, 1);
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
@@ -219,9 +309,14 @@ __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 // First half of the k-loop prologue: enqueue k-step 0 into stage 0.  Stage 0 is free
 // once the previous gemm_main on this workgroup has returned, so a persistent kernel
 // issues its next tile's loads before working on the previous tile's accumulators.
-__device__ inline void gemm_pre(Src ra, Src rb, const Offs& ao, const Offs& bo) {
+template <bool kNatA = false, bool kNatB = false>
+__device__ inline void gemm_pre_op(const Op<kNatA>& A, const Op<kNatB>& B, const Offs& ao,
+                                   const Offs& bo) {
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  stage_tiles<0>(ra, rb, ao, bo, 0, w);
+  stage_tiles<0>(A, B, ao, bo, 0, w);
+}
+__device__ inline void gemm_pre(Src ra, Src rb, const Offs& ao, const Offs& bo) {
+  gemm_pre_op(Op<false>{ra}, Op<false>{rb}, ao, bo);
 }
 
 // acc += A . B^T over nk k-steps of 64 (nk even and > 0), k-step 0 already enqueued by
@@ -229,33 +324,47 @@ __device__ inline void gemm_pre(Src ra, Src rb, const Offs& ao, const Offs& bo) 
 // of B's for k-step 0.  On return every wave has finished reading stage 0 (the last barrier
 // of the loop follows its last reads), so stage 0 may be refilled at once; stage 1 is
 // refilled only after the first barrier of the next call.
-template <class E>
-__device__ inline void gemm_main(Src ra, Src rb, const Offs& ao, const Offs& bo, int nk,
-                                 Acc& acc) {
+template <class E, bool kNatA = false, bool kNatB = false>
+__device__ inline void gemm_main_op(const Op<kNatA>& A, const Op<kNatB>& B, const Offs& ao,
+                                    const Offs& bo, int nk, Acc& acc) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int wm = w / kWN, wn = w % kWN;
   const int fr = lane & 15;
   const int fs = swz_f(fr);
-  const int fa = (wm * 128 + fr) * 128;
-  const int fb = (wn * kWaveN + fr) * 128;
+  // natural-layout fragments: lane base (k-row 8 g + s / 4, byte 8 (s % 4)) and F of it
+  const int g = lane >> 4;
+  const int nlb = (8 * g + (fr >> 2)) * 512 + 8 * (fr & 3);
+  const int F = nat_f(8 * g + (fr >> 2));
+  const int fa = kNatA ? nlb + wm * 256 : (wm * 128 + fr) * 128;
+  const int fb = kNatB ? nlb : (wn * kWaveN + fr) * 128;
   for (int kt = 0; kt < nk; kt += 2) {
     wait_vmem();
     __syncthreads();  // stage 0 holds k-step kt; every wave is done reading stage 1
-    stage_tiles<1>(ra, rb, ao, bo, kt + 1, w);
-    mma_stage<E, 0>(acc, fa, fb, fs, lane);
+    stage_tiles<1>(A, B, ao, bo, kt + 1, w);
+    mma_stage<E, 0, kNatA, kNatB>(acc, fa, fb, fs, lane, F, wn * 4, kt);
     wait_vmem();
     __syncthreads();  // stage 1 holds k-step kt + 1; every wave is done reading stage 0
-    if (kt + 2 < nk) stage_tiles<0>(ra, rb, ao, bo, kt + 2, w);
-    mma_stage<E, 1>(acc, fa, fb, fs, lane);
+    if (kt + 2 < nk) stage_tiles<0>(A, B, ao, bo, kt + 2, w);
+    mma_stage<E, 1, kNatA, kNatB>(acc, fa, fb, fs, lane, F, wn * 4, kt + 1);
   }
 }
+template <class E>
+__device__ inline void gemm_main(Src ra, Src rb, const Offs& ao, const Offs& bo, int nk,
+                                 Acc& acc) {
+  gemm_main_op<E>(Op<false>{ra}, Op<false>{rb}, ao, bo, nk, acc);
+}
 
+template <class E, bool kNatA = false, bool kNatB = false>
+__device__ inline void gemm_core_op(const Op<kNatA>& A, const Op<kNatB>& B, const Offs& ao,
+                                    const Offs& bo, int nk, Acc& acc) {
+  gemm_pre_op(A, B, ao, bo);
+  gemm_main_op<E>(A, B, ao, bo, nk, acc);
+}
 template <class E>
 __device__ inline void gemm_core(Src ra, Src rb, const Offs& ao, const Offs& bo, int nk,
                                  Acc& acc) {
-  gemm_pre(ra, rb, ao, bo);
-  gemm_main<E>(ra, rb, ao, bo, nk, acc);
+  gemm_core_op<E>(Op<false>{ra}, Op<false>{rb}, ao, bo, nk, acc);
 }
 
 // ------------------------------------------------------------------------------ forward
@@ -731,7 +840,8 @@ recompute_kernel(int64_t N, int64_t H, int64_t V, int64_t Vpad, int64_t c0, int 
 }
 
 // ------------------------------------------------------------------------------- dX
-// C[h][r] = sum_v W^T[h][v] T[r][v] over the padded vocabulary (or one split of it).
+// C[h][r] = sum_v W[v][h] T[r][v] over the padded vocabulary (or one split of it), with W
+// read in its own [V][H] layout (natural-layout A tiles; rows past V load as 0).
 // ksplit == 1: dX[idx[r]][h] = c * g_r * C, in the storage type.  ksplit > 1: fp32
 // partials to dxp[ks][r - c0][h], reduced by dx_reduce_kernel.
 //
@@ -741,9 +851,9 @@ recompute_kernel(int64_t N, int64_t H, int64_t V, int64_t Vpad, int64_t c0, int 
 // runs on XCD b % 8), so the items that share a T tile and k range run on one XCD.
 template <class E>
 __global__ void __launch_bounds__(kThreads, 1)
-dx_kernel(int64_t H, int64_t Vpad, int64_t R, int64_t c0, int nht, int ksplit,
+dx_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int nht, int ksplit,
           const int32_t* __restrict__ ntok_p, const int32_t* __restrict__ idx,
-          const char* __restrict__ WT, const char* __restrict__ T,
+          const char* __restrict__ W, const char* __restrict__ T,
           const float* __restrict__ saved, const float* __restrict__ grad_loss, float loss_scale,
           typename E::T* __restrict__ dX, float* __restrict__ dxp,
           int32_t* __restrict__ found_inf) {
@@ -758,13 +868,14 @@ dx_kernel(int64_t H, int64_t Vpad, int64_t R, int64_t c0, int nht, int ksplit,
   const int64_t first = (int64_t)(blockIdx.x % kXcds) * (nwg / kXcds) + blockIdx.x / kXcds;
   // k-steps of 64 split into ksplit ranges with even boundaries (Vpad / 64 is a multiple of 4)
   const int64_t npair = Vpad / 128;
-  const int64_t rowb = Vpad * 2;
+  const int64_t rowb = Vpad * 2;  // bytes per T row
+  const int64_t ldw = H * 2;      // bytes per W row
   Offs ao, bo;
+  nat_offsets(ldw, ao);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int sr = stage_row(i);
-    ao[i] = (uint32_t)(sr * rowb) + stage_chunk_bytes(sr);
-    bo[i] = ao[i];
+    bo[i] = (uint32_t)(sr * rowb) + stage_chunk_bytes(sr);
   }
   const float c = (grad_loss ? *grad_loss : 1.f) / loss_scale;
   bool bad = false;
@@ -777,9 +888,10 @@ dx_kernel(int64_t H, int64_t Vpad, int64_t R, int64_t c0, int nht, int ksplit,
     Acc acc;
     zero_acc(acc);
     if (kend > kbeg)
-      gemm_core<E>(make_src(WT + h0 * rowb + kbeg * 128, WT + H * rowb),
-                   make_src(T + tt * 256 * rowb + kbeg * 128, T + R * rowb), ao, bo,
-                   (int)(kend - kbeg), acc);
+      gemm_core_op<E, true, false>(
+          Op<true>{W + h0 * 2 + kbeg * 64 * ldw, (V - kbeg * 64) * ldw - h0 * 2, 64 * ldw},
+          Op<false>{make_src(T + tt * 256 * rowb + kbeg * 128, T + R * rowb)}, ao, bo,
+          (int)(kend - kbeg), acc);
     const int64_t hb = h0 + wm * 128 + 4 * (lane >> 4);
     if (ksplit == 1) {
 #pragma unroll
@@ -846,12 +958,14 @@ dx_reduce_kernel(int64_t H, int64_t R, int64_t c0, int ksplit, const int32_t* __
 }
 
 // ------------------------------------------------------------------------------- dW
-// C[h][v] = sum_r XgT[h][r] TT[v][r] over the chunk's rows; dW[v][h] (+)= C.
+// C[h][v] = sum_r Xg[r][h] T[r][v] over the chunk's rows; dW[v][h] (+)= C.  Both operands
+// are natural-layout tiles read in place: Xg [R][H] (gather_rows_kernel) and the chunk's
+// T [R][Vpad].
 template <class E>
 __global__ void __launch_bounds__(kThreads, 1)
-dw_kernel(int64_t H, int64_t V, int64_t R, int64_t c0, int nht, int accumulate,
-          const int32_t* __restrict__ ntok_p, const char* __restrict__ XgT,
-          const char* __restrict__ TT, float* __restrict__ dW, int32_t* __restrict__ found_inf) {
+dw_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int nht, int accumulate,
+          const int32_t* __restrict__ ntok_p, const char* __restrict__ Xg,
+          const char* __restrict__ T, float* __restrict__ dW, int32_t* __restrict__ found_inf) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / kWN, wn = w % kWN;
   const int64_t ht = blockIdx.x % nht, vt = blockIdx.x / nht;
   const int ntok = *ntok_p;
@@ -860,23 +974,19 @@ dw_kernel(int64_t H, int64_t V, int64_t R, int64_t c0, int nht, int accumulate,
   if (nrows <= 0 && accumulate) return;
   if (nrows < 0) nrows = 0;
   // rows padded to a multiple of 128 (an even number of k-steps); the padding rows of
-  // T^T and (g X)^T are zero
+  // T and Xg are zero
   const int64_t nk = 2 * ((nrows + 127) / 128);
   const int64_t h0 = ht * 256, v0 = vt * 256;
-  const int64_t rowb = R * 2;
+  const int64_t ldx = H * 2, ldt = Vpad * 2;
   Offs ao, bo;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int sr = stage_row(i);
-    ao[i] = (uint32_t)(sr * rowb) + stage_chunk_bytes(sr);
-    bo[i] = ao[i];
-  }
+  nat_offsets(ldx, ao);
+  nat_offsets(ldt, bo);
   Acc acc;
   zero_acc(acc);
-  const int64_t Vpad = (int64_t)(gridDim.x / nht) * 256;  // rows of T^T
   if (nk > 0)
-    gemm_core<E>(make_src(XgT + h0 * rowb, XgT + H * rowb), make_src(TT + v0 * rowb, TT + Vpad * rowb),
-                 ao, bo, (int)nk, acc);
+    gemm_core_op<E, true, true>(Op<true>{Xg + h0 * 2, R * ldx - h0 * 2, 64 * ldx},
+                                Op<true>{T + v0 * 2, R * ldt - v0 * 2, 64 * ldt}, ao, bo, (int)nk,
+                                acc);
   const int64_t hb = h0 + wm * 128 + 4 * (lane >> 4);
   bool bad = false;
 #pragma unroll
@@ -897,73 +1007,37 @@ dw_kernel(int64_t H, int64_t V, int64_t R, int64_t c0, int nht, int accumulate,
   if (bad) atomicOr(found_inf, 1);
 }
 
-// --------------------------------------------------------------------------- transposes
-// out[j][i] = scale_i * in[row(i)][j] for 16-bit data, through a 64 x 64 LDS tile.
-//   mode 0: row(i) = i, scale 1, rows i >= nvalid_i are written as 0 (W -> W^T padded, T -> T^T)
-//   mode 1: row(i) = idx[c0 + i], scale = c * g, rows past the last loss token are 0
-//           (X_q chunk -> (g X_q)^T)
-template <class E, int kMode>
+// --------------------------------------------------------------------------- dW operand
+// Xg[rl][h] = c g_r X_q[idx[c0 + rl]][h] in the storage type for the chunk's loss rows
+// rl < nrows, and 0 for the rows from nrows up to the next multiple of 128 (the k range of
+// dw_kernel).  One row per block, 8 entries (16 bytes) per thread and step.
+template <class E>
 __global__ void __launch_bounds__(256)
-transpose_kernel(const typename E::T* __restrict__ in, int64_t ld_in, int64_t nvalid_i,
-                 int64_t ncols_j, typename E::T* __restrict__ out, int64_t ld_out, int64_t c0,
-                 const int32_t* __restrict__ ntok_p, const int32_t* __restrict__ idx,
-                 const float* __restrict__ saved, const float* __restrict__ grad_loss,
-                 float loss_scale) {
-  __shared__ uint16_t tile[64][66];
-  const int64_t i0 = (int64_t)blockIdx.x * 64, j0 = (int64_t)blockIdx.y * 64;
-  const int tid = threadIdx.x;
-  int64_t ni = nvalid_i;
-  if (kMode == 1) {
-    int64_t nr = (int64_t)(*ntok_p) - c0;
-    if (nr < ni) ni = nr;
+gather_rows_kernel(const typename E::T* __restrict__ X, int64_t H, int64_t R, int64_t c0,
+                   const int32_t* __restrict__ ntok_p, const int32_t* __restrict__ idx,
+                   const float* __restrict__ saved, const float* __restrict__ grad_loss,
+                   float loss_scale, typename E::T* __restrict__ Xg) {
+  const int64_t rl = blockIdx.x;
+  int64_t nrows = (int64_t)(*ntok_p) - c0;
+  if (nrows > R) nrows = R;
+  if (nrows <= 0 || rl >= (nrows + 127) / 128 * 128) return;
+  uint4* dst = reinterpret_cast<uint4*>(Xg + rl * H);
+  if (rl >= nrows) {
+    for (int64_t h8 = threadIdx.x; h8 < H / 8; h8 += 256) dst[h8] = uint4{0u, 0u, 0u, 0u};
+    return;
   }
-  // load: thread -> row i0 + tid / 4, 16 consecutive j
-  {
-    const int li = tid >> 2, lj = (tid & 3) * 16;
-    const int64_t i = i0 + li;
-    uint16_t v[16];
-    if (i < ni && j0 + lj < ncols_j) {
-      int64_t row = i;
-      float sc = 1.f;
-      if (kMode == 1) {
-        row = idx[c0 + i];
-        sc = saved[row * 4 + 3] * ((grad_loss ? *grad_loss : 1.f) / loss_scale);
-      }
-      const uint4* src = reinterpret_cast<const uint4*>(in + row * ld_in + j0 + lj);
-      uint4 q0 = src[0], q1 = src[1];
-      const uint16_t* h0 = reinterpret_cast<const uint16_t*>(&q0);
-      const uint16_t* h1 = reinterpret_cast<const uint16_t*>(&q1);
+  const int64_t t = idx[c0 + rl];
+  const float sc = saved[t * 4 + 3] * ((grad_loss ? *grad_loss : 1.f) / loss_scale);
+  const uint4* src = reinterpret_cast<const uint4*>(X + t * H);
+  for (int64_t h8 = threadIdx.x; h8 < H / 8; h8 += 256) {
+    const uint4 q = src[h8];
+    const uint32_t in[4] = {q.x, q.y, q.z, q.w};
+    uint32_t out[4];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        v[k] = h0[k];
-        v[8 + k] = h1[k];
-      }
-      if (kMode == 1) {
-#pragma unroll
-        for (int k = 0; k < 16; ++k) v[k] = E::from_f32(sc * E::to_f32(v[k]));
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) v[k] = 0;
-    }
-#pragma unroll
-    for (int k = 0; k < 16; ++k) tile[li][lj + k] = v[k];
-  }
-  __syncthreads();
-  {
-    const int lj = tid >> 2, li = (tid & 3) * 16;
-    const int64_t j = j0 + lj;
-    if (j < ncols_j) {
-      uint16_t v[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) v[k] = tile[li + k][lj];
-      uint4 q0, q1;
-      __builtin_memcpy(&q0, v, 16);
-      __builtin_memcpy(&q1, v + 8, 16);
-      uint4* dst = reinterpret_cast<uint4*>(out + j * ld_out + i0 + li);
-      dst[0] = q0;
-      dst[1] = q1;
-    }
+    for (int k = 0; k < 4; ++k)
+      out[k] = E::pack2(sc * E::to_f32((typename E::T)(in[k] & 0xffffu)),
+                        sc * E::to_f32((typename E::T)(in[k] >> 16)));
+    dst[h8] = uint4{out[0], out[1], out[2], out[3]};
   }
 }
 
@@ -1024,31 +1098,19 @@ hipError_t fwd_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, con
   return hipGetLastError();
 }
 
-// W^T [H][Vpad], zero-padded past V.
-template <class E>
-hipError_t transpose_w(const Plan& p, void* ws, const void* W, hipStream_t st) {
-  typedef typename E::T T;
-  hipLaunchKernelGGL((transpose_kernel<E, 0>), dim3((unsigned)(p.Vpad / 64), (unsigned)(p.H / 64)),
-                     dim3(256), 0, st, (const T*)W, p.H, p.V, p.H, ws_ptr<T>(ws, p.off_WT), p.Vpad,
-                     (int64_t)0, ws_ptr<int32_t>(ws, p.off_ntok), ws_ptr<int32_t>(ws, p.off_idx),
-                     (const float*)nullptr, (const float*)nullptr, 1.f);
-  return hipGetLastError();
-}
-
 // dX (and dW) of the loss rows of chunk c0 from the chunk's T = onehot - softmax.
 template <class E>
-hipError_t chunk_grads(const Plan& p, void* ws, int64_t c0, const void* Xq, const float* saved,
-                       const float* grad_loss, float loss_scale, void* dX, float* dW,
-                       int accumulate_dW, int32_t* found_inf, hipStream_t st) {
+hipError_t chunk_grads(const Plan& p, void* ws, int64_t c0, const void* Xq, const void* W,
+                       const float* saved, const float* grad_loss, float loss_scale, void* dX,
+                       float* dW, int accumulate_dW, int32_t* found_inf, hipStream_t st) {
   typedef typename E::T T;
   const int32_t* ntok = ws_ptr<int32_t>(ws, p.off_ntok);
   const int32_t* idx = ws_ptr<int32_t>(ws, p.off_idx);
   T* Tb = ws_ptr<T>(ws, p.off_T);
-  T* WT = ws_ptr<T>(ws, p.off_WT);
-  const int ntt = (int)(p.R / 256), nvt = (int)(p.Vpad / 256), nht = (int)(p.H / 256);
+  const int nvt = (int)(p.Vpad / 256), nht = (int)(p.H / 256);
   hipError_t e;
   hipLaunchKernelGGL(dx_kernel<E>, dim3(kNumWG), dim3(kThreads), 0, st,
-                     p.H, p.Vpad, p.R, c0, nht, p.ksplit, ntok, idx, (const char*)WT,
+                     p.H, p.V, p.Vpad, p.R, c0, nht, p.ksplit, ntok, idx, (const char*)W,
                      (const char*)Tb, saved, grad_loss, loss_scale, (T*)dX,
                      ws_ptr<float>(ws, p.off_dxp), found_inf);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1059,19 +1121,13 @@ hipError_t chunk_grads(const Plan& p, void* ws, int64_t c0, const void* Xq, cons
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (dW) {
-    T* TT = ws_ptr<T>(ws, p.off_TT);
-    T* XgT = ws_ptr<T>(ws, p.off_XgT);
-    hipLaunchKernelGGL((transpose_kernel<E, 0>), dim3((unsigned)(p.R / 64), (unsigned)(p.Vpad / 64)),
-                       dim3(256), 0, st, (const T*)Tb, p.Vpad, p.R, p.Vpad, TT, p.R, c0, ntok,
-                       idx, saved, grad_loss, loss_scale);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((transpose_kernel<E, 1>), dim3((unsigned)(p.R / 64), (unsigned)(p.H / 64)),
-                       dim3(256), 0, st, (const T*)Xq, p.H, p.R, p.H, XgT, p.R, c0, ntok, idx,
-                       saved, grad_loss, loss_scale);
+    T* Xg = ws_ptr<T>(ws, p.off_Xg);
+    hipLaunchKernelGGL(gather_rows_kernel<E>, dim3((unsigned)p.R), dim3(256), 0, st,
+                       (const T*)Xq, p.H, p.R, c0, ntok, idx, saved, grad_loss, loss_scale, Xg);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(dw_kernel<E>, dim3((unsigned)(nht * nvt)), dim3(kThreads), 0, st, p.H,
-                       p.V, p.R, c0, nht, c0 == 0 ? accumulate_dW : 1, ntok, (const char*)XgT,
-                       (const char*)TT, dW, found_inf);
+                       p.V, p.Vpad, p.R, c0, nht, c0 == 0 ? accumulate_dW : 1, ntok,
+                       (const char*)Xg, (const char*)Tb, dW, found_inf);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
@@ -1087,8 +1143,7 @@ hipError_t bwd_impl(const Plan& p, void* ws, const void* Xq, const void* W,
   const int32_t* ntok = ws_ptr<int32_t>(ws, p.off_ntok);
   const int32_t* idx = ws_ptr<int32_t>(ws, p.off_idx);
   T* Tb = ws_ptr<T>(ws, p.off_T);
-  hipError_t e = transpose_w<E>(p, ws, W, st);
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
   if (kF8 && (e = quantize_operands(p, ws, Xq, nullptr, W, st)) != hipSuccess) return e;
   const char* Xop = kF8 ? ws_ptr<char>(ws, p.off_xq8) : (const char*)Xq;
   const char* Wop = kF8 ? ws_ptr<char>(ws, p.off_w8) : (const char*)W;
@@ -1099,7 +1154,7 @@ hipError_t bwd_impl(const Plan& p, void* ws, const void* Xq, const void* W,
                        saved, Tb, (const float*)ws_ptr<float>(ws, p.off_sw),
                        (const float*)ws_ptr<float>(ws, p.off_sxq));
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    e = chunk_grads<E>(p, ws, c0, Xq, saved, grad_loss, loss_scale, dX, dW, accumulate_dW,
+    e = chunk_grads<E>(p, ws, c0, Xq, W, saved, grad_loss, loss_scale, dX, dW, accumulate_dW,
                        found_inf, st);
     if (e != hipSuccess) return e;
   }
@@ -1124,7 +1179,6 @@ hipError_t fused_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, c
   const int64_t nvt = (p.V + 255) / 256;
   hipError_t e = launch_zero_masked_outputs(p, mask, saved, logp, ref_logp, kl, st);
   if (e != hipSuccess) return e;
-  if ((e = transpose_w<E>(p, ws, W, st)) != hipSuccess) return e;
   if (G::kBytes == 1 && (e = quantize_operands(p, ws, Xq, Xp, W, st)) != hipSuccess) return e;
   FwdArgs a = fwd_args(p, ws, Xq, Xp, W, targets);
   a.side0 = 1;
@@ -1146,7 +1200,7 @@ hipError_t fused_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, c
                        dim3(256), 0, st, p.Vpad, nvt, c0, ntok, idx, targets, saved,
                        (const float*)pm, Tb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    e = chunk_grads<E>(p, ws, c0, Xq, saved, grad_loss, loss_scale, dX, dW, accumulate_dW,
+    e = chunk_grads<E>(p, ws, c0, Xq, W, saved, grad_loss, loss_scale, dX, dW, accumulate_dW,
                        found_inf, st);
     if (e != hipSuccess) return e;
   }
