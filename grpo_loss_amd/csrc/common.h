@@ -102,7 +102,7 @@ struct Plan {
   int fp8;          // logits from per-row e4m3 copies of X and W
   // byte offsets into the workspace
   size_t off_ntok, off_idx, off_rank, off_part, off_lsum, off_seq, off_T, off_pm, off_Xg,
-      off_dxp, off_xq8, off_xp8, off_w8, off_sxq, off_sxp, off_sw, total;
+      off_redo, off_dxp, off_xq8, off_xp8, off_w8, off_sxq, off_sxp, off_sw, total;
 };
 
 constexpr int kTokTile = 256;    // rows per token tile of the MFMA kernels
@@ -154,10 +154,13 @@ hipError_t launch_merge(const Plan& p, const void* ws, const int64_t* targets,
                         hipStream_t st);
 // Single-pass forward: merge of compact rows [c0, c0 + R) (R = Plan::R), the zeroing of
 // masked rows' outputs, and the loss reduction (compact = 1: block sums over loss rows).
+// redo (non-null): the policy partials are fixed-reference ones, and a row out of their
+// range sets *redo; gate (non-null): merge only when *gate != 0.
 hipError_t launch_merge_rows(const Plan& p, const void* ws, int64_t c0, const int64_t* targets,
                              const uint8_t* mask, const float* adv, float beta, float* saved,
                              float* logp, float* ref_logp, float* kl, int32_t* status,
-                             hipStream_t st);
+                             hipStream_t st, int32_t* redo = nullptr,
+                             const int32_t* gate = nullptr);
 hipError_t launch_zero_masked_outputs(const Plan& p, const uint8_t* mask, float* saved,
                                       float* logp, float* ref_logp, float* kl, hipStream_t st);
 hipError_t launch_loss_final(const Plan& p, const void* ws, int compact, int32_t* status,

@@ -86,6 +86,12 @@ struct MergeArgs {
   int32_t* status;
   double* lsum;
   int64_t c0, R;        // chunked merge: compact rows [c0, c0 + R)
+  // Single-pass mode 3 (non-null): the policy partials share the row's reference mr as
+  // their maximum; a row whose sum of terms 2^(lse2_q - mr) lies outside [2^-60, 2^60]
+  // (overflowed, or so small that terms below 2^-126 were dropped) sets *redo, and its
+  // outputs, left for the fallback to rewrite, raise no status flag.
+  int32_t* redo;
+  const int32_t* gate;  // merge only when *gate != 0 (null: always)
 };
 
 // Per loss row t (compact index r):
@@ -111,8 +117,16 @@ __device__ inline double merge_row(const MergeArgs& a, int64_t t, int64_t r, int
   float lse_q, zq, lse_p, zp;
   merge_side(pm, ps, pz, used0, N, r, &lse_q, &zq);
   merge_side(pm + PN, ps + PN, pz + PN, used1, N, r, &lse_p, &zp);
+  bool quiet = false;
+  if (a.redo) {
+    const float l2s = lse_q * kLog2e - pm[r];
+    if (!(l2s >= -60.f && l2s <= 60.f)) {
+      atomicOr(a.redo, 1);
+      quiet = true;
+    }
+  }
   const int64_t y = a.targets[t];
-  if (y < 0 || y >= a.V) *flags |= GRPO_FLAG_BAD_TARGET;
+  if ((y < 0 || y >= a.V) && !quiet) *flags |= GRPO_FLAG_BAD_TARGET;
   const float q = zq * a.inv_tau - lse_q;
   const float ref = zp * a.inv_tau - lse_p;
   const float d = ref - q;
@@ -146,7 +160,8 @@ __device__ inline double merge_row(const MergeArgs& a, int64_t t, int64_t r, int
   if (a.logp) a.logp[t] = q;
   if (a.ref_logp) a.ref_logp[t] = ref;
   if (a.kl_out) a.kl_out[t] = klv;
-  if (!isfinite(lse_q) || !isfinite(q) || !isfinite(ref) || !isfinite(klv) || !isfinite(g))
+  if (!quiet &&
+      (!isfinite(lse_q) || !isfinite(q) || !isfinite(ref) || !isfinite(klv) || !isfinite(g)))
     *flags |= GRPO_FLAG_NONFINITE;
   return ell_d;
 }
@@ -193,6 +208,7 @@ __global__ void __launch_bounds__(kMergeBlock) merge_kernel(MergeArgs a) {
 // aligned to 256 compact rows, so lsum[r / 256] sums the same rows in the same order
 // whatever the chunking.
 __global__ void __launch_bounds__(kMergeBlock) merge_rows_kernel(MergeArgs a) {
+  if (a.gate && *a.gate == 0) return;
   const int32_t ntok = *a.ntok;
   const int64_t r = a.c0 + (int64_t)blockIdx.x * kMergeBlock + threadIdx.x;
   const int64_t blk0 = a.c0 / kMergeBlock + blockIdx.x;
@@ -389,6 +405,8 @@ hipError_t launch_merge(const Plan& p, const void* ws, const int64_t* targets,
   a.lsum = ws_ptr<double>(w, p.off_lsum);
   a.c0 = 0;
   a.R = p.N;
+  a.redo = nullptr;
+  a.gate = nullptr;
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)nblocks), dim3(kMergeBlock), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -410,7 +428,7 @@ hipError_t launch_loss_final(const Plan& p, const void* ws, int compact, int32_t
 hipError_t launch_merge_rows(const Plan& p, const void* ws, int64_t c0, const int64_t* targets,
                              const uint8_t* mask, const float* adv, float beta, float* saved,
                              float* logp, float* ref_logp, float* kl, int32_t* status,
-                             hipStream_t st) {
+                             hipStream_t st, int32_t* redo, const int32_t* gate) {
   void* w = const_cast<void*>(ws);
   MergeArgs a;
   a.N = p.N;
@@ -440,6 +458,8 @@ hipError_t launch_merge_rows(const Plan& p, const void* ws, int64_t c0, const in
   a.lsum = ws_ptr<double>(w, p.off_lsum);
   a.c0 = c0;
   a.R = p.R;
+  a.redo = redo;
+  a.gate = gate;
   hipLaunchKernelGGL(merge_rows_kernel, dim3((unsigned)(p.R / kMergeBlock)), dim3(kMergeBlock),
                      0, st, a);
   return hipGetLastError();

@@ -133,6 +133,8 @@ bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_d
   if (p->mfma) o = align_up(o + (size_t)p->R * (p->Vpad / kVocTile) * 4);
   p->off_Xg = o;
   if (p->mfma && need_dW) o = align_up(o + (size_t)p->R * H * p->esize);
+  p->off_redo = o;  // single-pass fallback flags, one per chunk
+  if (p->mfma) o = align_up(o + (size_t)((p->N + p->R - 1) / p->R) * 4);
   p->off_dxp = o;
   if (p->mfma && p->ksplit > 1) o = align_up(o + (size_t)p->ksplit * p->R * H * 4);
   if (p->fp8 && !p->mfma) return false;   // fp8 logits run on the MFMA kernels only

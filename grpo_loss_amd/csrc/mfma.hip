@@ -391,6 +391,8 @@ struct FwdArgs {
   char* pt;
   float* pm;
   int64_t Vpad;
+  // Launch only when *gate != 0 (null: always); the single-pass fallback of a chunk.
+  const int32_t* gate;
   // fp8 logits: per-row e4m3 copies of W [V][H] and of the loss rows of X_q and X_p
   // [compact row][H], with their fp32 scales; the logit is scale_w * scale_x * (W8 . X8)
   const char* W8;
@@ -575,6 +577,45 @@ __device__ inline void fwd_fold(const Acc& acc, float s2, int vlim, int vb, int 
   }
 }
 
+// Fixed-reference fold (single-pass mode 3): the terms of token column n are
+// exp2(z s2 - mr_n), mr_n the reference side's log-sum-exp of the row (log2 units), so no
+// running maximum is kept and the tiles of a row need no common reference.  The terms are
+// summed per lane and stored; mr_n = +inf (past the last loss row) stores zeros.
+template <class E, bool kFull>
+__device__ inline void fwd_fold_fixed(const Acc& acc, float s2, int vlim, int vb, int wn,
+                                      int lane, int tid, float (*s_run)[kNB][kThreads],
+                                      const int* s_y, float* s_zt, const float* s_mr,
+                                      const FoldOut& fo) {
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    const int n = wn * kWaveN + nb * 16 + (lane & 15);
+    const float mr = s_mr[n];
+    float sum = s_run[1][nb][tid];
+    const uint32_t so = (uint32_t)nb * fo.col16_t + fo.v0_t;
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) {
+      float e[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        e[j] = (kFull || mb * 16 + j < vlim) ? exp2_fast(fmaf(acc[mb][nb][j], s2, -mr)) : 0.f;
+        sum += e[j];
+      }
+      const u32x2 pk = {E::pack2(e[0], e[1]), E::pack2(e[2], e[3])};
+      __builtin_amdgcn_raw_buffer_store_b64(pk, fo.pt, fo.lane_t + mb * 32, so, 0);
+    }
+    s_run[1][nb][tid] = sum;
+    const int loc = s_y[n] - vb;
+    if ((unsigned)loc < 128u && (loc & 12) == 0) {  // this lane holds the target logit
+      float z = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) z = (loc == mb * 16 + j) ? acc[mb][nb][j] : z;
+      s_zt[n] = z;
+    }
+  }
+}
+
 // Persistent.  Workgroup w runs on XCD w % 8; its slot s = w / 8 picks a token block of
 // the current round and a vocabulary phase: the 32 workgroups of one XCD cover 32 / P
 // token blocks x P phases (P = fwd_phases(...), 8 for the long-context shape), so each W
@@ -586,17 +627,24 @@ __device__ inline void fwd_fold(const Acc& acc, float s2, int vlim, int vb, int 
 // each next tile are issued before the previous tile is folded, so the fold overlaps the
 // first k-step's memory latency.
 // kMode 0: both sides over all rows (two-pass forward); 1: one side over all rows
-// (single-pass reference); 2: policy rows of one chunk, softmax terms kept (single-pass).
-// Modes 0 and 1 run the same code; distinct instances keep their profiles apart.
+// (single-pass reference); 2: policy rows of one chunk, softmax terms kept relative to a
+// running maximum (single-pass); 3: as 2 with the reference side's log-sum-exp of each
+// row as the fixed reference of its terms, which mode 1 must have produced: its partials
+// are merged per row at the start of each token block, and workgroups of phase 0 store
+// the result at pm[r - row_lo].  The partials of mode 3 carry that reference as their
+// maximum.  Modes 0 and 1 run the same code; distinct instances keep their profiles apart.
 template <class E, class G, int kMode>
 __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
-  constexpr bool kStore = kMode == 2;
+  constexpr bool kFixed = kMode == 3;
+  constexpr bool kStore = kMode == 2 || kFixed;
   constexpr bool kF8 = G::kBytes == 1;   // operands are the fp8 copies
   __shared__ float mrg[2][2][256];
   __shared__ float s_run[2][kNB][kThreads];
   __shared__ int s_y[256];
   __shared__ float s_zt[256];
-  __shared__ float s_cm[kStore ? 2 : 1][256];
+  __shared__ float s_cm[kMode == 2 ? 2 : 1][256];
+  __shared__ float s_mr[kFixed ? 256 : 1];
+  if (a.gate && *a.gate == 0) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / kWN, wn = w % kWN;
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
   const int slots = gridDim.x / kXcds;           // workgroups per XCD
@@ -650,6 +698,26 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
       }
       s_y[tid] = yy;
       s_zt[tid] = 0.f;
+      if (kFixed) {
+        // the reference side's log-sum-exp of row r from the partials of the mode-1 launch
+        float mr = INFINITY;
+        if (r < fr.rhi) {
+          const int used = fwd_phases(((int64_t)ntok + 255) / 256, nvt);
+          const int64_t PN = (int64_t)kMaxPhases * a.N;
+          const float* pmx = a.part + (int64_t)kMaxPhases * a.N;  // side 1 maxima
+          const float* psx = pmx + 2 * PN;                          // side 1 sums
+          float M = -INFINITY;
+          for (int ph = 0; ph < used; ++ph) M = fmaxf(M, pmx[ph * a.N + r]);
+          float sm = 0.f;
+          for (int ph = 0; ph < used; ++ph) {
+            const float sp = psx[ph * a.N + r];
+            if (sp != 0.f) sm += sp * exp2f(pmx[ph * a.N + r] - M);
+          }
+          mr = M + log2f(sm);
+          if (phase == 0) a.pm[r - a.row_lo] = mr;
+        }
+        s_mr[tid] = mr;
+      }
     }
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
@@ -699,16 +767,26 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
         ft.v0_t = (uint32_t)(v0 * E::kBytes);
         ft.vt_m = (uint32_t)(vt * 4);
       }
-      if (v0 + 256 <= a.V)
-        fwd_fold<E, true, kStore>(acc, s2, 0, vb, wm, wn, lane, tid, s_run, s_y, s_zt, s_cm, ft);
-      else
-        fwd_fold<E, false, kStore>(acc, s2, (int)(a.V - vb), vb, wm, wn, lane, tid, s_run, s_y,
-                                   s_zt, s_cm, ft);
+      if constexpr (kFixed) {
+        if (v0 + 256 <= a.V)
+          fwd_fold_fixed<E, true>(acc, s2, 0, vb, wn, lane, tid, s_run, s_y, s_zt, s_mr, ft);
+        else
+          fwd_fold_fixed<E, false>(acc, s2, (int)(a.V - vb), vb, wn, lane, tid, s_run, s_y,
+                                   s_zt, s_mr, ft);
+      } else {
+        if (v0 + 256 <= a.V)
+          fwd_fold<E, true, kStore>(acc, s2, 0, vb, wm, wn, lane, tid, s_run, s_y, s_zt, s_cm,
+                                    ft);
+        else
+          fwd_fold<E, false, kStore>(acc, s2, (int)(a.V - vb), vb, wm, wn, lane, tid, s_run,
+                                     s_y, s_zt, s_cm, ft);
+      }
     }
     // merge the four lane groups holding each token column, then the two m-waves
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
-      float m = s_run[0][nb][tid], sum = s_run[1][nb][tid];
+      float m = kFixed ? s_mr[wn * kWaveN + nb * 16 + (lane & 15)] : s_run[0][nb][tid];
+      float sum = s_run[1][nb][tid];
 #pragma unroll
       for (int off = 16; off <= 32; off <<= 1) {
         const float m2 = __shfl_xor(m, off), s2x = __shfl_xor(sum, off);
@@ -746,14 +824,16 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
   }
 }
 
-// Single-pass mode, after the merge of a chunk: T = onehot(y) - pt * exp2(m_vt - lse2) in
-// place, 8 elements (16 bytes) per thread.  Rows past the last loss row stay 0.
+// Single-pass mode 2, after the merge of a chunk: T = onehot(y) - pt * exp2(m_vt - lse2) in
+// place, 8 elements (16 bytes) per thread, the target entry as -expm1(log p_y).  Rows past
+// the last loss row stay 0.  Runs only when *gate != 0 (null: always).
 template <class E>
 __global__ void __launch_bounds__(256)
 fixup_kernel(int64_t Vpad, int64_t nvt, int64_t c0, const int32_t* __restrict__ ntok_p,
              const int32_t* __restrict__ idx, const int64_t* __restrict__ targets,
              const float* __restrict__ saved, const float* __restrict__ pm,
-             typename E::T* __restrict__ T) {
+             typename E::T* __restrict__ T, const int32_t* __restrict__ gate) {
+  if (gate && *gate == 0) return;
   const int64_t row = blockIdx.y;
   const int64_t r = c0 + row;
   if (r >= *ntok_p) return;
@@ -763,13 +843,16 @@ fixup_kernel(int64_t Vpad, int64_t nvt, int64_t c0, const int32_t* __restrict__ 
   const float lse2 = saved[t * 4] * kLog2e;
   const int64_t y = targets[t];
   const float f = exp2f(pm[row * nvt + v / 256] - lse2);
+  // the target entry 1 - p_y = -expm1(q) from the row's log-probability, exact even
+  // where p_y is close to 1 (its kept term carries the 16-bit rounding of p_y)
+  const float ty = -expm1f(saved[t * 4 + 1]);
   uint4* p = reinterpret_cast<uint4*>(T + row * Vpad + v);
   uint4 q = *p;
   uint16_t h[8];
   __builtin_memcpy(h, &q, 16);
 #pragma unroll
   for (int j = 0; j < 8; ++j)
-    h[j] = E::from_f32((v + j == y ? 1.f : 0.f) - E::to_f32(h[j]) * f);
+    h[j] = E::from_f32(v + j == y ? ty : -E::to_f32(h[j]) * f);
   __builtin_memcpy(&q, h, 16);
   *p = q;
 }
@@ -839,11 +922,50 @@ recompute_kernel(int64_t N, int64_t H, int64_t V, int64_t Vpad, int64_t c0, int 
   }
 }
 
+// Per-row terms of the mode-3 dX epilogue (see dx_kernel): f_r, a_r and the row W[y_r]
+// (none for a target outside the vocabulary, whose one-hot row is zero).
+template <class E>
+struct DxFixed {
+  float f, a;
+  const typename E::T* wy;
+  __device__ inline void init(int64_t rl, int64_t t, const float* __restrict__ saved,
+                              const float* __restrict__ mr, const int64_t* __restrict__ targets,
+                              int64_t V, int64_t H, int64_t Vpad, const char* W, const char* T) {
+    const float4 sv = reinterpret_cast<const float4*>(saved)[t];  // lse, q, ref, g
+    f = exp2f(mr[rl] - sv.x * kLog2e);
+    a = 0.f;
+    wy = nullptr;
+    const int64_t y = targets[t];
+    if (y >= 0 && y < V) {
+      const typename E::T* trow = reinterpret_cast<const typename E::T*>(T) + rl * Vpad;
+      a = f * E::to_f32(trow[y]) - expm1f(sv.y);
+      wy = reinterpret_cast<const typename E::T*>(W) + y * H;
+    }
+  }
+  // a W[y][h .. h + 3] - f C
+  __device__ inline f32x4 apply(f32x4 C, int64_t h) const {
+    f32x4 wv = {0.f, 0.f, 0.f, 0.f};
+    if (wy) {
+      const uint2 q = *reinterpret_cast<const uint2*>(wy + h);
+      wv = f32x4{E::to_f32((typename E::T)(q.x & 0xffffu)), E::to_f32((typename E::T)(q.x >> 16)),
+                 E::to_f32((typename E::T)(q.y & 0xffffu)), E::to_f32((typename E::T)(q.y >> 16))};
+    }
+    return a * wv - f * C;
+  }
+};
+
 // ------------------------------------------------------------------------------- dX
 // C[h][r] = sum_v W[v][h] T[r][v] over the padded vocabulary (or one split of it), with W
 // read in its own [V][H] layout (natural-layout A tiles; rows past V load as 0).
-// ksplit == 1: dX[idx[r]][h] = c * g_r * C, in the storage type.  ksplit > 1: fp32
-// partials to dxp[ks][r - c0][h], reduced by dx_reduce_kernel.
+// ksplit == 1: dX[idx[r]][h] = c * g_r * D, in the storage type.  ksplit > 1: fp32
+// partials of C to dxp[ks][r - c0][h], reduced by dx_reduce_kernel, which applies the same.
+// D = C where the chunk buffer holds T = onehot - softmax (two-pass, single-pass mode 2,
+// or a mode-3 chunk whose fallback ran: redo null or *redo != 0).  Otherwise the buffer
+// holds the mode-3 terms e_v = p_v / f_r with f_r = exp2(mr_r - lse2_r) (mr: the
+// reference log-sum-exp the terms were taken against), and
+//   D = a_r W[y] - f_r C,  a_r = f_r e_y - expm1(q_r),
+// which is sum_v T_v W[v] with the target entry 1 - p_y = -expm1(q_r) exact: the kept term
+// of the target is taken out again with the value the GEMM used.
 //
 // Persistent over a work list of (k split, token tile, H tile) items, H tile fastest,
 // holding only the token tiles of this chunk that have loss rows, so every workgroup gets
@@ -856,7 +978,8 @@ dx_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int nht, in
           const char* __restrict__ W, const char* __restrict__ T,
           const float* __restrict__ saved, const float* __restrict__ grad_loss, float loss_scale,
           typename E::T* __restrict__ dX, float* __restrict__ dxp,
-          int32_t* __restrict__ found_inf) {
+          int32_t* __restrict__ found_inf, const int32_t* __restrict__ redo,
+          const float* __restrict__ mr, const int64_t* __restrict__ targets) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / kWN, wn = w % kWN;
   const int ntok = *ntok_p;
   int64_t rows = (int64_t)ntok - c0;
@@ -878,6 +1001,7 @@ dx_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int nht, in
     bo[i] = (uint32_t)(sr * rowb) + stage_chunk_bytes(sr);
   }
   const float c = (grad_loss ? *grad_loss : 1.f) / loss_scale;
+  const bool fixed = redo && *redo == 0;
   bool bad = false;
   for (int64_t item = first; item < n_items; item += nwg) {
     const int64_t ht = item % nht, rest = item / nht;
@@ -901,9 +1025,13 @@ dx_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int nht, in
         const int64_t t = idx[r];
         const float gs = saved[t * 4 + 3] * c;
         typename E::T* drow = dX + t * H;
+        DxFixed<E> fx;
+        if (fixed) fx.init(r - c0, t, saved, mr, targets, V, H, Vpad, W, T);
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb) {
-          const f32x4 v = acc[mb][nb] * gs;
+          f32x4 v = acc[mb][nb];
+          if (fixed) v = fx.apply(v, hb + mb * 16);
+          v *= gs;
           uint2 pk;
           pk.x = E::pack2(v[0], v[1]);
           pk.y = E::pack2(v[2], v[3]);
@@ -932,17 +1060,23 @@ dx_reduce_kernel(int64_t H, int64_t R, int64_t c0, int ksplit, const int32_t* __
                  const int32_t* __restrict__ idx, const float* __restrict__ dxp,
                  const float* __restrict__ saved, const float* __restrict__ grad_loss,
                  float loss_scale, typename E::T* __restrict__ dX,
-                 int32_t* __restrict__ found_inf) {
+                 int32_t* __restrict__ found_inf, const int32_t* __restrict__ redo,
+                 const float* __restrict__ mr, const int64_t* __restrict__ targets, int64_t V,
+                 int64_t Vpad, const char* __restrict__ W, const char* __restrict__ T) {
   const int64_t rl = blockIdx.x;
   const int ntok = *ntok_p;
   const int64_t r = c0 + rl;
   if (r >= ntok) return;
   const int64_t t = idx[r];
   const float gs = saved[t * 4 + 3] * ((grad_loss ? *grad_loss : 1.f) / loss_scale);
+  const bool fixed = redo && *redo == 0;
+  DxFixed<E> fx;
+  if (fixed) fx.init(rl, t, saved, mr, targets, V, H, Vpad, W, T);
   bool bad = false;
   for (int64_t h = threadIdx.x * 4; h < H; h += 256 * 4) {
     f32x4 s = *reinterpret_cast<const f32x4*>(dxp + rl * H + h);
     for (int k = 1; k < ksplit; ++k) s += *reinterpret_cast<const f32x4*>(dxp + (k * R + rl) * H + h);
+    if (fixed) s = fx.apply(s, h);
     uint16_t o[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -1041,6 +1175,11 @@ gather_rows_kernel(const typename E::T* __restrict__ X, int64_t H, int64_t R, in
   }
 }
 
+__global__ void __launch_bounds__(256) fill_i32_kernel(int32_t* __restrict__ p, int n, int v) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
 FwdArgs fwd_args(const Plan& p, void* ws, const void* Xq, const void* Xp, const void* W,
                  const int64_t* targets) {
   FwdArgs a;
@@ -1061,6 +1200,7 @@ FwdArgs fwd_args(const Plan& p, void* ws, const void* Xq, const void* Xp, const 
   a.nsides = 2;
   a.pt = nullptr;
   a.pm = nullptr;
+  a.gate = nullptr;
   a.Vpad = p.Vpad;
   a.W8 = ws_ptr<char>(ws, p.off_w8);
   a.Xq8 = ws_ptr<char>(ws, p.off_xq8);
@@ -1100,9 +1240,13 @@ hipError_t fwd_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, con
 
 // dX (and dW) of the loss rows of chunk c0 from the chunk's T = onehot - softmax.
 template <class E>
+// redo (non-null): the chunk buffer holds mode-3 terms unless *redo != 0 (see dx_kernel);
+// mr: their per-row reference.
 hipError_t chunk_grads(const Plan& p, void* ws, int64_t c0, const void* Xq, const void* W,
                        const float* saved, const float* grad_loss, float loss_scale, void* dX,
-                       float* dW, int accumulate_dW, int32_t* found_inf, hipStream_t st) {
+                       float* dW, int accumulate_dW, int32_t* found_inf, hipStream_t st,
+                       const int64_t* targets, const int32_t* redo = nullptr,
+                       const float* mr = nullptr) {
   typedef typename E::T T;
   const int32_t* ntok = ws_ptr<int32_t>(ws, p.off_ntok);
   const int32_t* idx = ws_ptr<int32_t>(ws, p.off_idx);
@@ -1112,12 +1256,13 @@ hipError_t chunk_grads(const Plan& p, void* ws, int64_t c0, const void* Xq, cons
   hipLaunchKernelGGL(dx_kernel<E>, dim3(kNumWG), dim3(kThreads), 0, st,
                      p.H, p.V, p.Vpad, p.R, c0, nht, p.ksplit, ntok, idx, (const char*)W,
                      (const char*)Tb, saved, grad_loss, loss_scale, (T*)dX,
-                     ws_ptr<float>(ws, p.off_dxp), found_inf);
+                     ws_ptr<float>(ws, p.off_dxp), found_inf, redo, mr, targets);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.ksplit > 1) {
     hipLaunchKernelGGL(dx_reduce_kernel<E>, dim3((unsigned)p.R), dim3(256), 0, st, p.H, p.R, c0,
                        p.ksplit, ntok, idx, (const float*)ws_ptr<float>(ws, p.off_dxp), saved,
-                       grad_loss, loss_scale, (T*)dX, found_inf);
+                       grad_loss, loss_scale, (T*)dX, found_inf, redo, mr, targets, p.V, p.Vpad,
+                       (const char*)W, (const char*)Tb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (dW) {
@@ -1155,16 +1300,22 @@ hipError_t bwd_impl(const Plan& p, void* ws, const void* Xq, const void* W,
                        (const float*)ws_ptr<float>(ws, p.off_sxq));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     e = chunk_grads<E>(p, ws, c0, Xq, W, saved, grad_loss, loss_scale, dX, dW, accumulate_dW,
-                       found_inf, st);
+                       found_inf, st, targets);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
 // Single pass: reference forward over all rows, then per chunk of R loss rows the policy
-// forward that also keeps its softmax terms, the chunk's merge, the fixup of the kept
-// terms into T = onehot - softmax, and dX (and dW) from T.  The logits of each row are
-// computed once per side instead of twice for the policy.
+// forward that also keeps its softmax terms, the chunk's merge, and dX (and dW) from the
+// kept terms.  The logits of each row are computed once per side instead of twice for
+// the policy.
+//   dX only (frozen W): the terms are taken against the row's reference-side log-sum-exp
+//   (mode 3) and dX applies the per-row correction itself (dx_kernel).  A chunk with a row
+//   whose policy and reference log-sum-exp lie more than 60 (log2 units) apart sets its
+//   flag in the merge, and then the mode-2 forward, merge and fixup below, which exit at
+//   once otherwise, redo the chunk with running maxima and T = onehot - softmax.
+//   With dW: mode 2, merge, fixup into T, dX and dW from T.
 template <class E, class G>
 hipError_t fused_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, const void* W,
                       const int64_t* targets, const uint8_t* mask, const float* adv, float beta,
@@ -1176,32 +1327,50 @@ hipError_t fused_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, c
   const int32_t* idx = ws_ptr<int32_t>(ws, p.off_idx);
   T* Tb = ws_ptr<T>(ws, p.off_T);
   float* pm = ws_ptr<float>(ws, p.off_pm);
+  int32_t* redo = ws_ptr<int32_t>(ws, p.off_redo);
+  const bool fixed = dW == nullptr;
   const int64_t nvt = (p.V + 255) / 256;
+  const int nchunks = (int)((p.N + p.R - 1) / p.R);
   hipError_t e = launch_zero_masked_outputs(p, mask, saved, logp, ref_logp, kl, st);
   if (e != hipSuccess) return e;
+  if (fixed) {
+    hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((nchunks + 255) / 256)), dim3(256), 0, st,
+                       redo, nchunks, 0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (G::kBytes == 1 && (e = quantize_operands(p, ws, Xq, Xp, W, st)) != hipSuccess) return e;
   FwdArgs a = fwd_args(p, ws, Xq, Xp, W, targets);
   a.side0 = 1;
   a.nsides = 1;
   hipLaunchKernelGGL((fwd_kernel<E, G, 1>), dim3(kNumWG), dim3(kThreads), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  for (int64_t c0 = 0; c0 < p.N; c0 += p.R) {
+  for (int64_t c0 = 0, ci = 0; c0 < p.N; c0 += p.R, ++ci) {
+    int32_t* rd = fixed ? redo + ci : nullptr;
     a.row_lo = c0;
     a.row_hi = c0 + p.R;
     a.side0 = 0;
     a.pt = reinterpret_cast<char*>(Tb);
     a.pm = pm;
+    if (fixed) {
+      a.gate = nullptr;
+      hipLaunchKernelGGL((fwd_kernel<E, G, 3>), dim3(kNumWG), dim3(kThreads), 0, st, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      e = launch_merge_rows(p, ws, c0, targets, mask, adv, beta, saved, logp, ref_logp, kl,
+                            status, st, rd, nullptr);
+      if (e != hipSuccess) return e;
+      a.gate = rd;
+    }
     hipLaunchKernelGGL((fwd_kernel<E, G, 2>), dim3(kNumWG), dim3(kThreads), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     e = launch_merge_rows(p, ws, c0, targets, mask, adv, beta, saved, logp, ref_logp, kl, status,
-                          st);
+                          st, nullptr, rd);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(fixup_kernel<E>, dim3((unsigned)((p.Vpad + 2047) / 2048), (unsigned)p.R),
                        dim3(256), 0, st, p.Vpad, nvt, c0, ntok, idx, targets, saved,
-                       (const float*)pm, Tb);
+                       (const float*)pm, Tb, (const int32_t*)rd);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     e = chunk_grads<E>(p, ws, c0, Xq, W, saved, grad_loss, loss_scale, dX, dW, accumulate_dW,
-                       found_inf, st);
+                       found_inf, st, targets, rd, pm);
     if (e != hipSuccess) return e;
   }
   return launch_loss_final(p, ws, 1, status, loss, st);

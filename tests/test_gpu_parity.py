@@ -179,6 +179,80 @@ def test_single_pass_matches_two_pass():
     assert e <= 5e-3
 
 
+def test_single_pass_fixed_reference_matches_two_pass():
+    """dX only (frozen W): the single pass keeps each row's terms against the reference
+    log-sum-exp of the row; across three chunks it agrees with the two-pass path as closely
+    as the running-maximum form does."""
+    wl = dataclasses.replace(workload_by_name("llama3.1-8b-train-bf16"), G=4, L=2600,
+                             H=1024, prefix=100, comp_min=2000, comp_max=2500, need_dW=False)
+    inp = generate(wl)
+    _say(f"[single (fixed reference) vs two pass] S={wl.S} L={wl.L} "
+         f"loss rows {int(inp.mask.sum())}")
+    a = run_gpu(wl, inp)
+    b = run_gpu(wl, inp, single_pass=True)
+    m = inp.mask.numpy() == 1
+    assert a["status"] == b["status"] == 0 and a["found_inf"] == b["found_inf"] == 0
+    assert abs(a["loss"] - b["loss"]) <= 1e-5 * abs(a["loss"])
+    for k in ("logp", "ref_logp", "kl"):
+        err = np.abs(a[k][m] - b[k][m]).max()
+        _say(f"  {k} max abs diff {err:.2e}")
+        assert err <= 1e-4
+    e = rel_l2(b["dX"], a["dX"])
+    _say(f"  dX rel-L2 between paths {e:.2e}")
+    assert e <= 5e-3
+    assert np.all(b["dX"][~m] == 0.0)
+
+
+@pytest.mark.parametrize("side", ["reference", "policy"])
+def test_single_pass_far_reference(side):
+    """Rows whose policy and reference log-sum-exp lie far apart (one side's hidden states
+    scaled by 32, about 110 nats apart): terms taken against the reference would overflow
+    or drop most of their mass, so the chunk is redone with running maxima, and the
+    result still matches the oracle.  With the policy far above, the forward estimator
+    keeps the KL finite."""
+    name = "qwen2.5-1.5b-bf16"
+    wl = dataclasses.replace(workload_by_name(name), **SMALL[name])
+    inp = generate(wl)
+    if side == "reference":
+        inp = dataclasses.replace(inp, xp=inp.xp * 32)
+    else:
+        inp = dataclasses.replace(inp, xq=inp.xq * 32)
+    variant = oracle.Variant(kl="forward") if side == "policy" else None
+    _say(f"[far reference] {side} side scaled by 32, S={wl.S} L={wl.L}")
+    check_small(wl, inp, variant=variant, single_pass=True)
+
+
+def test_single_pass_fallback_in_one_chunk():
+    """Two chunks; only the second holds rows with a far reference (the last sequence's
+    reference hidden states scaled by 32), so one chunk takes the fixed-reference form
+    and the other its fallback."""
+    wl = dataclasses.replace(workload_by_name("qwen2.5-1.5b-bf16"), G=8, L=640, V=8192,
+                             prefix=40, comp_min=600, comp_max=600)
+    inp = generate(wl)
+    xp = inp.xp.clone()
+    xp[7 * wl.L:] *= 32
+    inp = dataclasses.replace(inp, xp=xp)
+    _say(f"[fallback in one chunk] loss rows {int(inp.mask.sum())}")
+    check_small(wl, inp, single_pass=True)
+
+
+@pytest.mark.parametrize("single_pass", [False, True], ids=["two-pass", "single-pass"])
+@pytest.mark.parametrize("name", ["qwen2.5-1.5b-bf16", "llama3.1-8b-train-bf16"])
+def test_confident_targets(name, single_pass):
+    """Targets at the policy's argmax with both sides' hidden states scaled by 16, so most
+    rows have p_y near 1: the target entry 1 - p_y of the logit gradient must keep its
+    relative precision (it is taken from log p_y, not from the 16-bit kept term)."""
+    wl = dataclasses.replace(workload_by_name(name), **SMALL[name])
+    inp = generate(wl)
+    xq, xp = inp.xq * 16, inp.xp * 16
+    z = xq.float() @ inp.W.float().T
+    inp = dataclasses.replace(inp, xq=xq, xp=xp, targets=z.argmax(1).to(inp.targets.dtype))
+    p_y = torch.softmax(z.double(), 1).max(1).values
+    _say(f"[confident targets] {name} single_pass={single_pass} "
+         f"median p_y {float(p_y.median()):.3f}")
+    check_small(wl, inp, single_pass=single_pass)
+
+
 def test_scale_grad():
     g = _lib()
     x = torch.randn(37, 64, device="cuda").to(torch.bfloat16)
