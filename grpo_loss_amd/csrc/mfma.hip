@@ -824,22 +824,11 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
   }
 }
 
-// Single-pass mode 2, after the merge of a chunk: T = onehot(y) - pt * exp2(m_vt - lse2) in
-// place, 8 elements (16 bytes) per thread, the target entry as -expm1(log p_y).  Rows past
-// the last loss row stay 0.  Runs only when *gate != 0 (null: always).
 template <class E>
-__global__ void __launch_bounds__(256)
-fixup_kernel(int64_t Vpad, int64_t nvt, int64_t c0, const int32_t* __restrict__ ntok_p,
-             const int32_t* __restrict__ idx, const int64_t* __restrict__ targets,
-             const float* __restrict__ saved, const float* __restrict__ pm,
-             typename E::T* __restrict__ T, const int32_t* __restrict__ gate) {
-  if (gate && *gate == 0) return;
-  const int64_t row = blockIdx.y;
-  const int64_t r = c0 + row;
-  if (r >= *ntok_p) return;
-  const int64_t v = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
-  if (v >= Vpad) return;
-  const int64_t t = idx[r];
+__device__ inline void fixup_row(int64_t Vpad, int64_t nvt, int64_t row, int64_t v, int64_t t,
+                                 const int64_t* __restrict__ targets,
+                                 const float* __restrict__ saved, const float* __restrict__ pm,
+                                 typename E::T* __restrict__ T) {
   const float lse2 = saved[t * 4] * kLog2e;
   const int64_t y = targets[t];
   const float f = exp2f(pm[row * nvt + v / 256] - lse2);
@@ -855,6 +844,24 @@ fixup_kernel(int64_t Vpad, int64_t nvt, int64_t c0, const int32_t* __restrict__ 
     h[j] = E::from_f32(v + j == y ? ty : -E::to_f32(h[j]) * f);
   __builtin_memcpy(&q, h, 16);
   *p = q;
+}
+
+// Single-pass mode 2, after the merge of a chunk: T = onehot(y) - pt * exp2(m_vt - lse2) in
+// place, 8 elements (16 bytes) per thread and step, the target entry as -expm1(log p_y).
+// Rows past the last loss row stay 0.  A fixed grid strides over the chunk (row = y block
+// index + k gridDim.y), so a launch that *gate turns off (null: always on) costs little.
+template <class E>
+__global__ void __launch_bounds__(256)
+fixup_kernel(int64_t Vpad, int64_t nvt, int64_t c0, int64_t R, const int32_t* __restrict__ ntok_p,
+             const int32_t* __restrict__ idx, const int64_t* __restrict__ targets,
+             const float* __restrict__ saved, const float* __restrict__ pm,
+             typename E::T* __restrict__ T, const int32_t* __restrict__ gate) {
+  if (gate && *gate == 0) return;
+  const int64_t v = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (v >= Vpad) return;
+  const int ntok = *ntok_p;
+  for (int64_t row = blockIdx.y; c0 + row < ntok && row < R; row += gridDim.y)
+    fixup_row<E>(Vpad, nvt, row, v, idx[c0 + row], targets, saved, pm, T);
 }
 
 // ---------------------------------------------------------------------------- recompute
@@ -1365,8 +1372,9 @@ hipError_t fused_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, c
     e = launch_merge_rows(p, ws, c0, targets, mask, adv, beta, saved, logp, ref_logp, kl, status,
                           st, nullptr, rd);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fixup_kernel<E>, dim3((unsigned)((p.Vpad + 2047) / 2048), (unsigned)p.R),
-                       dim3(256), 0, st, p.Vpad, nvt, c0, ntok, idx, targets, saved,
+    hipLaunchKernelGGL(fixup_kernel<E>,
+                       dim3((unsigned)((p.Vpad + 2047) / 2048), (unsigned)(p.R < 64 ? p.R : 64)),
+                       dim3(256), 0, st, p.Vpad, nvt, c0, p.R, ntok, idx, targets, saved,
                        (const float*)pm, Tb, (const int32_t*)rd);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     e = chunk_grads<E>(p, ws, c0, Xq, W, saved, grad_loss, loss_scale, dX, dW, accumulate_dW,
