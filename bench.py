@@ -18,7 +18,8 @@ Prints ONE JSON line.  Default workload: the long-context Llama-3.1-8B shape
 (G = 8, L = 20480, H = 4096, V = 128256, bf16, frozen head).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--path P]
-                  [--no-cpu-baseline] [--cpu-rows R] [--calibrate-copy-gib X]
+                  [--no-two-pass] [--no-fp8] [--small-chunk ROWS] [--no-cpu-baseline]
+                  [--cpu-rows R] [--calibrate-copy-gib X]
 """
 
 import argparse
@@ -49,6 +50,9 @@ def parse():
                     help="time only the path given by --path")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the single-pass leg with fp8 (e4m3) logits")
+    ap.add_argument("--small-chunk", type=int, default=2048,
+                    help="rows per backward chunk of an extra single-pass leg that trades "
+                         "speed for workspace (0: skip it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=256, help="oracle rows per sequence")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
@@ -204,6 +208,7 @@ def main():
                       "mfma_peak_frac": n_exec[path] * gemm_eq / (ms * 1e-3) / (peak * 1e12),
                       "method_flops_frac": n_method * gemm_eq / (ms * 1e-3) / (peak * 1e12),
                       "status": int(f["status"].item()), "found_inf": int(found.item())}
+        f = None  # the result holds a reference to the workspace
     peak_extra = torch.cuda.max_memory_allocated() - base_mem
     main_leg = legs[args.path]
     out = {
@@ -242,6 +247,24 @@ def main():
         out["two_pass" if other[0] == "two" else "single_pass"] = legs[other[0]]
     out["status"] = main_leg["status"]
     out["found_inf"] = main_leg["found_inf"]
+    if args.small_chunk and args.path == "single":
+        # the same single-pass step with a smaller backward chunk: less workspace, more and
+        # smaller launches (reported beside the default, never as `value`)
+        oc = g.options(chunk_rows=args.small_chunk)
+        del ws
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        wsc_bytes = g.grpo_workspace_bytes(wl.S, wl.L, wl.H, wl.V, dt, need_dW, oc)
+        ws = torch.empty(wsc_bytes, dtype=torch.uint8, device="cuda")
+        opts["v"] = oc
+        ms, f = timed(step_single)
+        out[f"chunk_{args.small_chunk}"] = {
+            "value": n_tok / (ms * 1e-3), "ms_per_step": ms,
+            "method_flops_frac": n_method * gemm_eq / (ms * 1e-3) / (peak * 1e12),
+            "extra_gib": (torch.cuda.max_memory_allocated() - base_mem) / 2 ** 30,
+            "workspace_gib": wsc_bytes / 2 ** 30, "status": int(f["status"].item())}
+        f = None
+        opts["v"] = None
     if not args.no_fp8 and dtn != "f32":
         # the same single-pass step with both sides' logits from per-row e4m3 copies (a
         # lower-precision variant, reported beside the 16-bit result, never as `value`)

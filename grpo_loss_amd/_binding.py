@@ -24,7 +24,7 @@ class GRPOOptions(ctypes.Structure):
     """Mirror of struct grpo_options."""
     _fields_ = [("kl_estimator", ctypes.c_int), ("detach_ratio", ctypes.c_int),
                 ("normalization", ctypes.c_int), ("temperature", ctypes.c_float),
-                ("fp8_logits", ctypes.c_int)]
+                ("fp8_logits", ctypes.c_int), ("chunk_rows", ctypes.c_int)]
 
 
 KL_ESTIMATORS = {"reverse": 0, "forward": 1, "reverse_q": 2}
@@ -32,10 +32,12 @@ NORMALIZATIONS = {"tokens": 0, "sequences": 1}
 
 
 def options(kl: str = "reverse", detach: bool = True, norm: str = "tokens",
-            temperature: float = 1.0, fp8_logits: bool = False) -> GRPOOptions:
-    """A grpo_options value from names (the library validates the ranges)."""
+            temperature: float = 1.0, fp8_logits: bool = False,
+            chunk_rows: int = 0) -> GRPOOptions:
+    """A grpo_options value from names (the library validates the ranges).  chunk_rows:
+    loss rows per backward chunk (0: the library's default)."""
     return GRPOOptions(KL_ESTIMATORS[kl], int(bool(detach)), NORMALIZATIONS[norm],
-                       float(temperature), int(bool(fp8_logits)))
+                       float(temperature), int(bool(fp8_logits)), int(chunk_rows))
 
 
 def _as_options(o):

@@ -91,6 +91,7 @@ struct Plan {
   int need_dW;
   int phases;       // forward partial slots per row and side (phases actually used may be fewer)
   int64_t R;        // backward: rows per recompute chunk (multiple of 256)
+  int chunk_rows;   // grpo_options::chunk_rows (0: the default chunk)
   int ksplit;       // backward: split of the dX reduction over the vocabulary
   int mfma;         // 1: 16-bit MFMA kernels, 0: fp32 FMA kernels
   // loss variant (grpo_options)

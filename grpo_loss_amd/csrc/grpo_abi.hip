@@ -62,6 +62,9 @@ bool options_ok(const grpo_options* o) {
   if (o->normalization != GRPO_NORM_TOKENS && o->normalization != GRPO_NORM_SEQUENCES)
     return false;
   if (o->fp8_logits != 0 && o->fp8_logits != 1) return false;
+  if (o->chunk_rows != 0 &&
+      (o->chunk_rows % 256 != 0 || o->chunk_rows < 256 || o->chunk_rows > 65536))
+    return false;
   // the softmax argument z / tau must stay finite for finite logits
   return isfinite(o->temperature) && o->temperature >= 1e-3f && o->temperature <= 1e3f;
 }
@@ -93,7 +96,8 @@ bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_d
   // 16-bit operands with H a multiple of 256 take the MFMA kernels (256-wide tiles over H);
   // everything else takes the fp32-accumulating FMA kernels.
   const int64_t Npad = (p->N + kTokTile - 1) / kTokTile * kTokTile;
-  p->R = Npad < kChunkRows ? Npad : kChunkRows;
+  const int64_t chunk = p->chunk_rows > 0 ? p->chunk_rows : kChunkRows;
+  p->R = Npad < chunk ? Npad : chunk;
   // (the MFMA kernels address each operand with 32-bit byte offsets from a buffer base:
   // X, W and one chunk of onehot - softmax must each stay below 4 GiB)
   const uint64_t k4G = (uint64_t)1 << 32;
@@ -167,6 +171,7 @@ void plan_options(const grpo_options* o, Plan* p) {
   p->inv_tau = 1.0f / o->temperature;
   p->scale2 = kLog2e / o->temperature;
   p->fp8 = o->fp8_logits;
+  p->chunk_rows = o->chunk_rows;
 }
 
 }  // namespace grpo
@@ -197,6 +202,7 @@ void grpo_default_options(grpo_options* opts) {
   opts->normalization = GRPO_NORM_TOKENS;
   opts->temperature = 1.0f;
   opts->fp8_logits = 0;
+  opts->chunk_rows = 0;
 }
 
 size_t grpo_workspace_bytes(int64_t S, int64_t L, int64_t H, int64_t V, grpo_dtype dtype,

@@ -95,6 +95,11 @@ typedef struct grpo_options {
                              (scale amax / 448 per row, see grpo_quantize_e4m3); gradients
                              still use the original X and W.  16-bit inputs with H a
                              multiple of 256 only.  Needs grpo_workspace_bytes_opts.      */
+  int chunk_rows;         /* loss rows per backward chunk: 0 = 4096; else a multiple of 256
+                             in [256, 65536].  The workspace holds one chunk of rows x V
+                             16-bit entries, so this trades workspace for speed (fewer,
+                             larger GEMM launches); results do not depend on it beyond
+                             fp32 summation order.  Needs grpo_workspace_bytes_opts.      */
 } grpo_options;
 
 /* Bits of the forward's status word. */
@@ -105,14 +110,16 @@ typedef struct grpo_options {
 const char* grpo_status_string(int status);
 
 /* Bytes of device workspace that grpo_loss_fwd and grpo_loss_bwd need for these sizes
- * (S = sequences, L = positions per sequence).  The same workspace can serve both calls.
- * It grows with one chunk of rows times V and with V*H (a transposed copy of W for the
- * backward), never with S*L*V.  Returns 0 if the sizes are invalid. */
+ * (S = sequences, L = positions per sequence) with the default options.  The same
+ * workspace can serve both calls.  It grows with one chunk of rows times V (and with the
+ * rows S*L through 16-byte per-row partials), never with S*L*V.  Returns 0 if the sizes
+ * are invalid. */
 size_t grpo_workspace_bytes(int64_t S, int64_t L, int64_t H, int64_t V, grpo_dtype dtype,
                             int need_dW);
 
 /* The same for a loss variant (opts may be NULL): fp8_logits adds the e4m3 copies of W and
- * of the loss rows of X_q and X_p (N H + V H bytes and their scales). */
+ * of the loss rows of X_q and X_p (N H + V H bytes and their scales); chunk_rows sets the
+ * chunk.  Returns 0 if the sizes or the options are invalid. */
 size_t grpo_workspace_bytes_opts(int64_t S, int64_t L, int64_t H, int64_t V, grpo_dtype dtype,
                                  int need_dW, const grpo_options* opts);
 
@@ -136,7 +143,8 @@ int grpo_quantize_e4m3(const void* src, grpo_dtype dtype, int64_t rows, int64_t 
 int grpo_advantages(const float* rewards, int64_t B, int64_t G, int64_t K, float eps,
                     int unbiased, float* adv, grpo_stream_t stream);
 
-/* Defaults: reverse estimator, detached ratio, token mean, temperature 1, 16-bit logits. */
+/* Defaults: reverse estimator, detached ratio, token mean, temperature 1, 16-bit logits,
+ * chunks of 4096 rows. */
 void grpo_default_options(grpo_options* opts);
 
 /* Forward: loss and per-token terms, without materialising logits

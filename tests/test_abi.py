@@ -55,6 +55,23 @@ def test_workspace_bytes(lib):
     assert a < materialised / 20
 
 
+def test_workspace_follows_chunk_rows(lib):
+    """The chunk of rows x V entries dominates the workspace; chunk_rows sets it."""
+    import grpo_loss_amd as g
+    f = lib.grpo_workspace_bytes_opts
+    shape = (8, 20480, 4096, 128256, 1, 0)
+    default = f(*shape, None)
+    assert default == lib.grpo_workspace_bytes(*shape)
+    assert f(*shape, ctypes.byref(g.options(chunk_rows=4096))) == default
+    small = f(*shape, ctypes.byref(g.options(chunk_rows=2048)))
+    big = f(*shape, ctypes.byref(g.options(chunk_rows=8192)))
+    chunk = 2048 * 128256 * 2          # bf16 entries of 2048 more rows
+    # (the smaller chunk splits dX over V and adds 64 MB of fp32 partials)
+    assert default - small >= 0.85 * chunk and big - default >= chunk
+    assert small < 0.7 * 2 ** 30       # 0.67 GiB at the headline shape
+    assert f(*shape, ctypes.byref(g.options(chunk_rows=300))) == 0
+
+
 def test_bad_arguments_rejected_before_launch(lib):
     p = ctypes.c_void_p(16)   # never dereferenced: validation fails first
     nul = None
@@ -91,9 +108,11 @@ def test_options(lib):
     lib.grpo_default_options(None)               # tolerated
     p = ctypes.c_void_p(16)
     nul = None
+    assert (d.fp8_logits, d.chunk_rows) == (0, 0)
     bad = [g.options(temperature=0.0), g.options(temperature=float("nan")),
            g.options(temperature=1e4), g.GRPOOptions(3, 1, 0, 1.0), g.GRPOOptions(0, 2, 0, 1.0),
-           g.GRPOOptions(0, 1, 2, 1.0)]
+           g.GRPOOptions(0, 1, 2, 1.0), g.options(chunk_rows=100), g.options(chunk_rows=-256),
+           g.options(chunk_rows=128), g.options(chunk_rows=65536 + 256)]
     for o in bad:
         rc = lib.grpo_loss_fwd(p, p, p, 1, p, p, p, 2, 3, 64, 5, ctypes.c_float(0.04), p, p,
                                nul, nul, nul, p, ctypes.byref(o), p, ctypes.c_size_t(1 << 40),

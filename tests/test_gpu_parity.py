@@ -36,14 +36,19 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def run_gpu(wl, inp, need_dW=None, grad_scale=True, variant=None, single_pass=False):
+def run_gpu(wl, inp, need_dW=None, grad_scale=True, variant=None, single_pass=False,
+            chunk_rows=0):
     """advantages -> forward -> backward on the device (grpo_loss_fwd then grpo_loss_bwd,
     or grpo_loss_fwd_bwd when single_pass); host copies of every output.
-    variant: an oracle.Variant whose fields name the same options for the library."""
+    variant: an oracle.Variant whose fields name the same options for the library;
+    chunk_rows: the library's backward chunk (0: its default)."""
     g = _lib()
     d = to_device(inp)
     need_dW = wl.need_dW if need_dW is None else need_dW
-    opts = None if variant is None else g.options(**dataclasses.asdict(variant))
+    opts = None
+    if variant is not None or chunk_rows:
+        fields = {} if variant is None else dataclasses.asdict(variant)
+        opts = g.options(**fields, chunk_rows=chunk_rows)
     adv = g.grpo_advantages(d["rewards"], wl.eps)
     S = wl.loss_scale
     grad = torch.full((1,), S, dtype=torch.float32, device="cuda")
@@ -81,8 +86,8 @@ SMALL = {
 }
 
 
-def check_small(wl, inp, variant=None, single_pass=False):
-    gpu = run_gpu(wl, inp, variant=variant, single_pass=single_pass)
+def check_small(wl, inp, variant=None, single_pass=False, chunk_rows=0):
+    gpu = run_gpu(wl, inp, variant=variant, single_pass=single_pass, chunk_rows=chunk_rows)
     variant = oracle.DEFAULT if variant is None else variant
     adv = oracle.group_advantages(inp.rewards.numpy(), wl.eps)
     assert np.array_equal(gpu["adv"].view(np.uint32), adv.view(np.uint32)), (gpu["adv"], adv)
@@ -251,6 +256,44 @@ def test_confident_targets(name, single_pass):
     _say(f"[confident targets] {name} single_pass={single_pass} "
          f"median p_y {float(p_y.median()):.3f}")
     check_small(wl, inp, single_pass=single_pass)
+
+
+@pytest.mark.parametrize("single_pass", [False, True], ids=["two-pass", "single-pass"])
+@pytest.mark.parametrize("need_dW", [False, True], ids=["dX", "dX+dW"])
+def test_chunk_rows_parity(need_dW, single_pass):
+    """256-row backward chunks (three chunks, the last ragged; dX split over V): parity
+    with the oracle."""
+    wl = dataclasses.replace(workload_by_name("llama3.1-8b-train-bf16"), G=8, L=96, H=1024,
+                             prefix=16, comp_min=60, comp_max=80, need_dW=need_dW)
+    inp = generate(wl)
+    _say(f"[chunk_rows 256] loss rows {int(inp.mask.sum())} dW={need_dW} "
+         f"single_pass={single_pass}")
+    check_small(wl, inp, single_pass=single_pass, chunk_rows=256)
+
+
+def test_chunk_rows_agree():
+    """The same single-pass step with 256-, 2048- and 4096-row chunks over about 9000 loss
+    rows: the reference side is computed identically, and the policy side differs only in
+    how its partial sums are grouped (the vocabulary phases follow the chunk's size) and in
+    the fp32 order of the dX reduction."""
+    wl = dataclasses.replace(workload_by_name("llama3.1-8b-train-bf16"), G=4, L=2600,
+                             H=1024, prefix=100, comp_min=2000, comp_max=2500, need_dW=False)
+    inp = generate(wl)
+    base = run_gpu(wl, inp, single_pass=True)
+    m = inp.mask.numpy() == 1
+    for c in (256, 2048):
+        o = run_gpu(wl, inp, single_pass=True, chunk_rows=c)
+        assert o["status"] == 0 and o["found_inf"] == 0
+        assert abs(o["loss"] - base["loss"]) <= 1e-6 * abs(base["loss"])
+        assert np.array_equal(o["ref_logp"], base["ref_logp"])
+        for k in ("logp", "kl"):
+            err = np.abs(o[k][m] - base[k][m]).max()
+            _say(f"  chunk_rows {c}: {k} max abs diff {err:.2e}")
+            assert err <= 1e-4
+        e = rel_l2(o["dX"], base["dX"])
+        _say(f"  chunk_rows {c}: dX rel-L2 against 4096 {e:.2e}")
+        assert e <= 1e-5
+        assert np.all(o["dX"][~m] == 0.0)
 
 
 def test_scale_grad():
