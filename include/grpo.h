@@ -193,11 +193,14 @@ int grpo_loss_bwd(const void* Xq, const void* W, grpo_dtype dtype, const int64_t
 /* Forward and backward in one call: the loss and per-token terms of grpo_loss_fwd and the
  * gradients of grpo_loss_bwd, with the policy logits of each row computed once instead of
  * twice.  The reference side runs over all rows first; then, per chunk of rows, the policy
- * forward keeps its softmax terms (scaled by a per-row, per-vocabulary-tile running
- * maximum) in the workspace, the chunk's loss terms are merged, the kept terms are
- * rescaled into onehot - softmax, and dX (and dW) follow from them.  This is the chunked
- * algorithm of [Long-context GRPO, §3] with the backward's recomputation of the chunk's
- * logits replaced by the forward's own; memory stays one chunk of rows times V.
+ * forward keeps its softmax terms in the workspace, the chunk's loss terms are merged, and
+ * dX (and dW) follow from the kept terms.  Without dW the terms are taken against the
+ * row's reference-side log-sum-exp and dX corrects each row itself; a chunk holding a row
+ * whose two log-sum-exps lie more than 60 (in log2 units) apart is redone with terms taken
+ * against running maxima, turned into onehot - softmax in place, which is also the form
+ * used with dW.  This is the chunked algorithm of [Long-context GRPO, §3] with the
+ * backward's recomputation of the chunk's logits replaced by the forward's own; memory
+ * stays one chunk of rows times V.
  *   Arguments: those of grpo_loss_fwd, then grad_loss / loss_scale, dXq, dW,
  *   accumulate_dW and found_inf as in grpo_loss_bwd.  The upstream gradient must be known
  *   when the call is enqueued (grad_loss is read on the device; NULL means 1).  An
