@@ -487,6 +487,20 @@ def test_vocab_boundary_targets():
     assert abs(gpu["loss"] - f["loss"]) <= 1e-3 * abs(f["loss"])
 
 
+@pytest.mark.parametrize("single_pass", [False, True], ids=["two-pass", "single-pass"])
+@pytest.mark.parametrize("need_dW", [False, True], ids=["dX", "dX+dW"])
+@pytest.mark.parametrize("V", [100, 5003])
+def test_odd_vocabulary(V, need_dW, single_pass):
+    """A vocabulary that is not a multiple of the 64-row k-step (one partial tile, or a
+    prime size): the ragged tile's masks in the forward, W rows past V read as 0 by the
+    in-place dX operand, and dW rows past V never written."""
+    wl = dataclasses.replace(workload_by_name("qwen2.5-1.5b-bf16"), G=4, L=64, H=256, V=V,
+                             prefix=16, comp_min=8, comp_max=48, need_dW=need_dW)
+    inp = generate(wl)
+    _say(f"[odd vocabulary] V={V} dW={need_dW} single_pass={single_pass}")
+    check_small(wl, inp, single_pass=single_pass)
+
+
 def test_dw_accumulates():
     """accumulate_dW = 1 adds into dW: two backward calls give twice one call."""
     g = _lib()
