@@ -155,12 +155,13 @@ hipError_t launch_merge(const Plan& p, const void* ws, const int64_t* targets,
                         hipStream_t st);
 // Single-pass forward: merge of compact rows [c0, c0 + R) (R = Plan::R), the zeroing of
 // masked rows' outputs, and the loss reduction (compact = 1: block sums over loss rows).
-// redo (non-null): the policy partials are fixed-reference ones, and a row out of their
-// range sets *redo; gate (non-null): merge only when *gate != 0.
+// redo (non-null): the policy partials are fixed-reference ones, a row out of their range
+// sets *redo, and the other rows' target entries of the chunk buffer `patch` (Plan::Vpad
+// entries per row) are rewritten; gate (non-null): merge only when *gate != 0.
 hipError_t launch_merge_rows(const Plan& p, const void* ws, int64_t c0, const int64_t* targets,
                              const uint8_t* mask, const float* adv, float beta, float* saved,
                              float* logp, float* ref_logp, float* kl, int32_t* status,
-                             hipStream_t st, int32_t* redo = nullptr,
+                             hipStream_t st, int32_t* redo = nullptr, void* patch = nullptr,
                              const int32_t* gate = nullptr);
 hipError_t launch_zero_masked_outputs(const Plan& p, const uint8_t* mask, float* saved,
                                       float* logp, float* ref_logp, float* kl, hipStream_t st);

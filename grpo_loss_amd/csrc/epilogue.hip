@@ -89,8 +89,15 @@ struct MergeArgs {
   // Single-pass mode 3 (non-null): the policy partials share the row's reference mr as
   // their maximum; a row whose sum of terms 2^(lse2_q - mr) lies outside [2^-60, 2^60]
   // (overflowed, or so small that terms below 2^-126 were dropped) sets *redo, and its
-  // outputs, left for the fallback to rewrite, raise no status flag.
+  // outputs, left for the fallback to rewrite, raise no status flag.  Every other row
+  // gets its target entry of the chunk buffer (row r - c0, patch_ld entries per row, in
+  // the storage type patch_dtype) replaced by expm1(q) / f, f = 2^(mr - lse2_q), which
+  // makes the buffer row -T / f with the target entry 1 - p_y = -expm1(q) kept to the
+  // precision of the storage type.
   int32_t* redo;
+  char* patch;
+  int64_t patch_ld;
+  int patch_dtype;
   const int32_t* gate;  // merge only when *gate != 0 (null: always)
 };
 
@@ -118,8 +125,9 @@ __device__ inline double merge_row(const MergeArgs& a, int64_t t, int64_t r, int
   merge_side(pm, ps, pz, used0, N, r, &lse_q, &zq);
   merge_side(pm + PN, ps + PN, pz + PN, used1, N, r, &lse_p, &zp);
   bool quiet = false;
+  float l2s = 0.f;
   if (a.redo) {
-    const float l2s = lse_q * kLog2e - pm[r];
+    l2s = lse_q * kLog2e - pm[r];
     if (!(l2s >= -60.f && l2s <= 60.f)) {
       atomicOr(a.redo, 1);
       quiet = true;
@@ -129,6 +137,11 @@ __device__ inline double merge_row(const MergeArgs& a, int64_t t, int64_t r, int
   if ((y < 0 || y >= a.V) && !quiet) *flags |= GRPO_FLAG_BAD_TARGET;
   const float q = zq * a.inv_tau - lse_q;
   const float ref = zp * a.inv_tau - lse_p;
+  if (a.redo && !quiet && y >= 0 && y < a.V) {
+    const float ey = expm1f(q) * exp2f(l2s);
+    u16* e = reinterpret_cast<u16*>(a.patch) + (r - a.c0) * a.patch_ld + y;
+    *e = a.patch_dtype == GRPO_BF16 ? BF16T::from_f32(ey) : F16T::from_f32(ey);
+  }
   const float d = ref - q;
   float klv, dkl;
   if (a.kl == GRPO_KL_FORWARD) {
@@ -406,6 +419,9 @@ hipError_t launch_merge(const Plan& p, const void* ws, const int64_t* targets,
   a.c0 = 0;
   a.R = p.N;
   a.redo = nullptr;
+  a.patch = nullptr;
+  a.patch_ld = 0;
+  a.patch_dtype = 0;
   a.gate = nullptr;
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)nblocks), dim3(kMergeBlock), 0, st, a);
   hipError_t e = hipGetLastError();
@@ -428,7 +444,8 @@ hipError_t launch_loss_final(const Plan& p, const void* ws, int compact, int32_t
 hipError_t launch_merge_rows(const Plan& p, const void* ws, int64_t c0, const int64_t* targets,
                              const uint8_t* mask, const float* adv, float beta, float* saved,
                              float* logp, float* ref_logp, float* kl, int32_t* status,
-                             hipStream_t st, int32_t* redo, const int32_t* gate) {
+                             hipStream_t st, int32_t* redo, void* patch,
+                             const int32_t* gate) {
   void* w = const_cast<void*>(ws);
   MergeArgs a;
   a.N = p.N;
@@ -459,6 +476,9 @@ hipError_t launch_merge_rows(const Plan& p, const void* ws, int64_t c0, const in
   a.c0 = c0;
   a.R = p.R;
   a.redo = redo;
+  a.patch = reinterpret_cast<char*>(patch);
+  a.patch_ld = p.Vpad;
+  a.patch_dtype = p.dtype;
   a.gate = gate;
   hipLaunchKernelGGL(merge_rows_kernel, dim3((unsigned)(p.R / kMergeBlock)), dim3(kMergeBlock),
                      0, st, a);

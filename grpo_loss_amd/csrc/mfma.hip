@@ -1,7 +1,8 @@
 // The 16-bit path: MFMA kernels for gfx950 (v_mfma_f32_16x16x32_{bf16,f16}).
 //
-// Every GEMM here is C[m][n] = sum_k A[m][k] * B[n][k] with both operands stored
-// row-major with k contiguous.  Block tile 256 (m) x 256 (n) x 64 (k), 512 threads =
+// Every GEMM here is C[m][n] = sum_k A[m][k] * B[n][k], each operand stored either with k
+// contiguous (X and W in the forward, T in dX) or with k as its row index (W in dX, T and
+// g X in dW), both read in place.  Block tile 256 (m) x 256 (n) x 64 (k), 512 threads =
 // 8 waves in a 2 (m) x 4 (n) grid, each wave owning a 128 x 64 sub-tile as 8 x 4 MFMA
 // blocks of 16 x 16 (128 fp32 accumulators per lane).  Two waves share each SIMD, so the
 // accumulators fit in the architectural VGPRs with room to spare (a 128 x 128 wave tile
@@ -9,8 +10,8 @@
 // MFMAs), and one wave's LDS and barrier latency is covered by its neighbour's MFMAs.
 // Operand tiles go straight from global memory
 // into a double-buffered LDS ring (2 x 64 KB) with buffer_load_dwordx4 ... lds, so no
-// registers are spent on staging; each 128-byte row's eight 16-byte chunks are
-// XOR-swizzled so fragment reads are free of bank conflicts.
+// registers are spent on staging; the 16-byte chunks of a tile row are XOR-swizzled so
+// fragment reads are free of bank conflicts.
 //
 // In the 16 x 16 accumulator layout, lane l holds C[4*(l/16) + j][l % 16], j = 0..3.
 // All kernels put the vocabulary (or the hidden dimension) on m and tokens on n, so a
@@ -929,50 +930,22 @@ recompute_kernel(int64_t N, int64_t H, int64_t V, int64_t Vpad, int64_t c0, int 
   }
 }
 
-// Per-row terms of the mode-3 dX epilogue (see dx_kernel): f_r, a_r and the row W[y_r]
-// (none for a target outside the vocabulary, whose one-hot row is zero).
-template <class E>
-struct DxFixed {
-  float f, a;
-  const typename E::T* wy;
-  __device__ inline void init(int64_t rl, int64_t t, const float* __restrict__ saved,
-                              const float* __restrict__ mr, const int64_t* __restrict__ targets,
-                              int64_t V, int64_t H, int64_t Vpad, const char* W, const char* T) {
-    const float4 sv = reinterpret_cast<const float4*>(saved)[t];  // lse, q, ref, g
-    f = exp2f(mr[rl] - sv.x * kLog2e);
-    a = 0.f;
-    wy = nullptr;
-    const int64_t y = targets[t];
-    if (y >= 0 && y < V) {
-      const typename E::T* trow = reinterpret_cast<const typename E::T*>(T) + rl * Vpad;
-      a = f * E::to_f32(trow[y]) - expm1f(sv.y);
-      wy = reinterpret_cast<const typename E::T*>(W) + y * H;
-    }
-  }
-  // a W[y][h .. h + 3] - f C
-  __device__ inline f32x4 apply(f32x4 C, int64_t h) const {
-    f32x4 wv = {0.f, 0.f, 0.f, 0.f};
-    if (wy) {
-      const uint2 q = *reinterpret_cast<const uint2*>(wy + h);
-      wv = f32x4{E::to_f32((typename E::T)(q.x & 0xffffu)), E::to_f32((typename E::T)(q.x >> 16)),
-                 E::to_f32((typename E::T)(q.y & 0xffffu)), E::to_f32((typename E::T)(q.y >> 16))};
-    }
-    return a * wv - f * C;
-  }
-};
+// Row factor of a mode-3 chunk (see dx_kernel): -f_r, f_r = exp2(mr_r - lse2_r).
+__device__ inline float fixed_row_factor(int64_t rl, int64_t t, const float* __restrict__ saved,
+                                         const float* __restrict__ mr) {
+  return -exp2f(mr[rl] - saved[t * 4] * kLog2e);
+}
 
 // ------------------------------------------------------------------------------- dX
 // C[h][r] = sum_v W[v][h] T[r][v] over the padded vocabulary (or one split of it), with W
 // read in its own [V][H] layout (natural-layout A tiles; rows past V load as 0).
-// ksplit == 1: dX[idx[r]][h] = c * g_r * D, in the storage type.  ksplit > 1: fp32
-// partials of C to dxp[ks][r - c0][h], reduced by dx_reduce_kernel, which applies the same.
-// D = C where the chunk buffer holds T = onehot - softmax (two-pass, single-pass mode 2,
-// or a mode-3 chunk whose fallback ran: redo null or *redo != 0).  Otherwise the buffer
-// holds the mode-3 terms e_v = p_v / f_r with f_r = exp2(mr_r - lse2_r) (mr: the
-// reference log-sum-exp the terms were taken against), and
-//   D = a_r W[y] - f_r C,  a_r = f_r e_y - expm1(q_r),
-// which is sum_v T_v W[v] with the target entry 1 - p_y = -expm1(q_r) exact: the kept term
-// of the target is taken out again with the value the GEMM used.
+// ksplit == 1: dX[idx[r]][h] = c * g_r * s_r * C, in the storage type.  ksplit > 1: fp32
+// partials of C to dxp[ks][r - c0][h], reduced by dx_reduce_kernel, which scales the same.
+// s_r = 1 where the chunk buffer holds T = onehot - softmax (two-pass, single-pass mode 2,
+// or a mode-3 chunk whose fallback ran: redo null or *redo != 0).  Otherwise it holds the
+// mode-3 row E = -T / f_r: the kept terms e_v = p_v / f_r, f_r = exp2(mr_r - lse2_r) (mr:
+// the reference log-sum-exp the terms were taken against), with the target entry
+// replaced by expm1(q_r) / f_r in the merge; then s_r = -f_r.
 //
 // Persistent over a work list of (k split, token tile, H tile) items, H tile fastest,
 // holding only the token tiles of this chunk that have loss rows, so every workgroup gets
@@ -986,7 +959,7 @@ dx_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int nht, in
           const float* __restrict__ saved, const float* __restrict__ grad_loss, float loss_scale,
           typename E::T* __restrict__ dX, float* __restrict__ dxp,
           int32_t* __restrict__ found_inf, const int32_t* __restrict__ redo,
-          const float* __restrict__ mr, const int64_t* __restrict__ targets) {
+          const float* __restrict__ mr) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / kWN, wn = w % kWN;
   const int ntok = *ntok_p;
   int64_t rows = (int64_t)ntok - c0;
@@ -1030,15 +1003,12 @@ dx_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int nht, in
         const int64_t r = tok0 + wn * kWaveN + nb * 16 + (lane & 15);
         if (r >= ntok) continue;
         const int64_t t = idx[r];
-        const float gs = saved[t * 4 + 3] * c;
+        float gs = saved[t * 4 + 3] * c;
+        if (fixed) gs *= fixed_row_factor(r - c0, t, saved, mr);
         typename E::T* drow = dX + t * H;
-        DxFixed<E> fx;
-        if (fixed) fx.init(r - c0, t, saved, mr, targets, V, H, Vpad, W, T);
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb) {
-          f32x4 v = acc[mb][nb];
-          if (fixed) v = fx.apply(v, hb + mb * 16);
-          v *= gs;
+          const f32x4 v = acc[mb][nb] * gs;
           uint2 pk;
           pk.x = E::pack2(v[0], v[1]);
           pk.y = E::pack2(v[2], v[3]);
@@ -1068,22 +1038,18 @@ dx_reduce_kernel(int64_t H, int64_t R, int64_t c0, int ksplit, const int32_t* __
                  const float* __restrict__ saved, const float* __restrict__ grad_loss,
                  float loss_scale, typename E::T* __restrict__ dX,
                  int32_t* __restrict__ found_inf, const int32_t* __restrict__ redo,
-                 const float* __restrict__ mr, const int64_t* __restrict__ targets, int64_t V,
-                 int64_t Vpad, const char* __restrict__ W, const char* __restrict__ T) {
+                 const float* __restrict__ mr) {
   const int64_t rl = blockIdx.x;
   const int ntok = *ntok_p;
   const int64_t r = c0 + rl;
   if (r >= ntok) return;
   const int64_t t = idx[r];
-  const float gs = saved[t * 4 + 3] * ((grad_loss ? *grad_loss : 1.f) / loss_scale);
-  const bool fixed = redo && *redo == 0;
-  DxFixed<E> fx;
-  if (fixed) fx.init(rl, t, saved, mr, targets, V, H, Vpad, W, T);
+  float gs = saved[t * 4 + 3] * ((grad_loss ? *grad_loss : 1.f) / loss_scale);
+  if (redo && *redo == 0) gs *= fixed_row_factor(rl, t, saved, mr);
   bool bad = false;
   for (int64_t h = threadIdx.x * 4; h < H; h += 256 * 4) {
     f32x4 s = *reinterpret_cast<const f32x4*>(dxp + rl * H + h);
     for (int k = 1; k < ksplit; ++k) s += *reinterpret_cast<const f32x4*>(dxp + (k * R + rl) * H + h);
-    if (fixed) s = fx.apply(s, h);
     uint16_t o[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -1149,15 +1115,17 @@ dw_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int nht, in
 }
 
 // --------------------------------------------------------------------------- dW operand
-// Xg[rl][h] = c g_r X_q[idx[c0 + rl]][h] in the storage type for the chunk's loss rows
-// rl < nrows, and 0 for the rows from nrows up to the next multiple of 128 (the k range of
-// dw_kernel).  One row per block, 8 entries (16 bytes) per thread and step.
+// Xg[rl][h] = c g_r s_r X_q[idx[c0 + rl]][h] in the storage type for the chunk's loss rows
+// rl < nrows (s_r as in dx_kernel), and 0 for the rows from nrows up to the next multiple
+// of 128 (the k range of dw_kernel).  One row per block, 8 entries (16 bytes) per thread
+// and step.
 template <class E>
 __global__ void __launch_bounds__(256)
 gather_rows_kernel(const typename E::T* __restrict__ X, int64_t H, int64_t R, int64_t c0,
                    const int32_t* __restrict__ ntok_p, const int32_t* __restrict__ idx,
                    const float* __restrict__ saved, const float* __restrict__ grad_loss,
-                   float loss_scale, typename E::T* __restrict__ Xg) {
+                   float loss_scale, typename E::T* __restrict__ Xg,
+                   const int32_t* __restrict__ redo, const float* __restrict__ mr) {
   const int64_t rl = blockIdx.x;
   int64_t nrows = (int64_t)(*ntok_p) - c0;
   if (nrows > R) nrows = R;
@@ -1168,7 +1136,8 @@ gather_rows_kernel(const typename E::T* __restrict__ X, int64_t H, int64_t R, in
     return;
   }
   const int64_t t = idx[c0 + rl];
-  const float sc = saved[t * 4 + 3] * ((grad_loss ? *grad_loss : 1.f) / loss_scale);
+  float sc = saved[t * 4 + 3] * ((grad_loss ? *grad_loss : 1.f) / loss_scale);
+  if (redo && *redo == 0) sc *= fixed_row_factor(rl, t, saved, mr);
   const uint4* src = reinterpret_cast<const uint4*>(X + t * H);
   for (int64_t h8 = threadIdx.x; h8 < H / 8; h8 += 256) {
     const uint4 q = src[h8];
@@ -1247,13 +1216,12 @@ hipError_t fwd_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, con
 
 // dX (and dW) of the loss rows of chunk c0 from the chunk's T = onehot - softmax.
 template <class E>
-// redo (non-null): the chunk buffer holds mode-3 terms unless *redo != 0 (see dx_kernel);
-// mr: their per-row reference.
+// redo (non-null): the chunk buffer holds mode-3 rows -T / f unless *redo != 0 (see
+// dx_kernel); mr: their per-row reference.
 hipError_t chunk_grads(const Plan& p, void* ws, int64_t c0, const void* Xq, const void* W,
                        const float* saved, const float* grad_loss, float loss_scale, void* dX,
                        float* dW, int accumulate_dW, int32_t* found_inf, hipStream_t st,
-                       const int64_t* targets, const int32_t* redo = nullptr,
-                       const float* mr = nullptr) {
+                       const int32_t* redo = nullptr, const float* mr = nullptr) {
   typedef typename E::T T;
   const int32_t* ntok = ws_ptr<int32_t>(ws, p.off_ntok);
   const int32_t* idx = ws_ptr<int32_t>(ws, p.off_idx);
@@ -1263,19 +1231,19 @@ hipError_t chunk_grads(const Plan& p, void* ws, int64_t c0, const void* Xq, cons
   hipLaunchKernelGGL(dx_kernel<E>, dim3(kNumWG), dim3(kThreads), 0, st,
                      p.H, p.V, p.Vpad, p.R, c0, nht, p.ksplit, ntok, idx, (const char*)W,
                      (const char*)Tb, saved, grad_loss, loss_scale, (T*)dX,
-                     ws_ptr<float>(ws, p.off_dxp), found_inf, redo, mr, targets);
+                     ws_ptr<float>(ws, p.off_dxp), found_inf, redo, mr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.ksplit > 1) {
     hipLaunchKernelGGL(dx_reduce_kernel<E>, dim3((unsigned)p.R), dim3(256), 0, st, p.H, p.R, c0,
                        p.ksplit, ntok, idx, (const float*)ws_ptr<float>(ws, p.off_dxp), saved,
-                       grad_loss, loss_scale, (T*)dX, found_inf, redo, mr, targets, p.V, p.Vpad,
-                       (const char*)W, (const char*)Tb);
+                       grad_loss, loss_scale, (T*)dX, found_inf, redo, mr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (dW) {
     T* Xg = ws_ptr<T>(ws, p.off_Xg);
     hipLaunchKernelGGL(gather_rows_kernel<E>, dim3((unsigned)p.R), dim3(256), 0, st,
-                       (const T*)Xq, p.H, p.R, c0, ntok, idx, saved, grad_loss, loss_scale, Xg);
+                       (const T*)Xq, p.H, p.R, c0, ntok, idx, saved, grad_loss, loss_scale, Xg,
+                       redo, mr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(dw_kernel<E>, dim3((unsigned)(nht * nvt)), dim3(kThreads), 0, st, p.H,
                        p.V, p.Vpad, p.R, c0, nht, c0 == 0 ? accumulate_dW : 1, ntok,
@@ -1307,7 +1275,7 @@ hipError_t bwd_impl(const Plan& p, void* ws, const void* Xq, const void* W,
                        (const float*)ws_ptr<float>(ws, p.off_sxq));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     e = chunk_grads<E>(p, ws, c0, Xq, W, saved, grad_loss, loss_scale, dX, dW, accumulate_dW,
-                       found_inf, st, targets);
+                       found_inf, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -1316,13 +1284,12 @@ hipError_t bwd_impl(const Plan& p, void* ws, const void* Xq, const void* W,
 // Single pass: reference forward over all rows, then per chunk of R loss rows the policy
 // forward that also keeps its softmax terms, the chunk's merge, and dX (and dW) from the
 // kept terms.  The logits of each row are computed once per side instead of twice for
-// the policy.
-//   dX only (frozen W): the terms are taken against the row's reference-side log-sum-exp
-//   (mode 3) and dX applies the per-row correction itself (dx_kernel).  A chunk with a row
-//   whose policy and reference log-sum-exp lie more than 60 (log2 units) apart sets its
-//   flag in the merge, and then the mode-2 forward, merge and fixup below, which exit at
-//   once otherwise, redo the chunk with running maxima and T = onehot - softmax.
-//   With dW: mode 2, merge, fixup into T, dX and dW from T.
+// the policy.  The terms are taken against the row's reference-side log-sum-exp (mode 3)
+// and the merge rewrites each row's target entry, so the chunk buffer holds -T / f per row
+// and dX, dW scale their rows by -f (dx_kernel).  A chunk with a row whose policy and
+// reference log-sum-exp lie more than 60 (log2 units) apart sets its flag in the merge,
+// and then the mode-2 forward, merge and fixup below, which exit at once otherwise, redo
+// the chunk with running maxima into T = onehot - softmax.
 template <class E, class G>
 hipError_t fused_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, const void* W,
                       const int64_t* targets, const uint8_t* mask, const float* adv, float beta,
@@ -1335,16 +1302,13 @@ hipError_t fused_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, c
   T* Tb = ws_ptr<T>(ws, p.off_T);
   float* pm = ws_ptr<float>(ws, p.off_pm);
   int32_t* redo = ws_ptr<int32_t>(ws, p.off_redo);
-  const bool fixed = dW == nullptr;
   const int64_t nvt = (p.V + 255) / 256;
   const int nchunks = (int)((p.N + p.R - 1) / p.R);
   hipError_t e = launch_zero_masked_outputs(p, mask, saved, logp, ref_logp, kl, st);
   if (e != hipSuccess) return e;
-  if (fixed) {
-    hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((nchunks + 255) / 256)), dim3(256), 0, st,
-                       redo, nchunks, 0);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((nchunks + 255) / 256)), dim3(256), 0, st,
+                     redo, nchunks, 0);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (G::kBytes == 1 && (e = quantize_operands(p, ws, Xq, Xp, W, st)) != hipSuccess) return e;
   FwdArgs a = fwd_args(p, ws, Xq, Xp, W, targets);
   a.side0 = 1;
@@ -1352,25 +1316,24 @@ hipError_t fused_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, c
   hipLaunchKernelGGL((fwd_kernel<E, G, 1>), dim3(kNumWG), dim3(kThreads), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   for (int64_t c0 = 0, ci = 0; c0 < p.N; c0 += p.R, ++ci) {
-    int32_t* rd = fixed ? redo + ci : nullptr;
+    int32_t* rd = redo + ci;
     a.row_lo = c0;
     a.row_hi = c0 + p.R;
     a.side0 = 0;
     a.pt = reinterpret_cast<char*>(Tb);
     a.pm = pm;
-    if (fixed) {
-      a.gate = nullptr;
-      hipLaunchKernelGGL((fwd_kernel<E, G, 3>), dim3(kNumWG), dim3(kThreads), 0, st, a);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-      e = launch_merge_rows(p, ws, c0, targets, mask, adv, beta, saved, logp, ref_logp, kl,
-                            status, st, rd, nullptr);
-      if (e != hipSuccess) return e;
-      a.gate = rd;
-    }
+    a.gate = nullptr;
+    hipLaunchKernelGGL((fwd_kernel<E, G, 3>), dim3(kNumWG), dim3(kThreads), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    e = launch_merge_rows(p, ws, c0, targets, mask, adv, beta, saved, logp, ref_logp, kl,
+                          status, st, rd, Tb, nullptr);
+    if (e != hipSuccess) return e;
+    // fallback, gated on the chunk's flag
+    a.gate = rd;
     hipLaunchKernelGGL((fwd_kernel<E, G, 2>), dim3(kNumWG), dim3(kThreads), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     e = launch_merge_rows(p, ws, c0, targets, mask, adv, beta, saved, logp, ref_logp, kl, status,
-                          st, nullptr, rd);
+                          st, nullptr, nullptr, rd);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(fixup_kernel<E>,
                        dim3((unsigned)((p.Vpad + 2047) / 2048), (unsigned)(p.R < 64 ? p.R : 64)),
@@ -1378,7 +1341,7 @@ hipError_t fused_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, c
                        (const float*)pm, Tb, (const int32_t*)rd);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     e = chunk_grads<E>(p, ws, c0, Xq, W, saved, grad_loss, loss_scale, dX, dW, accumulate_dW,
-                       found_inf, st, targets, rd, pm);
+                       found_inf, st, rd, pm);
     if (e != hipSuccess) return e;
   }
   return launch_loss_final(p, ws, 1, status, loss, st);

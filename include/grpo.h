@@ -193,12 +193,13 @@ int grpo_loss_bwd(const void* Xq, const void* W, grpo_dtype dtype, const int64_t
 /* Forward and backward in one call: the loss and per-token terms of grpo_loss_fwd and the
  * gradients of grpo_loss_bwd, with the policy logits of each row computed once instead of
  * twice.  The reference side runs over all rows first; then, per chunk of rows, the policy
- * forward keeps its softmax terms in the workspace, the chunk's loss terms are merged, and
- * dX (and dW) follow from the kept terms.  Without dW the terms are taken against the
- * row's reference-side log-sum-exp and dX corrects each row itself; a chunk holding a row
- * whose two log-sum-exps lie more than 60 (in log2 units) apart is redone with terms taken
- * against running maxima, turned into onehot - softmax in place, which is also the form
- * used with dW.  This is the chunked algorithm of [Long-context GRPO, §3] with the
+ * forward keeps its softmax terms in the workspace, taken against the row's reference-side
+ * log-sum-exp, the chunk's loss terms are merged (which also rewrites each row's target
+ * entry, so that the row is -(onehot - softmax) / f for a per-row f), and dX (and dW)
+ * follow from the kept rows scaled by -f.  A chunk holding a row whose two log-sum-exps
+ * lie more than 60 (in log2 units) apart is redone with terms taken against running
+ * maxima, turned into onehot - softmax in place.  This is the chunked algorithm of
+ * [Long-context GRPO, §3] with the
  * backward's recomputation of the chunk's logits replaced by the forward's own; memory
  * stays one chunk of rows times V.
  *   Arguments: those of grpo_loss_fwd, then grad_loss / loss_scale, dXq, dW,

@@ -275,7 +275,8 @@ def test_chunk_rows_agree():
     """The same single-pass step with 256-, 2048- and 4096-row chunks over about 9000 loss
     rows: the reference side is computed identically, and the policy side differs only in
     how its partial sums are grouped (the vocabulary phases follow the chunk's size) and in
-    the fp32 order of the dX reduction."""
+    the fp32 order of the dX reduction.  A last-bit change of log p_y can move the 16-bit
+    target entry of a row by one unit (2^-8 relative), hence the dX bound of 5e-4."""
     wl = dataclasses.replace(workload_by_name("llama3.1-8b-train-bf16"), G=4, L=2600,
                              H=1024, prefix=100, comp_min=2000, comp_max=2500, need_dW=False)
     inp = generate(wl)
@@ -292,7 +293,7 @@ def test_chunk_rows_agree():
             assert err <= 1e-4
         e = rel_l2(o["dX"], base["dX"])
         _say(f"  chunk_rows {c}: dX rel-L2 against 4096 {e:.2e}")
-        assert e <= 1e-5
+        assert e <= 5e-4
         assert np.all(o["dX"][~m] == 0.0)
 
 
