@@ -383,6 +383,35 @@ def test_nonfinite_flags():
     assert out["status"] & 1 and out["found_inf"] == 1
 
 
+@pytest.mark.parametrize("single_pass", [False, True], ids=["two-pass", "single-pass"])
+@pytest.mark.parametrize("where", ["policy", "reference"])
+def test_nonfinite_flags_mfma(where, single_pass):
+    """On the MFMA kernels: NaN in masked-out rows of both sides sets nothing; inf in one
+    loss row of one side sets the forward's non-finite bit (the single pass reaches it
+    through its fallback: the row's log-sum-exp window check fails) and, for the policy
+    side, found_inf; the other rows' log-probs stay finite."""
+    name = "qwen2.5-1.5b-bf16"
+    wl = dataclasses.replace(workload_by_name(name), **SMALL[name])
+    inp = generate(wl)
+    m = inp.mask.numpy() == 1
+    mrow = int(np.nonzero(~m)[0][0])
+    inp.xq[mrow, 3] = float("nan")
+    inp.xp[mrow, 5] = float("nan")
+    out = run_gpu(wl, inp, single_pass=single_pass)
+    assert out["status"] == 0 and out["found_inf"] == 0 and np.isfinite(out["loss"])
+    lrow = int(np.nonzero(m)[0][5])
+    (inp.xq if where == "policy" else inp.xp)[lrow, 7] = float("inf")
+    out = run_gpu(wl, inp, single_pass=single_pass)
+    _say(f"[non-finite] {where} single_pass={single_pass} status={out['status']} "
+         f"found_inf={out['found_inf']}")
+    assert out["status"] & 1
+    if where == "policy":
+        assert out["found_inf"] == 1
+    others = m.copy()
+    others[lrow] = False
+    assert np.all(np.isfinite(out["logp"][others])) and np.all(np.isfinite(out["ref_logp"][others]))
+
+
 def test_repeat_is_bit_identical():
     """Two runs on the same inputs agree bit for bit (fixed-order reductions, no atomics
     on values)."""
