@@ -383,12 +383,13 @@ struct FwdArgs {
   // side0 + nsides - 1 (side 0: policy X_q, side 1: reference X_p).
   int64_t row_lo, row_hi;
   int side0, nsides;
-  // Single-pass mode (pt != nullptr; policy rows of one chunk): every softmax term
-  // exp2(z s2 - m_vt) is also stored, in the storage type, at pt[(r - row_lo) Vpad + v]
-  // (0 for v >= V and for rows past the last loss row), with m_vt the running maximum of
-  // row r after vocabulary tile vt, identical for all lanes of the row, stored at
-  // pm[(r - row_lo) nvt + vt].  The backward's logit gradient is then
-  // onehot - pt * exp2(m_vt - lse2) without recomputing the logits.
+  // Single-pass modes (policy rows of one chunk): every softmax term is also stored, in
+  // the storage type, at pt[(r - row_lo) Vpad + v] (0 for v >= V and for rows past the
+  // last loss row).  Mode 2: the term is exp2(z s2 - m_vt) with m_vt the running maximum
+  // of row r after vocabulary tile vt, identical for all lanes of the row, stored at
+  // pm[(r - row_lo) nvt + vt]; the backward's logit gradient is then
+  // onehot - pt * exp2(m_vt - lse2) without recomputing the logits.  Mode 3: the term is
+  // exp2(z s2 - mr) with mr the row's reference-side log-sum-exp, stored at pm[r - row_lo].
   char* pt;
   float* pm;
   int64_t Vpad;
@@ -1012,7 +1013,7 @@ dx_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int nht, in
           uint2 pk;
           pk.x = E::pack2(v[0], v[1]);
           pk.y = E::pack2(v[2], v[3]);
-          bad |= E::nonfinite2(pk.x) | E::nonfinite2(pk.y);
+          bad |= E::nonfinite2(pk.x) || E::nonfinite2(pk.y);
           *reinterpret_cast<uint2*>(drow + hb + mb * 16) = pk;
         }
       }
