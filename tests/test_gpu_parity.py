@@ -297,6 +297,75 @@ def test_chunk_rows_agree():
         assert np.all(o["dX"][~m] == 0.0)
 
 
+def test_single_pass_graph_replay():
+    """The single-pass call captured in a HIP graph and replayed three times, with eager work
+    and synchronisations between the replays (outputs overwritten with NaN, another eager
+    call of the library on other buffers): every replay reproduces the eager result bit for
+    bit.  A replay after the inputs were changed in place matches an eager call on them."""
+    g = _lib()
+    name = "qwen2.5-1.5b-bf16"
+    wl = dataclasses.replace(workload_by_name(name), **SMALL[name])
+    inp = generate(wl)
+    d = to_device(inp)
+    adv = g.grpo_advantages(d["rewards"], wl.eps)
+    dt = d["xq"].dtype
+    ws = torch.empty(g.grpo_workspace_bytes(wl.S, wl.L, wl.H, wl.V, dt, False),
+                     dtype=torch.uint8, device="cuda")
+    dX = torch.empty_like(d["xq"])
+    found = torch.zeros(1, dtype=torch.int32, device="cuda")
+    grad = torch.ones(1, dtype=torch.float32, device="cuda")
+    keys = ("loss", "saved", "logp", "ref_logp", "kl", "status", "dXq")
+
+    def call(ws_, dX_, found_):
+        found_.zero_()
+        return g.grpo_loss_fwd_bwd(d["xq"], d["xp"], d["W"], d["targets"], d["mask"], adv,
+                                   wl.beta, wl.L, grad, 1.0, workspace=ws_, dXq=dX_,
+                                   found_inf=found_)
+
+    def snapshot(o):
+        return {k: o[k].clone() for k in keys}
+
+    eager = snapshot(call(ws, dX, found))
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(ws, dX, found)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = call(ws, dX, found)
+    ws2 = torch.empty_like(ws)
+    dX2 = torch.empty_like(dX)
+    found2 = torch.zeros_like(found)
+    for rep in range(3):
+        for k in keys:
+            if out[k].dtype.is_floating_point:
+                out[k].fill_(float("nan"))
+            else:
+                out[k].fill_(-1)
+        other = call(ws2, dX2, found2)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _say(f"[graph replay] {rep}: loss {float(out['loss'].item()):.8g}")
+        for k in keys:
+            assert torch.equal(out[k], eager[k]), (rep, k)
+            assert torch.equal(other[k], eager[k]), (rep, k)
+        assert int(found.item()) == 0
+    d["xq"].mul_(2.0)   # exact in bf16: the replay must read the new values
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    fresh = call(ws2, dX2, found2)
+    torch.cuda.synchronize()
+    for k in keys:
+        assert torch.equal(out[k], fresh[k]), k
+    assert not torch.equal(out["dXq"], eager["dXq"])
+    del graph
+
+
 def test_scale_grad():
     g = _lib()
     x = torch.randn(37, 64, device="cuda").to(torch.bfloat16)
