@@ -87,9 +87,12 @@ struct MergeArgs {
   double* lsum;
   int64_t c0, R;        // chunked merge: compact rows [c0, c0 + R)
   // Single-pass mode 3 (non-null): the policy partials share the row's reference mr as
-  // their maximum; a row whose sum of terms 2^(lse2_q - mr) lies outside [2^-60, 2^60]
-  // (overflowed, or so small that terms below 2^-126 were dropped) sets *redo, and its
-  // outputs, left for the fallback to rewrite, raise no status flag.  Every other row
+  // their maximum; a row whose sum of terms 2^(lse2_q - mr) lies outside the window of the
+  // storage type sets *redo, and its outputs, left for the fallback to rewrite, raise no
+  // status flag.  bf16: [2^-60, 2^60] (beyond it the fp32 sum overflows, or terms below
+  // 2^-126 drop out of it).  fp16: [2^-4, 2^14]: a stored term p 2^(lse2_q - mr) must stay
+  // below 65504, and when lse2_q < mr the terms that turn subnormal carry a rounding error
+  // that dX multiplies by f = 2^(mr - lse2_q), which the window keeps below 16.  Every other row
   // gets its target entry of the chunk buffer (row r - c0, patch_ld entries per row, in
   // the storage type patch_dtype) replaced by expm1(q) / f, f = 2^(mr - lse2_q), which
   // makes the buffer row -T / f with the target entry 1 - p_y = -expm1(q) kept to the
@@ -128,7 +131,8 @@ __device__ inline double merge_row(const MergeArgs& a, int64_t t, int64_t r, int
   float l2s = 0.f;
   if (a.redo) {
     l2s = lse_q * kLog2e - pm[r];
-    if (!(l2s >= -60.f && l2s <= 60.f)) {
+    const bool f16 = a.patch_dtype == GRPO_F16;
+    if (!(l2s >= (f16 ? -4.f : -60.f) && l2s <= (f16 ? 14.f : 60.f))) {
       atomicOr(a.redo, 1);
       quiet = true;
     }

@@ -1288,7 +1288,8 @@ hipError_t bwd_impl(const Plan& p, void* ws, const void* Xq, const void* W,
 // the policy.  The terms are taken against the row's reference-side log-sum-exp (mode 3)
 // and the merge rewrites each row's target entry, so the chunk buffer holds -T / f per row
 // and dX, dW scale their rows by -f (dx_kernel).  A chunk with a row whose policy and
-// reference log-sum-exp lie more than 60 (log2 units) apart sets its flag in the merge,
+// reference log-sum-exp lie too far apart (outside [-60, 60] in log2 units for bf16,
+// [-4, 14] for fp16, whose stored terms must fit fp16) sets its flag in the merge,
 // and then the mode-2 forward, merge and fixup below, which exit at once otherwise, redo
 // the chunk with running maxima into T = onehot - softmax.
 template <class E, class G>

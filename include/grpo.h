@@ -198,7 +198,8 @@ int grpo_loss_bwd(const void* Xq, const void* W, grpo_dtype dtype, const int64_t
  * entry, so that the row is -(onehot - softmax) / f for a per-row f), and dX (and dW)
  * follow from the kept rows scaled by -f.  A chunk holding a row whose two log-sum-exps
  * lie more than 60 (in log2 units) apart is redone with terms taken against running
- * maxima, turned into onehot - softmax in place.  This is the chunked algorithm of
+ * maxima, turned into onehot - softmax in place (for fp16, a row outside [-4, 14] does so:
+ * the kept terms must fit fp16).  This is the chunked algorithm of
  * [Long-context GRPO, §3] with the
  * backward's recomputation of the chunk's logits replaced by the forward's own; memory
  * stays one chunk of rows times V.

@@ -227,6 +227,22 @@ def test_single_pass_far_reference(side):
     check_small(wl, inp, variant=variant, single_pass=True)
 
 
+@pytest.mark.parametrize("side,scale,kl", [("xp", 2.0, "reverse"), ("xq", 1.5, "reverse"),
+                                           ("xq", 3.0, "forward")],
+                         ids=["policy-below", "policy-above-inside", "policy-far-above"])
+def test_fp16_reference_window(side, scale, kl):
+    """fp16 keeps terms p 2^(lse2_q - mr) in fp16, so its window is [-4, 14] (log2 units).
+    Reference hidden states x2 put the policy 8 to 19 below (fallback), policy x1.5 puts
+    it 2 to 10 above (kept terms up to 2^10, no fallback), policy x3 21 to 40 above
+    (fallback; the forward estimator keeps the KL finite).  All three match the oracle."""
+    name = "phi4-f16"
+    wl = dataclasses.replace(workload_by_name(name), **SMALL[name])
+    inp = generate(wl)
+    inp = dataclasses.replace(inp, **{side: getattr(inp, side) * scale})
+    _say(f"[fp16 window] {side} x{scale} kl={kl}")
+    check_small(wl, inp, variant=oracle.Variant(kl=kl), single_pass=True)
+
+
 def test_single_pass_fallback_in_one_chunk():
     """Two chunks; only the second holds rows with a far reference (the last sequence's
     reference hidden states scaled by 32), so one chunk takes the fixed-reference form
