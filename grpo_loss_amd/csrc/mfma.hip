@@ -141,14 +141,19 @@ typedef uint32_t Offs[4];
 // (l % 32) ^ 2 F(row) of that row.
 __device__ inline int nat_f(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
 
-// Staging offsets of a natural-layout operand with ld bytes per k-row.
+// Staging offsets of a natural-layout operand with ld bytes per k-row, for instructions
+// i = 0 and 1.  Instruction i + 2 writes the k-rows 4 further on, whose F is the same
+// (r & 3 repeats with period 4 in i, and (r >> 3) & 1 = w & 1 for all four), so it reuses
+// the offset of i from a resource based 4 k-rows further (Op<true>::at_hi): two VGPRs per
+// operand instead of four, and loads past the operand's end still return 0.
 __device__ inline void nat_offsets(int64_t ld, Offs& o) {
   const int l = (int)threadIdx.x & 63, w = (int)(threadIdx.x >> 6);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 2; ++i) {
     const int r = 8 * w + 2 * i + (l >> 5);
     o[i] = (uint32_t)(r * ld) + (uint32_t)(((l & 31) ^ (2 * nat_f(r))) << 4);
   }
+  o[2] = o[3] = 0;
 }
 
 // An operand of the k loop.  kNat = false: rows are m (n) with k contiguous; k-step kt is
@@ -172,7 +177,11 @@ struct Op<true> {
   int64_t kstep;
   __device__ inline Src at(int kt, int& so) const {
     so = 0;
-    const int64_t o = (int64_t)kt * kstep;
+    return from((int64_t)kt * kstep);
+  }
+  // k-step kt's second half of staged k-rows: 4 k-rows (kstep / 16 bytes) further on
+  __device__ inline Src at_hi(int kt) const { return from((int64_t)kt * kstep + (kstep >> 4)); }
+  __device__ inline Src from(int64_t o) const {
     const int64_t n = left - o;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + o), (short)0,
                                              n > 0 ? (int)(uint32_t)n : 0, 0x00020000);
@@ -210,12 +219,17 @@ __device__ inline void stage_tiles(const Op<kNatA>& A, const Op<kNatB>& B, const
   char* sb = (S ? g_sB1 : g_sB0) + w * 4 * 1024;
   int soa, sob;
   const Src ra = A.at(kt, soa), rb = B.at(kt, sob);
+  Src ra2 = ra, rb2 = rb;
+  if constexpr (kNatA) ra2 = A.at_hi(kt);
+  if constexpr (kNatB) rb2 = B.at_hi(kt);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(sa + i * 1024), 16, (int)ao[i],
-                                             soa, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(sb + i * 1024), 16, (int)bo[i],
-                                             sob, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kNatA && i >= 2 ? ra2 : ra,
+                                             (lds_void_t*)(sa + i * 1024), 16,
+                                             (int)ao[kNatA ? (i & 1) : i], soa, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kNatB && i >= 2 ? rb2 : rb,
+                                             (lds_void_t*)(sb + i * 1024), 16,
+                                             (int)bo[kNatB ? (i & 1) : i], sob, 0, 0);
   }
 }
 
@@ -1097,19 +1111,33 @@ dw_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int nht, in
                                 acc);
   const int64_t hb = h0 + wm * 128 + 4 * (lane >> 4);
   bool bad = false;
+  if (accumulate) {
+    // every old value of the lane's columns in flight at once: one memory round trip per
+    // tile instead of one per 16-byte piece
+    f32x4 old[kNB][kMB];
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      const int64_t v = v0 + wn * kWaveN + nb * 16 + (lane & 15);
+      const f32x4* p = reinterpret_cast<const f32x4*>(dW + (v < V ? v : 0) * H + hb);
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) old[nb][mb] = p[mb * 4];
+    }
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) acc[mb][nb] += old[nb][mb];
+  }
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
     const int64_t v = v0 + wn * kWaveN + nb * 16 + (lane & 15);
     if (v >= V) continue;
-    float* drow = dW + v * H;
+    f32x4* p = reinterpret_cast<f32x4*>(dW + v * H + hb);
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) {
-      f32x4* p = reinterpret_cast<f32x4*>(drow + hb + mb * 16);
-      f32x4 val = acc[mb][nb];
-      if (accumulate) val += *p;
+      const f32x4 val = acc[mb][nb];
 #pragma unroll
       for (int j = 0; j < 4; ++j) bad |= !isfinite(val[j]);
-      *p = val;
+      p[mb * 4] = val;
     }
   }
   if (bad) atomicOr(found_inf, 1);
