@@ -334,11 +334,90 @@ __device__ inline void gemm_pre(Src ra, Src rb, const Offs& ao, const Offs& bo) 
   gemm_pre_op(Op<false>{ra}, Op<false>{rb}, ao, bo);
 }
 
+// Fragment reads of one k-step for the pipelined core below.  A fragment (A row block mb,
+// k half hf) and B fragment (B row block nb, k half hf) of stage S, in either tile layout.
+struct FragBase {
+  int fa, fb, c0, c1, F, wn4;
+};
+template <int S, bool kNat>
+__device__ inline uint4 frag_a(const FragBase& q, int mb, int hf) {
+  const char* As = S ? g_sA1 : g_sA0;
+  if constexpr (kNat) return nat_frag(As, q.fa, mb ^ q.F, hf);
+  else return *reinterpret_cast<const uint4*>(As + q.fa + mb * 2048 + (hf ? q.c1 : q.c0));
+}
+template <int S, bool kNat>
+__device__ inline uint4 frag_b(const FragBase& q, int nb, int hf) {
+  const char* Bs = S ? g_sB1 : g_sB0;
+  if constexpr (kNat) return nat_frag(Bs, q.fb, (q.wn4 + nb) ^ q.F, hf);
+  else return *reinterpret_cast<const uint4*>(Bs + q.fb + nb * 2048 + (hf ? q.c1 : q.c0));
+}
+// One k-step of the pipelined 16-bit core, stage S.  A k-step is eight groups of 8 MFMAs
+// (k half 0, A row blocks 0-1, 2-3, 4-5, 6-7 against the four B row blocks; then k half
+// 1), and each group's fragments are requested while the group before it runs, so the
+// matrix unit does not wait on an LDS read that could have been issued earlier.  On entry
+// a and b hold (or are receiving) the first group's fragments; on exit the next k-step's.
+// The hand-over barrier comes before the last group: this wave's reads of stage S have
+// all been issued by then (the barrier waits for them), stage S ^ 1 is complete for every
+// wave, so the next k-step's first fragments are requested from it while the last 8 MFMAs
+// run, and the stage just read is refilled with k-step kt + 2.  Peak fragment registers:
+// the current group's and the next one's, 48 at a k-half boundary.
+template <class G, int S, bool kNatA, bool kNatB>
+__device__ inline void kstep_pipe(const Op<kNatA>& A, const Op<kNatB>& B, const Offs& ao,
+                                  const Offs& bo, int kt, int nk, int w, FragBase q, Acc& acc,
+                                  uint4 (&a)[2], uint4 (&b)[kNB]) {
+  // keep the natural-layout fragment addresses from being hoisted out of the k loop and
+  // held in registers (they are one v_xad each at the read)
+  if constexpr (kNatA || kNatB) asm("" : "+v"(q.F) : "s"(kt));
+  __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint4 na[2], nb[kNB];
+      if (h == 1 && j == 3) {
+        __builtin_amdgcn_s_setprio(0);
+        wait_vmem();
+        __syncthreads();  // stage S ^ 1 holds k-step kt + 1; every wave is done reading stage S
+        if (kt + 2 < nk) stage_tiles<S>(A, B, ao, bo, kt + 2, w);
+        // After the last k-step these read stage 0, which nothing is filling then; the
+        // values are dead.  Reading unconditionally keeps selects out of the hand-over.
+        na[0] = frag_a<S ^ 1, kNatA>(q, 0, 0);
+        na[1] = frag_a<S ^ 1, kNatA>(q, 1, 0);
+#pragma unroll
+        for (int jj = 0; jj < kNB; ++jj) nb[jj] = frag_b<S ^ 1, kNatB>(q, jj, 0);
+        __builtin_amdgcn_s_setprio(1);
+      } else if (j < 3) {
+        na[0] = frag_a<S, kNatA>(q, 2 * j + 2, h);
+        na[1] = frag_a<S, kNatA>(q, 2 * j + 3, h);
+      } else {
+        na[0] = frag_a<S, kNatA>(q, 0, 1);
+        na[1] = frag_a<S, kNatA>(q, 1, 1);
+#pragma unroll
+        for (int jj = 0; jj < kNB; ++jj) nb[jj] = frag_b<S, kNatB>(q, jj, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int n = 0; n < kNB; ++n)
+          acc[2 * j + i][n] = Mma<G>::op(a[i], b[n], acc[2 * j + i][n]);
+      __builtin_amdgcn_sched_barrier(0);
+      a[0] = na[0];
+      a[1] = na[1];
+      if (j == 3) {
+#pragma unroll
+        for (int jj = 0; jj < kNB; ++jj) b[jj] = nb[jj];
+      }
+    }
+  }
+  __builtin_amdgcn_s_setprio(0);
+}
+
 // acc += A . B^T over nk k-steps of 64 (nk even and > 0), k-step 0 already enqueued by
 // gemm_pre.  Row i of this thread's staging set is at byte ao[i] of A's buffer and bo[i]
-// of B's for k-step 0.  On return every wave has finished reading stage 0 (the last barrier
-// of the loop follows its last reads), so stage 0 may be refilled at once; stage 1 is
-// refilled only after the first barrier of the next call.
+// of B's for k-step 0.  On return every wave has finished reading stage 0 (a barrier
+// follows its last reads), so stage 0 may be refilled at once; stage 1 is refilled only
+// after the first barrier of the next call.
 template <class E, bool kNatA = false, bool kNatB = false>
 __device__ inline void gemm_main_op(const Op<kNatA>& A, const Op<kNatB>& B, const Offs& ao,
                                     const Offs& bo, int nk, Acc& acc) {
@@ -353,15 +432,31 @@ __device__ inline void gemm_main_op(const Op<kNatA>& A, const Op<kNatB>& B, cons
   const int F = nat_f(8 * g + (fr >> 2));
   const int fa = kNatA ? nlb + wm * 256 : (wm * 128 + fr) * 128;
   const int fb = kNatB ? nlb : (wn * kWaveN + fr) * 128;
-  for (int kt = 0; kt < nk; kt += 2) {
+  if constexpr (E::kBytes == 1) {
+    for (int kt = 0; kt < nk; kt += 2) {
+      wait_vmem();
+      __syncthreads();  // stage 0 holds k-step kt; every wave is done reading stage 1
+      stage_tiles<1>(A, B, ao, bo, kt + 1, w);
+      mma_stage<E, 0, kNatA, kNatB>(acc, fa, fb, fs, lane, F, wn * 4, kt);
+      wait_vmem();
+      __syncthreads();  // stage 1 holds k-step kt + 1; every wave is done reading stage 0
+      if (kt + 2 < nk) stage_tiles<0>(A, B, ao, bo, kt + 2, w);
+      mma_stage<E, 1, kNatA, kNatB>(acc, fa, fb, fs, lane, F, wn * 4, kt + 1);
+    }
+  } else {
+    const FragBase q{fa, fb, (g ^ fs) << 4, ((4 + g) ^ fs) << 4, F, wn * 4};
+    uint4 a[2], b[kNB];
     wait_vmem();
-    __syncthreads();  // stage 0 holds k-step kt; every wave is done reading stage 1
-    stage_tiles<1>(A, B, ao, bo, kt + 1, w);
-    mma_stage<E, 0, kNatA, kNatB>(acc, fa, fb, fs, lane, F, wn * 4, kt);
-    wait_vmem();
-    __syncthreads();  // stage 1 holds k-step kt + 1; every wave is done reading stage 0
-    if (kt + 2 < nk) stage_tiles<0>(A, B, ao, bo, kt + 2, w);
-    mma_stage<E, 1, kNatA, kNatB>(acc, fa, fb, fs, lane, F, wn * 4, kt + 1);
+    __syncthreads();  // stage 0 holds k-step 0; every wave is done reading stage 1
+    stage_tiles<1>(A, B, ao, bo, 1, w);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) a[i] = frag_a<0, kNatA>(q, i, 0);
+#pragma unroll
+    for (int j = 0; j < kNB; ++j) b[j] = frag_b<0, kNatB>(q, j, 0);
+    for (int kt = 0; kt < nk; kt += 2) {
+      kstep_pipe<E, 0>(A, B, ao, bo, kt, nk, w, q, acc, a, b);
+      kstep_pipe<E, 1>(A, B, ao, bo, kt + 1, nk, w, q, acc, a, b);
+    }
   }
 }
 template <class E>
