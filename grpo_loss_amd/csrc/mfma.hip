@@ -378,13 +378,17 @@ __device__ inline void kstep_pipe(const Op<kNatA>& A, const Op<kNatB>& B, const 
         __builtin_amdgcn_s_setprio(0);
         wait_vmem();
         __syncthreads();  // stage S ^ 1 holds k-step kt + 1; every wave is done reading stage S
-        if (kt + 2 < nk) stage_tiles<S>(A, B, ao, bo, kt + 2, w);
         // After the last k-step these read stage 0, which nothing is filling then; the
         // values are dead.  Reading unconditionally keeps selects out of the hand-over.
+        // The reads go before the refill of stage S: issued after it, the compiler's
+        // wait insertion put an s_waitcnt vmcnt on reads inside the k loop (a full memory
+        // round trip for the loads just issued), although no read touches the stage
+        // being filled.
         na[0] = frag_a<S ^ 1, kNatA>(q, 0, 0);
         na[1] = frag_a<S ^ 1, kNatA>(q, 1, 0);
 #pragma unroll
         for (int jj = 0; jj < kNB; ++jj) nb[jj] = frag_b<S ^ 1, kNatB>(q, jj, 0);
+        if (kt + 2 < nk) stage_tiles<S>(A, B, ao, bo, kt + 2, w);
         __builtin_amdgcn_s_setprio(1);
       } else if (j < 3) {
         na[0] = frag_a<S, kNatA>(q, 2 * j + 2, h);
