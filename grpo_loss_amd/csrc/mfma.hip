@@ -374,7 +374,8 @@ __device__ inline void kstep_pipe(const Op<kNatA>& A, const Op<kNatB>& B, const 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint4 na[2], nb[kNB];
-      if (h == 1 && j == 3) {
+      const bool last = h == 1 && j == 3;
+      if (last) {
         __builtin_amdgcn_s_setprio(0);
         wait_vmem();
         __syncthreads();  // stage S ^ 1 holds k-step kt + 1; every wave is done reading stage S
@@ -388,7 +389,6 @@ __device__ inline void kstep_pipe(const Op<kNatA>& A, const Op<kNatB>& B, const 
         na[1] = frag_a<S ^ 1, kNatA>(q, 1, 0);
 #pragma unroll
         for (int jj = 0; jj < kNB; ++jj) nb[jj] = frag_b<S ^ 1, kNatB>(q, jj, 0);
-        if (kt + 2 < nk) stage_tiles<S>(A, B, ao, bo, kt + 2, w);
         __builtin_amdgcn_s_setprio(1);
       } else if (j < 3) {
         na[0] = frag_a<S, kNatA>(q, 2 * j + 2, h);
@@ -401,10 +401,18 @@ __device__ inline void kstep_pipe(const Op<kNatA>& A, const Op<kNatB>& B, const 
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i) {
 #pragma unroll
         for (int n = 0; n < kNB; ++n)
           acc[2 * j + i][n] = Mma<G>::op(a[i], b[n], acc[2 * j + i][n]);
+        // the refill of the stage just read is issued after the last group's first 4
+        // MFMAs, so the matrix unit restarts right after the barrier
+        if (last && i == 0) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (kt + 2 < nk) stage_tiles<S>(A, B, ao, bo, kt + 2, w);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
       a[0] = na[0];
       a[1] = na[1];
