@@ -112,13 +112,14 @@ constexpr int kMergeBlock = 256; // rows per block of the merge kernel
 constexpr int kMaxPhases = 32;   // forward partials per row and side (layout stride)
 
 // Vocabulary phases of the MFMA forward.  Its persistent grid (8 XCDs x 32 workgroups)
-// covers 32 / P token blocks per XCD x P phases per round; pick P in {8, 16, 32} that
+// covers 32 / P token blocks per XCD x P phases per round; pick P in {4, 8, 16, 32} that
 // minimises the tiles per workgroup, ceil(blocks / (8 * 32 / P)) * ceil(tiles / P),
-// preferring fewer phases (each W tile then feeds more workgroups of an XCD).
+// preferring fewer phases (each W tile then feeds more workgroups of an XCD; W tiles are
+// also shared across XCDs, X blocks are not).
 __host__ __device__ inline int fwd_phases(int64_t token_blocks, int64_t vocab_tiles) {
-  int best = 8;
+  int best = 4;
   int64_t best_cost = -1;
-  for (int P = 8; P <= kMaxPhases; P *= 2) {
+  for (int P = 4; P <= kMaxPhases; P *= 2) {
     const int64_t per_round = 8 * (32 / P);
     const int64_t cost = ((token_blocks + per_round - 1) / per_round) * ((vocab_tiles + P - 1) / P);
     if (best_cost < 0 || cost < best_cost) {

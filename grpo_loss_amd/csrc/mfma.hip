@@ -741,7 +741,7 @@ __device__ inline void fwd_fold_fixed(const Acc& acc, float s2, int vlim, int vb
 
 // Persistent.  Workgroup w runs on XCD w % 8; its slot s = w / 8 picks a token block of
 // the current round and a vocabulary phase: the 32 workgroups of one XCD cover 32 / P
-// token blocks x P phases (P = fwd_phases(...), 8 for the long-context shape), so each W
+// token blocks x P phases (P = fwd_phases(...), 4 for the long-context shape), so each W
 // tile in flight on an XCD is shared by 32 / P workgroups and each X block by P, and all
 // XCDs sweep the same W tiles together.  A workgroup keeps its token block for a whole
 // round and walks the vocabulary tiles of its phase (vt = phase, phase + P, ...), folding
