@@ -233,22 +233,19 @@ __device__ inline void stage_tiles(const Op<kNatA>& A, const Op<kNatB>& B, const
   }
 }
 
-// acc += (64-wide k slab of stage S).  Fragment rows wm*128 + mb*16 + (lane & 15) of A and
-// wn*64 + nb*16 + (lane & 15) of B,
-// chunk ks*4 + (lane >> 4).  Both 32-wide halves' fragments are requested up front so the
-// second half's LDS reads are in flight while the first half's 64 MFMAs run.
-// For a natural-layout A (B), fa (fb) is the lane base of nat_frag plus 256 wm (0), F is
-// the lane's F, and fragment mb (nb) is unit wm * 8 + mb (wn * 4 + nb).
-template <class G, int S, bool kNatA = false, bool kNatB = false>
-__device__ inline void mma_stage(Acc& acc, int fa, int fb, int fs, int lane, int F = 0,
-                                 int wn4 = 0, int kt = 0) {
+// fp8 operands: acc += (128-wide k slab of stage S), one 16 x 16 x 128 MFMA per block.
+// Fragment rows wm*128 + mb*16 + (lane & 15) of A and wn*64 + nb*16 + (lane & 15) of B,
+// chunks 2 g and 2 g + 1 of each row (g = lane / 16); all fragments are requested up front.
+// (The 16-bit operands go through the pipelined kstep_pipe below.)
+template <int S>
+__device__ inline void mma_stage_fp8(Acc& acc, int fa, int fb, int fs, int lane) {
   const char* As = S ? g_sA1 : g_sA0;
   const char* Bs = S ? g_sB1 : g_sB0;
   // Raised wave priority while this wave feeds the matrix unit: the arbiter then prefers
-  // the MFMA-issuing wave over its SIMD neighbour that is between bursts (+10% measured).
+  // the MFMA-issuing wave over its SIMD neighbour that is between bursts (+10% measured
+  // with this stage-at-a-time schedule).
   __builtin_amdgcn_s_setprio(1);
-  if constexpr (G::kBytes == 1) {
-    static_assert(!kNatA && !kNatB, "fp8 operands are k-contiguous copies");
+  {
     // fp8: one 16 x 16 x 128 MFMA per block and k-step, chunks 2 g and 2 g + 1 per lane
     const int g2 = 2 * (lane >> 4);
     const int c0 = (g2 ^ fs) << 4;
@@ -269,38 +266,6 @@ __device__ inline void mma_stage(Acc& acc, int fa, int fb, int fs, int lane, int
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb)
         acc[mb][nb] = Mma<FP8T>::op(a0[mb], a1[mb], b0[nb], b1[nb], acc[mb][nb]);
-  } else {
-    const int c0 = ((lane >> 4) ^ fs) << 4;
-    const int c1 = ((4 + (lane >> 4)) ^ fs) << 4;
-    uint4 a0[kMB], b0[kNB], a1[kMB], b1[kNB];
-    // F passed through an empty asm that depends on the k-step: the per-fragment addresses
-    // of natural-layout tiles are then formed at each read (one v_xad) instead of being
-    // held in registers across the k loop
-    if constexpr (kNatA || kNatB) asm("" : "+v"(F) : "s"(kt));
-    auto fa_ = [&](int mb, int hf) {
-      if constexpr (kNatA) return nat_frag(As, fa, mb ^ F, hf);
-      else return *reinterpret_cast<const uint4*>(As + fa + mb * 2048 + (hf ? c1 : c0));
-    };
-    auto fb_ = [&](int nb, int hf) {
-      if constexpr (kNatB) return nat_frag(Bs, fb, (wn4 + nb) ^ F, hf);
-      else return *reinterpret_cast<const uint4*>(Bs + fb + nb * 2048 + (hf ? c1 : c0));
-    };
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) a0[mb] = fa_(mb, 0);
-#pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) b0[nb] = fb_(nb, 0);
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) a1[mb] = fa_(mb, 1);
-#pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) b1[nb] = fb_(nb, 1);
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = Mma<G>::op(a0[mb], b0[nb], acc[mb][nb]);
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = Mma<G>::op(a1[mb], b1[nb], acc[mb][nb]);
   }
   __builtin_amdgcn_s_setprio(0);
 }
@@ -445,15 +410,16 @@ __device__ inline void gemm_main_op(const Op<kNatA>& A, const Op<kNatB>& B, cons
   const int fa = kNatA ? nlb + wm * 256 : (wm * 128 + fr) * 128;
   const int fb = kNatB ? nlb : (wn * kWaveN + fr) * 128;
   if constexpr (E::kBytes == 1) {
+    static_assert(!kNatA && !kNatB, "fp8 operands are k-contiguous copies");
     for (int kt = 0; kt < nk; kt += 2) {
       wait_vmem();
       __syncthreads();  // stage 0 holds k-step kt; every wave is done reading stage 1
       stage_tiles<1>(A, B, ao, bo, kt + 1, w);
-      mma_stage<E, 0, kNatA, kNatB>(acc, fa, fb, fs, lane, F, wn * 4, kt);
+      mma_stage_fp8<0>(acc, fa, fb, fs, lane);
       wait_vmem();
       __syncthreads();  // stage 1 holds k-step kt + 1; every wave is done reading stage 0
       if (kt + 2 < nk) stage_tiles<0>(A, B, ao, bo, kt + 2, w);
-      mma_stage<E, 1, kNatA, kNatB>(acc, fa, fb, fs, lane, F, wn * 4, kt + 1);
+      mma_stage_fp8<1>(acc, fa, fb, fs, lane);
     }
   } else {
     const FragBase q{fa, fb, (g ^ fs) << 4, ((4 + g) ^ fs) << 4, F, wn * 4};
