@@ -104,10 +104,30 @@ def cpu_baseline(wl, inp, adv_host, rows_per_seq):
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
+    blas, blas_threads = "unknown", None
+    try:
+        import threadpoolctl
+        info = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            blas = f"{info[0].get('internal_api')} {info[0].get('version')}"
+            blas_threads = info[0].get("num_threads")
+    except ImportError:
+        pass
     return {"value": len(rows) / dt, "unit": "completion tokens/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": _cpu_model(), "blas": blas,
+            "blas_threads": blas_threads,
             "sample": f"{len(rows)} loss rows ({rows_per_seq} per sequence, seeded), fp64 "
                       f"forward + backward incl. full-vocabulary logits, {dt:.1f} s"}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():

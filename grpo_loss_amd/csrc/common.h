@@ -89,7 +89,7 @@ struct Plan {
   int dtype;        // grpo_dtype
   int esize;        // bytes per element of X / W / T
   int need_dW;
-  int phases;       // forward partial slots per row and side (phases actually used may be fewer)
+  int phases;       // fp32 FMA forward: vocabulary phases (fixed; partial stride N)
   int64_t R;        // backward: rows per recompute chunk (multiple of 256)
   int chunk_rows;   // grpo_options::chunk_rows (0: the default chunk)
   int ksplit;       // backward: split of the dX reduction over the vocabulary
@@ -104,12 +104,15 @@ struct Plan {
   // byte offsets into the workspace
   size_t off_ntok, off_idx, off_rank, off_part, off_lsum, off_seq, off_T, off_pm, off_Xg,
       off_redo, off_dxp, off_xq8, off_xp8, off_w8, off_sxq, off_sxp, off_sw, total;
+  size_t off_cpart;  // forward partials of one chunk of policy rows (single pass)
+  size_t off_xgs;    // dW operand's chunk scale (2^k, 2^-k)
+  size_t fwd_total;  // bytes the forward alone (grpo_loss_fwd) uses: a prefix of the plan
 };
 
 constexpr int kTokTile = 256;    // rows per token tile of the MFMA kernels
 constexpr int kVocTile = 256;    // vocabulary entries per tile
 constexpr int kMergeBlock = 256; // rows per block of the merge kernel
-constexpr int kMaxPhases = 32;   // forward partials per row and side (layout stride)
+constexpr int kMaxPhases = 32;   // most vocabulary phases of one forward launch
 
 // Vocabulary phases of the MFMA forward.  Its persistent grid (8 XCDs x 32 workgroups)
 // covers 32 / P token blocks per XCD x P phases per round; pick P in {4, 8, 16, 32} that
@@ -129,6 +132,31 @@ __host__ __device__ inline int fwd_phases(int64_t token_blocks, int64_t vocab_ti
   }
   return best;
 }
+
+// Where a forward launch keeps its partials: for `rows` loss rows of `nsides` sides it
+// runs P = fwd_phases(nsides * ntbs, nvt) phases (ntbs = ceil(rows / 256)) and holds, per
+// (side, phase, row), the running maximum in log2 units (q = 0), the sum of exp2 (q = 1)
+// and the target logit (q = 2) at at(q, sd, ph, r), rows padded to whole token blocks.
+// The device derives the layout from the number of loss rows it counted; the host sizes
+// the buffer for the largest layout any count up to the rows it knows of can produce.
+struct PartLayout {
+  int P;
+  int nsides;
+  int64_t stride;  // rows per (quantity, side, phase) slot
+  __host__ __device__ inline int64_t at(int q, int sd, int ph, int64_t r) const {
+    return ((int64_t)(q * nsides + sd) * P + ph) * stride + r;
+  }
+};
+__host__ __device__ inline PartLayout part_layout(int64_t rows, int nsides, int64_t nvt) {
+  const int64_t ntbs = (rows + 255) / 256;
+  PartLayout l;
+  l.P = fwd_phases(nsides * ntbs, nvt);
+  l.nsides = nsides;
+  l.stride = ntbs * 256;
+  return l;
+}
+// Floats of the largest part_layout(rows, nsides, nvt) over 0 <= rows <= max_rows.
+size_t part_floats_max(int64_t max_rows, int nsides, int64_t nvt);
 
 bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_dW, Plan* p,
                const grpo_options* opts = nullptr);

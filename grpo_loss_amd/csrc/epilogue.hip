@@ -47,23 +47,35 @@ compact_kernel(const uint8_t* __restrict__ mask, int64_t N, int32_t* __restrict_
   }
 }
 
-// Merge of the per-phase partials of one side (policy or reference) for compact row r:
-// log-sum-exp in natural units and the target logit.  Partial maxima are kept in log2
-// units (logit * log2 e); sums are of exp2(logit*log2e - max).
-__device__ inline void merge_side(const float* __restrict__ pm, const float* __restrict__ ps,
-                                  const float* __restrict__ pz, int used, int64_t N,
+// Merge of the per-phase partials of one side (policy or reference) of one row, held at
+// l.at(., sd, ., r) of `part`: log-sum-exp in natural units and the target logit.
+// Partial maxima are kept in log2 units (logit * log2 e); sums are of
+// exp2(logit*log2e - max).
+__device__ inline void merge_side(const float* __restrict__ part, const PartLayout& l, int sd,
                                   int64_t r, float* lse, float* zt) {
   float M = -INFINITY;
-  for (int p = 0; p < used; ++p) M = fmaxf(M, pm[p * N + r]);
+  for (int p = 0; p < l.P; ++p) M = fmaxf(M, part[l.at(0, sd, p, r)]);
   float s = 0.0f, z = 0.0f;
-  for (int p = 0; p < used; ++p) {
-    const float sp = ps[p * N + r];
-    if (sp != 0.0f) s += sp * exp2f(pm[p * N + r] - M);
-    z += pz[p * N + r];
+  for (int p = 0; p < l.P; ++p) {
+    const float sp = part[l.at(1, sd, p, r)];
+    if (sp != 0.0f) s += sp * exp2f(part[l.at(0, sd, p, r)] - M);
+    z += part[l.at(2, sd, p, r)];
   }
   *lse = (M + log2f(s)) * kLn2;
   *zt = z;
 }
+
+// Where the two sides' partials of one row are.
+struct PartRefs {
+  const float* q;  // policy
+  PartLayout lq;
+  int sdq;
+  int64_t rq;
+  const float* p;  // reference
+  PartLayout lp;
+  int sdp;
+  int64_t rp;
+};
 
 struct MergeArgs {
   int64_t N, L, V;
@@ -73,7 +85,8 @@ struct MergeArgs {
   const int32_t* ntok;
   const int32_t* rank;
   const int32_t* idx;
-  const float* part;
+  const float* part;     // the forward's partials over all loss rows
+  const float* cpart;    // single pass: the policy partials of the chunk
   const int32_t* seq;   // [S] loss rows per sequence, then the count of non-empty sequences
   int64_t S;
   const int64_t* targets;
@@ -87,17 +100,20 @@ struct MergeArgs {
   double* lsum;
   int64_t c0, R;        // chunked merge: compact rows [c0, c0 + R)
   // Single-pass mode 3 (non-null): the policy partials share the row's reference mr as
-  // their maximum; a row whose sum of terms 2^(lse2_q - mr) lies outside the window of the
-  // storage type sets *redo, and its outputs, left for the fallback to rewrite, raise no
-  // status flag.  bf16: [2^-60, 2^60] (beyond it the fp32 sum overflows, or terms below
-  // 2^-126 drop out of it).  fp16: [2^-4, 2^14]: a stored term p 2^(lse2_q - mr) must stay
-  // below 65504, and when lse2_q < mr the terms that turn subnormal carry a rounding error
-  // that dX multiplies by f = 2^(mr - lse2_q), which the window keeps below 16.  Every other row
+  // their maximum; a row whose sum of terms 2^(lse2_q - mr) lies outside the window
+  // [2^win_lo, 2^win_hi] sets *redo, and its outputs, left for the fallback to rewrite,
+  // raise no status flag.  bf16: [2^-60, 2^60] (beyond it the fp32 sum overflows, or terms
+  // below 2^-126 drop out of it).  fp16: [2^-4, 2^14]: a stored term p 2^(lse2_q - mr) must
+  // stay below 65504, and when lse2_q < mr the terms that turn subnormal carry a rounding
+  // error that dX multiplies by f = 2^(mr - lse2_q), which the window keeps below 16.  With
+  // dW, fp16 takes [2^-4, 2^4]: the dW operand carries f per row, and a chunk whose f span
+  // 2^18 would push its smallest rows into fp16's subnormals.  Every other row
   // gets its target entry of the chunk buffer (row r - c0, patch_ld entries per row, in
   // the storage type patch_dtype) replaced by expm1(q) / f, f = 2^(mr - lse2_q), which
   // makes the buffer row -T / f with the target entry 1 - p_y = -expm1(q) kept to the
   // precision of the storage type.
   int32_t* redo;
+  float win_lo, win_hi;
   char* patch;
   int64_t patch_ld;
   int patch_dtype;
@@ -113,26 +129,20 @@ struct MergeArgs {
 //   l = beta * KL - A_s                      (loss value; the ratio is 1 at q = sg(q))
 //   g = w_t (-A_s [if detached] + beta dKL/dq)   (dloss/dq)
 // with w_t = 1 / N_tok (token mean) or 1 / (n_s S') (sequence mean: n_s loss rows of the
-// row's sequence, S' sequences with any) [Long-context GRPO, §4].  used0 / used1: the
-// vocabulary phases the forward wrote for the policy and the reference side.  Returns
-// the row's contribution to the loss sum (l, or l / n_s for the sequence mean) and ORs
-// status bits into *flags.
-__device__ inline double merge_row(const MergeArgs& a, int64_t t, int64_t r, int used0,
-                                   int used1, int32_t ntok, int* flags) {
-  const int64_t N = a.N;
-  const int64_t PN = (int64_t)a.phases * N;
-  const float* pm = a.part;
-  const float* ps = a.part + 2 * PN;
-  const float* pz = a.part + 4 * PN;
+// row's sequence, S' sequences with any) [Long-context GRPO, §4].  pr: where the row's
+// partials are (r: its compact index).  Returns the row's contribution to the loss sum
+// (l, or l / n_s for the sequence mean) and ORs status bits into *flags.
+__device__ inline double merge_row(const MergeArgs& a, int64_t t, int64_t r, const PartRefs& pr,
+                                   int32_t ntok, int* flags) {
   float lse_q, zq, lse_p, zp;
-  merge_side(pm, ps, pz, used0, N, r, &lse_q, &zq);
-  merge_side(pm + PN, ps + PN, pz + PN, used1, N, r, &lse_p, &zp);
+  merge_side(pr.q, pr.lq, pr.sdq, pr.rq, &lse_q, &zq);
+  merge_side(pr.p, pr.lp, pr.sdp, pr.rp, &lse_p, &zp);
   bool quiet = false;
   float l2s = 0.f;
   if (a.redo) {
-    l2s = lse_q * kLog2e - pm[r];
-    const bool f16 = a.patch_dtype == GRPO_F16;
-    if (!(l2s >= (f16 ? -4.f : -60.f) && l2s <= (f16 ? 14.f : 60.f))) {
+    // every policy partial of a mode-3 chunk carries the row's reference as its maximum
+    l2s = lse_q * kLog2e - pr.q[pr.lq.at(0, pr.sdq, 0, pr.rq)];
+    if (!(l2s >= a.win_lo && l2s <= a.win_hi)) {
       atomicOr(a.redo, 1);
       quiet = true;
     }
@@ -201,14 +211,23 @@ __device__ inline void block_sum_store(double v, double* out) {
 __global__ void __launch_bounds__(kMergeBlock) merge_kernel(MergeArgs a) {
   const int64_t t = (int64_t)blockIdx.x * kMergeBlock + threadIdx.x;
   const int32_t ntok = *a.ntok;
-  // partial slots written by the forward: all of them, or the adaptive phase count
-  const int used = a.adaptive ? fwd_phases(2 * (((int64_t)ntok + 255) / 256), (a.V + 255) / 256)
-                              : a.phases;
+  // the layout the forward wrote: the MFMA kernels' adaptive one (both sides in one
+  // launch), or the FMA kernels' fixed phases with row stride N
+  PartLayout l;
+  if (a.adaptive) {
+    l = part_layout(ntok, 2, (a.V + 255) / 256);
+  } else {
+    l.P = a.phases;
+    l.nsides = 2;
+    l.stride = a.N;
+  }
   double ell_d = 0.0;
   int flags = 0;
   if (t < a.N) {
     if (a.mask[t]) {
-      ell_d = merge_row(a, t, a.rank[t], used, used, ntok, &flags);
+      const int64_t r = a.rank[t];
+      const PartRefs pr{a.part, l, 0, r, a.part, l, 1, r};
+      ell_d = merge_row(a, t, r, pr, ntok, &flags);
     } else {
       reinterpret_cast<float4*>(a.saved)[t] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (a.logp) a.logp[t] = 0.f;
@@ -232,11 +251,12 @@ __global__ void __launch_bounds__(kMergeBlock) merge_rows_kernel(MergeArgs a) {
   if ((int64_t)blk0 * kMergeBlock >= ntok) return;   // whole block past the last row
   const int64_t nvt = (a.V + 255) / 256;
   const int64_t crow = (ntok - a.c0 < a.R ? ntok - a.c0 : a.R);
-  const int used0 = fwd_phases((crow + 255) / 256, nvt);
-  const int used1 = fwd_phases(((int64_t)ntok + 255) / 256, nvt);
+  // policy: the chunk's own launch over its rows; reference: one launch over all rows
+  const PartRefs pr{a.cpart, part_layout(crow, 1, nvt), 0, r - a.c0,
+                    a.part, part_layout(ntok, 1, nvt), 0, r};
   double ell_d = 0.0;
   int flags = 0;
-  if (r < ntok && r < a.c0 + a.R) ell_d = merge_row(a, a.idx[r], r, used0, used1, ntok, &flags);
+  if (r < ntok && r < a.c0 + a.R) ell_d = merge_row(a, a.idx[r], r, pr, ntok, &flags);
   if (flags) atomicOr(a.status, flags);
   block_sum_store(ell_d, a.lsum + blk0);
 }
@@ -409,6 +429,7 @@ hipError_t launch_merge(const Plan& p, const void* ws, const int64_t* targets,
   a.rank = ws_ptr<int32_t>(w, p.off_rank);
   a.idx = ws_ptr<int32_t>(w, p.off_idx);
   a.part = ws_ptr<float>(w, p.off_part);
+  a.cpart = nullptr;
   a.seq = ws_ptr<int32_t>(w, p.off_seq);
   a.S = p.N / p.L;
   a.targets = targets;
@@ -423,6 +444,7 @@ hipError_t launch_merge(const Plan& p, const void* ws, const int64_t* targets,
   a.c0 = 0;
   a.R = p.N;
   a.redo = nullptr;
+  a.win_lo = a.win_hi = 0.f;
   a.patch = nullptr;
   a.patch_ld = 0;
   a.patch_dtype = 0;
@@ -466,6 +488,7 @@ hipError_t launch_merge_rows(const Plan& p, const void* ws, int64_t c0, const in
   a.rank = ws_ptr<int32_t>(w, p.off_rank);
   a.idx = ws_ptr<int32_t>(w, p.off_idx);
   a.part = ws_ptr<float>(w, p.off_part);
+  a.cpart = ws_ptr<float>(w, p.off_cpart);
   a.seq = ws_ptr<int32_t>(w, p.off_seq);
   a.S = p.N / p.L;
   a.targets = targets;
@@ -480,6 +503,8 @@ hipError_t launch_merge_rows(const Plan& p, const void* ws, int64_t c0, const in
   a.c0 = c0;
   a.R = p.R;
   a.redo = redo;
+  a.win_lo = p.dtype == GRPO_F16 ? -4.f : -60.f;
+  a.win_hi = p.dtype == GRPO_F16 ? (p.need_dW ? 4.f : 14.f) : 60.f;
   a.patch = reinterpret_cast<char*>(patch);
   a.patch_ld = p.Vpad;
   a.patch_dtype = p.dtype;

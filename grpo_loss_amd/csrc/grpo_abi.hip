@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "common.h"
 
 namespace grpo {
@@ -118,6 +120,8 @@ bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_d
       }
     }
   }
+  const int64_t nvt = p->Vpad / kVocTile;
+  // what the forward uses comes first, so that its size is a prefix of the plan
   size_t o = 0;
   p->off_ntok = o;
   o = align_up(o + 16);
@@ -126,21 +130,16 @@ bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_d
   p->off_rank = o;
   o = align_up(o + (size_t)p->N * 4);
   p->off_part = o;
-  o = align_up(o + (size_t)6 * p->phases * p->N * 4);
+  // MFMA: the larger of the two-pass forward's (both sides in one launch) and the single
+  // pass's reference-side layouts; FMA: a fixed phase count with row stride N
+  const size_t part_floats =
+      p->mfma ? std::max(part_floats_max(p->N, 2, nvt), part_floats_max(p->N, 1, nvt))
+              : (size_t)6 * p->phases * p->N;
+  o = align_up(o + part_floats * 4);
   p->off_lsum = o;
   o = align_up(o + (size_t)((p->N + kMergeBlock - 1) / kMergeBlock) * 8);
   p->off_seq = o;
   o = align_up(o + (size_t)(S + 1) * 4);
-  p->off_T = o;
-  o = align_up(o + (size_t)p->R * p->Vpad * p->esize);
-  p->off_pm = o;
-  if (p->mfma) o = align_up(o + (size_t)p->R * (p->Vpad / kVocTile) * 4);
-  p->off_Xg = o;
-  if (p->mfma && need_dW) o = align_up(o + (size_t)p->R * H * p->esize);
-  p->off_redo = o;  // single-pass fallback flags, one per chunk
-  if (p->mfma) o = align_up(o + (size_t)((p->N + p->R - 1) / p->R) * 4);
-  p->off_dxp = o;
-  if (p->mfma && p->ksplit > 1) o = align_up(o + (size_t)p->ksplit * p->R * H * 4);
   if (p->fp8 && !p->mfma) return false;   // fp8 logits run on the MFMA kernels only
   p->off_xq8 = p->off_xp8 = p->off_w8 = p->off_sxq = p->off_sxp = p->off_sw = o;
   if (p->fp8) {
@@ -157,8 +156,38 @@ bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_d
     p->off_sw = o;
     o = align_up(o + (size_t)V * 4);
   }
+  p->fwd_total = o;
+  p->off_cpart = o;  // single pass: the policy partials of one chunk
+  if (p->mfma) o = align_up(o + part_floats_max(p->R, 1, nvt) * 4);
+  p->off_T = o;
+  o = align_up(o + (size_t)p->R * p->Vpad * p->esize);
+  p->off_pm = o;
+  if (p->mfma) o = align_up(o + (size_t)p->R * (p->Vpad / kVocTile) * 4);
+  p->off_Xg = o;
+  if (p->mfma && need_dW) o = align_up(o + (size_t)p->R * H * p->esize);
+  p->off_xgs = o;
+  if (p->mfma && need_dW) o = align_up(o + 16);
+  p->off_redo = o;  // single-pass fallback flags, one per chunk
+  if (p->mfma) o = align_up(o + (size_t)((p->N + p->R - 1) / p->R) * 4);
+  p->off_dxp = o;
+  if (p->mfma && p->ksplit > 1) o = align_up(o + (size_t)p->ksplit * p->R * H * 4);
   p->total = o;
   return true;
+}
+
+size_t part_floats_max(int64_t max_rows, int nsides, int64_t nvt) {
+  // the phase count depends on the token blocks through a ceiling, so the product is not
+  // monotone in the rows: take the maximum over every block count (P <= kMaxPhases bounds
+  // the blocks past a million, which no workload reaches)
+  const int64_t nb = (max_rows + 255) / 256;
+  const int64_t lim = nb < ((int64_t)1 << 20) ? nb : ((int64_t)1 << 20);
+  size_t best = 0;
+  for (int64_t b = 1; b <= lim; ++b) {
+    const size_t f = (size_t)3 * nsides * fwd_phases(nsides * b, nvt) * b * 256;
+    best = std::max(best, f);
+  }
+  if (nb > lim) best = std::max(best, (size_t)3 * nsides * kMaxPhases * nb * 256);
+  return best;
 }
 
 void plan_options(const grpo_options* o, Plan* p) {

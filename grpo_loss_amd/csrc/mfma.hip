@@ -464,7 +464,11 @@ struct FwdArgs {
   const char* Xp;
   const char* W;
   const int64_t* targets;
-  float* part;  // [3][2 sides][kMaxPhases][N]: running max (log2 units), sum, target logit
+  // Partials of this launch (PartLayout over its rows, row index r - row_lo): the running
+  // maximum (log2 units), sum of exp2 and target logit per side, phase and row.
+  float* part;
+  // Mode 3: the reference side's partials written by the mode-1 launch over all loss rows.
+  const float* ref_part;
   float scale2; // log2(e) / temperature
   // This launch covers the loss rows [row_lo, min(row_hi, ntok)) of sides side0 ..
   // side0 + nsides - 1 (side 0: policy X_q, side 1: reference X_p).
@@ -741,7 +745,8 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
   const FwdRange fr = fwd_range(a, ntok);
   const int TB = fr.TB;
   const int64_t nvt = (a.V + 255) / 256;
-  const int P = fwd_phases(TB, nvt);
+  const PartLayout pl = part_layout(fr.rhi > a.row_lo ? fr.rhi - a.row_lo : 0, a.nsides, nvt);
+  const int P = pl.P;  // = fwd_phases(TB, nvt)
   const int tb_per_xcd = slots / P;
   const int phase = slot % P;
   const int tbg = kXcds * tb_per_xcd;            // token blocks per round
@@ -791,16 +796,13 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
         // the reference side's log-sum-exp of row r from the partials of the mode-1 launch
         float mr = INFINITY;
         if (r < fr.rhi) {
-          const int used = fwd_phases(((int64_t)ntok + 255) / 256, nvt);
-          const int64_t PN = (int64_t)kMaxPhases * a.N;
-          const float* pmx = a.part + (int64_t)kMaxPhases * a.N;  // side 1 maxima
-          const float* psx = pmx + 2 * PN;                          // side 1 sums
+          const PartLayout rl = part_layout(ntok, 1, nvt);
           float M = -INFINITY;
-          for (int ph = 0; ph < used; ++ph) M = fmaxf(M, pmx[ph * a.N + r]);
+          for (int ph = 0; ph < rl.P; ++ph) M = fmaxf(M, a.ref_part[rl.at(0, 0, ph, r)]);
           float sm = 0.f;
-          for (int ph = 0; ph < used; ++ph) {
-            const float sp = psx[ph * a.N + r];
-            if (sp != 0.f) sm += sp * exp2f(pmx[ph * a.N + r] - M);
+          for (int ph = 0; ph < rl.P; ++ph) {
+            const float sp = a.ref_part[rl.at(1, 0, ph, r)];
+            if (sp != 0.f) sm += sp * exp2f(a.ref_part[rl.at(0, 0, ph, r)] - M);
           }
           mr = M + log2f(sm);
           if (phase == 0) a.pm[r - a.row_lo] = mr;
@@ -813,6 +815,11 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
       s_run[0][nb][tid] = -INFINITY;
       s_run[1][nb][tid] = 0.f;
     }
+    // The block state written above is read by other waves: in the folds (after the k
+    // loop's barriers) and in the final merge of the token block, which a phase with no
+    // vocabulary tile reaches without any barrier in between.  LDS only, so the next
+    // tile's loads in flight are not waited for.
+    lds_barrier();
     FoldOut fo;
     if (kStore) {
       const int64_t rt = a.Vpad * E::kBytes, rm = nvt * 4;  // bytes per pt, pm row
@@ -902,11 +909,9 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
                               ? 0.f
                               : (m0 == -INFINITY ? 0.f : mrg[0][1][n] * exp2f(m0 - M)) +
                                     (m1 == -INFINITY ? 0.f : mrg[1][1][n] * exp2f(m1 - M));
-        const int64_t PN = (int64_t)kMaxPhases * a.N;
-        const int64_t o = (int64_t)(side * kMaxPhases + phase) * a.N + r;
-        a.part[o] = M;
-        a.part[2 * PN + o] = sum;
-        a.part[4 * PN + o] = s_zt[n];
+        a.part[pl.at(0, sd, phase, r - a.row_lo)] = M;
+        a.part[pl.at(1, sd, phase, r - a.row_lo)] = sum;
+        a.part[pl.at(2, sd, phase, r - a.row_lo)] = s_zt[n];
       }
     }
     __syncthreads();
@@ -1160,7 +1165,8 @@ template <class E>
 __global__ void __launch_bounds__(kThreads, 1)
 dw_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int nht, int accumulate,
           const int32_t* __restrict__ ntok_p, const char* __restrict__ Xg,
-          const char* __restrict__ T, float* __restrict__ dW, int32_t* __restrict__ found_inf) {
+          const char* __restrict__ T, float* __restrict__ dW, int32_t* __restrict__ found_inf,
+          const float* __restrict__ xg_scale) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / kWN, wn = w % kWN;
   const int64_t ht = blockIdx.x % nht, vt = blockIdx.x / nht;
   const int ntok = *ntok_p;
@@ -1184,6 +1190,14 @@ dw_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int nht, in
                                 acc);
   const int64_t hb = h0 + wm * 128 + 4 * (lane >> 4);
   bool bad = false;
+  {
+    // undo the chunk's power-of-two scale of Xg (exact)
+    const float inv = xg_scale[1];
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] *= inv;
+  }
   if (accumulate) {
     // every old value of the lane's columns in flight at once: one memory round trip per
     // tile instead of one per 16-byte piece
@@ -1217,17 +1231,64 @@ dw_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int nht, in
 }
 
 // --------------------------------------------------------------------------- dW operand
-// Xg[rl][h] = c g_r s_r X_q[idx[c0 + rl]][h] in the storage type for the chunk's loss rows
-// rl < nrows (s_r as in dx_kernel), and 0 for the rows from nrows up to the next multiple
-// of 128 (the k range of dw_kernel).  One row per block, 8 entries (16 bytes) per thread
-// and step.
+// The chunk's row factors c g_r s_r (s_r as in dx_kernel) of the dW operand.
+__device__ inline float xg_row_factor(int64_t rl, int64_t t, const float* __restrict__ saved,
+                                      float c, bool fixed, const float* __restrict__ mr) {
+  float sc = saved[t * 4 + 3] * c;
+  if (fixed) sc *= fixed_row_factor(rl, t, saved, mr);
+  return sc;
+}
+
+// xg_scale = (2^k, 2^-k) with 2^k max_r |c g_r s_r| in [1/2, 1) over the chunk's loss rows
+// (k = 0 when the maximum is 0 or not finite), one block.  The dW operand is stored in
+// the 16-bit type as 2^k c g s X: with g about 1 / N_tok and s down to 2^-14 (fp16
+// single-pass window), c g s X alone falls into fp16's subnormals and loses its bits;
+// scaled, the largest row sits just below |X| (never above it, so no overflow), and
+// dw_kernel multiplies its fp32 tile by 2^-k, exactly.
+__global__ void __launch_bounds__(256)
+xg_scale_kernel(int64_t R, int64_t c0, const int32_t* __restrict__ ntok_p,
+                const int32_t* __restrict__ idx, const float* __restrict__ saved,
+                const float* __restrict__ grad_loss, float loss_scale,
+                const int32_t* __restrict__ redo, const float* __restrict__ mr,
+                float* __restrict__ xg_scale) {
+  __shared__ float red[256];
+  int64_t nrows = (int64_t)(*ntok_p) - c0;
+  if (nrows > R) nrows = R;
+  const float c = (grad_loss ? *grad_loss : 1.f) / loss_scale;
+  const bool fixed = redo && *redo == 0;
+  float m = 0.f;
+  for (int64_t rl = threadIdx.x; rl < nrows; rl += 256)
+    m = fmaxf(m, fabsf(xg_row_factor(rl, idx[c0 + rl], saved, c, fixed, mr)));
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (threadIdx.x < (unsigned)off) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + off]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    int e = 0;
+    const float M = red[0];
+    if (M > 0.f && isfinite(M)) {
+      frexpf(M, &e);                 // M = f 2^e, f in [1/2, 1)
+      e = e < -100 ? -100 : (e > 100 ? 100 : e);
+    }
+    xg_scale[0] = ldexpf(1.f, -e);
+    xg_scale[1] = ldexpf(1.f, e);
+  }
+}
+
+// Xg[rl][h] = 2^k c g_r s_r X_q[idx[c0 + rl]][h] in the storage type for the chunk's loss
+// rows rl < nrows (2^k = xg_scale[0]), and 0 for the rows from nrows up to the next
+// multiple of 128 (the k range of dw_kernel).  One row per block, 8 entries (16 bytes)
+// per thread and step.
 template <class E>
 __global__ void __launch_bounds__(256)
 gather_rows_kernel(const typename E::T* __restrict__ X, int64_t H, int64_t R, int64_t c0,
                    const int32_t* __restrict__ ntok_p, const int32_t* __restrict__ idx,
                    const float* __restrict__ saved, const float* __restrict__ grad_loss,
                    float loss_scale, typename E::T* __restrict__ Xg,
-                   const int32_t* __restrict__ redo, const float* __restrict__ mr) {
+                   const int32_t* __restrict__ redo, const float* __restrict__ mr,
+                   const float* __restrict__ xg_scale) {
   const int64_t rl = blockIdx.x;
   int64_t nrows = (int64_t)(*ntok_p) - c0;
   if (nrows > R) nrows = R;
@@ -1238,8 +1299,8 @@ gather_rows_kernel(const typename E::T* __restrict__ X, int64_t H, int64_t R, in
     return;
   }
   const int64_t t = idx[c0 + rl];
-  float sc = saved[t * 4 + 3] * ((grad_loss ? *grad_loss : 1.f) / loss_scale);
-  if (redo && *redo == 0) sc *= fixed_row_factor(rl, t, saved, mr);
+  const float sc = xg_row_factor(rl, t, saved, (grad_loss ? *grad_loss : 1.f) / loss_scale,
+                                 redo && *redo == 0, mr) * xg_scale[0];
   const uint4* src = reinterpret_cast<const uint4*>(X + t * H);
   for (int64_t h8 = threadIdx.x; h8 < H / 8; h8 += 256) {
     const uint4 q = src[h8];
@@ -1271,6 +1332,7 @@ FwdArgs fwd_args(const Plan& p, void* ws, const void* Xq, const void* Xp, const 
   a.W = (const char*)W;
   a.targets = targets;
   a.part = ws_ptr<float>(ws, p.off_part);
+  a.ref_part = ws_ptr<float>(ws, p.off_part);
   a.scale2 = p.scale2;
   a.row_lo = 0;
   a.row_hi = p.N;
@@ -1343,13 +1405,17 @@ hipError_t chunk_grads(const Plan& p, void* ws, int64_t c0, const void* Xq, cons
   }
   if (dW) {
     T* Xg = ws_ptr<T>(ws, p.off_Xg);
+    float* xs = ws_ptr<float>(ws, p.off_xgs);
+    hipLaunchKernelGGL(xg_scale_kernel, dim3(1), dim3(256), 0, st, p.R, c0, ntok, idx, saved,
+                       grad_loss, loss_scale, redo, mr, xs);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(gather_rows_kernel<E>, dim3((unsigned)p.R), dim3(256), 0, st,
                        (const T*)Xq, p.H, p.R, c0, ntok, idx, saved, grad_loss, loss_scale, Xg,
-                       redo, mr);
+                       redo, mr, (const float*)xs);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(dw_kernel<E>, dim3((unsigned)(nht * nvt)), dim3(kThreads), 0, st, p.H,
                        p.V, p.Vpad, p.R, c0, nht, c0 == 0 ? accumulate_dW : 1, ntok,
-                       (const char*)Xg, (const char*)Tb, dW, found_inf);
+                       (const char*)Xg, (const char*)Tb, dW, found_inf, (const float*)xs);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
@@ -1423,6 +1489,7 @@ hipError_t fused_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, c
     a.row_lo = c0;
     a.row_hi = c0 + p.R;
     a.side0 = 0;
+    a.part = ws_ptr<float>(ws, p.off_cpart);
     a.pt = reinterpret_cast<char*>(Tb);
     a.pm = pm;
     a.gate = nullptr;

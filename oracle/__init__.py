@@ -29,6 +29,7 @@ from .grpo_oracle import (  # noqa: F401
     reverse_kl_q,
     token_weights,
     backward,
+    dw_rows,
     forward,
     found_inf,
     group_advantages,

@@ -460,6 +460,42 @@ def backward(xq, W, targets, mask, fwd: dict, grad_loss: float = 1.0,
             "naive_fp16_overflow": worst >= 65520.0, "naive_max_abs": worst}
 
 
+def dw_rows(xq, W, targets, mask, fwd: dict, vrows, grad_loss: float = 1.0,
+            loss_scale: float = 1.0, block: int = 1024) -> np.ndarray:
+    """Rows ``vrows`` of dW = sum_t c * g_t * (onehot(y_t) - P_t)^T x_q[t], summed over
+    every loss row t, without forming the other rows of dW: P_tv = exp(z_tv / tau - lse_t)
+    needs only the selected vocabulary columns of each row's logits once lse_t is known,
+    and ``fwd``'s lse_q holds it from the row's full vocabulary.  The same definition as
+    ``backward``'s dW, read one row of W at a time, for vocabulary sizes where the full
+    [V, H] product is too slow to check.  xq: the loss rows in ascending order (the rows
+    ``fwd`` computed); c = grad_loss / loss_scale / tau.  Returns [len(vrows), H] fp64.
+    Pinned by test_pin[pin_dx_dw_finite_differences] and test_dw_rows_match_backward.
+    """
+    targets = np.asarray(targets).reshape(-1)
+    mask = np.asarray(mask).reshape(-1).astype(np.int64)
+    vrows = np.asarray(vrows, dtype=np.int64)
+    variant = fwd.get("variant", DEFAULT)
+    tau = float(variant.temperature)
+    c = grad_factor(grad_loss, loss_scale, tau)
+    Wd = _f64(W)
+    Wv = Wd[vrows]
+    Wl = dequantize_e4m3_rows(Wd)[vrows] if variant.fp8_logits else Wv
+    rows = np.nonzero(mask)[0]
+    X = _f64(xq)
+    if X.shape[0] != len(rows):
+        raise ValueError("xq must hold the loss rows, in order")
+    out = np.zeros((len(vrows), Wd.shape[1]))
+    for i0 in range(0, len(rows), block):
+        r = rows[i0:i0 + block]
+        x = X[i0:i0 + block]
+        xl = dequantize_e4m3_rows(x) if variant.fp8_logits else x
+        z = logits(xl, Wl, tau)                                   # [rows, len(vrows)]
+        T = (targets[r][:, None] == vrows[None, :]).astype(np.float64)
+        T -= np.exp(z - fwd["lse_q"][r][:, None])
+        out += (T * (c * fwd["g"][r])[:, None]).T @ x
+    return out
+
+
 def found_inf(fwd: dict, bwd: dict | None = None) -> bool:
     """The non-finite predicate a mixed-precision caller needs: anything read on a
     loss row, the loss, g, dX or dW is inf/NaN."""

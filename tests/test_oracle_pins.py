@@ -192,12 +192,17 @@ def pin_dx_dw_finite_differences():
             P[t, j] += h
             M[t, j] -= h
             assert abs((F(P, W) - F(M, W)) / (2 * h) - dX[t, j]) < 1e-8
+    # dW whole, and one vocabulary row at a time from the loss rows alone
+    rows = np.nonzero(m)[0]
+    dWr = oracle.dw_rows(xq[rows], W, y, m, f, np.arange(W.shape[0])[::-1])[::-1]
     for v in range(W.shape[0]):
         for j in range(W.shape[1]):
             P, M = W.copy(), W.copy()
             P[v, j] += h
             M[v, j] -= h
-            assert abs((F(xq, P) - F(xq, M)) / (2 * h) - b["dW"][v, j]) < 1e-8
+            fd = (F(xq, P) - F(xq, M)) / (2 * h)
+            assert abs(fd - b["dW"][v, j]) < 1e-8
+            assert abs(fd - dWr[v, j]) < 1e-8
 
 
 def pin_cross_entropy_reduction():
@@ -226,12 +231,35 @@ def pin_loss_scale_cancels():
     assert np.allclose(b1["dX"], b2["dX"], rtol=1e-15) and np.allclose(b1["dW"], b2["dW"])
 
 
+def pin_naive_fp16_overflow():
+    """The mixed-precision diagnostic, by hand: W = 0 makes every softmax uniform, so with
+    V = 2 and target 0 the logit gradient row is (1/2, -1/2); X_p = X_q makes KL = 0, so
+    g_t = -A_t / N_tok, here -+2 / 2.  A naive path forming grad_loss * g * (onehot - P) then
+    peaks at grad_loss / 2 (over tau: the temperature divides it), and it overflows fp16
+    exactly when that reaches 65520, the first magnitude that rounds to inf."""
+    xq = np.array([[0.3], [-1.1]])
+    W = np.zeros((2, 1))
+    y = np.array([0, 0])
+    m = np.array([1, 1])
+    adv = np.array([2.0, -2.0], np.float32)
+    f = oracle.forward(xq, xq.copy(), W, y, m, adv, 1, BETA)
+    assert np.array_equal(f["g"], [-1.0, 1.0]), f["g"]
+    for grad_loss, over in ((131040.0, True), (131038.0, False)):
+        b = oracle.backward(xq, W, y, m, f, grad_loss=grad_loss, loss_scale=grad_loss)
+        assert b["naive_max_abs"] == grad_loss / 2 and b["naive_fp16_overflow"] is over
+    with np.errstate(over="ignore"):
+        assert float(np.float16(65520.0)) == np.inf and float(np.float16(65519.0)) == 65504.0
+    fv = oracle.forward(xq, xq.copy(), W, y, m, adv, 1, BETA, variant=og.Variant(temperature=2.0))
+    b = oracle.backward(xq, W, y, m, fv, grad_loss=131040.0, loss_scale=131040.0)
+    assert b["naive_max_abs"] == 131040.0 / 4 and not b["naive_fp16_overflow"]
+
+
 PINS = [pin_advantages_equal_rewards, pin_advantages_two_closed_form,
         pin_advantages_match_torch_std, pin_advantages_moments,
         pin_advantages_sequential_order, pin_logsoftmax_normalised,
         pin_kl_direction_exact_expectation, pin_policy_equals_reference, pin_brute_force,
         pin_g_matches_surrogate_fd, pin_dx_dw_finite_differences,
-        pin_cross_entropy_reduction, pin_loss_scale_cancels]
+        pin_cross_entropy_reduction, pin_loss_scale_cancels, pin_naive_fp16_overflow]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -281,6 +309,21 @@ def test_sampled_rows_match_full():
     full[b["rows"]] = b["dX"]
     assert np.allclose(bs["dX"], full[rows], atol=1e-15)
     assert fs["loss"] is None
+
+
+@pytest.mark.parametrize("variant", [og.Variant(), og.Variant(temperature=0.6),
+                                     og.Variant(kl="forward", norm="sequences")],
+                         ids=["default", "temperature", "forward-seq"])
+def test_dw_rows_match_backward(variant):
+    """Selected vocabulary rows of dW from the loss rows alone equal the same rows of the
+    full dW (pinned by finite differences), for any row order and with a loss scale."""
+    xq, xp, W, y, m, adv, L = _case(97, S=3, L=6, H=5, V=23)
+    f = oracle.forward(xq, xp, W, y, m, adv, L, BETA, variant=variant)
+    b = oracle.backward(xq, W, y, m, f, grad_loss=3.0, loss_scale=2.0, need_dW=True)
+    vr = np.array([22, 0, 7, int(y[np.nonzero(m)[0][0]]), 13])
+    got = oracle.dw_rows(xq[np.nonzero(m)[0]], W, y, m, f, vr, grad_loss=3.0, loss_scale=2.0,
+                         block=4)
+    assert np.allclose(got, b["dW"][vr], rtol=1e-12, atol=1e-15)
 
 
 def test_memory_figures_golden():
@@ -382,6 +425,12 @@ def _mut_adv_pairwise(rewards, eps=1e-4, unbiased=True):
 
 
 _REAL_ADV = og.group_advantages
+_REAL_DW_ROWS = og.dw_rows
+
+
+def _mut_dw_rows_no_onehot(xq, W, targets, mask, fwd, vrows, **kw):
+    # the softmax part only: as if every target were outside the selected rows
+    return _REAL_DW_ROWS(xq, W, np.full_like(np.asarray(targets), -1), mask, fwd, vrows, **kw)
 
 MUTATIONS = {
     "forward_kl": ("reverse_kl_k3", _mut_forward_kl),
@@ -397,6 +446,7 @@ MUTATIONS = {
     "adv_population_std": ("group_advantages", _mut_adv_population),
     "adv_eps_in_variance": ("group_advantages", _mut_adv_eps_in_var),
     "adv_other_sum_order": ("group_advantages", _mut_adv_pairwise),
+    "dw_rows_no_onehot": ("dw_rows", _mut_dw_rows_no_onehot),
 }
 
 
