@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     grpo_loss_bwd,
     grpo_loss_fwd,
     grpo_loss_fwd_bwd,
+    grpo_loss_fwd_noalloc,
     grpo_quantize_e4m3,
     grpo_scale_grad,
     grpo_workspace_bytes,

@@ -83,6 +83,10 @@ def load_library():
     lib.grpo_loss_fwd.argtypes = [_c_p, _c_p, _c_p, ctypes.c_int, _c_p, _c_p, _c_p, _c_i64,
                                   _c_i64, _c_i64, _c_i64, ctypes.c_float, _c_p, _c_p, _c_p, _c_p,
                                   _c_p, _c_p, opt_p, _c_p, ctypes.c_size_t, _c_p]
+    lib.grpo_loss_fwd_noalloc.restype = ctypes.c_int
+    lib.grpo_loss_fwd_noalloc.argtypes = [_c_p, _c_p, _c_p, ctypes.c_int, _c_p, _c_p, _c_p,
+                                          _c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_float, _c_p,
+                                          _c_p, _c_p, _c_p, _c_p, _c_p, opt_p, _c_p]
     lib.grpo_loss_bwd.restype = ctypes.c_int
     lib.grpo_loss_bwd.argtypes = [_c_p, _c_p, ctypes.c_int, _c_p, _c_p, _c_p, _c_i64, _c_i64,
                                   _c_i64, _c_i64, _c_p, ctypes.c_float, _c_p, _c_p, ctypes.c_int,
@@ -209,6 +213,38 @@ def grpo_loss_fwd(xq, xp, W, targets, mask, adv, beta: float = 0.04, L: int | No
                               _opts(opts), _ptr(workspace), workspace.numel(), _stream(stream)))
     return {"loss": loss, "saved": saved, "logp": terms[0], "ref_logp": terms[1],
             "kl": terms[2], "status": status, "workspace": workspace}
+
+
+def grpo_loss_fwd_noalloc(xq, xp, W, targets, mask, adv, beta: float = 0.04,
+                          L: int | None = None, want_terms: bool = True, stream=None,
+                          opts=None):
+    """grpo_loss_fwd without a workspace: the library uses its fixed per-GPU scratch
+    array (GRPOError with GRPO_ERR_SCRATCH when the sizes need more).  Returns dict(loss,
+    saved, logp, ref_logp, kl, status); the outputs are allocated here, by the caller."""
+    for t, n in ((xq, "xq"), (xp, "xp"), (W, "W"), (targets, "targets"), (mask, "mask"),
+                 (adv, "adv")):
+        _need(t, n)
+    S, L, H = _shape(xq, L)
+    V = W.shape[0]
+    dt = _dt(xq)
+    if xp.dtype != xq.dtype or W.dtype != xq.dtype:
+        raise TypeError("xq, xp and W must share one dtype")
+    if targets.dtype != torch.int64 or mask.dtype != torch.uint8 or adv.dtype != torch.float32:
+        raise TypeError("targets int64, mask uint8, adv float32 expected")
+    dev = xq.device
+    N = S * L
+    f32 = dict(dtype=torch.float32, device=dev)
+    loss = torch.empty(1, **f32)
+    saved = torch.empty(N, 4, **f32)
+    terms = [torch.empty(N, **f32) for _ in range(3)] if want_terms else [None] * 3
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(_LIB.grpo_loss_fwd_noalloc(_ptr(xq), _ptr(xp), _ptr(W), dt, _ptr(targets),
+                                      _ptr(mask), _ptr(adv), S, L, H, V, beta, _ptr(loss),
+                                      _ptr(saved), _ptr(terms[0]), _ptr(terms[1]),
+                                      _ptr(terms[2]), _ptr(status), _opts(opts),
+                                      _stream(stream)))
+    return {"loss": loss, "saved": saved, "logp": terms[0], "ref_logp": terms[1],
+            "kl": terms[2], "status": status}
 
 
 def grpo_loss_bwd(xq, W, targets, mask, saved, L: int | None = None, grad_loss=None,

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "common.h"
 
@@ -39,6 +40,25 @@ constexpr int64_t kChunkRows = GRPO_CHUNK_ROWS;
 constexpr int kMaxDevices = 64;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Device memory of grpo_loss_fwd_noalloc, for callers that cannot allocate: a fixed array
+// in place of a workspace.  Each GPU the library runs on holds its own copy until the
+// process ends; every call on one GPU uses the same copy.
+constexpr size_t kScratchBytes = GRPO_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+// This device's address of `scratch`, looked up once per device.  On the host the symbol
+// names a stand-in, not device memory, so only this address may reach a kernel.
+void* scratch_address() {
+  static std::atomic<void*> addr[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  addr[dev].store(p, std::memory_order_release);
+  return p;
+}
 
 bool valid_dtype(int dt) { return dt == GRPO_F32 || dt == GRPO_BF16 || dt == GRPO_F16; }
 
@@ -220,6 +240,7 @@ const char* grpo_status_string(int status) {
     case GRPO_ERR_HIP: return "HIP runtime error while enqueuing";
     case GRPO_ERR_DEVICE: return "current device is not gfx950";
     case GRPO_ERR_OPTIONS: return "a loss option is out of range";
+    case GRPO_ERR_SCRATCH: return "the forward needs more than the fixed scratch array holds";
     default: return "unknown status";
   }
 }
@@ -273,13 +294,16 @@ int grpo_advantages(const float* rewards, int64_t B, int64_t G, int64_t K, float
   return GRPO_OK;
 }
 
-int grpo_loss_fwd(const void* Xq, const void* Xp, const void* W, grpo_dtype dtype,
-                  const int64_t* targets, const uint8_t* mask, const float* adv, int64_t S,
-                  int64_t L, int64_t H, int64_t V, float beta, float* loss, float* saved,
-                  float* logp_out, float* ref_logp_out, float* kl_out, int32_t* status,
-                  const grpo_options* opts, void* workspace, size_t workspace_bytes,
-                  grpo_stream_t stream) {
-  if (!Xq || !Xp || !W || !targets || !mask || !adv || !loss || !saved || !status || !workspace)
+// The forward shared by grpo_loss_fwd and grpo_loss_fwd_noalloc.  workspace NULL: use
+// this device's scratch array, which must hold the forward's part of the plan.
+static int loss_fwd(const void* Xq, const void* Xp, const void* W, grpo_dtype dtype,
+                    const int64_t* targets, const uint8_t* mask, const float* adv, int64_t S,
+                    int64_t L, int64_t H, int64_t V, float beta, float* loss, float* saved,
+                    float* logp_out, float* ref_logp_out, float* kl_out, int32_t* status,
+                    const grpo_options* opts, void* workspace, size_t workspace_bytes,
+                    grpo_stream_t stream) {
+  const bool own = workspace == nullptr;
+  if (!Xq || !Xp || !W || !targets || !mask || !adv || !loss || !saved || !status)
     return GRPO_ERR_NULL;
   if (!valid_dtype(dtype)) return GRPO_ERR_DTYPE;
   if (!sizes_ok(S, L, H, V) || !isfinite(beta)) return GRPO_ERR_SHAPE;
@@ -290,10 +314,12 @@ int grpo_loss_fwd(const void* Xq, const void* Xp, const void* W, grpo_dtype dtyp
   if (!options_ok(opts)) return GRPO_ERR_OPTIONS;
   if (!make_plan(S, L, H, V, dtype, 0, &p)) return GRPO_ERR_SHAPE;
   if (!make_plan(S, L, H, V, dtype, 0, &p, opts)) return GRPO_ERR_OPTIONS;
-  if (workspace_bytes < p.total) return GRPO_ERR_WORKSPACE;
+  if (own ? p.fwd_total > kScratchBytes : workspace_bytes < p.total)
+    return own ? GRPO_ERR_SCRATCH : GRPO_ERR_WORKSPACE;
   if (!device_ok()) return GRPO_ERR_DEVICE;
   hipStream_t st = (hipStream_t)stream;
-  void* ws = workspace;
+  void* ws = own ? scratch_address() : workspace;
+  if (!ws) return GRPO_ERR_HIP;
   if (launch_compact_status(mask, p.N, ws_ptr<int32_t>(ws, p.off_ntok),
                             ws_ptr<int32_t>(ws, p.off_idx), ws_ptr<int32_t>(ws, p.off_rank),
                             status, st) != hipSuccess)
@@ -307,6 +333,27 @@ int grpo_loss_fwd(const void* Xq, const void* Xp, const void* W, grpo_dtype dtyp
                    status, loss, st) != hipSuccess)
     return GRPO_ERR_HIP;
   return GRPO_OK;
+}
+
+int grpo_loss_fwd(const void* Xq, const void* Xp, const void* W, grpo_dtype dtype,
+                  const int64_t* targets, const uint8_t* mask, const float* adv, int64_t S,
+                  int64_t L, int64_t H, int64_t V, float beta, float* loss, float* saved,
+                  float* logp_out, float* ref_logp_out, float* kl_out, int32_t* status,
+                  const grpo_options* opts, void* workspace, size_t workspace_bytes,
+                  grpo_stream_t stream) {
+  if (!workspace) return GRPO_ERR_NULL;
+  return loss_fwd(Xq, Xp, W, dtype, targets, mask, adv, S, L, H, V, beta, loss, saved,
+                  logp_out, ref_logp_out, kl_out, status, opts, workspace, workspace_bytes,
+                  stream);
+}
+
+int grpo_loss_fwd_noalloc(const void* Xq, const void* Xp, const void* W, grpo_dtype dtype,
+                          const int64_t* targets, const uint8_t* mask, const float* adv,
+                          int64_t S, int64_t L, int64_t H, int64_t V, float beta, float* loss,
+                          float* saved, float* logp_out, float* ref_logp_out, float* kl_out,
+                          int32_t* status, const grpo_options* opts, grpo_stream_t stream) {
+  return loss_fwd(Xq, Xp, W, dtype, targets, mask, adv, S, L, H, V, beta, loss, saved,
+                  logp_out, ref_logp_out, kl_out, status, opts, nullptr, 0, stream);
 }
 
 int grpo_loss_bwd(const void* Xq, const void* W, grpo_dtype dtype, const int64_t* targets,

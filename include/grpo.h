@@ -66,8 +66,10 @@ typedef enum grpo_status {
   GRPO_ERR_WORKSPACE = -5, /* workspace smaller than grpo_workspace_bytes()               */
   GRPO_ERR_HIP = -6,       /* the HIP runtime reported an error when enqueuing           */
   GRPO_ERR_DEVICE = -7,    /* the current device is not a gfx950 GPU                      */
-  GRPO_ERR_OPTIONS = -8    /* a grpo_options field is out of range, or not supported for  */
+  GRPO_ERR_OPTIONS = -8,   /* a grpo_options field is out of range, or not supported for  */
                            /* these inputs (fp8_logits with fp32 data)                     */
+  GRPO_ERR_SCRATCH = -9    /* grpo_loss_fwd_noalloc: the forward of these sizes needs more */
+                           /* than GRPO_NOALLOC_SCRATCH_BYTES                              */
 } grpo_status;
 
 /* Loss variants: the four experiments of [Long-context GRPO, §4] and two readings the
@@ -167,6 +169,28 @@ int grpo_loss_fwd(const void* Xq, const void* Xp, const void* W, grpo_dtype dtyp
                   float* logp_out, float* ref_logp_out, float* kl_out, int32_t* status,
                   const grpo_options* opts, void* workspace, size_t workspace_bytes,
                   grpo_stream_t stream);
+
+/* Bytes of the fixed device array behind grpo_loss_fwd_noalloc (one per GPU). */
+#define GRPO_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* grpo_loss_fwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments, results
+ * and error behaviour as grpo_loss_fwd (bit for bit), without the workspace: the library
+ * keeps the forward's working buffers in a fixed array of GRPO_NOALLOC_SCRATCH_BYTES in
+ * device memory, one copy per GPU it runs on, held until the process ends.  The call
+ * allocates nothing (the array's address is looked up once per device, on the first
+ * call there).  Sizes whose forward needs more than the array holds return
+ * GRPO_ERR_SCRATCH before anything is enqueued (with 16-bit logits the forward of every
+ * documented workload fits except the 8 x 20480 long-context one; fp8_logits adds the
+ * e4m3 copies of W and of the loss rows).  Every call on one GPU shares that array: calls that
+ * overlap in time on one GPU (different streams, or threads) race and must not be made;
+ * calls ordered on one stream are safe, and each call rewrites every part of the array it
+ * reads. */
+int grpo_loss_fwd_noalloc(const void* Xq, const void* Xp, const void* W, grpo_dtype dtype,
+                          const int64_t* targets, const uint8_t* mask, const float* adv,
+                          int64_t S, int64_t L, int64_t H, int64_t V, float beta, float* loss,
+                          float* saved, float* logp_out, float* ref_logp_out, float* kl_out,
+                          int32_t* status, const grpo_options* opts, grpo_stream_t stream);
 
 /* Backward: dloss/dXq (and dloss/dW) by recomputing the vocabulary chunks.
  *   Xq, W, targets, mask, saved: as given to / produced by grpo_loss_fwd.

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, -9, -1):
+    for code in range(0, -10, -1):
         s = lib.grpo_status_string(code)
         assert s and s != b"unknown status"
     assert lib.grpo_status_string(-99) == b"unknown status"
