@@ -50,10 +50,12 @@ def parse():
                     help="time only the path given by --path")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the single-pass leg with fp8 (e4m3) logits")
-    ap.add_argument("--small-chunk", type=int, default=2048,
+    ap.add_argument("--small-chunk", type=int, default=0,
                     help="rows per backward chunk of an extra single-pass leg that trades "
-                         "speed for workspace (0: skip it)")
+                         "speed for workspace (0: no such leg)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-trace", action="store_true",
+                    help="no kernel event brackets (no roofline block)")
     ap.add_argument("--cpu-rows", type=int, default=256, help="oracle rows per sequence")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                     help="run one device-to-device copy of this many GiB first, so a "
@@ -61,11 +63,17 @@ def parse():
     return ap.parse_args()
 
 
-def measured_traffic(workload):
-    """HBM-side bytes per launch of fwd_kernel from the committed counter summary, or None
-    when there is none for this workload or the kernel source changed since it was taken."""
+# counter summaries under profiles/ are named for the kernel they cover
+TRAFFIC_FILES = {"fwd_all": "fwd_kernel_all_rows", "fwd_chunk": "fwd_kernel_chunk",
+                 "dx": "dx_kernel", "dw": "dw_kernel", "recompute": "recompute_kernel"}
+
+
+def measured_traffic(workload, kind):
+    """HBM-side bytes per launch of one GEMM kernel from the committed counter summary, or
+    None when there is none for this kernel and workload or the kernel source changed
+    since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"traffic_fwd_kernel_{workload}.md")
+    path = os.path.join(ROOT, "profiles", f"traffic_{TRAFFIC_FILES[kind]}_{workload}.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -176,37 +184,57 @@ def main():
         torch.cuda.empty_cache()
         torch.cuda.reset_peak_memory_stats()
 
-    ev = []
-
-    def step_two(record):
-        g.grpo_advantages(d["rewards"], wl.eps, out=adv)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        f = g.grpo_loss_fwd(d["xq"], d["xp"], d["W"], d["targets"], d["mask"], adv, wl.beta,
-                            wl.L, workspace=ws, want_terms=False)
-        e1.record()
-        g.grpo_loss_bwd(d["xq"], d["W"], d["targets"], d["mask"], f["saved"], wl.L, grad,
-                        wl.loss_scale, dW=dW, found_inf=found, workspace=ws, dXq=dX)
-        if record:
-            ev.append((e0, e1))
-        return f
+    # Kernel timing inside the timed steps: each timed step of the leg reported as `value`
+    # has the library bracket every launch of one GEMM kernel with a pair of HIP events of
+    # its own, recorded on the stream the kernel runs on; the steps take the kernels in
+    # turn, and all events are read after the timed region.
+    kinds = {"single": ["fwd_all", "fwd_chunk", "dx"] + (["dw"] if need_dW else []),
+             "two": ["fwd_all", "recompute", "dx"] + (["dw"] if need_dW else [])}
+    max_launches = -(-wl.N // 256) + 1        # chunks of at least 256 rows
+    step_traces = []
+    if not args.no_trace:
+        for i in range(args.steps):
+            k = kinds[args.path][i % len(kinds[args.path])]
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * max_launches)]
+            for e in evs:
+                e.record()   # creates the HIP event
+            step_traces.append(g.KernelTrace(k, evs))
+        torch.cuda.synchronize()
 
     opts = {"v": None}
 
-    def step_single(record):
+    def with_trace(step_no):
+        base = opts["v"]
+        if step_no is None or not step_traces:
+            return base
+        o = g.options() if base is None else g.GRPOOptions.from_buffer_copy(base)
+        return step_traces[step_no].attach(o)
+
+    def step_two(step_no):
+        g.grpo_advantages(d["rewards"], wl.eps, out=adv)
+        o = with_trace(step_no)
+        f = g.grpo_loss_fwd(d["xq"], d["xp"], d["W"], d["targets"], d["mask"], adv, wl.beta,
+                            wl.L, workspace=ws, want_terms=False, opts=o)
+        if o is not None and o.trace_kernel == g.TRACE_KERNELS["fwd_all"]:
+            o = opts["v"]   # the forward's brackets are taken; the backward has none of it
+        g.grpo_loss_bwd(d["xq"], d["W"], d["targets"], d["mask"], f["saved"], wl.L, grad,
+                        wl.loss_scale, dW=dW, found_inf=found, workspace=ws, dXq=dX, opts=o)
+        return f
+
+    def step_single(step_no):
         g.grpo_advantages(d["rewards"], wl.eps, out=adv)
         return g.grpo_loss_fwd_bwd(d["xq"], d["xp"], d["W"], d["targets"], d["mask"], adv,
                                    wl.beta, wl.L, grad, wl.loss_scale, dW=dW, found_inf=found,
-                                   workspace=ws, dXq=dX, want_terms=False, opts=opts["v"])
+                                   workspace=ws, dXq=dX, want_terms=False,
+                                   opts=with_trace(step_no))
 
-    def timed(step):
+    def timed(step, trace=False):
         for _ in range(args.warmup):
-            step(False)
+            step(None)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(args.steps):
-            f = step(True)
+        for i in range(args.steps):
+            f = step(i if trace else None)
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / args.steps * 1e3, f
 
@@ -214,21 +242,51 @@ def main():
     dtn = wl.dtype
     peak = PEAK_TFLOPS[dtn]
     # GEMM-equivalents executed per step: policy and reference forward, dX, dW if trainable,
-    # plus the recompute in the two-pass path; the method's count (4 or 5 GEMM-equivalents)
-    # always includes the recompute
+    # plus the recompute in the two-pass path.  The survey's method count (4 or 5) always
+    # includes the recompute, which the single pass does not execute: reported beside,
+    # labelled as a recompute-equivalent rate.
     n_exec = {"single": 3 + need_dW, "two": 4 + need_dW}
     n_method = 4 + need_dW
+    flops_kind = {("single", "fwd_all"): gemm_eq, ("single", "fwd_chunk"): gemm_eq,
+                  ("single", "dx"): gemm_eq, ("single", "dw"): gemm_eq,
+                  ("two", "fwd_all"): 2 * gemm_eq, ("two", "recompute"): gemm_eq,
+                  ("two", "dx"): gemm_eq, ("two", "dw"): gemm_eq}
+    kernel_names = {"fwd_all": {"single": "fwd_kernel<E, E, 1> (reference side, all loss rows)",
+                                "two": "fwd_kernel<E, E, 0> (both sides, all loss rows)"},
+                    "fwd_chunk": {"single": "fwd_kernel<E, E, 3> (policy side, one chunk, "
+                                            "softmax terms kept)"},
+                    "recompute": {"two": "recompute_kernel (one chunk)"},
+                    "dx": {"single": "dx_kernel (one chunk)", "two": "dx_kernel (one chunk)"},
+                    "dw": {"single": "dw_kernel (one chunk)", "two": "dw_kernel (one chunk)"}}
     legs = {}
+    kernels = {}
     order = [args.path]
     if not args.no_two_pass:
         order.append("two" if args.path == "single" else "single")
     for path in order:
-        ms, f = timed(step_single if path == "single" else step_two)
+        step = step_single if path == "single" else step_two
+        ms, f = timed(step, trace=bool(step_traces) and path == args.path)
         legs[path] = {"value": n_tok / (ms * 1e-3), "ms_per_step": ms,
                       "mfma_peak_frac": n_exec[path] * gemm_eq / (ms * 1e-3) / (peak * 1e12),
-                      "method_flops_frac": n_method * gemm_eq / (ms * 1e-3) / (peak * 1e12),
+                      "recompute_equiv_frac": n_method * gemm_eq / (ms * 1e-3) / (peak * 1e12),
                       "status": int(f["status"].item()), "found_inf": int(found.item())}
         f = None  # the result holds a reference to the workspace
+    per_kind = {}
+    for tr in step_traces:
+        launches = tr.launch_ms()
+        if launches:
+            per_kind.setdefault(tr.kernel, []).append(launches)
+    names = {v: k for k, v in g.TRACE_KERNELS.items()}
+    for kid, steps in per_kind.items():
+        k = names[kid]
+        n = len(steps[0])
+        tot = float(np.mean([np.sum(x) for x in steps]))       # ms per step
+        kernels[k] = {"kernel": kernel_names[k][args.path], "launches_per_step": n,
+                      "ms_per_step": tot, "launch_ms": tot / n,
+                      "flop_per_launch": flops_kind[(args.path, k)] / n,
+                      "tflops": flops_kind[(args.path, k)] / (tot * 1e-3) / 1e12,
+                      "steps_traced": len(steps)}
+        kernels[k]["frac"] = kernels[k]["tflops"] / peak
     peak_extra = torch.cuda.max_memory_allocated() - base_mem
     main_leg = legs[args.path]
     out = {
@@ -248,20 +306,20 @@ def main():
                    "completion_tokens": n_tok, "trainable_head": need_dW,
                    "path": "single-pass" if args.path == "single" else "two-pass"},
         "mfma_peak_frac": main_leg["mfma_peak_frac"],
-        "method_flops_frac": main_leg["method_flops_frac"],
+        "recompute_equiv_frac": main_leg["recompute_equiv_frac"],
         "extra_gib": peak_extra / 2 ** 30,
         "workspace_gib": ws_bytes / 2 ** 30,
         "materialized_logits_gib": 2 * 2 * wl.S * wl.L * wl.V / 2 ** 30,
     }
-    if ev:
-        fwd_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-        fwd_tflops = 2 * gemm_eq / (fwd_ms * 1e-3) / 1e12
-        out["roofline"] = {"bound": "mfma",
-                           "kernel": "fwd_kernel mode 0 (policy + reference logits, online "
-                                     "logsumexp; one launch per two-pass forward)",
-                           "achieved": fwd_tflops, "peak": peak, "unit": "TFLOP/s",
-                           "frac": fwd_tflops / peak, "traffic": measured_traffic(wl.name),
-                           "launch_ms": fwd_ms, "flop_per_launch": 2 * gemm_eq}
+    if kernels:
+        dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+        kd = kernels[dom]
+        out["roofline"] = {"bound": "mfma", "kernel": kd["kernel"], "achieved": kd["tflops"],
+                           "peak": peak, "unit": "TFLOP/s", "frac": kd["frac"],
+                           "traffic": measured_traffic(wl.name, dom),
+                           "launch_ms": kd["launch_ms"], "flop_per_launch": kd["flop_per_launch"],
+                           "launches_per_step": kd["launches_per_step"]}
+        out["kernels"] = kernels
     other = [p for p in legs if p != args.path]
     if other:
         out["two_pass" if other[0] == "two" else "single_pass"] = legs[other[0]]
@@ -280,7 +338,7 @@ def main():
         ms, f = timed(step_single)
         out[f"chunk_{args.small_chunk}"] = {
             "value": n_tok / (ms * 1e-3), "ms_per_step": ms,
-            "method_flops_frac": n_method * gemm_eq / (ms * 1e-3) / (peak * 1e12),
+            "recompute_equiv_frac": n_method * gemm_eq / (ms * 1e-3) / (peak * 1e12),
             "extra_gib": (torch.cuda.max_memory_allocated() - base_mem) / 2 ** 30,
             "workspace_gib": wsc_bytes / 2 ** 30, "status": int(f["status"].item())}
         f = None

@@ -14,6 +14,8 @@ Importing this package loads the library and fails loudly if it is not built
 from ._binding import (  # noqa: F401
     GRPOError,
     GRPOOptions,
+    KernelTrace,
+    TRACE_KERNELS,
     grpo_advantages,
     grpo_loss,
     grpo_loss_bwd,

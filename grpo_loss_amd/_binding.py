@@ -24,7 +24,38 @@ class GRPOOptions(ctypes.Structure):
     """Mirror of struct grpo_options."""
     _fields_ = [("kl_estimator", ctypes.c_int), ("detach_ratio", ctypes.c_int),
                 ("normalization", ctypes.c_int), ("temperature", ctypes.c_float),
-                ("fp8_logits", ctypes.c_int), ("chunk_rows", ctypes.c_int)]
+                ("fp8_logits", ctypes.c_int), ("chunk_rows", ctypes.c_int),
+                ("vocab_piece", ctypes.c_int),
+                ("trace_kernel", ctypes.c_int), ("trace_capacity", ctypes.c_int),
+                ("trace_events", ctypes.POINTER(ctypes.c_void_p)),
+                ("trace_count", ctypes.POINTER(ctypes.c_int))]
+
+
+TRACE_KERNELS = {"none": 0, "fwd_all": 1, "fwd_chunk": 2, "recompute": 3, "dx": 4, "dw": 5}
+
+
+class KernelTrace:
+    """Event pairs for grpo_options' kernel tracing: the library records them on the call's
+    stream around each launch of one kernel.  ``events`` are torch.cuda.Event objects with
+    timing enabled, already recorded once (so that their HIP events exist)."""
+
+    def __init__(self, kernel: str, events):
+        self.kernel = TRACE_KERNELS[kernel]
+        self.events = list(events)
+        self._handles = (ctypes.c_void_p * len(self.events))(*[e.cuda_event for e in self.events])
+        self.count = ctypes.c_int(0)
+
+    def attach(self, o: "GRPOOptions") -> "GRPOOptions":
+        o.trace_kernel = self.kernel
+        o.trace_capacity = len(self.events) // 2
+        o.trace_events = ctypes.cast(self._handles, ctypes.POINTER(ctypes.c_void_p))
+        o.trace_count = ctypes.pointer(self.count)
+        return o
+
+    def launch_ms(self):
+        """Milliseconds of each bracketed launch of the last call (after a synchronise)."""
+        n = min(self.count.value, len(self.events) // 2)
+        return [self.events[2 * i].elapsed_time(self.events[2 * i + 1]) for i in range(n)]
 
 
 KL_ESTIMATORS = {"reverse": 0, "forward": 1, "reverse_q": 2}
@@ -33,11 +64,13 @@ NORMALIZATIONS = {"tokens": 0, "sequences": 1}
 
 def options(kl: str = "reverse", detach: bool = True, norm: str = "tokens",
             temperature: float = 1.0, fp8_logits: bool = False,
-            chunk_rows: int = 0) -> GRPOOptions:
+            chunk_rows: int = 0, vocab_piece: int = 0) -> GRPOOptions:
     """A grpo_options value from names (the library validates the ranges).  chunk_rows:
-    loss rows per backward chunk (0: the library's default)."""
+    loss rows per backward chunk; vocab_piece: vocabulary entries per piece of a chunk's
+    softmax terms (0: the library's defaults)."""
     return GRPOOptions(KL_ESTIMATORS[kl], int(bool(detach)), NORMALIZATIONS[norm],
-                       float(temperature), int(bool(fp8_logits)), int(chunk_rows))
+                       float(temperature), int(bool(fp8_logits)), int(chunk_rows),
+                       int(vocab_piece))
 
 
 def _as_options(o):

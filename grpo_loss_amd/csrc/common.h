@@ -92,8 +92,16 @@ struct Plan {
   int phases;       // fp32 FMA forward: vocabulary phases (fixed; partial stride N)
   int64_t R;        // backward: rows per recompute chunk (multiple of 256)
   int chunk_rows;   // grpo_options::chunk_rows (0: the default chunk)
+  int vocab_piece;  // grpo_options::vocab_piece (0: the default piece)
   int ksplit;       // backward: split of the dX reduction over the vocabulary
   int mfma;         // 1: 16-bit MFMA kernels, 0: fp32 FMA kernels
+  // Vocabulary split of the backward (MFMA, no dW): a chunk's terms are produced and
+  // consumed one piece of ptiles vocabulary tiles at a time (npieces per chunk), so the
+  // chunk buffer holds R x (ptiles * 256) entries, and dX accumulates in fp32 [ksplit][R][H]
+  int vsplit;
+  int npieces;
+  int64_t ptiles;
+  int64_t pt_ld;    // entries per row of the chunk buffer: ptiles * 256, or Vpad
   // loss variant (grpo_options)
   int kl;           // grpo_kl_estimator
   int detach;       // 1: ratio exp(q - sg(q)), 0: exp(q - q)
@@ -101,6 +109,11 @@ struct Plan {
   float inv_tau;    // 1 / temperature
   float scale2;     // log2(e) / temperature: logits -> log2 units of the softmax argument
   int fp8;          // logits from per-row e4m3 copies of X and W
+  // event brackets around one kernel's launches (grpo_options.trace_*); trace_n counts the
+  // launches of this call (a counter owned by the entry point, may be null)
+  int trace_kernel, trace_cap;
+  void* const* trace_ev;
+  int* trace_n;
   // byte offsets into the workspace
   size_t off_ntok, off_idx, off_rank, off_part, off_lsum, off_seq, off_T, off_pm, off_Xg,
       off_redo, off_dxp, off_xq8, off_xp8, off_w8, off_sxq, off_sxp, off_sw, total;
@@ -113,6 +126,7 @@ constexpr int kTokTile = 256;    // rows per token tile of the MFMA kernels
 constexpr int kVocTile = 256;    // vocabulary entries per tile
 constexpr int kMergeBlock = 256; // rows per block of the merge kernel
 constexpr int kMaxPhases = 32;   // most vocabulary phases of one forward launch
+constexpr int kPieceTiles = 128; // vocabulary tiles per piece of the split backward (32768)
 
 // Vocabulary phases of the MFMA forward.  Its persistent grid (8 XCDs x 32 workgroups)
 // covers 32 / P token blocks per XCD x P phases per round; pick P in {4, 8, 16, 32} that
@@ -155,13 +169,39 @@ __host__ __device__ inline PartLayout part_layout(int64_t rows, int nsides, int6
   l.stride = ntbs * 256;
   return l;
 }
-// Floats of the largest part_layout(rows, nsides, nvt) over 0 <= rows <= max_rows.
-size_t part_floats_max(int64_t max_rows, int nsides, int64_t nvt);
+// Several launches over the same rows of one side, one per vocabulary piece of ptiles
+// tiles: each runs P = fwd_phases(ntbs, ptiles) phases (the last piece's empty phases
+// write empty partials) and piece j's phase ph lands in slot j P + ph.  With one piece of
+// every tile this is part_layout(rows, 1, nvt).
+__host__ __device__ inline PartLayout split_layout(int64_t rows, int64_t ptiles, int npieces) {
+  const int64_t ntbs = (rows + 255) / 256;
+  PartLayout l;
+  l.P = npieces * fwd_phases(ntbs, ptiles);
+  l.nsides = 1;
+  l.stride = ntbs * 256;
+  return l;
+}
+// Floats of the largest layout over 0 <= rows <= max_rows: part_layout(rows, nsides, tiles)
+// (npieces = 1), or split_layout(rows, tiles, npieces) (nsides = 1).
+size_t part_floats_max(int64_t max_rows, int nsides, int64_t tiles, int npieces = 1);
 
 bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_dW, Plan* p,
                const grpo_options* opts = nullptr);
 // Copies a validated grpo_options (NULL = defaults) into the plan.
 void plan_options(const grpo_options* o, Plan* p);
+
+// Event brackets around the launches of the kernel the caller asked to time (no-ops for
+// any other kernel).  Recording is a stream operation: nothing synchronises.
+inline void trace_begin(const Plan& p, int kernel, hipStream_t st) {
+  if (p.trace_kernel != kernel || !p.trace_n || !p.trace_ev || *p.trace_n >= p.trace_cap) return;
+  (void)hipEventRecord((hipEvent_t)p.trace_ev[2 * *p.trace_n], st);
+}
+inline void trace_end(const Plan& p, int kernel, hipStream_t st) {
+  if (p.trace_kernel != kernel || !p.trace_n) return;
+  if (p.trace_ev && *p.trace_n < p.trace_cap)
+    (void)hipEventRecord((hipEvent_t)p.trace_ev[2 * *p.trace_n + 1], st);
+  ++*p.trace_n;
+}
 
 template <typename P>
 inline P* ws_ptr(void* ws, size_t off) {
@@ -185,13 +225,16 @@ hipError_t launch_merge(const Plan& p, const void* ws, const int64_t* targets,
 // Single-pass forward: merge of compact rows [c0, c0 + R) (R = Plan::R), the zeroing of
 // masked rows' outputs, and the loss reduction (compact = 1: block sums over loss rows).
 // redo (non-null): the policy partials are fixed-reference ones, a row out of their range
-// sets *redo, and the other rows' target entries of the chunk buffer `patch` (Plan::Vpad
-// entries per row) are rewritten; gate (non-null): merge only when *gate != 0.
+// sets *redo, and (patch non-null) the other rows' target entries of the chunk buffer
+// `patch` (Plan::Vpad entries per row) are rewritten; gate (non-null): merge only when
+// *gate != 0.  The chunk's policy partials follow split_layout(rows, cp_tiles, cp_pieces)
+// (cp_tiles 0: every tile, one piece).
 hipError_t launch_merge_rows(const Plan& p, const void* ws, int64_t c0, const int64_t* targets,
                              const uint8_t* mask, const float* adv, float beta, float* saved,
                              float* logp, float* ref_logp, float* kl, int32_t* status,
                              hipStream_t st, int32_t* redo = nullptr, void* patch = nullptr,
-                             const int32_t* gate = nullptr);
+                             const int32_t* gate = nullptr, int64_t cp_tiles = 0,
+                             int cp_pieces = 1);
 hipError_t launch_zero_masked_outputs(const Plan& p, const uint8_t* mask, float* saved,
                                       float* logp, float* ref_logp, float* kl, hipStream_t st);
 hipError_t launch_loss_final(const Plan& p, const void* ws, int compact, int32_t* status,

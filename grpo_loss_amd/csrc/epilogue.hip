@@ -86,7 +86,10 @@ struct MergeArgs {
   const int32_t* rank;
   const int32_t* idx;
   const float* part;     // the forward's partials over all loss rows
-  const float* cpart;    // single pass: the policy partials of the chunk
+  const float* cpart;    // single pass: the policy partials of the chunk, in the
+                         // split_layout of cp_pieces launches of cp_tiles tiles each
+  int64_t cp_tiles;
+  int cp_pieces;
   const int32_t* seq;   // [S] loss rows per sequence, then the count of non-empty sequences
   int64_t S;
   const int64_t* targets;
@@ -151,7 +154,7 @@ __device__ inline double merge_row(const MergeArgs& a, int64_t t, int64_t r, con
   if ((y < 0 || y >= a.V) && !quiet) *flags |= GRPO_FLAG_BAD_TARGET;
   const float q = zq * a.inv_tau - lse_q;
   const float ref = zp * a.inv_tau - lse_p;
-  if (a.redo && !quiet && y >= 0 && y < a.V) {
+  if (a.redo && a.patch && !quiet && y >= 0 && y < a.V) {
     const float ey = expm1f(q) * exp2f(l2s);
     u16* e = reinterpret_cast<u16*>(a.patch) + (r - a.c0) * a.patch_ld + y;
     *e = a.patch_dtype == GRPO_BF16 ? BF16T::from_f32(ey) : F16T::from_f32(ey);
@@ -252,7 +255,7 @@ __global__ void __launch_bounds__(kMergeBlock) merge_rows_kernel(MergeArgs a) {
   const int64_t nvt = (a.V + 255) / 256;
   const int64_t crow = (ntok - a.c0 < a.R ? ntok - a.c0 : a.R);
   // policy: the chunk's own launch over its rows; reference: one launch over all rows
-  const PartRefs pr{a.cpart, part_layout(crow, 1, nvt), 0, r - a.c0,
+  const PartRefs pr{a.cpart, split_layout(crow, a.cp_tiles, a.cp_pieces), 0, r - a.c0,
                     a.part, part_layout(ntok, 1, nvt), 0, r};
   double ell_d = 0.0;
   int flags = 0;
@@ -430,6 +433,8 @@ hipError_t launch_merge(const Plan& p, const void* ws, const int64_t* targets,
   a.idx = ws_ptr<int32_t>(w, p.off_idx);
   a.part = ws_ptr<float>(w, p.off_part);
   a.cpart = nullptr;
+  a.cp_tiles = 0;
+  a.cp_pieces = 1;
   a.seq = ws_ptr<int32_t>(w, p.off_seq);
   a.S = p.N / p.L;
   a.targets = targets;
@@ -471,7 +476,7 @@ hipError_t launch_merge_rows(const Plan& p, const void* ws, int64_t c0, const in
                              const uint8_t* mask, const float* adv, float beta, float* saved,
                              float* logp, float* ref_logp, float* kl, int32_t* status,
                              hipStream_t st, int32_t* redo, void* patch,
-                             const int32_t* gate) {
+                             const int32_t* gate, int64_t cp_tiles, int cp_pieces) {
   void* w = const_cast<void*>(ws);
   MergeArgs a;
   a.N = p.N;
@@ -489,6 +494,8 @@ hipError_t launch_merge_rows(const Plan& p, const void* ws, int64_t c0, const in
   a.idx = ws_ptr<int32_t>(w, p.off_idx);
   a.part = ws_ptr<float>(w, p.off_part);
   a.cpart = ws_ptr<float>(w, p.off_cpart);
+  a.cp_tiles = cp_tiles > 0 ? cp_tiles : p.Vpad / kVocTile;
+  a.cp_pieces = cp_pieces;
   a.seq = ws_ptr<int32_t>(w, p.off_seq);
   a.S = p.N / p.L;
   a.targets = targets;

@@ -87,6 +87,10 @@ bool options_ok(const grpo_options* o) {
   if (o->chunk_rows != 0 &&
       (o->chunk_rows % 256 != 0 || o->chunk_rows < 256 || o->chunk_rows > 65536))
     return false;
+  if (o->vocab_piece != 0 && (o->vocab_piece % 256 != 0 || o->vocab_piece < 256)) return false;
+  if (o->trace_kernel < GRPO_TRACE_NONE || o->trace_kernel > GRPO_TRACE_DW ||
+      o->trace_capacity < 0 || (o->trace_capacity > 0 && !o->trace_events))
+    return false;
   // the softmax argument z / tau must stay finite for finite logits
   return isfinite(o->temperature) && o->temperature >= 1e-3f && o->temperature <= 1e3f;
 }
@@ -141,6 +145,18 @@ bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_d
     }
   }
   const int64_t nvt = p->Vpad / kVocTile;
+  // Vocabulary split of the backward (everything on the MFMA kernels but the single pass
+  // with dW, whose row factor is known only once the chunk's whole vocabulary has been
+  // swept): pieces of at most kPieceTiles tiles (vocab_piece entries if given), balanced.
+  p->vsplit = p->mfma && !need_dW;
+  p->npieces = 1;
+  p->ptiles = nvt;
+  if (p->vsplit) {
+    const int64_t want = p->vocab_piece > 0 ? p->vocab_piece / kVocTile : kPieceTiles;
+    p->npieces = (int)((nvt + want - 1) / want);
+    p->ptiles = (nvt + p->npieces - 1) / p->npieces;
+  }
+  p->pt_ld = p->ptiles * kVocTile;
   // what the forward uses comes first, so that its size is a prefix of the plan
   size_t o = 0;
   p->off_ntok = o;
@@ -177,25 +193,34 @@ bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_d
     o = align_up(o + (size_t)V * 4);
   }
   p->fwd_total = o;
-  p->off_cpart = o;  // single pass: the policy partials of one chunk
-  if (p->mfma) o = align_up(o + part_floats_max(p->R, 1, nvt) * 4);
-  p->off_T = o;
-  o = align_up(o + (size_t)p->R * p->Vpad * p->esize);
-  p->off_pm = o;
-  if (p->mfma) o = align_up(o + (size_t)p->R * (p->Vpad / kVocTile) * 4);
+  p->off_cpart = o;  // single pass: the policy partials of one chunk (pieces, or one sweep)
+  if (p->mfma)
+    o = align_up(o + std::max(part_floats_max(p->R, 1, p->ptiles, p->npieces),
+                              part_floats_max(p->R, 1, nvt)) * 4);
+  p->off_T = o;      // the chunk buffer: R rows of one piece (or of the whole vocabulary)
+  o = align_up(o + (size_t)p->R * p->pt_ld * p->esize);
+  p->off_pm = o;     // per row (vocabulary split) or per row and tile (running maxima)
+  if (p->mfma) o = align_up(o + (size_t)p->R * (p->vsplit ? 1 : nvt) * 4);
   p->off_Xg = o;
   if (p->mfma && need_dW) o = align_up(o + (size_t)p->R * H * p->esize);
   p->off_xgs = o;
   if (p->mfma && need_dW) o = align_up(o + 16);
   p->off_redo = o;  // single-pass fallback flags, one per chunk
   if (p->mfma) o = align_up(o + (size_t)((p->N + p->R - 1) / p->R) * 4);
-  p->off_dxp = o;
-  if (p->mfma && p->ksplit > 1) o = align_up(o + (size_t)p->ksplit * p->R * H * 4);
+  p->off_dxp = o;    // fp32 dX partials [ksplit][R][H]: split reductions, or the pieces' sums
+  if (p->mfma && (p->ksplit > 1 || p->vsplit))
+    o = align_up(o + (size_t)p->ksplit * p->R * H * 4);
   p->total = o;
   return true;
 }
 
-size_t part_floats_max(int64_t max_rows, int nsides, int64_t nvt) {
+// The traced launches of a call, for its caller (grpo_options.trace_count).
+static int traced(const grpo_options* opts, int launches) {
+  if (opts && opts->trace_count) *opts->trace_count = launches;
+  return GRPO_OK;
+}
+
+size_t part_floats_max(int64_t max_rows, int nsides, int64_t tiles, int npieces) {
   // the phase count depends on the token blocks through a ceiling, so the product is not
   // monotone in the rows: take the maximum over every block count (P <= kMaxPhases bounds
   // the blocks past a million, which no workload reaches)
@@ -203,10 +228,10 @@ size_t part_floats_max(int64_t max_rows, int nsides, int64_t nvt) {
   const int64_t lim = nb < ((int64_t)1 << 20) ? nb : ((int64_t)1 << 20);
   size_t best = 0;
   for (int64_t b = 1; b <= lim; ++b) {
-    const size_t f = (size_t)3 * nsides * fwd_phases(nsides * b, nvt) * b * 256;
+    const size_t f = (size_t)3 * nsides * npieces * fwd_phases(nsides * b, tiles) * b * 256;
     best = std::max(best, f);
   }
-  if (nb > lim) best = std::max(best, (size_t)3 * nsides * kMaxPhases * nb * 256);
+  if (nb > lim) best = std::max(best, (size_t)3 * nsides * npieces * kMaxPhases * nb * 256);
   return best;
 }
 
@@ -221,6 +246,11 @@ void plan_options(const grpo_options* o, Plan* p) {
   p->scale2 = kLog2e / o->temperature;
   p->fp8 = o->fp8_logits;
   p->chunk_rows = o->chunk_rows;
+  p->vocab_piece = o->vocab_piece;
+  p->trace_kernel = o->trace_kernel;
+  p->trace_cap = o->trace_capacity;
+  p->trace_ev = o->trace_events;
+  p->trace_n = nullptr;  // set by the entry point that launches
 }
 
 }  // namespace grpo
@@ -253,6 +283,11 @@ void grpo_default_options(grpo_options* opts) {
   opts->temperature = 1.0f;
   opts->fp8_logits = 0;
   opts->chunk_rows = 0;
+  opts->vocab_piece = 0;
+  opts->trace_kernel = GRPO_TRACE_NONE;
+  opts->trace_capacity = 0;
+  opts->trace_events = nullptr;
+  opts->trace_count = nullptr;
 }
 
 size_t grpo_workspace_bytes(int64_t S, int64_t L, int64_t H, int64_t V, grpo_dtype dtype,
@@ -318,6 +353,8 @@ static int loss_fwd(const void* Xq, const void* Xp, const void* W, grpo_dtype dt
     return own ? GRPO_ERR_SCRATCH : GRPO_ERR_WORKSPACE;
   if (!device_ok()) return GRPO_ERR_DEVICE;
   hipStream_t st = (hipStream_t)stream;
+  int launches = 0;  // launches of the traced kernel
+  p.trace_n = &launches;
   void* ws = own ? scratch_address() : workspace;
   if (!ws) return GRPO_ERR_HIP;
   if (launch_compact_status(mask, p.N, ws_ptr<int32_t>(ws, p.off_ntok),
@@ -332,7 +369,7 @@ static int loss_fwd(const void* Xq, const void* Xp, const void* W, grpo_dtype dt
   if (launch_merge(p, ws, targets, mask, adv, beta, saved, logp_out, ref_logp_out, kl_out,
                    status, loss, st) != hipSuccess)
     return GRPO_ERR_HIP;
-  return GRPO_OK;
+  return traced(opts, launches);
 }
 
 int grpo_loss_fwd(const void* Xq, const void* Xp, const void* W, grpo_dtype dtype,
@@ -380,6 +417,8 @@ int grpo_loss_bwd(const void* Xq, const void* W, grpo_dtype dtype, const int64_t
   if (workspace_bytes < p.total) return GRPO_ERR_WORKSPACE;
   if (!device_ok()) return GRPO_ERR_DEVICE;
   hipStream_t st = (hipStream_t)stream;
+  int launches = 0;  // launches of the traced kernel
+  p.trace_n = &launches;
   void* ws = workspace;
   if (launch_compact(mask, p.N, ws_ptr<int32_t>(ws, p.off_ntok), ws_ptr<int32_t>(ws, p.off_idx),
                      ws_ptr<int32_t>(ws, p.off_rank), st) != hipSuccess)
@@ -391,7 +430,7 @@ int grpo_loss_bwd(const void* Xq, const void* W, grpo_dtype dtype, const int64_t
              : simple_backward(p, ws, Xq, W, targets, saved, grad_loss, ls_eff, dXq, dW,
                                accumulate_dW, found_inf, st);
   if (be != hipSuccess) return GRPO_ERR_HIP;
-  return GRPO_OK;
+  return traced(opts, launches);
 }
 
 int grpo_loss_fwd_bwd(const void* Xq, const void* Xp, const void* W, grpo_dtype dtype,
@@ -419,6 +458,8 @@ int grpo_loss_fwd_bwd(const void* Xq, const void* Xp, const void* W, grpo_dtype 
   if (workspace_bytes < p.total) return GRPO_ERR_WORKSPACE;
   if (!device_ok()) return GRPO_ERR_DEVICE;
   hipStream_t st = (hipStream_t)stream;
+  int launches = 0;  // launches of the traced kernel
+  p.trace_n = &launches;
   void* ws = workspace;
   if (launch_compact_status(mask, p.N, ws_ptr<int32_t>(ws, p.off_ntok),
                             ws_ptr<int32_t>(ws, p.off_idx), ws_ptr<int32_t>(ws, p.off_rank),
@@ -432,7 +473,7 @@ int grpo_loss_fwd_bwd(const void* Xq, const void* Xp, const void* W, grpo_dtype 
                    kl_out, status, loss, grad_loss, ls_eff, dXq, dW, accumulate_dW, found_inf,
                    st) != hipSuccess)
       return GRPO_ERR_HIP;
-    return GRPO_OK;
+    return traced(opts, launches);
   }
   // fp32 (or H not a multiple of 256): the two passes back to back
   if (simple_fwd_partials(p, ws, Xq, Xp, W, targets, st) != hipSuccess) return GRPO_ERR_HIP;
@@ -442,7 +483,7 @@ int grpo_loss_fwd_bwd(const void* Xq, const void* Xp, const void* W, grpo_dtype 
   if (simple_backward(p, ws, Xq, W, targets, saved, grad_loss, ls_eff, dXq, dW, accumulate_dW,
                       found_inf, st) != hipSuccess)
     return GRPO_ERR_HIP;
-  return GRPO_OK;
+  return traced(opts, launches);
 }
 
 int grpo_scale_grad(void* dXq, grpo_dtype dtype, int64_t rows, int64_t H, float* dW, int64_t V,

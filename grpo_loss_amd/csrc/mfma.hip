@@ -395,10 +395,21 @@ __device__ inline void kstep_pipe(const Op<kNatA>& A, const Op<kNatB>& B, const 
 // of B's for k-step 0.  On return every wave has finished reading stage 0 (a barrier
 // follows its last reads), so stage 0 may be refilled at once; stage 1 is refilled only
 // after the first barrier of the next call.
+// threadIdx.x, opaque to the optimiser: values derived from it after this point are
+// recomputed where they are used (a few VALU operations) instead of being hoisted out of
+// a persistent kernel's tile loop and held, or spilled, across the epilogue.  A spill
+// reload there costs far more than the arithmetic: its s_waitcnt vmcnt also waits for
+// every direct-to-LDS load issued before it.
+__device__ inline int tid_opaque() {
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 template <class E, bool kNatA = false, bool kNatB = false>
 __device__ inline void gemm_main_op(const Op<kNatA>& A, const Op<kNatB>& B, const Offs& ao,
                                     const Offs& bo, int nk, Acc& acc) {
-  const int lane = threadIdx.x & 63;
+  const int lane = tid_opaque() & 63;
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int wm = w / kWN, wn = w % kWN;
   const int fr = lane & 15;
@@ -440,7 +451,7 @@ __device__ inline void gemm_main_op(const Op<kNatA>& A, const Op<kNatB>& B, cons
 template <class E>
 __device__ inline void gemm_main(Src ra, Src rb, const Offs& ao, const Offs& bo, int nk,
                                  Acc& acc) {
-  gemm_main_op<E>(Op<false>{ra}, Op<false>{rb}, ao, bo, nk, acc);
+  gemm_main_op<E, false, false>(Op<false>{ra}, Op<false>{rb}, ao, bo, nk, acc);
 }
 
 template <class E, bool kNatA = false, bool kNatB = false>
@@ -483,7 +494,18 @@ struct FwdArgs {
   // exp2(z s2 - mr) with mr the row's reference-side log-sum-exp, stored at pm[r - row_lo].
   char* pt;
   float* pm;
-  int64_t Vpad;
+  int64_t pt_ld;  // entries per pt row (the chunk buffer's width: a piece, or Vpad)
+  // Vocabulary piece `piece` of `npieces`, each of ptiles tiles: the launch sweeps tiles
+  // [piece ptiles, min((piece + 1) ptiles, nvt)) with P = fwd_phases(blocks, ptiles)
+  // phases, writes its partials at slots piece P + phase of split_layout (one side) or
+  // part_layout (npieces 1), and its terms at pt column v - piece ptiles 256.
+  int piece, npieces;
+  int64_t ptiles;
+  // Mode 3: store 0 at each row's target entry (the vocabulary split leaves the target
+  // to the final dX kernel), and take the fixed reference from saved[idx[r] * 4] (the row's
+  // own policy log-sum-exp: the split's fallback) instead of ref_part.
+  int zero_target, ref_from_saved;
+  const float* saved;
   // Launch only when *gate != 0 (null: always); the single-pass fallback of a chunk.
   const int32_t* gate;
   // fp8 logits: per-row e4m3 copies of W [V][H] and of the loss rows of X_q and X_p
@@ -529,9 +551,9 @@ __device__ inline void x_offsets(int64_t tok0, int64_t rhi, const int32_t* __res
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int sr = stage_row(i);
-    int64_t r = tok0 + sr;
-    if (r >= rhi) r = rhi - 1;
-    bo[i] = (uint32_t)(idx[r] * rowb) + stage_chunk_bytes(sr);
+    int r = (int)tok0 + sr;  // 32-bit rows and byte offsets: the operand is below 4 GiB
+    if (r >= rhi) r = (int)rhi - 1;
+    bo[i] = (uint32_t)idx[r] * (uint32_t)rowb + stage_chunk_bytes(sr);
   }
 }
 
@@ -541,9 +563,9 @@ __device__ inline void xc_offsets(int64_t tok0, int64_t rhi, int64_t rowb, Offs&
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int sr = stage_row(i);
-    int64_t r = tok0 + sr;
-    if (r >= rhi) r = rhi - 1;
-    bo[i] = (uint32_t)(r * rowb) + stage_chunk_bytes(sr);
+    int r = (int)tok0 + sr;
+    if (r >= rhi) r = (int)rhi - 1;
+    bo[i] = (uint32_t)r * (uint32_t)rowb + stage_chunk_bytes(sr);
   }
 }
 
@@ -644,7 +666,7 @@ __device__ inline void fwd_fold(const Acc& acc, float s2, int vlim, int vb, int 
           sum += e[j];
         }
         const u32x2 pk = {E::pack2(e[0], e[1]), E::pack2(e[2], e[3])};
-        __builtin_amdgcn_raw_buffer_store_b64(pk, fo.pt, fo.lane_t + mb * 32, so, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(pk, fo.pt, fo.lane_t, so + mb * 32, 0);
       }
       if (wm == 0 && lane < 16 && ok)
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(nm), fo.pm, fo.lane_m,
@@ -678,7 +700,7 @@ template <class E, bool kFull>
 __device__ inline void fwd_fold_fixed(const Acc& acc, float s2, int vlim, int vb, int wn,
                                       int lane, int tid, float (*s_run)[kNB][kThreads],
                                       const int* s_y, float* s_zt, const float* s_mr,
-                                      const FoldOut& fo) {
+                                      const FoldOut& fo, int zero_target) {
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
     const int n = wn * kWaveN + nb * 16 + (lane & 15);
@@ -694,7 +716,7 @@ __device__ inline void fwd_fold_fixed(const Acc& acc, float s2, int vlim, int vb
         sum += e[j];
       }
       const u32x2 pk = {E::pack2(e[0], e[1]), E::pack2(e[2], e[3])};
-      __builtin_amdgcn_raw_buffer_store_b64(pk, fo.pt, fo.lane_t + mb * 32, so, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(pk, fo.pt, fo.lane_t, so + mb * 32, 0);
     }
     s_run[1][nb][tid] = sum;
     const int loc = s_y[n] - vb;
@@ -705,6 +727,12 @@ __device__ inline void fwd_fold_fixed(const Acc& acc, float s2, int vlim, int vb
 #pragma unroll
         for (int j = 0; j < 4; ++j) z = (loc == mb * 16 + j) ? acc[mb][nb][j] : z;
       s_zt[n] = z;
+      // the kept term of the target is replaced by 0 (after the packed store above, same
+      // lane and address, so it lands last); its term is still in the row's sum
+      if (zero_target)
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, fo.pt,
+                                              fo.lane_t + (loc >> 4) * 32 + (loc & 3) * 2, so,
+                                              0);
     }
   }
 }
@@ -738,15 +766,21 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
   __shared__ float s_cm[kMode == 2 ? 2 : 1][256];
   __shared__ float s_mr[kFixed ? 256 : 1];
   if (a.gate && *a.gate == 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / kWN, wn = w % kWN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w / kWN, wn = w % kWN;
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
   const int slots = gridDim.x / kXcds;           // workgroups per XCD
   const int ntok = *a.ntok;
   const FwdRange fr = fwd_range(a, ntok);
   const int TB = fr.TB;
-  const int64_t nvt = (a.V + 255) / 256;
-  const PartLayout pl = part_layout(fr.rhi > a.row_lo ? fr.rhi - a.row_lo : 0, a.nsides, nvt);
-  const int P = pl.P;  // = fwd_phases(TB, nvt)
+  const int64_t nvt_all = (a.V + 255) / 256;
+  const int64_t vt_lo = a.piece * a.ptiles;                      // this launch's tiles
+  const int64_t nvt = vt_lo + a.ptiles < nvt_all ? vt_lo + a.ptiles : nvt_all;  // end
+  const int P = fwd_phases(TB, a.ptiles);
+  PartLayout pl;  // part_layout(rows, nsides, nvt) for one piece, else split_layout
+  pl.P = a.npieces * P;
+  pl.nsides = a.nsides;
+  pl.stride = (int64_t)fr.ntbs * 256;
   const int tb_per_xcd = slots / P;
   const int phase = slot % P;
   const int tbg = kXcds * tb_per_xcd;            // token blocks per round
@@ -764,17 +798,19 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
       x_offsets(tok0, fr.rhi, a.idx, rowb, bo);
   };
 
+  const int slot_ph = a.piece * P + phase;      // this phase's partial slot
   int tb = xcd * tb_per_xcd + slot / P;
   if (tb >= TB) return;
-  // loads of the first tile.  A phase with no vocabulary tile (V below P tiles) still
-  // writes its empty partials (max -inf, sum 0) for every token block.
+  // loads of the first tile.  A phase with no vocabulary tile (the piece has fewer than P
+  // tiles) still writes its empty partials (max -inf, sum 0) for every token block.
   Offs ao, bo;
-  if (phase < nvt) {
+  if (vt_lo + phase < nvt) {
     const int sd = (int)(tb / fr.ntbs);
     xoffs(a.row_lo + (tb - sd * fr.ntbs) * 256, bo);
-    w_offsets(phase * 256, a.V, rowb, ao);
+    const int64_t f0 = (vt_lo + phase) * 256;
+    w_offsets(f0, a.V, rowb, ao);
     const char* X0 = xop(a.side0 + sd);
-    gemm_pre(make_src(Wop + phase * 256 * rowb, wend), make_src(X0, X0 + xbytes), ao, bo);
+    gemm_pre(make_src(Wop + f0 * rowb, wend), make_src(X0, X0 + xbytes), ao, bo);
   }
   for (; tb < TB; tb += tbg) {
     const int sd = (int)(tb / fr.ntbs);
@@ -784,7 +820,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
     // per-block state lives in LDS so the GEMM loop keeps its registers: target id and
     // target logit per token column, running (max, sum) per lane and column block
     if (tid < 256) {
-      const int64_t r = tok0 + tid;
+      const int r = (int)tok0 + tid;  // row indices fit int32 (checked at the boundary)
       int yy = -1;
       if (r < fr.rhi) {
         const int64_t t = a.targets[a.idx[r]];
@@ -796,15 +832,19 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
         // the reference side's log-sum-exp of row r from the partials of the mode-1 launch
         float mr = INFINITY;
         if (r < fr.rhi) {
-          const PartLayout rl = part_layout(ntok, 1, nvt);
-          float M = -INFINITY;
-          for (int ph = 0; ph < rl.P; ++ph) M = fmaxf(M, a.ref_part[rl.at(0, 0, ph, r)]);
-          float sm = 0.f;
-          for (int ph = 0; ph < rl.P; ++ph) {
-            const float sp = a.ref_part[rl.at(1, 0, ph, r)];
-            if (sp != 0.f) sm += sp * exp2f(a.ref_part[rl.at(0, 0, ph, r)] - M);
+          if (a.ref_from_saved) {
+            mr = a.saved[(int64_t)a.idx[r] * 4] * kLog2e;
+          } else {
+            const PartLayout rl = part_layout(ntok, 1, nvt_all);
+            float M = -INFINITY;
+            for (int ph = 0; ph < rl.P; ++ph) M = fmaxf(M, a.ref_part[rl.at(0, 0, ph, r)]);
+            float sm = 0.f;
+            for (int ph = 0; ph < rl.P; ++ph) {
+              const float sp = a.ref_part[rl.at(1, 0, ph, r)];
+              if (sp != 0.f) sm += sp * exp2f(a.ref_part[rl.at(0, 0, ph, r)] - M);
+            }
+            mr = M + log2f(sm);
           }
-          mr = M + log2f(sm);
           if (phase == 0) a.pm[r - a.row_lo] = mr;
         }
         s_mr[tid] = mr;
@@ -822,7 +862,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
     lds_barrier();
     FoldOut fo;
     if (kStore) {
-      const int64_t rt = a.Vpad * E::kBytes, rm = nvt * 4;  // bytes per pt, pm row
+      const int64_t rt = a.pt_ld * E::kBytes, rm = nvt_all * 4;  // bytes per pt, pm row
       const char* pt0 = a.pt + (tok0 - a.row_lo) * rt;
       const char* pm0 = reinterpret_cast<const char*>(a.pm + (tok0 - a.row_lo) * nvt);
       fo.pt = make_src(pt0, pt0 + 256 * rt);
@@ -834,18 +874,22 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
       fo.col16_m = (uint32_t)(16 * rm);
       fo.nvalid = (int)(fr.rhi - tok0 < 256 ? fr.rhi - tok0 : 256);
     }
-    for (int64_t vt = phase; vt < nvt; vt += P) {
+    for (int64_t vt = vt_lo + phase; vt < nvt; vt += P) {
       const int64_t v0 = vt * 256;
       Acc acc;
       zero_acc(acc);
-      gemm_main<G>(make_src(Wop + v0 * rowb, wend), make_src(X, X + xbytes), ao, bo, nk, acc);
+      // the previous tile's fold stored kMB x kNB packed terms per thread after this tile's
+      // first loads: the k loop starts without waiting for them (16-bit kept terms only;
+      // the fp8 core's stage loop waits for everything)
+      gemm_main<G>(
+          make_src(Wop + v0 * rowb, wend), make_src(X, X + xbytes), ao, bo, nk, acc);
       // enqueue the next tile: the next vocabulary tile of this block, else the first
       // tile of this workgroup's next token block
       {
         int64_t nv = vt + P;
         int ntb = tb;
         if (nv >= nvt) {
-          nv = phase;
+          nv = vt_lo + phase;
           ntb = tb + tbg;
         }
         if (ntb < TB) {
@@ -856,19 +900,22 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
           gemm_pre(make_src(Wop + nv * 256 * rowb, wend), make_src(Xn, Xn + xbytes), ao, bo);
         }
       }
-      const int vb = (int)(v0 + wm * 128 + 4 * (lane >> 4));  // vocab of acc[mb][.][j] = vb + 16 mb + j
+      // vocab of acc[mb][.][j] = vb + 16 mb + j (the lane part recomputed here, not held
+      // across the k loop)
+      const int vb = (int)(v0 + wm * 128 + 4 * ((tid_opaque() & 63) >> 4));
       if (kF8) scale_acc(acc, a.sw, side ? a.sxp : a.sxq, vb, a.V, tok0, fr.rhi, wn, lane);
       FoldOut ft = fo;
       if (kStore) {
-        ft.v0_t = (uint32_t)(v0 * E::kBytes);
+        ft.v0_t = (uint32_t)((v0 - vt_lo * 256) * E::kBytes);
         ft.vt_m = (uint32_t)(vt * 4);
       }
       if constexpr (kFixed) {
         if (v0 + 256 <= a.V)
-          fwd_fold_fixed<E, true>(acc, s2, 0, vb, wn, lane, tid, s_run, s_y, s_zt, s_mr, ft);
+          fwd_fold_fixed<E, true>(acc, s2, 0, vb, wn, lane, tid, s_run, s_y, s_zt, s_mr, ft,
+                                  a.zero_target);
         else
           fwd_fold_fixed<E, false>(acc, s2, (int)(a.V - vb), vb, wn, lane, tid, s_run, s_y,
-                                   s_zt, s_mr, ft);
+                                   s_zt, s_mr, ft, a.zero_target);
       } else {
         if (v0 + 256 <= a.V)
           fwd_fold<E, true, kStore>(acc, s2, 0, vb, wm, wn, lane, tid, s_run, s_y, s_zt, s_cm,
@@ -901,7 +948,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
     __syncthreads();
     if (tid < 256) {  // one thread per token column of the block
       const int n = tid;
-      const int64_t r = tok0 + n;
+      const int r = (int)tok0 + n;
       if (r < fr.rhi) {
         const float m0 = mrg[0][0][n], m1 = mrg[1][0][n];
         const float M = fmaxf(m0, m1);
@@ -909,9 +956,9 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
                               ? 0.f
                               : (m0 == -INFINITY ? 0.f : mrg[0][1][n] * exp2f(m0 - M)) +
                                     (m1 == -INFINITY ? 0.f : mrg[1][1][n] * exp2f(m1 - M));
-        a.part[pl.at(0, sd, phase, r - a.row_lo)] = M;
-        a.part[pl.at(1, sd, phase, r - a.row_lo)] = sum;
-        a.part[pl.at(2, sd, phase, r - a.row_lo)] = s_zt[n];
+        a.part[pl.at(0, sd, slot_ph, r - a.row_lo)] = M;
+        a.part[pl.at(1, sd, slot_ph, r - a.row_lo)] = sum;
+        a.part[pl.at(2, sd, slot_ph, r - a.row_lo)] = s_zt[n];
       }
     }
     __syncthreads();
@@ -959,22 +1006,26 @@ fixup_kernel(int64_t Vpad, int64_t nvt, int64_t c0, int64_t R, const int32_t* __
 }
 
 // ---------------------------------------------------------------------------- recompute
-// T[r - c0][v] = onehot(y_r)[v] - exp(z_rv / tau - lse_r) for one 256-token x
+// T[r - c0][v - vt0 256] = onehot(y_r)[v] - exp(z_rv / tau - lse_r) for one 256-token x
 // 256-vocabulary tile of the chunk (scale2 = log2(e) / tau); zero for v >= V and for rows
-// past the last loss token.  G = FP8T: Xq and W are the fp8 copies (Xq by compact row)
-// with scales sxq and sw.
+// past the last loss token.  The grid covers the vocabulary tiles vt0 .. of one piece and
+// T rows hold ld entries.  kept = 1 (the vocabulary split): the plain softmax terms
+// exp(z_rv / tau - lse_r), with 0 at the target entry, which the final dX kernel adds
+// back as 1 - p_y = -expm1(q).  G = FP8T: Xq and W are the fp8 copies (Xq by compact
+// row) with scales sxq and sw.
 template <class E, class G>
 __global__ void __launch_bounds__(kThreads, 1)
-recompute_kernel(int64_t N, int64_t H, int64_t V, int64_t Vpad, int64_t c0, int ntt, float scale2,
-                 const int32_t* __restrict__ ntok_p, const int32_t* __restrict__ idx,
-                 const char* __restrict__ Xq, const char* __restrict__ W,
-                 const int64_t* __restrict__ targets, const float* __restrict__ saved,
-                 typename E::T* __restrict__ T, const float* __restrict__ sw,
-                 const float* __restrict__ sxq) {
+recompute_kernel(int64_t N, int64_t H, int64_t V, int64_t ld, int64_t vt0, int64_t c0, int ntt,
+                 float scale2, int kept, const int32_t* __restrict__ ntok_p,
+                 const int32_t* __restrict__ idx, const char* __restrict__ Xq,
+                 const char* __restrict__ W, const int64_t* __restrict__ targets,
+                 const float* __restrict__ saved, typename E::T* __restrict__ T,
+                 const float* __restrict__ sw, const float* __restrict__ sxq) {
   constexpr bool kF8 = G::kBytes == 1;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / kWN, wn = w % kWN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w / kWN, wn = w % kWN;
   // token tiles vary fastest so consecutive workgroups share a W tile
-  const int64_t tt = blockIdx.x % ntt, vt = blockIdx.x / ntt;
+  const int64_t tt = blockIdx.x % ntt, vt = vt0 + blockIdx.x / ntt;
   const int ntok = *ntok_p;
   const int64_t tok0 = c0 + tt * 256;
   if (tok0 >= ntok) return;
@@ -1003,7 +1054,7 @@ recompute_kernel(int64_t N, int64_t H, int64_t V, int64_t Vpad, int64_t c0, int 
       lse2 = saved[t * 4] * kLog2e;
       y = targets[t];
     }
-    typename E::T* trow = T + (r - c0) * Vpad;
+    typename E::T* trow = T + (r - c0) * ld - vt0 * 256;
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) {
       const int64_t v = vb + mb * 16;
@@ -1011,8 +1062,10 @@ recompute_kernel(int64_t N, int64_t H, int64_t V, int64_t Vpad, int64_t c0, int 
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float val = 0.f;
-        if (ok && v + j < V)
-          val = (v + j == y ? 1.f : 0.f) - exp2_fast(fmaf(acc[mb][nb][j], scale2, -lse2));
+        if (ok && v + j < V) {
+          const float pv = exp2_fast(fmaf(acc[mb][nb][j], scale2, -lse2));
+          val = kept ? (v + j == y ? 0.f : pv) : (v + j == y ? 1.f : 0.f) - pv;
+        }
         o[j] = E::from_f32(val);
       }
       uint2 pk;
@@ -1029,11 +1082,23 @@ __device__ inline float fixed_row_factor(int64_t rl, int64_t t, const float* __r
   return -exp2f(mr[rl] - saved[t * 4] * kLog2e);
 }
 
+// Float offset of accumulator block (mb, nb) of lane `lane` of wave w in tile `tile` of the
+// vocabulary split's dX sums: each tile takes 65536 floats, wave-major, then block
+// q = nb 8 + mb (1 KB), then lane (16 bytes).
+__host__ __device__ inline int64_t dx_sum_offset(int64_t tile, int w, int nb, int mb, int lane) {
+  return tile * 65536 + w * 8192 + (nb * 8 + mb) * 256 + lane * 4;
+}
+
 // ------------------------------------------------------------------------------- dX
-// C[h][r] = sum_v W[v][h] T[r][v] over the padded vocabulary (or one split of it), with W
-// read in its own [V][H] layout (natural-layout A tiles; rows past V load as 0).
-// ksplit == 1: dX[idx[r]][h] = c * g_r * s_r * C, in the storage type.  ksplit > 1: fp32
-// partials of C to dxp[ks][r - c0][h], reduced by dx_reduce_kernel, which scales the same.
+// C[h][r] = sum_v W[v][h] T[r][v] over the chunk buffer's vocabulary columns (the padded
+// vocabulary, or one piece of it: columns 0 .. kcols - 1 of rows of ld entries hold
+// vocabulary rows v_base ..), or one split of them, with W read in its own [V][H] layout
+// (natural-layout A tiles; rows past V load as 0).
+// acc_mode 0, ksplit == 1: dX[idx[r]][h] = c * g_r * s_r * C, in the storage type.
+// acc_mode 0, ksplit > 1: fp32 partials of C to dxp[ks][r - c0][h], reduced by
+// dx_reduce_kernel, which scales the same.  acc_mode 1: fp32 partials for every ksplit
+// (the first piece of a vocabulary-split chunk); acc_mode 2: added to them (the later
+// pieces: the k loop starts from the stored sums), scaled by dx_final_kernel.
 // s_r = 1 where the chunk buffer holds T = onehot - softmax (two-pass, single-pass mode 2,
 // or a mode-3 chunk whose fallback ran: redo null or *redo != 0).  Otherwise it holds the
 // mode-3 row E = -T / f_r: the kept terms e_v = p_v / f_r, f_r = exp2(mr_r - lse2_r) (mr:
@@ -1043,17 +1108,22 @@ __device__ inline float fixed_row_factor(int64_t rl, int64_t t, const float* __r
 // Persistent over a work list of (k split, token tile, H tile) items, H tile fastest,
 // holding only the token tiles of this chunk that have loss rows, so every workgroup gets
 // the same number of items up to one.  Workgroups are numbered XCD-major (workgroup b
-// runs on XCD b % 8), so the items that share a T tile and k range run on one XCD.
+// runs on XCD b % 8), so the items that share a T tile and k range run on one XCD.  Each
+// item's first k-step is enqueued before the previous item's epilogue, so its memory
+// latency overlaps the epilogue's instead of following it.
 template <class E>
 __global__ void __launch_bounds__(kThreads, 1)
-dx_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int nht, int ksplit,
-          const int32_t* __restrict__ ntok_p, const int32_t* __restrict__ idx,
-          const char* __restrict__ W, const char* __restrict__ T,
-          const float* __restrict__ saved, const float* __restrict__ grad_loss, float loss_scale,
+dx_kernel(int64_t H, int64_t V, int64_t ld, int64_t kcols, int64_t v_base, int64_t R,
+          int64_t c0, int nht, int ksplit, int acc_mode, const int32_t* __restrict__ ntok_p,
+          const int32_t* __restrict__ idx, const char* __restrict__ W,
+          const char* __restrict__ T, const float* __restrict__ saved,
+          const float* __restrict__ grad_loss, float loss_scale,
           typename E::T* __restrict__ dX, float* __restrict__ dxp,
           int32_t* __restrict__ found_inf, const int32_t* __restrict__ redo,
-          const float* __restrict__ mr) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / kWN, wn = w % kWN;
+          const float* __restrict__ mr, const int32_t* __restrict__ gate) {
+  if (gate && *gate == 0) return;   // the vocabulary split's fallback
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w / kWN, wn = w % kWN;
   const int ntok = *ntok_p;
   int64_t rows = (int64_t)ntok - c0;
   if (rows <= 0) return;
@@ -1062,9 +1132,11 @@ dx_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int nht, in
   const int64_t n_items = ntt * nht * ksplit;
   const int nwg = gridDim.x;                       // a multiple of 8
   const int64_t first = (int64_t)(blockIdx.x % kXcds) * (nwg / kXcds) + blockIdx.x / kXcds;
-  // k-steps of 64 split into ksplit ranges with even boundaries (Vpad / 64 is a multiple of 4)
-  const int64_t npair = Vpad / 128;
-  const int64_t rowb = Vpad * 2;  // bytes per T row
+  // k-steps of 64 over the kcols columns written for this launch (a multiple of 256; the
+  // last piece of a split chunk leaves the buffer's later columns as the previous piece
+  // wrote them), split into ksplit ranges with even boundaries
+  const int64_t npair = kcols / 128;
+  const int64_t rowb = ld * 2;    // bytes per T row
   const int64_t ldw = H * 2;      // bytes per W row
   Offs ao, bo;
   nat_offsets(ldw, ao);
@@ -1075,25 +1147,75 @@ dx_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int nht, in
   }
   const float c = (grad_loss ? *grad_loss : 1.f) / loss_scale;
   const bool fixed = redo && *redo == 0;
+  const bool to_slots = acc_mode != 0 || ksplit > 1;
   bool bad = false;
+  // item -> (token tile, H tile, k range) and its two operands
+  struct Item {
+    int64_t tt, ks, h0, kbeg, kend;
+  };
+  auto decode = [&](int64_t item) {
+    Item d;
+    const int64_t rest = item / nht;
+    d.h0 = (item % nht) * 256;
+    d.tt = rest % ntt;
+    d.ks = rest / ntt;
+    d.kbeg = 2 * (npair * d.ks / ksplit);
+    d.kend = 2 * (npair * (d.ks + 1) / ksplit);
+    return d;
+  };
+  auto opA = [&](const Item& d) {
+    const int64_t v = v_base + d.kbeg * 64;
+    return Op<true>{W + v * ldw + d.h0 * 2, (V - v) * ldw - d.h0 * 2, 64 * ldw};
+  };
+  auto opB = [&](const Item& d) {
+    return Op<false>{make_src(T + d.tt * 256 * rowb + d.kbeg * 128, T + R * rowb)};
+  };
+  // The fp32 sums of an item's tile.  ksplit > 1 with acc_mode 0: row-major partials
+  // dxp[ks][r - c0][h] for dx_reduce_kernel.  acc_mode 1 and 2: the tile's own 256 KB in
+  // the accumulator layout (dx_sum_offset), so that each of the 32 stores (and, for the
+  // later pieces, loads) of a wave covers 1 KB of consecutive bytes.
+  auto slot_ptr = [&](const Item& d, int nb, int mb) {
+    const int lq = tid_opaque() & 63;
+    if (acc_mode != 0)
+      return reinterpret_cast<f32x4*>(
+          dxp + dx_sum_offset((d.ks * (R / 256) + d.tt) * nht + d.h0 / 256, w, nb, mb, lq));
+    const int rl = (int)d.tt * 256 + wn * kWaveN + nb * 16 + (lq & 15);
+    const int hb = (int)d.h0 + wm * 128 + 4 * (lq >> 4);
+    return reinterpret_cast<f32x4*>(dxp + (d.ks * R + rl) * H + hb + mb * 16);
+  };
+  auto init_acc = [&](Acc& acc, const Item& d) {
+    if (acc_mode != 2) {
+      zero_acc(acc);
+      return;
+    }
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) acc[mb][nb] = *slot_ptr(d, nb, mb);
+  };
+  Acc acc;
+  if (first < n_items) {
+    const Item d = decode(first);
+    if (d.kend > d.kbeg) gemm_pre_op(opA(d), opB(d), ao, bo);
+    init_acc(acc, d);
+  }
   for (int64_t item = first; item < n_items; item += nwg) {
-    const int64_t ht = item % nht, rest = item / nht;
-    const int64_t tt = rest % ntt, ks = rest / ntt;
-    const int64_t tok0 = c0 + tt * 256;
-    const int64_t h0 = ht * 256;
-    const int64_t kbeg = 2 * (npair * ks / ksplit), kend = 2 * (npair * (ks + 1) / ksplit);
-    Acc acc;
-    zero_acc(acc);
-    if (kend > kbeg)
-      gemm_core_op<E, true, false>(
-          Op<true>{W + h0 * 2 + kbeg * 64 * ldw, (V - kbeg * 64) * ldw - h0 * 2, 64 * ldw},
-          Op<false>{make_src(T + tt * 256 * rowb + kbeg * 128, T + R * rowb)}, ao, bo,
-          (int)(kend - kbeg), acc);
-    const int64_t hb = h0 + wm * 128 + 4 * (lane >> 4);
-    if (ksplit == 1) {
+    const Item d = decode(item);
+    const int64_t tok0 = c0 + d.tt * 256;
+    if (d.kend > d.kbeg)
+      gemm_main_op<E, true, false>(opA(d), opB(d), ao, bo, (int)(d.kend - d.kbeg), acc);
+    if (item + nwg < n_items) {
+      const Item dn = decode(item + nwg);
+      if (dn.kend > dn.kbeg) gemm_pre_op(opA(dn), opB(dn), ao, bo);
+    }
+    if (!to_slots) {
+      // lane-derived indices recomputed here (32-bit: rows and H fit), not held across
+      // the k loop
+      const int lq = tid_opaque() & 63;
+      const int hb = (int)d.h0 + wm * 128 + 4 * (lq >> 4);
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) {
-        const int64_t r = tok0 + wn * kWaveN + nb * 16 + (lane & 15);
+        const int r = (int)tok0 + wn * kWaveN + nb * 16 + (lq & 15);
         if (r >= ntok) continue;
         const int64_t t = idx[r];
         float gs = saved[t * 4 + 3] * c;
@@ -1111,14 +1233,11 @@ dx_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int nht, in
       }
     } else {
 #pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) {
-        const int64_t rl = tt * 256 + wn * kWaveN + nb * 16 + (lane & 15);
-        float* prow = dxp + (ks * R + rl) * H;
+      for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
-        for (int mb = 0; mb < kMB; ++mb)
-          *reinterpret_cast<f32x4*>(prow + hb + mb * 16) = acc[mb][nb];
-      }
+        for (int mb = 0; mb < kMB; ++mb) *slot_ptr(d, nb, mb) = acc[mb][nb];
     }
+    if (item + nwg < n_items) init_acc(acc, decode(item + nwg));
   }
   if (bad) atomicOr(found_inf, 1);
 }
@@ -1157,18 +1276,88 @@ dx_reduce_kernel(int64_t H, int64_t R, int64_t c0, int ksplit, const int32_t* __
   if (bad) atomicOr(found_inf, 1);
 }
 
+// dX of a vocabulary-split chunk from the fp32 sums of its pieces (dx_kernel, acc_mode 1 and
+// 2): each piece's buffer held p_v / f_r for v != y_r and 0 at the target, so
+//   dX[idx[r]][h] = c g_r ((1 - p_y) W[y_r][h] - f_r sum_ks C_ks[r][h])
+// with 1 - p_y = -expm1(q_r) from the row's log-probability (exact even for p_y near 1),
+// f_r = exp2(pm[r - c0] - lse2_r) (pm: the reference the single pass's terms were taken
+// against; null: 1, the two-pass recompute's plain softmax terms).  One workgroup per
+// (token tile, H tile) of the chunk, its threads in the accumulator layout of dx_kernel,
+// so the sums are read as they were written; a target outside [0, V) (flagged by the
+// forward) adds no W row.
+template <class E>
+__global__ void __launch_bounds__(kThreads)
+dx_final_kernel(int64_t H, int64_t V, int64_t R, int64_t c0, int nht, int ksplit,
+                const int32_t* __restrict__ ntok_p, const int32_t* __restrict__ idx,
+                const int64_t* __restrict__ targets, const float* __restrict__ dxp,
+                const float* __restrict__ saved, const float* __restrict__ grad_loss,
+                float loss_scale, const float* __restrict__ pm,
+                const typename E::T* __restrict__ W, typename E::T* __restrict__ dX,
+                int32_t* __restrict__ found_inf) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w / kWN, wn = w % kWN;
+  const int64_t tt = blockIdx.x / nht, ht = blockIdx.x % nht;
+  const int ntok = *ntok_p;
+  const int64_t tok0 = c0 + tt * 256;
+  if (tok0 >= ntok) return;
+  const float c = (grad_loss ? *grad_loss : 1.f) / loss_scale;
+  const int64_t hb = ht * 256 + wm * 128 + 4 * (lane >> 4);
+  bool bad = false;
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    const int64_t rl = tt * 256 + wn * kWaveN + nb * 16 + (lane & 15);
+    const int64_t r = c0 + rl;
+    if (r >= ntok) continue;
+    const int64_t t = idx[r];
+    const int64_t y = targets[t];
+    const float lse2 = saved[t * 4] * kLog2e;
+    const float gs = saved[t * 4 + 3] * c;
+    const float f = pm ? exp2f(pm[rl] - lse2) : 1.f;
+    const bool yok = y >= 0 && y < V;
+    const float ty = yok ? -expm1f(saved[t * 4 + 1]) : 0.f;
+    const typename E::T* wy = W + (yok ? y : 0) * H + hb;
+    typename E::T* drow = dX + t * H + hb;
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) {
+      f32x4 sm = *reinterpret_cast<const f32x4*>(dxp + dx_sum_offset(tt * nht + ht, w, nb, mb, lane));
+      for (int k = 1; k < ksplit; ++k)
+        sm += *reinterpret_cast<const f32x4*>(
+            dxp + dx_sum_offset((k * (R / 256) + tt) * nht + ht, w, nb, mb, lane));
+      const uint2 wv = *reinterpret_cast<const uint2*>(wy + mb * 16);
+      const float w0 = E::to_f32((typename E::T)(wv.x & 0xffffu));
+      const float w1 = E::to_f32((typename E::T)(wv.x >> 16));
+      const float w2 = E::to_f32((typename E::T)(wv.y & 0xffffu));
+      const float w3 = E::to_f32((typename E::T)(wv.y >> 16));
+      uint2 pk;
+      pk.x = E::pack2(gs * (ty * w0 - f * sm[0]), gs * (ty * w1 - f * sm[1]));
+      pk.y = E::pack2(gs * (ty * w2 - f * sm[2]), gs * (ty * w3 - f * sm[3]));
+      bad |= E::nonfinite2(pk.x) || E::nonfinite2(pk.y);
+      *reinterpret_cast<uint2*>(drow + mb * 16) = pk;
+    }
+  }
+  if (bad) atomicOr(found_inf, 1);
+}
+
 // ------------------------------------------------------------------------------- dW
-// C[h][v] = sum_r Xg[r][h] T[r][v] over the chunk's rows; dW[v][h] (+)= C.  Both operands
-// are natural-layout tiles read in place: Xg [R][H] (gather_rows_kernel) and the chunk's
-// T [R][Vpad].
+// C[h][v] = sum_r Xg[r][h] T[r][v] over the chunk's rows; dW[v][h] = 2^-k C (+ dW[v][h]),
+// 2^k the chunk's scale of Xg (xg_scale).  Both operands are natural-layout tiles read in
+// place: Xg [R][H] (gather_rows_kernel) and the chunk's T [R][Vpad].
+//
+// Persistent over the (vocabulary tile, H tile) items, H tile fastest, numbered so that
+// workgroup b (on XCD b % 8) takes item 256 r + 32 (b % 8) + b / 8 in round r: the items
+// sharing a T slice run on one XCD.  Each item's first k-step is enqueued before the
+// previous item's epilogue, so the epilogue's read of the old dW tile and that k-step's
+// loads are in flight together.  (The old tile is added after the GEMM, not used as the
+// k loop's starting value: that would round every step at the scale of the accumulated
+// dW instead of the chunk's own contribution.)
 template <class E>
 __global__ void __launch_bounds__(kThreads, 1)
 dw_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int nht, int accumulate,
           const int32_t* __restrict__ ntok_p, const char* __restrict__ Xg,
           const char* __restrict__ T, float* __restrict__ dW, int32_t* __restrict__ found_inf,
           const float* __restrict__ xg_scale) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / kWN, wn = w % kWN;
-  const int64_t ht = blockIdx.x % nht, vt = blockIdx.x / nht;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w / kWN, wn = w % kWN;
   const int ntok = *ntok_p;
   int64_t nrows = (int64_t)ntok - c0;
   if (nrows > R) nrows = R;
@@ -1176,55 +1365,66 @@ dw_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int nht, in
   if (nrows < 0) nrows = 0;
   // rows padded to a multiple of 128 (an even number of k-steps); the padding rows of
   // T and Xg are zero
-  const int64_t nk = 2 * ((nrows + 127) / 128);
-  const int64_t h0 = ht * 256, v0 = vt * 256;
+  const int nk = (int)(2 * ((nrows + 127) / 128));
   const int64_t ldx = H * 2, ldt = Vpad * 2;
+  const int64_t n_items = (int64_t)nht * (Vpad / 256);
+  const int nwg = gridDim.x;  // a multiple of 8
+  const int64_t first = (int64_t)(blockIdx.x % kXcds) * (nwg / kXcds) + blockIdx.x / kXcds;
   Offs ao, bo;
   nat_offsets(ldx, ao);
   nat_offsets(ldt, bo);
-  Acc acc;
-  zero_acc(acc);
-  if (nk > 0)
-    gemm_core_op<E, true, true>(Op<true>{Xg + h0 * 2, R * ldx - h0 * 2, 64 * ldx},
-                                Op<true>{T + v0 * 2, R * ldt - v0 * 2, 64 * ldt}, ao, bo, (int)nk,
-                                acc);
-  const int64_t hb = h0 + wm * 128 + 4 * (lane >> 4);
+  auto opA = [&](int64_t it) {
+    const int64_t h0 = (it % nht) * 256;
+    return Op<true>{Xg + h0 * 2, R * ldx - h0 * 2, 64 * ldx};
+  };
+  auto opB = [&](int64_t it) {
+    const int64_t v0 = (it / nht) * 256;
+    return Op<true>{T + v0 * 2, R * ldt - v0 * 2, 64 * ldt};
+  };
+  const float inv = xg_scale[1];
   bool bad = false;
-  {
-    // undo the chunk's power-of-two scale of Xg (exact)
-    const float inv = xg_scale[1];
+  if (first < n_items && nk > 0) gemm_pre_op(opA(first), opB(first), ao, bo);
+  for (int64_t it = first; it < n_items; it += nwg) {
+    Acc acc;
+    zero_acc(acc);
+    if (nk > 0) gemm_main_op<E, true, true>(opA(it), opB(it), ao, bo, nk, acc);
+    const int64_t next = it + nwg;
+    if (next < n_items && nk > 0) gemm_pre_op(opA(next), opB(next), ao, bo);
+    const int lq = tid_opaque() & 63;
+    const int hb = (int)((it % nht) * 256) + wm * 128 + 4 * (lq >> 4);
+    const int64_t v0 = (it / nht) * 256;
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] *= inv;
-  }
-  if (accumulate) {
-    // every old value of the lane's columns in flight at once: one memory round trip per
-    // tile instead of one per 16-byte piece
-    f32x4 old[kNB][kMB];
+      for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] *= inv;  // undo the chunk's 2^k (exact)
+    if (accumulate) {
+      // every old value of the lane's columns in flight at once (with the next item's
+      // first loads): one memory round trip per item
+      f32x4 old[kNB][kMB];
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-      const int64_t v = v0 + wn * kWaveN + nb * 16 + (lane & 15);
-      const f32x4* p = reinterpret_cast<const f32x4*>(dW + (v < V ? v : 0) * H + hb);
+      for (int nb = 0; nb < kNB; ++nb) {
+        const int64_t v = v0 + wn * kWaveN + nb * 16 + (lq & 15);
+        const f32x4* p = reinterpret_cast<const f32x4*>(dW + (v < V ? v : 0) * H + hb);
 #pragma unroll
-      for (int mb = 0; mb < kMB; ++mb) old[nb][mb] = p[mb * 4];
+        for (int mb = 0; mb < kMB; ++mb) old[nb][mb] = p[mb * 4];
+      }
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb) acc[mb][nb] += old[nb][mb];
     }
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb)
+    for (int nb = 0; nb < kNB; ++nb) {
+      const int64_t v = v0 + wn * kWaveN + nb * 16 + (lq & 15);
+      if (v >= V) continue;
+      f32x4* p = reinterpret_cast<f32x4*>(dW + v * H + hb);
 #pragma unroll
-      for (int mb = 0; mb < kMB; ++mb) acc[mb][nb] += old[nb][mb];
-  }
+      for (int mb = 0; mb < kMB; ++mb) {
+        const f32x4 val = acc[mb][nb];
 #pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) {
-    const int64_t v = v0 + wn * kWaveN + nb * 16 + (lane & 15);
-    if (v >= V) continue;
-    f32x4* p = reinterpret_cast<f32x4*>(dW + v * H + hb);
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) {
-      const f32x4 val = acc[mb][nb];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bad |= !isfinite(val[j]);
-      p[mb * 4] = val;
+        for (int j = 0; j < 4; ++j) bad |= !isfinite(val[j]);
+        p[mb * 4] = val;
+      }
     }
   }
   if (bad) atomicOr(found_inf, 1);
@@ -1341,7 +1541,13 @@ FwdArgs fwd_args(const Plan& p, void* ws, const void* Xq, const void* Xp, const 
   a.pt = nullptr;
   a.pm = nullptr;
   a.gate = nullptr;
-  a.Vpad = p.Vpad;
+  a.pt_ld = p.pt_ld;
+  a.piece = 0;
+  a.npieces = 1;
+  a.ptiles = p.Vpad / kVocTile;
+  a.zero_target = 0;
+  a.ref_from_saved = 0;
+  a.saved = nullptr;
   a.W8 = ws_ptr<char>(ws, p.off_w8);
   a.Xq8 = ws_ptr<char>(ws, p.off_xq8);
   a.Xp8 = ws_ptr<char>(ws, p.off_xp8);
@@ -1374,7 +1580,9 @@ hipError_t fwd_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, con
     if (e != hipSuccess) return e;
   }
   FwdArgs a = fwd_args(p, ws, Xq, Xp, W, targets);
+  trace_begin(p, GRPO_TRACE_FWD_ALL, st);
   hipLaunchKernelGGL((fwd_kernel<E, G, 0>), dim3(kNumWG), dim3(kThreads), 0, st, a);
+  trace_end(p, GRPO_TRACE_FWD_ALL, st);
   return hipGetLastError();
 }
 
@@ -1392,10 +1600,13 @@ hipError_t chunk_grads(const Plan& p, void* ws, int64_t c0, const void* Xq, cons
   T* Tb = ws_ptr<T>(ws, p.off_T);
   const int nvt = (int)(p.Vpad / 256), nht = (int)(p.H / 256);
   hipError_t e;
+  trace_begin(p, GRPO_TRACE_DX, st);
   hipLaunchKernelGGL(dx_kernel<E>, dim3(kNumWG), dim3(kThreads), 0, st,
-                     p.H, p.V, p.Vpad, p.R, c0, nht, p.ksplit, ntok, idx, (const char*)W,
-                     (const char*)Tb, saved, grad_loss, loss_scale, (T*)dX,
-                     ws_ptr<float>(ws, p.off_dxp), found_inf, redo, mr);
+                     p.H, p.V, p.Vpad, p.Vpad, (int64_t)0, p.R, c0, nht, p.ksplit, 0, ntok, idx,
+                     (const char*)W, (const char*)Tb, saved, grad_loss, loss_scale, (T*)dX,
+                     ws_ptr<float>(ws, p.off_dxp), found_inf, redo, mr,
+                     (const int32_t*)nullptr);
+  trace_end(p, GRPO_TRACE_DX, st);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.ksplit > 1) {
     hipLaunchKernelGGL(dx_reduce_kernel<E>, dim3((unsigned)p.R), dim3(256), 0, st, p.H, p.R, c0,
@@ -1413,9 +1624,11 @@ hipError_t chunk_grads(const Plan& p, void* ws, int64_t c0, const void* Xq, cons
                        (const T*)Xq, p.H, p.R, c0, ntok, idx, saved, grad_loss, loss_scale, Xg,
                        redo, mr, (const float*)xs);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(dw_kernel<E>, dim3((unsigned)(nht * nvt)), dim3(kThreads), 0, st, p.H,
+    trace_begin(p, GRPO_TRACE_DW, st);
+    hipLaunchKernelGGL(dw_kernel<E>, dim3(kNumWG), dim3(kThreads), 0, st, p.H,
                        p.V, p.Vpad, p.R, c0, nht, c0 == 0 ? accumulate_dW : 1, ntok,
                        (const char*)Xg, (const char*)Tb, dW, found_inf, (const float*)xs);
+    trace_end(p, GRPO_TRACE_DW, st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
@@ -1437,10 +1650,12 @@ hipError_t bwd_impl(const Plan& p, void* ws, const void* Xq, const void* W,
   const char* Wop = kF8 ? ws_ptr<char>(ws, p.off_w8) : (const char*)W;
   const int ntt = (int)(p.R / 256), nvt = (int)(p.Vpad / 256);
   for (int64_t c0 = 0; c0 < p.N; c0 += p.R) {
+    trace_begin(p, GRPO_TRACE_RECOMPUTE, st);
     hipLaunchKernelGGL((recompute_kernel<E, G>), dim3((unsigned)(ntt * nvt)), dim3(kThreads), 0,
-                       st, p.N, p.H, p.V, p.Vpad, c0, ntt, p.scale2, ntok, idx, Xop, Wop, targets,
-                       saved, Tb, (const float*)ws_ptr<float>(ws, p.off_sw),
+                       st, p.N, p.H, p.V, p.Vpad, (int64_t)0, c0, ntt, p.scale2, 0, ntok, idx,
+                       Xop, Wop, targets, saved, Tb, (const float*)ws_ptr<float>(ws, p.off_sw),
                        (const float*)ws_ptr<float>(ws, p.off_sxq));
+    trace_end(p, GRPO_TRACE_RECOMPUTE, st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     e = chunk_grads<E>(p, ws, c0, Xq, W, saved, grad_loss, loss_scale, dX, dW, accumulate_dW,
                        found_inf, st);
@@ -1482,7 +1697,9 @@ hipError_t fused_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, c
   FwdArgs a = fwd_args(p, ws, Xq, Xp, W, targets);
   a.side0 = 1;
   a.nsides = 1;
+  trace_begin(p, GRPO_TRACE_FWD_ALL, st);
   hipLaunchKernelGGL((fwd_kernel<E, G, 1>), dim3(kNumWG), dim3(kThreads), 0, st, a);
+  trace_end(p, GRPO_TRACE_FWD_ALL, st);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   for (int64_t c0 = 0, ci = 0; c0 < p.N; c0 += p.R, ++ci) {
     int32_t* rd = redo + ci;
@@ -1493,7 +1710,9 @@ hipError_t fused_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, c
     a.pt = reinterpret_cast<char*>(Tb);
     a.pm = pm;
     a.gate = nullptr;
+    trace_begin(p, GRPO_TRACE_FWD_CHUNK, st);
     hipLaunchKernelGGL((fwd_kernel<E, G, 3>), dim3(kNumWG), dim3(kThreads), 0, st, a);
+    trace_end(p, GRPO_TRACE_FWD_CHUNK, st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     e = launch_merge_rows(p, ws, c0, targets, mask, adv, beta, saved, logp, ref_logp, kl,
                           status, st, rd, Tb, nullptr);
@@ -1517,6 +1736,171 @@ hipError_t fused_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, c
   return launch_loss_final(p, ws, 1, status, loss, st);
 }
 
+// Vocabulary split: dX of chunk c0 from one piece of its buffer (columns 0 .. pt_ld - 1
+// hold vocabulary rows piece ptiles 256 ..), into the chunk's fp32 sums: the first piece
+// writes them, the later ones add to them.  gate: the fallback's launches.
+template <class E>
+hipError_t piece_dx(const Plan& p, void* ws, int64_t c0, int piece, const void* W,
+                    int32_t* found_inf, hipStream_t st, const int32_t* gate, bool traced) {
+  typedef typename E::T T;
+  const int nht = (int)(p.H / 256);
+  const int64_t nvt = p.Vpad / kVocTile, vt0 = (int64_t)piece * p.ptiles;
+  const int64_t tiles = nvt - vt0 < p.ptiles ? nvt - vt0 : p.ptiles;
+  if (traced) trace_begin(p, GRPO_TRACE_DX, st);
+  hipLaunchKernelGGL(dx_kernel<E>, dim3(kNumWG), dim3(kThreads), 0, st, p.H, p.V, p.pt_ld,
+                     tiles * kVocTile, vt0 * kVocTile, p.R, c0, nht, p.ksplit,
+                     piece == 0 ? 1 : 2, ws_ptr<int32_t>(ws, p.off_ntok),
+                     ws_ptr<int32_t>(ws, p.off_idx), (const char*)W,
+                     (const char*)ws_ptr<T>(ws, p.off_T), (const float*)nullptr,
+                     (const float*)nullptr, 1.f, (T*)nullptr, ws_ptr<float>(ws, p.off_dxp),
+                     found_inf, (const int32_t*)nullptr, (const float*)nullptr, gate);
+  if (traced) trace_end(p, GRPO_TRACE_DX, st);
+  return hipGetLastError();
+}
+
+// dX of a vocabulary-split chunk from its pieces' sums (dx_final_kernel).
+template <class E>
+hipError_t split_dx_final(const Plan& p, void* ws, int64_t c0, const void* W,
+                          const int64_t* targets, const float* saved, const float* grad_loss,
+                          float loss_scale, const float* pm, void* dX, int32_t* found_inf,
+                          hipStream_t st) {
+  typedef typename E::T T;
+  const int nht = (int)(p.H / 256);
+  hipLaunchKernelGGL(dx_final_kernel<E>, dim3((unsigned)(p.R / 256 * nht)), dim3(kThreads), 0,
+                     st, p.H, p.V, p.R, c0, nht, p.ksplit, ws_ptr<int32_t>(ws, p.off_ntok),
+                     ws_ptr<int32_t>(ws, p.off_idx), targets,
+                     (const float*)ws_ptr<float>(ws, p.off_dxp), saved, grad_loss, loss_scale, pm,
+                     (const T*)W, (T*)dX, found_inf);
+  return hipGetLastError();
+}
+
+// Two-pass backward with the vocabulary split: per chunk and piece, the softmax terms of
+// the piece (target entry 0) recomputed from the forward's log-sum-exp, and their dX sums;
+// then the chunk's dX.
+template <class E, class G>
+hipError_t bwd_split_impl(const Plan& p, void* ws, const void* Xq, const void* W,
+                          const int64_t* targets, const float* saved, const float* grad_loss,
+                          float loss_scale, void* dX, int32_t* found_inf, hipStream_t st) {
+  typedef typename E::T T;
+  constexpr bool kF8 = G::kBytes == 1;
+  const int32_t* ntok = ws_ptr<int32_t>(ws, p.off_ntok);
+  const int32_t* idx = ws_ptr<int32_t>(ws, p.off_idx);
+  T* Tb = ws_ptr<T>(ws, p.off_T);
+  hipError_t e = hipSuccess;
+  if (kF8 && (e = quantize_operands(p, ws, Xq, nullptr, W, st)) != hipSuccess) return e;
+  const char* Xop = kF8 ? ws_ptr<char>(ws, p.off_xq8) : (const char*)Xq;
+  const char* Wop = kF8 ? ws_ptr<char>(ws, p.off_w8) : (const char*)W;
+  const int ntt = (int)(p.R / 256);
+  const int64_t nvt = p.Vpad / 256;
+  for (int64_t c0 = 0; c0 < p.N; c0 += p.R) {
+    for (int j = 0; j < p.npieces; ++j) {
+      const int64_t vt0 = (int64_t)j * p.ptiles;
+      const int64_t tiles = nvt - vt0 < p.ptiles ? nvt - vt0 : p.ptiles;
+      trace_begin(p, GRPO_TRACE_RECOMPUTE, st);
+      hipLaunchKernelGGL((recompute_kernel<E, G>), dim3((unsigned)(ntt * tiles)),
+                         dim3(kThreads), 0, st, p.N, p.H, p.V, p.pt_ld, vt0, c0, ntt, p.scale2,
+                         1, ntok, idx, Xop, Wop, targets, saved, Tb,
+                         (const float*)ws_ptr<float>(ws, p.off_sw),
+                         (const float*)ws_ptr<float>(ws, p.off_sxq));
+      trace_end(p, GRPO_TRACE_RECOMPUTE, st);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = piece_dx<E>(p, ws, c0, j, W, found_inf, st, nullptr, true)) != hipSuccess)
+        return e;
+    }
+    e = split_dx_final<E>(p, ws, c0, W, targets, saved, grad_loss, loss_scale, nullptr, dX,
+                          found_inf, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Single pass with the vocabulary split (no dW).  The reference side runs over all rows;
+// then per chunk, piece by piece, the policy forward keeps the piece's terms against the
+// row's reference log-sum-exp (target entry 0) and dX sums them; the chunk's merge then
+// knows each row's log-sum-exp, and dx_final_kernel applies the row factor and adds the
+// target's term.  A chunk whose merge finds a row outside the window redoes it: the
+// policy forward over the chunk's rows without kept terms (a robust log-sum-exp), the
+// merge again, and the pieces once more against that log-sum-exp, whose terms are then
+// the softmax itself (these launches exit at once when the chunk's flag is clear).
+template <class E, class G>
+hipError_t fused_split_impl(const Plan& p, void* ws, const void* Xq, const void* Xp,
+                            const void* W, const int64_t* targets, const uint8_t* mask,
+                            const float* adv, float beta, float* saved, float* logp,
+                            float* ref_logp, float* kl, int32_t* status, float* loss,
+                            const float* grad_loss, float loss_scale, void* dX,
+                            int32_t* found_inf, hipStream_t st) {
+  typedef typename E::T T;
+  T* Tb = ws_ptr<T>(ws, p.off_T);
+  float* pm = ws_ptr<float>(ws, p.off_pm);
+  int32_t* redo = ws_ptr<int32_t>(ws, p.off_redo);
+  const int64_t nvt = p.Vpad / 256;
+  const int nchunks = (int)((p.N + p.R - 1) / p.R);
+  hipError_t e = launch_zero_masked_outputs(p, mask, saved, logp, ref_logp, kl, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((nchunks + 255) / 256)), dim3(256), 0, st,
+                     redo, nchunks, 0);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (G::kBytes == 1 && (e = quantize_operands(p, ws, Xq, Xp, W, st)) != hipSuccess) return e;
+  FwdArgs a = fwd_args(p, ws, Xq, Xp, W, targets);
+  a.side0 = 1;
+  a.nsides = 1;
+  trace_begin(p, GRPO_TRACE_FWD_ALL, st);
+  hipLaunchKernelGGL((fwd_kernel<E, G, 1>), dim3(kNumWG), dim3(kThreads), 0, st, a);
+  trace_end(p, GRPO_TRACE_FWD_ALL, st);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  for (int64_t c0 = 0, ci = 0; c0 < p.N; c0 += p.R, ++ci) {
+    int32_t* rd = redo + ci;
+    FwdArgs c = a;
+    c.row_lo = c0;
+    c.row_hi = c0 + p.R;
+    c.side0 = 0;
+    c.part = ws_ptr<float>(ws, p.off_cpart);
+    c.pt = reinterpret_cast<char*>(Tb);
+    c.pm = pm;
+    c.npieces = p.npieces;
+    c.ptiles = p.ptiles;
+    c.zero_target = 1;
+    for (int j = 0; j < p.npieces; ++j) {
+      c.piece = j;
+      trace_begin(p, GRPO_TRACE_FWD_CHUNK, st);
+      hipLaunchKernelGGL((fwd_kernel<E, G, 3>), dim3(kNumWG), dim3(kThreads), 0, st, c);
+      trace_end(p, GRPO_TRACE_FWD_CHUNK, st);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = piece_dx<E>(p, ws, c0, j, W, found_inf, st, nullptr, true)) != hipSuccess)
+        return e;
+    }
+    e = launch_merge_rows(p, ws, c0, targets, mask, adv, beta, saved, logp, ref_logp, kl,
+                          status, st, rd, nullptr, nullptr, p.ptiles, p.npieces);
+    if (e != hipSuccess) return e;
+    // fallback, gated on the chunk's flag: a robust policy sweep, its merge, the pieces
+    FwdArgs f = c;
+    f.gate = rd;
+    f.piece = 0;
+    f.npieces = 1;
+    f.ptiles = nvt;
+    f.pt = nullptr;
+    f.zero_target = 0;
+    hipLaunchKernelGGL((fwd_kernel<E, G, 1>), dim3(kNumWG), dim3(kThreads), 0, st, f);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    e = launch_merge_rows(p, ws, c0, targets, mask, adv, beta, saved, logp, ref_logp, kl,
+                          status, st, nullptr, nullptr, rd, nvt, 1);
+    if (e != hipSuccess) return e;
+    c.gate = rd;
+    c.ref_from_saved = 1;
+    c.saved = saved;
+    for (int j = 0; j < p.npieces; ++j) {
+      c.piece = j;
+      hipLaunchKernelGGL((fwd_kernel<E, G, 3>), dim3(kNumWG), dim3(kThreads), 0, st, c);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = piece_dx<E>(p, ws, c0, j, W, found_inf, st, rd, false)) != hipSuccess) return e;
+    }
+    e = split_dx_final<E>(p, ws, c0, W, targets, saved, grad_loss, loss_scale, pm, dX,
+                          found_inf, st);
+    if (e != hipSuccess) return e;
+  }
+  return launch_loss_final(p, ws, 1, status, loss, st);
+}
+
 }  // namespace
 
 hipError_t mfma_fwd_partials(const Plan& p, void* ws, const void* Xq, const void* Xp,
@@ -1534,8 +1918,12 @@ hipError_t mfma_fused(const Plan& p, void* ws, const void* Xq, const void* Xp, c
                       float* loss, const float* grad_loss, float loss_scale, void* dX, float* dW,
                       int accumulate_dW, int32_t* found_inf, hipStream_t st) {
 #define GRPO_FUSED(E, G)                                                                       \
-  fused_impl<E, G>(p, ws, Xq, Xp, W, targets, mask, adv, beta, saved, logp, ref_logp, kl,     \
-                   status, loss, grad_loss, loss_scale, dX, dW, accumulate_dW, found_inf, st)
+  (p.vsplit ? fused_split_impl<E, G>(p, ws, Xq, Xp, W, targets, mask, adv, beta, saved, logp, \
+                                     ref_logp, kl, status, loss, grad_loss, loss_scale, dX,    \
+                                     found_inf, st)                                            \
+            : fused_impl<E, G>(p, ws, Xq, Xp, W, targets, mask, adv, beta, saved, logp,        \
+                               ref_logp, kl, status, loss, grad_loss, loss_scale, dX, dW,       \
+                               accumulate_dW, found_inf, st))
   if (p.dtype == GRPO_BF16) return p.fp8 ? GRPO_FUSED(BF16T, FP8T) : GRPO_FUSED(BF16T, BF16T);
   return p.fp8 ? GRPO_FUSED(F16T, FP8T) : GRPO_FUSED(F16T, F16T);
 #undef GRPO_FUSED
@@ -1546,8 +1934,10 @@ hipError_t mfma_backward(const Plan& p, void* ws, const void* Xq, const void* W,
                          float loss_scale, void* dX, float* dW, int accumulate_dW,
                          int32_t* found_inf, hipStream_t st) {
 #define GRPO_BWD(E, G)                                                                         \
-  bwd_impl<E, G>(p, ws, Xq, W, targets, saved, grad_loss, loss_scale, dX, dW, accumulate_dW,  \
-                 found_inf, st)
+  (p.vsplit ? bwd_split_impl<E, G>(p, ws, Xq, W, targets, saved, grad_loss, loss_scale, dX,   \
+                                   found_inf, st)                                              \
+            : bwd_impl<E, G>(p, ws, Xq, W, targets, saved, grad_loss, loss_scale, dX, dW,      \
+                             accumulate_dW, found_inf, st))
   if (p.dtype == GRPO_BF16) return p.fp8 ? GRPO_BWD(BF16T, FP8T) : GRPO_BWD(BF16T, BF16T);
   return p.fp8 ? GRPO_BWD(F16T, FP8T) : GRPO_BWD(F16T, F16T);
 #undef GRPO_BWD

@@ -87,6 +87,17 @@ typedef enum grpo_normalization {
   GRPO_NORM_SEQUENCES = 1 /* loss = mean over sequences with tokens of their token means     */
 } grpo_normalization;
 
+/* Kernels whose launches grpo_options.trace_kernel can bracket with events. */
+typedef enum grpo_trace_kernel {
+  GRPO_TRACE_NONE = 0,
+  GRPO_TRACE_FWD_ALL = 1,   /* the forward GEMM over all loss rows: both sides (grpo_loss_fwd)
+                               or the reference side (grpo_loss_fwd_bwd)                     */
+  GRPO_TRACE_FWD_CHUNK = 2, /* single pass: one chunk's policy forward that keeps its terms  */
+  GRPO_TRACE_RECOMPUTE = 3, /* two-pass backward: one chunk's onehot - softmax               */
+  GRPO_TRACE_DX = 4,        /* one chunk's dX GEMM                                            */
+  GRPO_TRACE_DW = 5         /* one chunk's dW GEMM                                            */
+} grpo_trace_kernel;
+
 typedef struct grpo_options {
   int kl_estimator;       /* grpo_kl_estimator                                             */
   int detach_ratio;       /* 1: advantage times exp(q - sg(q)) (value 1, gradient A dq);
@@ -102,6 +113,23 @@ typedef struct grpo_options {
                              16-bit entries, so this trades workspace for speed (fewer,
                              larger GEMM launches); results do not depend on it beyond
                              fp32 summation order.  Needs grpo_workspace_bytes_opts.      */
+  int vocab_piece;        /* vocabulary entries per piece of a chunk's softmax terms when the
+                             backward is split over the vocabulary (16-bit inputs on the
+                             MFMA kernels, except grpo_loss_fwd_bwd with dW): 0 = about
+                             32768 (pieces balanced over V); else a multiple of 256.  The
+                             workspace holds one chunk of rows x one piece, plus fp32 dX
+                             sums of one chunk.  Needs grpo_workspace_bytes_opts.          */
+  /* Timing of one kernel as launched inside a call (16-bit MFMA path; the fp32 kernels are
+   * not bracketed).  trace_events: hipEvent_t[2 * trace_capacity], created by the caller
+   * with timing enabled; the library records events 2i and 2i + 1 on the call's stream
+   * just before and just after the i-th launch of the kernel named by trace_kernel (the
+   * gated fallback launches excepted), up to trace_capacity launches, and stores the
+   * number of such launches in *trace_count (host memory, written before the call returns;
+   * may be NULL).  trace_kernel 0 records nothing.                                        */
+  int trace_kernel;       /* grpo_trace_kernel                                             */
+  int trace_capacity;
+  void* const* trace_events;
+  int* trace_count;
 } grpo_options;
 
 /* Bits of the forward's status word. */
@@ -146,7 +174,7 @@ int grpo_advantages(const float* rewards, int64_t B, int64_t G, int64_t K, float
                     int unbiased, float* adv, grpo_stream_t stream);
 
 /* Defaults: reverse estimator, detached ratio, token mean, temperature 1, 16-bit logits,
- * chunks of 4096 rows. */
+ * chunks of 4096 rows, no tracing. */
 void grpo_default_options(grpo_options* opts);
 
 /* Forward: loss and per-token terms, without materialising logits

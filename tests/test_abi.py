@@ -56,20 +56,28 @@ def test_workspace_bytes(lib):
 
 
 def test_workspace_follows_chunk_rows(lib):
-    """The chunk of rows x V entries dominates the workspace; chunk_rows sets it."""
+    """Without dW the backward is split over the vocabulary: the chunk buffer holds one
+    chunk of rows x one piece of about 32768 entries (chunk_rows and vocab_piece set
+    them), plus the chunk's fp32 dX sums; the headline shape stays under 0.5 GiB.  With
+    dW the single pass keeps one chunk of rows x the whole vocabulary."""
     import grpo_loss_amd as g
     f = lib.grpo_workspace_bytes_opts
     shape = (8, 20480, 4096, 128256, 1, 0)
     default = f(*shape, None)
     assert default == lib.grpo_workspace_bytes(*shape)
+    assert default < 0.5 * 2 ** 30
     assert f(*shape, ctypes.byref(g.options(chunk_rows=4096))) == default
-    small = f(*shape, ctypes.byref(g.options(chunk_rows=2048)))
+    assert f(*shape, ctypes.byref(g.options(vocab_piece=32768))) == default  # 4 x 126 tiles
+    # 501 tiles in pieces of at most 64 tiles: 8 pieces of 63 tiles (16128 entries)
+    half = f(*shape, ctypes.byref(g.options(vocab_piece=16384)))
+    assert default - half >= 0.95 * 4096 * (32256 - 16128) * 2   # (more partial slots)
     big = f(*shape, ctypes.byref(g.options(chunk_rows=8192)))
-    chunk = 2048 * 128256 * 2          # bf16 entries of 2048 more rows
-    # (the smaller chunk splits dX over V and adds 64 MB of fp32 partials)
-    assert default - small >= 0.85 * chunk and big - default >= chunk
-    assert small < 0.7 * 2 ** 30       # 0.67 GiB at the headline shape
+    assert big - default >= 4096 * 32256 * 2 + 4096 * 4096 * 4     # terms + dX sums
+    # with dW: one chunk of rows x the padded vocabulary
+    train = lib.grpo_workspace_bytes(8, 4096, 4096, 128256, 1, 1)
+    assert train >= 4096 * 128256 * 2
     assert f(*shape, ctypes.byref(g.options(chunk_rows=300))) == 0
+    assert f(*shape, ctypes.byref(g.options(vocab_piece=100))) == 0
 
 
 def test_bad_arguments_rejected_before_launch(lib):
@@ -185,3 +193,39 @@ def test_fp8_options_and_quantizer_arguments(lib):
     assert lib.grpo_quantize_e4m3(p, 1, 4, 62, p, p, nul) == -2
     assert lib.grpo_quantize_e4m3(p, 5, 4, 64, p, p, nul) == -3
     assert lib.grpo_quantize_e4m3(p, 1, 4, 64, ctypes.c_void_p(17), p, nul) == -4
+
+
+def test_trace_options_validated(lib):
+    """Kernel tracing: an unknown kernel, a negative capacity, or events missing for a
+    positive capacity are option errors, raised before any launch."""
+    import grpo_loss_amd as g
+    p = ctypes.c_void_p(16)
+    nul = None
+    for kernel, cap, with_events in ((6, 0, False), (-1, 0, False), (1, -1, False),
+                                     (1, 4, False)):
+        o = g.options()
+        o.trace_kernel, o.trace_capacity = kernel, cap
+        if with_events:
+            o.trace_events = (ctypes.c_void_p * 8)()
+        rc = lib.grpo_loss_fwd(p, p, p, 1, p, p, p, 2, 3, 64, 5, ctypes.c_float(0.04), p, p,
+                               nul, nul, nul, p, ctypes.byref(o), p, ctypes.c_size_t(1 << 40),
+                               nul)
+        assert rc == -8, (kernel, cap)
+    d = g.GRPOOptions()
+    lib.grpo_default_options(ctypes.byref(d))
+    assert (d.trace_kernel, d.trace_capacity) == (0, 0) and not d.trace_events
+
+
+def test_noalloc_rejects_before_launch(lib):
+    """grpo_loss_fwd_noalloc validates like grpo_loss_fwd and rejects a forward larger than
+    its fixed array with GRPO_ERR_SCRATCH, all before touching a device."""
+    p = ctypes.c_void_p(256)
+    nul = None
+    f = ctypes.c_float(0.04)
+    assert lib.grpo_loss_fwd_noalloc(nul, p, p, 1, p, p, p, 2, 3, 64, 5, f, p, p, nul, nul,
+                                     nul, p, nul, nul) == -1
+    assert lib.grpo_loss_fwd_noalloc(p, p, p, 1, p, p, p, 2, 3, 96, 5, f, p, p, nul, nul, nul,
+                                     p, nul, nul) == -2
+    # the long-context forward: 118 MB of partials, past the 64 MiB array
+    assert lib.grpo_loss_fwd_noalloc(p, p, p, 1, p, p, p, 8, 20480, 4096, 128256, f, p, p,
+                                     nul, nul, nul, p, nul, nul) == -9

@@ -38,7 +38,7 @@ def _say(msg):
 
 
 def run_gpu(wl, inp, need_dW=None, grad_scale=True, variant=None, single_pass=False,
-            chunk_rows=0):
+            chunk_rows=0, vocab_piece=0):
     """advantages -> forward -> backward on the device (grpo_loss_fwd then grpo_loss_bwd,
     or grpo_loss_fwd_bwd when single_pass); host copies of every output.
     variant: an oracle.Variant whose fields name the same options for the library;
@@ -47,9 +47,9 @@ def run_gpu(wl, inp, need_dW=None, grad_scale=True, variant=None, single_pass=Fa
     d = to_device(inp)
     need_dW = wl.need_dW if need_dW is None else need_dW
     opts = None
-    if variant is not None or chunk_rows:
+    if variant is not None or chunk_rows or vocab_piece:
         fields = {} if variant is None else dataclasses.asdict(variant)
-        opts = g.options(**fields, chunk_rows=chunk_rows)
+        opts = g.options(**fields, chunk_rows=chunk_rows, vocab_piece=vocab_piece)
     adv = g.grpo_advantages(d["rewards"], wl.eps)
     S = wl.loss_scale
     grad = torch.full((1,), S, dtype=torch.float32, device="cuda")
@@ -87,8 +87,9 @@ SMALL = {
 }
 
 
-def check_small(wl, inp, variant=None, single_pass=False, chunk_rows=0):
-    gpu = run_gpu(wl, inp, variant=variant, single_pass=single_pass, chunk_rows=chunk_rows)
+def check_small(wl, inp, variant=None, single_pass=False, chunk_rows=0, vocab_piece=0):
+    gpu = run_gpu(wl, inp, variant=variant, single_pass=single_pass, chunk_rows=chunk_rows,
+                  vocab_piece=vocab_piece)
     variant = oracle.DEFAULT if variant is None else variant
     adv = oracle.group_advantages(inp.rewards.numpy(), wl.eps)
     assert np.array_equal(gpu["adv"].view(np.uint32), adv.view(np.uint32)), (gpu["adv"], adv)
@@ -209,8 +210,23 @@ def test_single_pass_fixed_reference_matches_two_pass():
     assert np.all(b["dX"][~m] == 0.0)
 
 
+@pytest.mark.parametrize("single_pass", [False, True], ids=["two-pass", "single-pass"])
+@pytest.mark.parametrize("V,piece", [(5003, 768), (5003, 1024), (151936, 32768)])
+def test_vocab_pieces_parity(V, piece, single_pass):
+    """The backward split over the vocabulary: pieces of 3 or 4 tiles over a prime
+    vocabulary of 20 tiles (the last piece ragged, two of them shorter than the others),
+    and the default-sized pieces of a 594-tile vocabulary, over two chunks of rows; the
+    target of a row falls in every piece.  Against the oracle."""
+    wl = dataclasses.replace(workload_by_name("qwen2.5-1.5b-bf16"), G=4, L=160, H=512, V=V,
+                             prefix=8, comp_min=120, comp_max=150)
+    inp = generate(wl)
+    _say(f"[vocab pieces] V={V} piece={piece} single_pass={single_pass}")
+    check_small(wl, inp, single_pass=single_pass, vocab_piece=piece, chunk_rows=256)
+
+
 @pytest.mark.parametrize("side", ["reference", "policy"])
-def test_single_pass_far_reference(side):
+@pytest.mark.parametrize("piece", [0, 768])
+def test_single_pass_far_reference(side, piece):
     """Rows whose policy and reference log-sum-exp lie far apart (one side's hidden states
     scaled by 32, about 110 nats apart): terms taken against the reference would overflow
     or drop most of their mass, so the chunk is redone with running maxima, and the
@@ -224,8 +240,8 @@ def test_single_pass_far_reference(side):
     else:
         inp = dataclasses.replace(inp, xq=inp.xq * 32)
     variant = oracle.Variant(kl="forward") if side == "policy" else None
-    _say(f"[far reference] {side} side scaled by 32, S={wl.S} L={wl.L}")
-    check_small(wl, inp, variant=variant, single_pass=True)
+    _say(f"[far reference] {side} side scaled by 32, S={wl.S} L={wl.L} piece={piece}")
+    check_small(wl, inp, variant=variant, single_pass=True, vocab_piece=piece)
 
 
 @pytest.mark.parametrize("side,scale,kl", [("xp", 2.0, "reverse"), ("xq", 1.5, "reverse"),
@@ -901,3 +917,33 @@ def test_fp8_nonfinite_row_flagged():
     inp.xq[lrow, 11] = float("inf")
     out = run_gpu(wl, inp, single_pass=True, variant=FP8)
     assert out["status"] & 1
+
+
+@pytest.mark.parametrize("kernel", ["fwd_all", "fwd_chunk", "dx", "dw"])
+def test_kernel_trace_brackets_launches(kernel):
+    """grpo_options' kernel tracing: one event pair per launch of the named kernel (one
+    reference forward, one policy forward, dX and dW per chunk of rows), positive
+    durations, and results bit-identical to an untraced call."""
+    g = _lib()
+    wl = dataclasses.replace(workload_by_name("llama3.1-8b-train-bf16"), G=4, L=768, H=1024,
+                             prefix=16, comp_min=600, comp_max=700)
+    inp = generate(wl)
+    d = to_device(inp)
+    adv = g.grpo_advantages(d["rewards"], wl.eps)
+    ref = g.grpo_loss_fwd_bwd(d["xq"], d["xp"], d["W"], d["targets"], d["mask"], adv, wl.beta,
+                              wl.L, need_dW=True, opts=g.options(chunk_rows=1024))
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(16)]
+    for e in evs:
+        e.record()
+    tr = g.KernelTrace(kernel, evs)
+    o = tr.attach(g.options(chunk_rows=1024))
+    got = g.grpo_loss_fwd_bwd(d["xq"], d["xp"], d["W"], d["targets"], d["mask"], adv, wl.beta,
+                              wl.L, need_dW=True, opts=o)
+    torch.cuda.synchronize()
+    n_chunks = -(-wl.N // 1024)
+    expect = 1 if kernel == "fwd_all" else n_chunks
+    ms = tr.launch_ms()
+    _say(f"[trace] {kernel}: {tr.count.value} launches, ms {np.round(ms, 3).tolist()}")
+    assert tr.count.value == expect and len(ms) == expect and all(t > 0 for t in ms)
+    for k in ("loss", "dXq", "dW", "saved"):
+        assert torch.equal(ref[k], got[k]), k
