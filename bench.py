@@ -54,6 +54,8 @@ def parse():
                     help="rows per backward chunk of an extra single-pass leg that trades "
                          "speed for workspace (0: no such leg)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-offload", action="store_true",
+                    help="skip the single-pass leg with the gradients offloaded to host memory")
     ap.add_argument("--no-trace", action="store_true",
                     help="no kernel event brackets (no roofline block)")
     ap.add_argument("--cpu-rows", type=int, default=256, help="oracle rows per sequence")
@@ -343,6 +345,54 @@ def main():
             "workspace_gib": wsc_bytes / 2 ** 30, "status": int(f["status"].item())}
         f = None
         opts["v"] = None
+    if not args.no_offload and args.path == "single":
+        # the single pass with its gradients kept in pinned host memory between forward and
+        # backward: each chunk's dX rows are copied out on a second stream while the next
+        # chunks compute, and grpo_grad_restore brings them back (a host-to-device copy the
+        # step waits for).  Reported beside the default, never as `value`.
+        del ws
+        torch.cuda.empty_cache()
+        cs = g.offload_stream()
+        dx_host = torch.empty(wl.N, wl.H, dtype=dt, pin_memory=True)
+        dw_host = (torch.empty(wl.V, wl.H, dtype=torch.float32, pin_memory=True) if need_dW
+                   else None)
+        oo = g.options()
+        oo.dx_host, oo.copy_stream = dx_host.data_ptr(), cs.cuda_stream
+        wso_bytes = g.grpo_workspace_bytes(wl.S, wl.L, wl.H, wl.V, dt, need_dW, oo)
+        ws = torch.empty(wso_bytes, dtype=torch.uint8, device="cuda")
+        rws = torch.empty(g.grpo_restore_workspace_bytes(wl.N, wl.H, dt), dtype=torch.uint8,
+                          device="cuda")
+
+        def step_offload_fwd(step_no):
+            g.grpo_advantages(d["rewards"], wl.eps, out=adv)
+            return g.grpo_loss_fwd_bwd(d["xq"], d["xp"], d["W"], d["targets"], d["mask"], adv,
+                                       wl.beta, wl.L, grad, wl.loss_scale, dW=dW,
+                                       found_inf=found, workspace=ws, want_terms=False,
+                                       dx_host=dx_host, dw_host=dw_host, copy_stream=cs)
+
+        def step_offload(step_no):
+            f = step_offload_fwd(step_no)
+            g.grpo_grad_restore(d["mask"], dx_host, dw_host, None, 1.0, dXq=dX, dW=dW,
+                                found_inf=found, copy_stream=cs, workspace=rws)
+            return f
+
+        ms_fwd, f = timed(step_offload_fwd)
+        ms, f = timed(step_offload)
+        single_ms = legs["single"]["ms_per_step"]
+        held = wl.N * wl.H * d["xq"].element_size() + (wl.V * wl.H * 4 if need_dW else 0)
+        ring = wso_bytes - g.grpo_workspace_bytes(wl.S, wl.L, wl.H, wl.V, dt, need_dW)
+        out["offload"] = {
+            "value": n_tok / (ms * 1e-3), "ms_per_step": ms,
+            "fwd_bwd_ms": ms_fwd, "restore_ms": ms - ms_fwd,
+            "step_overhead_frac": ms / single_ms - 1.0,
+            "fwd_bwd_overhead_frac": ms_fwd / single_ms - 1.0,
+            "held_device_gib_saved": (held - ring) / 2 ** 30,
+            "host_gib": held / 2 ** 30, "status": int(f["status"].item()),
+            "found_inf": int(found.item())}
+        f = None
+        del ws, rws, dx_host, dw_host
+        torch.cuda.empty_cache()
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     if not args.no_fp8 and dtn != "f32":
         # the same single-pass step with both sides' logits from per-row e4m3 copies (a
         # lower-precision variant, reported beside the 16-bit result, never as `value`)

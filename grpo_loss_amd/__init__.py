@@ -17,15 +17,18 @@ from ._binding import (  # noqa: F401
     KernelTrace,
     TRACE_KERNELS,
     grpo_advantages,
+    grpo_grad_restore,
     grpo_loss,
     grpo_loss_bwd,
     grpo_loss_fwd,
     grpo_loss_fwd_bwd,
     grpo_loss_fwd_noalloc,
     grpo_quantize_e4m3,
+    grpo_restore_workspace_bytes,
     grpo_scale_grad,
     grpo_workspace_bytes,
     library_path,
     load_library,
+    offload_stream,
     options,
 )

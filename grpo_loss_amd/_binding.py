@@ -28,7 +28,9 @@ class GRPOOptions(ctypes.Structure):
                 ("vocab_piece", ctypes.c_int),
                 ("trace_kernel", ctypes.c_int), ("trace_capacity", ctypes.c_int),
                 ("trace_events", ctypes.POINTER(ctypes.c_void_p)),
-                ("trace_count", ctypes.POINTER(ctypes.c_int))]
+                ("trace_count", ctypes.POINTER(ctypes.c_int)),
+                ("dx_host", ctypes.c_void_p), ("dw_host", ctypes.c_void_p),
+                ("copy_stream", ctypes.c_void_p)]
 
 
 TRACE_KERNELS = {"none": 0, "fwd_all": 1, "fwd_chunk": 2, "recompute": 3, "dx": 4, "dw": 5}
@@ -84,6 +86,38 @@ def _opts(o):
     return None if o is None else ctypes.byref(o)
 
 
+def _copy_options(o) -> GRPOOptions:
+    """A separate GRPOOptions holding o's fields (the library's defaults for None)."""
+    o = _as_options(o)
+    c = GRPOOptions()
+    if o is None:
+        _LIB.grpo_default_options(ctypes.byref(c))
+    else:
+        ctypes.memmove(ctypes.byref(c), ctypes.byref(o), ctypes.sizeof(c))
+    return c
+
+
+_COPY_STREAMS = {}
+
+
+def offload_stream(device=None) -> torch.cuda.Stream:
+    """The stream the gradient offload copies on, one per device, created with the
+    default priority (as every stream here is)."""
+    dev = torch.device("cuda", torch.cuda.current_device() if device is None
+                       else torch.device(device).index or 0)
+    s = _COPY_STREAMS.get(dev.index)
+    if s is None:
+        s = _COPY_STREAMS[dev.index] = torch.cuda.Stream(device=dev)
+    return s
+
+
+def _need_host(t: torch.Tensor, name: str, dtype, shape):
+    if t.is_cuda or not t.is_pinned():
+        raise ValueError(f"{name} must be pinned host memory (pin_memory=True)")
+    if not t.is_contiguous() or t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+
+
 def library_path() -> str:
     return os.path.join(_HERE, "libgrpo.so")
 
@@ -133,6 +167,12 @@ def load_library():
     lib.grpo_scale_grad.restype = ctypes.c_int
     lib.grpo_scale_grad.argtypes = [_c_p, ctypes.c_int, _c_i64, _c_i64, _c_p, _c_i64, _c_p,
                                     ctypes.c_float, _c_p, _c_p]
+    lib.grpo_restore_workspace_bytes.restype = ctypes.c_size_t
+    lib.grpo_restore_workspace_bytes.argtypes = [_c_i64, _c_i64, _c_i64, ctypes.c_int, opt_p]
+    lib.grpo_grad_restore.restype = ctypes.c_int
+    lib.grpo_grad_restore.argtypes = [_c_p, _c_p, ctypes.c_int, _c_p, _c_i64, _c_i64, _c_i64,
+                                      _c_i64, _c_p, ctypes.c_float, _c_p, _c_p, _c_p, opt_p,
+                                      _c_p, ctypes.c_size_t, _c_p]
     _LIB = lib
     return lib
 
@@ -318,10 +358,17 @@ def grpo_loss_fwd_bwd(xq, xp, W, targets, mask, adv, beta: float = 0.04, L: int 
                       dW: torch.Tensor | None = None, accumulate_dW: bool = False,
                       found_inf: torch.Tensor | None = None,
                       workspace: torch.Tensor | None = None, dXq: torch.Tensor | None = None,
-                      want_terms: bool = True, stream=None, opts=None):
+                      want_terms: bool = True, stream=None, opts=None,
+                      dx_host: torch.Tensor | None = None, dw_host: torch.Tensor | None = None,
+                      copy_stream=None):
     """Forward and backward in one call (the policy logits are computed once).  Returns
     dict(loss, saved, logp, ref_logp, kl, status, dXq, dW (or None), found_inf,
-    workspace)."""
+    workspace).
+
+    Gradient offload: dx_host (pinned host [S*L, H] in X's dtype) receives dX in loss-row
+    order instead of a device dXq (returned as None), dw_host (pinned host [V, H] fp32)
+    receives dW; both are copied on copy_stream (default: offload_stream()) while later
+    chunks compute.  grpo_grad_restore brings them back."""
     for t, n in ((xq, "xq"), (xp, "xp"), (W, "W"), (targets, "targets"), (mask, "mask"),
                  (adv, "adv")):
         _need(t, n)
@@ -334,7 +381,19 @@ def grpo_loss_fwd_bwd(xq, xp, W, targets, mask, adv, beta: float = 0.04, L: int 
         raise TypeError("targets int64, mask uint8, adv float32 expected")
     dev = xq.device
     N = S * L
-    need_dW = need_dW or dW is not None
+    need_dW = need_dW or dW is not None or dw_host is not None
+    if dx_host is not None or dw_host is not None:
+        opts = _copy_options(opts)
+        cs = offload_stream(dev) if copy_stream is None else copy_stream
+        opts.copy_stream = cs.cuda_stream
+        if dx_host is not None:
+            if dXq is not None:
+                raise ValueError("dXq and dx_host are exclusive")
+            _need_host(dx_host, "dx_host", xq.dtype, (N, H))
+            opts.dx_host = dx_host.data_ptr()
+        if dw_host is not None:
+            _need_host(dw_host, "dw_host", torch.float32, (V, H))
+            opts.dw_host = dw_host.data_ptr()
     need = grpo_workspace_bytes(S, L, H, V, xq.dtype, need_dW, opts)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -343,7 +402,7 @@ def grpo_loss_fwd_bwd(xq, xp, W, targets, mask, adv, beta: float = 0.04, L: int 
     saved = torch.empty(N, 4, **f32)
     terms = [torch.empty(N, **f32) for _ in range(3)] if want_terms else [None] * 3
     status = torch.empty(1, dtype=torch.int32, device=dev)
-    if dXq is None:
+    if dXq is None and dx_host is None:
         dXq = torch.empty_like(xq)
     if need_dW and dW is None:
         dW = torch.empty(V, H, **f32)
@@ -361,6 +420,81 @@ def grpo_loss_fwd_bwd(xq, xp, W, targets, mask, adv, beta: float = 0.04, L: int 
     return {"loss": loss, "saved": saved, "logp": terms[0], "ref_logp": terms[1],
             "kl": terms[2], "status": status, "dXq": dXq, "dW": dW if need_dW else None,
             "found_inf": found_inf, "workspace": workspace}
+
+
+def grpo_restore_workspace_bytes(N: int, H: int, dtype: torch.dtype, opts=None) -> int:
+    return int(_LIB.grpo_restore_workspace_bytes(1, N, H, _DTYPE[dtype], _opts(opts)))
+
+
+def grpo_grad_restore(mask, dx_host=None, dw_host=None, grad_loss=None, loss_scale: float = 1.0,
+                      dXq=None, dW=None, found_inf=None, copy_stream=None, workspace=None,
+                      stream=None, opts=None):
+    """The way back of the gradient offload: dXq [S*L, H] (device, X's dtype; masked rows
+    0) from dx_host, and dW [V, H] fp32 from dw_host, both times grad_loss / loss_scale as
+    grpo_scale_grad applies it.  Returns dict(dXq, dW, found_inf).  The host tensors must
+    outlive the copies: they are ordered before any work enqueued on `stream` after this
+    call."""
+    _need(mask, "mask")
+    if dx_host is None and dw_host is None:
+        raise ValueError("nothing to restore")
+    N = mask.numel()
+    dev = mask.device
+    o = _copy_options(opts)
+    cs = offload_stream(dev) if copy_stream is None else copy_stream
+    o.copy_stream = cs.cuda_stream
+    H = (dx_host if dx_host is not None else dw_host).shape[1]
+    V = dw_host.shape[0] if dw_host is not None else 0
+    if dx_host is not None:
+        _need_host(dx_host, "dx_host", dx_host.dtype, (N, H))
+        if dXq is None:
+            dXq = torch.empty(N, H, dtype=dx_host.dtype, device=dev)
+        _need(dXq, "dXq")
+    if dw_host is not None:
+        _need_host(dw_host, "dw_host", torch.float32, (V, H))
+        if dW is None:
+            dW = torch.empty(V, H, dtype=torch.float32, device=dev)
+        _need(dW, "dW")
+    dtype = (dx_host if dx_host is not None else dw_host).dtype
+    if found_inf is None:
+        found_inf = torch.zeros(1, dtype=torch.int32, device=dev)
+    if grad_loss is not None:
+        _need(grad_loss, "grad_loss")
+    need = int(_LIB.grpo_restore_workspace_bytes(1, N, H, _DTYPE[dtype], ctypes.byref(o)))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(_LIB.grpo_grad_restore(_ptr(dx_host), _ptr(dw_host), _DTYPE[dtype], _ptr(mask), 1, N,
+                                  H, V, _ptr(grad_loss), float(loss_scale),
+                                  _ptr(dXq) if dx_host is not None else None,
+                                  _ptr(dW) if dw_host is not None else None, _ptr(found_inf),
+                                  ctypes.byref(o), _ptr(workspace), workspace.numel(),
+                                  _stream(stream)))
+    return {"dXq": dXq if dx_host is not None else None,
+            "dW": dW if dw_host is not None else None, "found_inf": found_inf}
+
+
+class _PinnedPool:
+    """Pinned host buffers of the autograd offload, reused across steps.  A buffer is out
+    from the forward that fills it until its restore is enqueued; the copies that touch it
+    all run on the device's one offload stream, in order, so a later forward's copies into
+    a returned buffer follow the restore's copies out of it."""
+
+    def __init__(self):
+        self._free = {}
+
+    def take(self, shape, dtype, device):
+        key = (tuple(shape), dtype, torch.device(device).index)
+        lst = self._free.get(key)
+        if lst:
+            return lst.pop()
+        return torch.empty(shape, dtype=dtype, pin_memory=True)
+
+    def give(self, t, device):
+        if t is not None:
+            self._free.setdefault((tuple(t.shape), t.dtype, torch.device(device).index),
+                                  []).append(t)
+
+
+_PINNED = _PinnedPool()
 
 
 def grpo_scale_grad(dXq, grad_loss, loss_scale: float = 1.0, dW=None, found_inf=None,
@@ -386,16 +520,33 @@ def grpo_scale_grad(dXq, grad_loss, loss_scale: float = 1.0, dW=None, found_inf=
 class _GRPOLoss(torch.autograd.Function):
     @staticmethod
     def forward(ctx, xq, xp, W, targets, mask, adv, beta, L, loss_scale, need_dW, opts,
-                single_pass):
+                single_pass, offload, grad_hint):
         ctx.L, ctx.loss_scale, ctx.need_dW, ctx.opts = L, loss_scale, need_dW, opts
-        ctx.single_pass = single_pass
+        ctx.single_pass, ctx.offload = single_pass, offload
         ctx.w_dtype = W.dtype
         if single_pass:
-            # gradients for an upstream gradient of 1 now; backward only rescales them
-            out = grpo_loss_fwd_bwd(xq, xp, W, targets, mask, adv, beta, L, None, 1.0,
-                                    need_dW=need_dW and ctx.needs_input_grad[2],
-                                    want_terms=False, opts=opts)
-            ctx.grads = (out["dXq"], out["dW"], out["found_inf"])
+            # the gradients now, for an upstream gradient of grad_hint: they are narrowed to
+            # X's dtype with it applied, and the backward multiplies them by
+            # grad / grad_hint, exactly 1 when the hint was right
+            ctx.hint = float(loss_scale if grad_hint is None else grad_hint)
+            want_dW = need_dW and ctx.needs_input_grad[2]
+            dev = xq.device
+            host = {}
+            if offload:
+                N, H = targets.numel(), xq.shape[-1]
+                host["dx_host"] = _PINNED.take((N, H), xq.dtype, dev)
+                if want_dW:
+                    host["dw_host"] = _PINNED.take((W.shape[0], H), torch.float32, dev)
+            hint = torch.full((1,), ctx.hint, dtype=torch.float32, device=dev)
+            out = grpo_loss_fwd_bwd(xq, xp, W, targets, mask, adv, beta, L, hint, loss_scale,
+                                    need_dW=want_dW, want_terms=False, opts=opts, **host)
+            if offload:
+                # device dX was never written and device dW is dropped here: both live in
+                # host memory until the backward
+                ctx.host = (host.get("dx_host"), host.get("dw_host"), mask, dev, xq.shape)
+                ctx.grads = (None, None, out["found_inf"])
+            else:
+                ctx.grads = (out["dXq"], out["dW"], out["found_inf"])
             ctx.mark_non_differentiable(out["status"])
             return out["loss"][0], out["status"]
         out = grpo_loss_fwd(xq, xp, W, targets, mask, adv, beta, L, want_terms=False,
@@ -408,34 +559,53 @@ class _GRPOLoss(torch.autograd.Function):
     @staticmethod
     def backward(ctx, grad_loss, _grad_status):
         g = grad_loss.reshape(1).to(torch.float32).contiguous()
+        nones = (None,) * 11  # targets .. grad_hint
         if ctx.single_pass:
             dX, dW32, found = ctx.grads
             ctx.grads = None
-            grpo_scale_grad(dX, g, ctx.loss_scale, dW=dW32, found_inf=found)
+            if ctx.offload:
+                dx_host, dw_host, mask, dev, xshape = ctx.host
+                ctx.host = None
+                r = grpo_grad_restore(mask, dx_host, dw_host, g, ctx.hint, found_inf=found)
+                dX, dW32 = r["dXq"].view(xshape), r["dW"]
+                _PINNED.give(dx_host, dev)
+                _PINNED.give(dw_host, dev)
+            else:
+                grpo_scale_grad(dX, g, ctx.hint, dW=dW32, found_inf=found)
             ctx.found_inf = found
             dW = dW32.to(ctx.w_dtype) if dW32 is not None else None
-            return dX, None, dW, None, None, None, None, None, None, None, None, None
+            return (dX, None, dW) + nones
         xq, W, targets, mask, saved = ctx.saved_tensors
         out = grpo_loss_bwd(xq, W, targets, mask, saved, ctx.L, g, ctx.loss_scale,
                             need_dW=ctx.need_dW and W.requires_grad, workspace=None,
                             opts=ctx.opts)
         dW = out["dW"].to(W.dtype) if out["dW"] is not None else None
         ctx.found_inf = out["found_inf"]
-        return out["dXq"], None, dW, None, None, None, None, None, None, None, None, None
+        return (out["dXq"], None, dW) + nones
 
 
 def grpo_loss(xq, xp, W, targets, mask, rewards, beta: float = 0.04, eps: float = 1e-4,
               loss_scale: float = 1.0, need_dW: bool = False, L: int | None = None,
-              opts=None, single_pass: bool = False):
+              opts=None, single_pass: bool = False, offload: bool = False,
+              grad_hint: float | None = None):
     """The GRPO loss with autograd.  xq, xp [S, L, H] (or [S*L, H] with L), W [V, H],
     targets int64 and mask (bool/uint8) of S*L elements, rewards fp32 [S] or [B, G(, K)].
 
     Returns (loss, status).  Gradients flow to xq (and W when need_dW); xp and the
     reference path get none.  With loss scaling, back-propagate loss * loss_scale and pass
     the same loss_scale here: the returned gradients are unscaled.  opts selects the loss
-    variant (see options()).  single_pass computes the gradients during the forward
-    (grpo_loss_fwd_bwd) and keeps them, X_q-sized (plus dW), until the backward, which then
-    only applies the upstream gradient."""
+    variant (see options()).
+
+    single_pass computes the gradients during the forward (grpo_loss_fwd_bwd) and keeps
+    them, X_q-sized (plus dW), until the backward.  They are narrowed to X's dtype with
+    the upstream gradient grad_hint already applied (default: loss_scale, the gradient of
+    loss * loss_scale); the backward multiplies them by the actual upstream gradient over
+    grad_hint, which is exactly 1, and changes nothing, when the hint was right.  offload
+    (single pass only) keeps them in pinned host memory instead, copied there on a second
+    stream while later chunks compute and brought back by the backward
+    (grpo_grad_restore); the gradients are the same bits."""
+    if offload and not single_pass:
+        raise ValueError("offload applies to the single pass")
     r = rewards.float()
     if r.dim() == 1:
         r = r.unsqueeze(0)
@@ -444,4 +614,4 @@ def grpo_loss(xq, xp, W, targets, mask, rewards, beta: float = 0.04, eps: float 
     y = targets.reshape(-1).contiguous()
     return _GRPOLoss.apply(xq.contiguous(), xp.contiguous(), W.contiguous(), y, m, adv,
                            float(beta), L if xq.dim() == 2 else xq.shape[1], float(loss_scale),
-                           bool(need_dW), opts, bool(single_pass))
+                           bool(need_dW), opts, bool(single_pass), bool(offload), grad_hint)

@@ -79,6 +79,62 @@ struct FP8T {
   static constexpr int kBytes = 1;
 };
 
+// ------------------------------------------------------------------------ gradient offload
+// Two staging slots of a chunk's rows, handed between the call's stream and a copy stream
+// with events: the producer fills a slot, the consumer drains it, and a slot is refilled
+// only after its previous contents were drained.  grpo_loss_fwd_bwd produces dX rows
+// into it and copies them to host memory (device to host); grpo_grad_restore copies host
+// rows in and scatters them (host to device).  Event handles are created and destroyed by
+// the entry point that owns the ring; nothing here allocates memory.
+struct CopyRing {
+  char* slots = nullptr;   // 2 x rows x row_bytes of device memory (the workspace)
+  char* host = nullptr;    // pinned host rows, row r at host + r row_bytes
+  size_t row_bytes = 0;
+  int64_t rows = 0;        // rows per slot
+  int64_t total = 0;       // rows of the host buffer
+  hipStream_t st = nullptr, cs = nullptr;
+  hipEvent_t ready[2] = {nullptr, nullptr}, freed[2] = {nullptr, nullptr};
+  int used[2] = {0, 0};
+  int to_host = 1;         // 1: kernels on st fill, copies on cs drain; 0: the reverse
+
+  int slot_of(int64_t r0) const { return (int)((r0 / rows) & 1); }
+  char* slot(int64_t r0) const { return slots + (size_t)slot_of(r0) * rows * row_bytes; }
+  // the producer's stream waits until slot(r0) is free again
+  hipError_t acquire(int64_t r0) {
+    const int s = slot_of(r0);
+    if (!used[s]) return hipSuccess;
+    return hipStreamWaitEvent(to_host ? st : cs, freed[s], 0);
+  }
+  // host rows [r0, r0 + rows) through slot(r0): to the host after the producer's kernels,
+  // or from the host (the copy is the producer; the consumer's stream then waits for it)
+  hipError_t transfer(int64_t r0) {
+    const int s = slot_of(r0);
+    const int64_t n = total - r0 < rows ? total - r0 : rows;
+    hipStream_t prod = to_host ? st : cs, cons = to_host ? cs : st;
+    hipError_t e;
+    if (to_host) {
+      if ((e = hipEventRecord(ready[s], prod)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(cons, ready[s], 0)) != hipSuccess) return e;
+      e = hipMemcpyAsync(host + (size_t)r0 * row_bytes, slot(r0), (size_t)n * row_bytes,
+                         hipMemcpyDeviceToHost, cons);
+      if (e != hipSuccess) return e;
+      used[s] = 1;
+      return hipEventRecord(freed[s], cons);
+    }
+    e = hipMemcpyAsync(slot(r0), host + (size_t)r0 * row_bytes, (size_t)n * row_bytes,
+                       hipMemcpyHostToDevice, prod);
+    if (e != hipSuccess) return e;
+    if ((e = hipEventRecord(ready[s], prod)) != hipSuccess) return e;
+    return hipStreamWaitEvent(cons, ready[s], 0);
+  }
+  // (host to device) the scatter of slot(r0) on st is enqueued: the slot may be refilled
+  hipError_t release(int64_t r0) {
+    const int s = slot_of(r0);
+    used[s] = 1;
+    return hipEventRecord(freed[s], st);
+  }
+};
+
 // ------------------------------------------------------------------------ workspace plan
 // One plan describes every buffer carved out of the caller's workspace.  The host fills
 // it from the sizes alone (the number of loss tokens lives on the device).
@@ -120,13 +176,33 @@ struct Plan {
   size_t off_cpart;  // forward partials of one chunk of policy rows (single pass)
   size_t off_xgs;    // dW operand's chunk scale (2^k, 2^-k)
   size_t fwd_total;  // bytes the forward alone (grpo_loss_fwd) uses: a prefix of the plan
+  size_t off_ring;   // gradient offload: two staging slots of R rows x H (grpo_options.dx_host)
+  int offload;       // grpo_options.dx_host is set
+  // gradient offload of this call (null: dX rows go to dX[idx[r]]).  A chunk's dX writer
+  // then takes dx_out(p, dX, c0) as its base and stage_row0(p, c0) as the row of c0.
+  CopyRing* ring;
 };
+
+// Base pointer and the loss-row origin of the chunk at c0's dX writes: with the offload,
+// the chunk's staging slot, loss row r landing in its row r - c0; without, dX itself with
+// rows idx[r] (origin -1).
+inline void* dx_out(const Plan& p, void* dX, int64_t c0) {
+  return p.ring ? (void*)p.ring->slot(c0) : dX;
+}
+inline int64_t stage_row0(const Plan& p, int64_t c0) { return p.ring ? c0 : -1; }
 
 constexpr int kTokTile = 256;    // rows per token tile of the MFMA kernels
 constexpr int kVocTile = 256;    // vocabulary entries per tile
 constexpr int kMergeBlock = 256; // rows per block of the merge kernel
 constexpr int kMaxPhases = 32;   // most vocabulary phases of one forward launch
 constexpr int kPieceTiles = 128; // vocabulary tiles per piece of the split backward (32768)
+constexpr int kCompactRows = 4096; // rows per workgroup of the row compaction
+
+// Bytes of the loss-row count's slot in a workspace: the count (16 bytes), then the row
+// compaction's per-block counts.
+inline size_t compact_bytes(int64_t N) {
+  return 16 + (size_t)((N + kCompactRows - 1) / kCompactRows) * 4;
+}
 
 // Vocabulary phases of the MFMA forward.  Its persistent grid (8 XCDs x 32 workgroups)
 // covers 32 / P token blocks per XCD x P phases per round; pick P in {4, 8, 16, 32} that
@@ -213,6 +289,7 @@ inline P* ws_ptr(void* ws, size_t off) {
 // loss tokens from device memory (ntok), so no host synchronisation is needed.
 hipError_t launch_advantages(const float* rewards, int64_t B, int64_t G, int64_t K, float eps,
                              int unbiased, float* adv, hipStream_t st);
+// ntok: compact_bytes(N) bytes (the count, then scratch of the compaction).
 hipError_t launch_compact(const uint8_t* mask, int64_t N, int32_t* ntok, int32_t* idx,
                           int32_t* rank, hipStream_t st);
 // Same, and clears the forward's status word first.
@@ -246,9 +323,15 @@ hipError_t launch_quant_rows(int dtype, const void* src, int64_t H, const int32_
                              hipStream_t st);
 // x *= grad_loss / loss_scale over n16 elements of the storage type and nW fp32 elements;
 // found_inf on a non-finite result.  Nothing happens when the factor is exactly 1.
+// grad_loss null: 1.
 hipError_t launch_scale_grad(void* dX, int dtype, int64_t nX, float* dW, int64_t nW,
                              const float* grad_loss, float loss_scale, int32_t* found_inf,
                              hipStream_t st);
+// Gradient offload: dX[idx[r]] = rows[r - r0] * grad_loss / loss_scale (grad_loss null: 1)
+// for the loss rows r < *ntok in [r0, r0 + n), with the arithmetic of launch_scale_grad.
+hipError_t launch_restore_rows(int dtype, const void* rows, int64_t r0, int64_t n, int64_t H,
+                               const int32_t* ntok, const int32_t* idx, const float* grad_loss,
+                               float loss_scale, void* dX, int32_t* found_inf, hipStream_t st);
 // Loss rows per sequence and the number of sequences that have any (sequence-mean
 // normalisation only).
 hipError_t launch_seq_counts(const Plan& p, const uint8_t* mask, void* ws, hipStream_t st);

@@ -6,44 +6,87 @@
 namespace grpo {
 namespace {
 
-constexpr int kCompactThreads = 1024;
+constexpr int kScanThreads = 1024;
 
-// Loss rows in ascending order: idx[r] = row of the r-th loss token, rank[t] = r or -1.
-// One workgroup; each thread owns a contiguous segment of the mask, counts its ones, the
-// block scans the counts, then each thread writes its segment's indices in order.  The
-// result does not depend on scheduling.  Also clears the forward's status word.
-__global__ void __launch_bounds__(kCompactThreads)
-compact_kernel(const uint8_t* __restrict__ mask, int64_t N, int32_t* __restrict__ ntok,
-               int32_t* __restrict__ idx, int32_t* __restrict__ rank,
-               int32_t* __restrict__ status) {
-  __shared__ int32_t scan[kCompactThreads];
-  const int64_t seg = (N + kCompactThreads - 1) / kCompactThreads;
-  const int64_t lo = (int64_t)threadIdx.x * seg;
-  const int64_t hi = lo + seg < N ? lo + seg : N;
+// Loss rows in ascending order, idx[r] = row of the r-th loss token and rank[t] = r or -1,
+// in three launches whose results do not depend on scheduling (no atomics, no waits
+// between workgroups).  Blocks of kCompactRows rows, read as 16 rounds of 256 consecutive
+// mask bytes (one byte per thread and round):
+//   1. compact_count_kernel: loss rows per block -> bsum[b];
+//   2. compact_scan_kernel (one workgroup): bsum[b] <- rows before block b, in block order;
+//      *ntok = the total; the forward's status word cleared;
+//   3. compact_scatter_kernel: each block numbers its loss rows from bsum[b] in row order
+//      (per round: a ballot within each wave, the waves' counts through LDS).
+__global__ void __launch_bounds__(256)
+compact_count_kernel(const uint8_t* __restrict__ mask, int64_t N, int32_t* __restrict__ bsum) {
+  __shared__ int32_t red[4];
+  const int64_t base = (int64_t)blockIdx.x * kCompactRows;
   int32_t c = 0;
-  for (int64_t t = lo; t < hi; ++t) c += mask[t] ? 1 : 0;
-  scan[threadIdx.x] = c;
+  for (int j = 0; j < kCompactRows / 256; ++j) {
+    const int64_t t = base + j * 256 + threadIdx.x;
+    c += (t < N && mask[t]) ? 1 : 0;
+  }
+  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
   __syncthreads();
-  // Hillis-Steele inclusive scan over the block
-  for (int off = 1; off < kCompactThreads; off <<= 1) {
-    int32_t v = threadIdx.x >= (unsigned)off ? scan[threadIdx.x - off] : 0;
+  if (threadIdx.x == 0) bsum[blockIdx.x] = red[0] + red[1] + red[2] + red[3];
+}
+
+__global__ void __launch_bounds__(kScanThreads)
+compact_scan_kernel(int64_t nblocks, int32_t* __restrict__ bsum, int32_t* __restrict__ ntok,
+                    int32_t* __restrict__ status) {
+  __shared__ int32_t s[kScanThreads];
+  int32_t carry = 0;
+  for (int64_t b0 = 0; b0 < nblocks; b0 += kScanThreads) {
+    const int64_t b = b0 + threadIdx.x;
+    const int32_t v = b < nblocks ? bsum[b] : 0;
+    s[threadIdx.x] = v;
     __syncthreads();
-    scan[threadIdx.x] += v;
-    __syncthreads();
-  }
-  int32_t pos = scan[threadIdx.x] - c;
-  for (int64_t t = lo; t < hi; ++t) {
-    if (mask[t]) {
-      idx[pos] = (int32_t)t;
-      rank[t] = pos;
-      ++pos;
-    } else {
-      rank[t] = -1;
+    // Hillis-Steele inclusive scan over the workgroup
+    for (int off = 1; off < kScanThreads; off <<= 1) {
+      const int32_t u = threadIdx.x >= (unsigned)off ? s[threadIdx.x - off] : 0;
+      __syncthreads();
+      s[threadIdx.x] += u;
+      __syncthreads();
     }
+    if (b < nblocks) bsum[b] = carry + s[threadIdx.x] - v;
+    carry += s[kScanThreads - 1];
+    __syncthreads();
   }
-  if (threadIdx.x == kCompactThreads - 1) {
-    *ntok = scan[kCompactThreads - 1];
+  if (threadIdx.x == 0) {
+    *ntok = carry;
     if (status) *status = 0;
+  }
+}
+
+__global__ void __launch_bounds__(256)
+compact_scatter_kernel(const uint8_t* __restrict__ mask, int64_t N,
+                       const int32_t* __restrict__ bsum, int32_t* __restrict__ idx,
+                       int32_t* __restrict__ rank) {
+  __shared__ int32_t wsum[4];
+  const int64_t base = (int64_t)blockIdx.x * kCompactRows;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int32_t pos = bsum[blockIdx.x];
+  for (int j = 0; j < kCompactRows / 256; ++j) {
+    const int64_t t = base + j * 256 + threadIdx.x;
+    const bool f = t < N && mask[t];
+    const uint64_t bal = __ballot(f);
+    const int32_t below = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[w] = __popcll(bal);
+    __syncthreads();
+    int32_t woff = 0;
+    for (int k = 0; k < w; ++k) woff += wsum[k];
+    const int32_t round = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    if (t < N) {
+      if (f) {
+        idx[pos + woff + below] = (int32_t)t;
+        rank[t] = pos + woff + below;
+      } else {
+        rank[t] = -1;
+      }
+    }
+    pos += round;
+    __syncthreads();  // wsum is rewritten by the next round
   }
 }
 
@@ -343,13 +386,24 @@ zero_rows_kernel(const uint8_t* __restrict__ mask, int64_t N, int64_t row_bytes,
   for (int64_t i = threadIdx.x % 64; i < n16; i += 64) row[i] = make_uint4(0, 0, 0, 0);
 }
 
+// x * c rounded to fp32, then to the storage type.  The product is pinned in a register
+// first, so that the compiler cannot fold the multiply and the narrowing into one
+// mixed-precision instruction (one rounding instead of two) in some kernels and not in
+// others: every kernel that scales a gradient gets the same bits.
+template <class E>
+__device__ inline typename E::T scaled(typename E::T x, float c) {
+  float p = E::to_f32(x) * c;
+  asm volatile("" : "+v"(p));
+  return E::from_f32(p);
+}
+
 // In-place scaling of a gradient by grad_loss / loss_scale, 8 elements per thread
 // (16 bytes of 16-bit data, or two 16-byte fp32 vectors), grid-stride.
 template <class E>
 __global__ void __launch_bounds__(256)
 scale_kernel(typename E::T* __restrict__ x, int64_t n, const float* __restrict__ grad_loss,
              float loss_scale, int32_t* __restrict__ found_inf) {
-  const float c = *grad_loss / loss_scale;
+  const float c = (grad_loss ? *grad_loss : 1.0f) / loss_scale;
   if (c == 1.0f) return;
   bool bad = false;
   const int64_t stride = (int64_t)gridDim.x * 256 * 8;
@@ -359,16 +413,51 @@ scale_kernel(typename E::T* __restrict__ x, int64_t n, const float* __restrict__
       __builtin_memcpy(h, x + i, sizeof(h));
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        h[j] = E::from_f32(E::to_f32(h[j]) * c);
+        h[j] = scaled<E>(h[j], c);
         bad |= !isfinite(E::to_f32(h[j]));
       }
       __builtin_memcpy(x + i, h, sizeof(h));
     } else {
       for (int64_t k = i; k < n; ++k) {
-        x[k] = E::from_f32(E::to_f32(x[k]) * c);
+        x[k] = scaled<E>(x[k], c);
         bad |= !isfinite(E::to_f32(x[k]));
       }
     }
+  }
+  if (bad) atomicOr(found_inf, 1);
+}
+
+// Gradient offload, the way back: dX[idx[r]] = rows[r - r0] * grad_loss / loss_scale for
+// the loss rows r in [r0, r0 + n) of a staging slot, with the arithmetic of scale_kernel
+// (the product skipped when the factor is exactly 1), so the result equals a device-held
+// gradient scaled by grpo_scale_grad bit for bit.  One row per block, 16 bytes per thread
+// and step.
+template <class E>
+__global__ void __launch_bounds__(256)
+restore_rows_kernel(const typename E::T* __restrict__ rows, int64_t r0, int64_t n, int64_t H,
+                    const int32_t* __restrict__ ntok_p, const int32_t* __restrict__ idx,
+                    const float* __restrict__ grad_loss, float loss_scale,
+                    typename E::T* __restrict__ dX, int32_t* __restrict__ found_inf) {
+  typedef typename E::T T;
+  constexpr int kPer = 16 / sizeof(T);
+  const int64_t rl = blockIdx.x;
+  const int64_t r = r0 + rl;
+  if (rl >= n || r >= *ntok_p) return;
+  const float c = (grad_loss ? *grad_loss : 1.0f) / loss_scale;
+  const T* src = rows + rl * H;
+  T* dst = dX + (int64_t)idx[r] * H;
+  bool bad = false;
+  for (int64_t h = (int64_t)threadIdx.x * kPer; h < H; h += 256 * kPer) {
+    T v[kPer];
+    __builtin_memcpy(v, src + h, 16);
+    if (c != 1.0f) {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        v[j] = scaled<E>(v[j], c);
+        bad |= !isfinite(E::to_f32(v[j]));
+      }
+    }
+    __builtin_memcpy(dst + h, v, 16);
   }
   if (bad) atomicOr(found_inf, 1);
 }
@@ -399,6 +488,28 @@ hipError_t launch_scale_grad(void* dX, int dtype, int64_t nX, float* dW, int64_t
   return scale_one<F32T>(dW, nW, grad_loss, loss_scale, found_inf, st);
 }
 
+hipError_t launch_restore_rows(int dtype, const void* rows, int64_t r0, int64_t n, int64_t H,
+                               const int32_t* ntok, const int32_t* idx, const float* grad_loss,
+                               float loss_scale, void* dX, int32_t* found_inf, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const dim3 grid((unsigned)n), block(256);
+  switch (dtype) {
+    case GRPO_F32:
+      hipLaunchKernelGGL(restore_rows_kernel<F32T>, grid, block, 0, st, (const float*)rows, r0,
+                         n, H, ntok, idx, grad_loss, loss_scale, (float*)dX, found_inf);
+      break;
+    case GRPO_BF16:
+      hipLaunchKernelGGL(restore_rows_kernel<BF16T>, grid, block, 0, st, (const u16*)rows, r0,
+                         n, H, ntok, idx, grad_loss, loss_scale, (u16*)dX, found_inf);
+      break;
+    default:
+      hipLaunchKernelGGL(restore_rows_kernel<F16T>, grid, block, 0, st, (const u16*)rows, r0,
+                         n, H, ntok, idx, grad_loss, loss_scale, (u16*)dX, found_inf);
+      break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_compact(const uint8_t* mask, int64_t N, int32_t* ntok, int32_t* idx,
                           int32_t* rank, hipStream_t st) {
   return launch_compact_status(mask, N, ntok, idx, rank, nullptr, st);
@@ -406,8 +517,16 @@ hipError_t launch_compact(const uint8_t* mask, int64_t N, int32_t* ntok, int32_t
 
 hipError_t launch_compact_status(const uint8_t* mask, int64_t N, int32_t* ntok, int32_t* idx,
                                  int32_t* rank, int32_t* status, hipStream_t st) {
-  hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(kCompactThreads), 0, st, mask, N, ntok, idx,
-                     rank, status);
+  int32_t* bsum = ntok + 4;  // the block counts follow the count (compact_bytes)
+  const int64_t nb = (N + kCompactRows - 1) / kCompactRows;
+  hipLaunchKernelGGL(compact_count_kernel, dim3((unsigned)nb), dim3(256), 0, st, mask, N, bsum);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(compact_scan_kernel, dim3(1), dim3(kScanThreads), 0, st, nb, bsum, ntok,
+                     status);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(compact_scatter_kernel, dim3((unsigned)nb), dim3(256), 0, st, mask, N,
+                     (const int32_t*)bsum, idx, rank);
   return hipGetLastError();
 }
 

@@ -91,13 +91,16 @@ bool options_ok(const grpo_options* o) {
   if (o->trace_kernel < GRPO_TRACE_NONE || o->trace_kernel > GRPO_TRACE_DW ||
       o->trace_capacity < 0 || (o->trace_capacity > 0 && !o->trace_events))
     return false;
+  if ((o->dx_host || o->dw_host) && !o->copy_stream) return false;
+  if ((o->dx_host && !aligned16(o->dx_host)) || (o->dw_host && !aligned16(o->dw_host)))
+    return false;
   // the softmax argument z / tau must stay finite for finite logits
   return isfinite(o->temperature) && o->temperature >= 1e-3f && o->temperature <= 1e3f;
 }
 
 bool sizes_ok(int64_t S, int64_t L, int64_t H, int64_t V) {
-  if (S < 1 || L < 1 || H < 64 || V < 1) return false;
-  if (H % 64 != 0) return false;
+  if (S < 1 || L < 1 || H < 8 || V < 1) return false;
+  if (H % 8 != 0) return false;                   // 16-byte rows of 16-bit data
   if (S > INT32_MAX / L) return false;            // row indices are int32
   if (V > (int64_t)1 << 30 || H > (int64_t)1 << 20) return false;
   return true;
@@ -160,7 +163,7 @@ bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_d
   // what the forward uses comes first, so that its size is a prefix of the plan
   size_t o = 0;
   p->off_ntok = o;
-  o = align_up(o + 16);
+  o = align_up(o + compact_bytes(p->N));
   p->off_idx = o;
   o = align_up(o + (size_t)p->N * 4);
   p->off_rank = o;
@@ -210,6 +213,8 @@ bool make_plan(int64_t S, int64_t L, int64_t H, int64_t V, int dtype, int need_d
   p->off_dxp = o;    // fp32 dX partials [ksplit][R][H]: split reductions, or the pieces' sums
   if (p->mfma && (p->ksplit > 1 || p->vsplit))
     o = align_up(o + (size_t)p->ksplit * p->R * H * 4);
+  p->off_ring = o;   // gradient offload: two staging slots of a chunk's dX rows
+  if (p->offload) o = align_up(o + (size_t)2 * p->R * H * p->esize);
   p->total = o;
   return true;
 }
@@ -251,6 +256,60 @@ void plan_options(const grpo_options* o, Plan* p) {
   p->trace_cap = o->trace_capacity;
   p->trace_ev = o->trace_events;
   p->trace_n = nullptr;  // set by the entry point that launches
+  p->offload = o->dx_host != nullptr;
+  p->ring = nullptr;     // set by grpo_loss_fwd_bwd for the call
+}
+
+// Events of a CopyRing (and two more for the call's own hand-overs), created for one call
+// and destroyed at its end (a destroyed event still pending completes normally).
+struct RingEvents {
+  hipEvent_t ev[6] = {};
+  hipError_t create(CopyRing* r) {
+    for (hipEvent_t& e : ev) {
+      const hipError_t rc = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+      if (rc != hipSuccess) return rc;
+    }
+    if (r) {
+      r->ready[0] = ev[0];
+      r->ready[1] = ev[1];
+      r->freed[0] = ev[2];
+      r->freed[1] = ev[3];
+    }
+    return hipSuccess;
+  }
+  ~RingEvents() {
+    for (hipEvent_t e : ev)
+      if (e) (void)hipEventDestroy(e);
+  }
+};
+
+// `to` waits for everything enqueued on `from` so far.
+hipError_t stream_after(hipStream_t to, hipStream_t from, hipEvent_t ev) {
+  hipError_t e = hipEventRecord(ev, from);
+  return e != hipSuccess ? e : hipStreamWaitEvent(to, ev, 0);
+}
+
+// Workspace of grpo_grad_restore: the loss-row list, then two staging slots of R rows.
+struct RestorePlan {
+  int64_t R;
+  size_t off_ntok, off_idx, off_rank, off_ring, total;
+};
+RestorePlan restore_plan(int64_t S, int64_t L, int64_t H, int dtype, const grpo_options* opts) {
+  RestorePlan r;
+  const int64_t N = S * L;
+  const int64_t chunk = opts && opts->chunk_rows > 0 ? opts->chunk_rows : kChunkRows;
+  r.R = N < chunk ? N : chunk;
+  size_t o = 0;
+  r.off_ntok = o;
+  o = align_up(o + compact_bytes(N));
+  r.off_idx = o;
+  o = align_up(o + (size_t)N * 4);
+  r.off_rank = o;
+  o = align_up(o + (size_t)N * 4);
+  r.off_ring = o;
+  o = align_up(o + (size_t)2 * r.R * H * (dtype == GRPO_F32 ? 4 : 2));
+  r.total = o;
+  return r;
 }
 
 }  // namespace grpo
@@ -288,6 +347,9 @@ void grpo_default_options(grpo_options* opts) {
   opts->trace_capacity = 0;
   opts->trace_events = nullptr;
   opts->trace_count = nullptr;
+  opts->dx_host = nullptr;
+  opts->dw_host = nullptr;
+  opts->copy_stream = nullptr;
 }
 
 size_t grpo_workspace_bytes(int64_t S, int64_t L, int64_t H, int64_t V, grpo_dtype dtype,
@@ -440,8 +502,9 @@ int grpo_loss_fwd_bwd(const void* Xq, const void* Xp, const void* W, grpo_dtype 
                       float* ref_logp_out, float* kl_out, int32_t* status, void* dXq, float* dW,
                       int accumulate_dW, int32_t* found_inf, const grpo_options* opts,
                       void* workspace, size_t workspace_bytes, grpo_stream_t stream) {
-  if (!Xq || !Xp || !W || !targets || !mask || !adv || !loss || !saved || !status || !dXq ||
-      !found_inf || !workspace)
+  const bool offload = opts && opts->dx_host;
+  if (!Xq || !Xp || !W || !targets || !mask || !adv || !loss || !saved || !status ||
+      (!dXq && !offload) || !found_inf || !workspace)
     return GRPO_ERR_NULL;
   if (!valid_dtype(dtype)) return GRPO_ERR_DTYPE;
   if (!sizes_ok(S, L, H, V) || !isfinite(beta) || !(loss_scale > 0.0f) || !isfinite(loss_scale))
@@ -450,6 +513,10 @@ int grpo_loss_fwd_bwd(const void* Xq, const void* Xp, const void* W, grpo_dtype 
       !aligned16(dXq) || (dW && !aligned16(dW)) || !aligned16(workspace))
     return GRPO_ERR_ALIGN;
   if (!options_ok(opts)) return GRPO_ERR_OPTIONS;
+  // the offload writes no device dX, and dW goes to the host only from a device dW
+  if ((offload && dXq) || (opts && opts->dw_host && !dW) ||
+      (opts && (opts->dx_host || opts->dw_host) && opts->copy_stream == stream))
+    return GRPO_ERR_OPTIONS;
   Plan p;
   if (!make_plan(S, L, H, V, dtype, dW != nullptr, &p)) return GRPO_ERR_SHAPE;
   if (!make_plan(S, L, H, V, dtype, dW != nullptr, &p, opts)) return GRPO_ERR_OPTIONS;
@@ -461,28 +528,56 @@ int grpo_loss_fwd_bwd(const void* Xq, const void* Xp, const void* W, grpo_dtype 
   int launches = 0;  // launches of the traced kernel
   p.trace_n = &launches;
   void* ws = workspace;
+  // gradient offload: the staging ring and its events
+  const bool host_copies = opts && (opts->dx_host || opts->dw_host);
+  hipStream_t cs = host_copies ? (hipStream_t)opts->copy_stream : nullptr;
+  CopyRing ring;
+  RingEvents evs;
+  if (host_copies) {
+    if (evs.create(&ring) != hipSuccess) return GRPO_ERR_HIP;
+    if (offload) {
+      ring.slots = ws_ptr<char>(ws, p.off_ring);
+      ring.host = reinterpret_cast<char*>(opts->dx_host);
+      ring.row_bytes = (size_t)H * p.esize;
+      ring.rows = p.R;
+      ring.total = p.N;
+      ring.st = st;
+      ring.cs = cs;
+      ring.to_host = 1;
+      p.ring = &ring;
+    }
+  }
   if (launch_compact_status(mask, p.N, ws_ptr<int32_t>(ws, p.off_ntok),
                             ws_ptr<int32_t>(ws, p.off_idx), ws_ptr<int32_t>(ws, p.off_rank),
                             status, st) != hipSuccess)
     return GRPO_ERR_HIP;
   if (p.norm == GRPO_NORM_SEQUENCES && launch_seq_counts(p, mask, ws, st) != hipSuccess)
     return GRPO_ERR_HIP;
-  if (launch_zero_masked_rows(p, mask, dXq, st) != hipSuccess) return GRPO_ERR_HIP;
+  if (!offload && launch_zero_masked_rows(p, mask, dXq, st) != hipSuccess) return GRPO_ERR_HIP;
   if (p.mfma) {
     if (mfma_fused(p, ws, Xq, Xp, W, targets, mask, adv, beta, saved, logp_out, ref_logp_out,
                    kl_out, status, loss, grad_loss, ls_eff, dXq, dW, accumulate_dW, found_inf,
                    st) != hipSuccess)
       return GRPO_ERR_HIP;
-    return traced(opts, launches);
+  } else {
+    // fp32 (or H not a multiple of 256): the two passes back to back
+    if (simple_fwd_partials(p, ws, Xq, Xp, W, targets, st) != hipSuccess) return GRPO_ERR_HIP;
+    if (launch_merge(p, ws, targets, mask, adv, beta, saved, logp_out, ref_logp_out, kl_out,
+                     status, loss, st) != hipSuccess)
+      return GRPO_ERR_HIP;
+    if (simple_backward(p, ws, Xq, W, targets, saved, grad_loss, ls_eff, dXq, dW, accumulate_dW,
+                        found_inf, st) != hipSuccess)
+      return GRPO_ERR_HIP;
   }
-  // fp32 (or H not a multiple of 256): the two passes back to back
-  if (simple_fwd_partials(p, ws, Xq, Xp, W, targets, st) != hipSuccess) return GRPO_ERR_HIP;
-  if (launch_merge(p, ws, targets, mask, adv, beta, saved, logp_out, ref_logp_out, kl_out,
-                   status, loss, st) != hipSuccess)
-    return GRPO_ERR_HIP;
-  if (simple_backward(p, ws, Xq, W, targets, saved, grad_loss, ls_eff, dXq, dW, accumulate_dW,
-                      found_inf, st) != hipSuccess)
-    return GRPO_ERR_HIP;
+  if (host_copies) {
+    if (opts->dw_host) {
+      if (stream_after(cs, st, evs.ev[4]) != hipSuccess ||
+          hipMemcpyAsync(opts->dw_host, dW, (size_t)V * H * 4, hipMemcpyDeviceToHost, cs) !=
+              hipSuccess)
+        return GRPO_ERR_HIP;
+    }
+    if (stream_after(st, cs, evs.ev[5]) != hipSuccess) return GRPO_ERR_HIP;
+  }
   return traced(opts, launches);
 }
 
@@ -499,6 +594,76 @@ int grpo_scale_grad(void* dXq, grpo_dtype dtype, int64_t rows, int64_t H, float*
   if (launch_scale_grad(dXq, dtype, rows * H, dW, dW ? V * H : 0, grad_loss, loss_scale,
                         found_inf, (hipStream_t)stream) != hipSuccess)
     return GRPO_ERR_HIP;
+  return GRPO_OK;
+}
+
+size_t grpo_restore_workspace_bytes(int64_t S, int64_t L, int64_t H, grpo_dtype dtype,
+                                    const grpo_options* opts) {
+  if (!valid_dtype(dtype) || !sizes_ok(S, L, H, 1) || !options_ok(opts)) return 0;
+  return restore_plan(S, L, H, dtype, opts).total;
+}
+
+int grpo_grad_restore(const void* dx_host, const float* dw_host, grpo_dtype dtype,
+                      const uint8_t* mask, int64_t S, int64_t L, int64_t H, int64_t V,
+                      const float* grad_loss, float loss_scale, void* dXq, float* dW,
+                      int32_t* found_inf, const grpo_options* opts, void* workspace,
+                      size_t workspace_bytes, grpo_stream_t stream) {
+  if (!mask || !found_inf || !workspace || !opts || !opts->copy_stream ||
+      (!dx_host != !dXq) || (!dw_host != !dW) || (!dx_host && !dw_host))
+    return GRPO_ERR_NULL;
+  if (!valid_dtype(dtype)) return GRPO_ERR_DTYPE;
+  if (!sizes_ok(S, L, H, dW ? V : 1) || !(loss_scale > 0.0f) || !isfinite(loss_scale))
+    return GRPO_ERR_SHAPE;
+  if (!aligned16(dx_host) || !aligned16(dw_host) || !aligned16(dXq) || !aligned16(dW) ||
+      !aligned16(workspace))
+    return GRPO_ERR_ALIGN;
+  if (!options_ok(opts) || opts->copy_stream == stream) return GRPO_ERR_OPTIONS;
+  const RestorePlan rp = restore_plan(S, L, H, dtype, opts);
+  if (workspace_bytes < rp.total) return GRPO_ERR_WORKSPACE;
+  if (!device_ok()) return GRPO_ERR_DEVICE;
+  hipStream_t st = (hipStream_t)stream, cs = (hipStream_t)opts->copy_stream;
+  CopyRing ring;
+  RingEvents evs;
+  if (evs.create(&ring) != hipSuccess) return GRPO_ERR_HIP;
+  // the copies start after the work already on `stream` (the forward's own copies)
+  if (stream_after(cs, st, evs.ev[4]) != hipSuccess) return GRPO_ERR_HIP;
+  if (dx_host) {
+    const int64_t N = S * L;
+    int32_t* ntok = ws_ptr<int32_t>(workspace, rp.off_ntok);
+    int32_t* idx = ws_ptr<int32_t>(workspace, rp.off_idx);
+    Plan p;
+    memset(&p, 0, sizeof(p));
+    p.N = N;
+    p.H = H;
+    p.esize = dtype == GRPO_F32 ? 4 : 2;
+    if (launch_compact(mask, N, ntok, idx, ws_ptr<int32_t>(workspace, rp.off_rank), st) !=
+            hipSuccess ||
+        launch_zero_masked_rows(p, mask, dXq, st) != hipSuccess)
+      return GRPO_ERR_HIP;
+    ring.slots = ws_ptr<char>(workspace, rp.off_ring);
+    ring.host = reinterpret_cast<char*>(const_cast<void*>(dx_host));
+    ring.row_bytes = (size_t)H * p.esize;
+    ring.rows = rp.R;
+    ring.total = N;
+    ring.st = st;
+    ring.cs = cs;
+    ring.to_host = 0;
+    for (int64_t r0 = 0; r0 < N; r0 += rp.R) {
+      const int64_t n = N - r0 < rp.R ? N - r0 : rp.R;
+      if (ring.acquire(r0) != hipSuccess || ring.transfer(r0) != hipSuccess ||
+          launch_restore_rows(dtype, ring.slot(r0), r0, n, H, ntok, idx, grad_loss, loss_scale,
+                              dXq, found_inf, st) != hipSuccess ||
+          ring.release(r0) != hipSuccess)
+        return GRPO_ERR_HIP;
+    }
+  }
+  if (dw_host) {
+    if (hipMemcpyAsync(dW, dw_host, (size_t)V * H * 4, hipMemcpyHostToDevice, cs) != hipSuccess ||
+        stream_after(st, cs, evs.ev[5]) != hipSuccess ||
+        launch_scale_grad(nullptr, GRPO_F32, 0, dW, V * H, grad_loss, loss_scale, found_inf,
+                          st) != hipSuccess)
+      return GRPO_ERR_HIP;
+  }
   return GRPO_OK;
 }
 

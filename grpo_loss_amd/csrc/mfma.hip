@@ -1094,7 +1094,8 @@ __host__ __device__ inline int64_t dx_sum_offset(int64_t tile, int w, int nb, in
 // vocabulary, or one piece of it: columns 0 .. kcols - 1 of rows of ld entries hold
 // vocabulary rows v_base ..), or one split of them, with W read in its own [V][H] layout
 // (natural-layout A tiles; rows past V load as 0).
-// acc_mode 0, ksplit == 1: dX[idx[r]][h] = c * g_r * s_r * C, in the storage type.
+// acc_mode 0, ksplit == 1: dX[idx[r]][h] = c * g_r * s_r * C, in the storage type (row
+// r - srow0 instead of idx[r] when srow0 >= 0: a staging slot of the gradient offload).
 // acc_mode 0, ksplit > 1: fp32 partials of C to dxp[ks][r - c0][h], reduced by
 // dx_reduce_kernel, which scales the same.  acc_mode 1: fp32 partials for every ksplit
 // (the first piece of a vocabulary-split chunk); acc_mode 2: added to them (the later
@@ -1118,7 +1119,7 @@ dx_kernel(int64_t H, int64_t V, int64_t ld, int64_t kcols, int64_t v_base, int64
           const int32_t* __restrict__ idx, const char* __restrict__ W,
           const char* __restrict__ T, const float* __restrict__ saved,
           const float* __restrict__ grad_loss, float loss_scale,
-          typename E::T* __restrict__ dX, float* __restrict__ dxp,
+          typename E::T* __restrict__ dX, int64_t srow0, float* __restrict__ dxp,
           int32_t* __restrict__ found_inf, const int32_t* __restrict__ redo,
           const float* __restrict__ mr, const int32_t* __restrict__ gate) {
   if (gate && *gate == 0) return;   // the vocabulary split's fallback
@@ -1220,7 +1221,7 @@ dx_kernel(int64_t H, int64_t V, int64_t ld, int64_t kcols, int64_t v_base, int64
         const int64_t t = idx[r];
         float gs = saved[t * 4 + 3] * c;
         if (fixed) gs *= fixed_row_factor(r - c0, t, saved, mr);
-        typename E::T* drow = dX + t * H;
+        typename E::T* drow = dX + (srow0 < 0 ? t : r - srow0) * H;
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb) {
           const f32x4 v = acc[mb][nb] * gs;
@@ -1242,13 +1243,14 @@ dx_kernel(int64_t H, int64_t V, int64_t ld, int64_t kcols, int64_t v_base, int64
   if (bad) atomicOr(found_inf, 1);
 }
 
-// dX[idx[r]][h] = c * g_r * sum_ks dxp[ks][r - c0][h], ks ascending.
+// dX[idx[r]][h] = c * g_r * sum_ks dxp[ks][r - c0][h], ks ascending (row r - srow0 when
+// srow0 >= 0).
 template <class E>
 __global__ void __launch_bounds__(256)
 dx_reduce_kernel(int64_t H, int64_t R, int64_t c0, int ksplit, const int32_t* __restrict__ ntok_p,
                  const int32_t* __restrict__ idx, const float* __restrict__ dxp,
                  const float* __restrict__ saved, const float* __restrict__ grad_loss,
-                 float loss_scale, typename E::T* __restrict__ dX,
+                 float loss_scale, typename E::T* __restrict__ dX, int64_t srow0,
                  int32_t* __restrict__ found_inf, const int32_t* __restrict__ redo,
                  const float* __restrict__ mr) {
   const int64_t rl = blockIdx.x;
@@ -1271,7 +1273,7 @@ dx_reduce_kernel(int64_t H, int64_t R, int64_t c0, int ksplit, const int32_t* __
     uint2 pk;
     pk.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
     pk.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
-    *reinterpret_cast<uint2*>(dX + t * H + h) = pk;
+    *reinterpret_cast<uint2*>(dX + (srow0 < 0 ? t : r - srow0) * H + h) = pk;
   }
   if (bad) atomicOr(found_inf, 1);
 }
@@ -1284,7 +1286,7 @@ dx_reduce_kernel(int64_t H, int64_t R, int64_t c0, int ksplit, const int32_t* __
 // against; null: 1, the two-pass recompute's plain softmax terms).  One workgroup per
 // (token tile, H tile) of the chunk, its threads in the accumulator layout of dx_kernel,
 // so the sums are read as they were written; a target outside [0, V) (flagged by the
-// forward) adds no W row.
+// forward) adds no W row.  srow0 >= 0: row r goes to row r - srow0 of dX (a staging slot).
 template <class E>
 __global__ void __launch_bounds__(kThreads)
 dx_final_kernel(int64_t H, int64_t V, int64_t R, int64_t c0, int nht, int ksplit,
@@ -1293,7 +1295,7 @@ dx_final_kernel(int64_t H, int64_t V, int64_t R, int64_t c0, int nht, int ksplit
                 const float* __restrict__ saved, const float* __restrict__ grad_loss,
                 float loss_scale, const float* __restrict__ pm,
                 const typename E::T* __restrict__ W, typename E::T* __restrict__ dX,
-                int32_t* __restrict__ found_inf) {
+                int64_t srow0, int32_t* __restrict__ found_inf) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w / kWN, wn = w % kWN;
   const int64_t tt = blockIdx.x / nht, ht = blockIdx.x % nht;
@@ -1316,7 +1318,7 @@ dx_final_kernel(int64_t H, int64_t V, int64_t R, int64_t c0, int nht, int ksplit
     const bool yok = y >= 0 && y < V;
     const float ty = yok ? -expm1f(saved[t * 4 + 1]) : 0.f;
     const typename E::T* wy = W + (yok ? y : 0) * H + hb;
-    typename E::T* drow = dX + t * H + hb;
+    typename E::T* drow = dX + (srow0 < 0 ? t : r - srow0) * H + hb;
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) {
       f32x4 sm = *reinterpret_cast<const f32x4*>(dxp + dx_sum_offset(tt * nht + ht, w, nb, mb, lane));
@@ -1339,9 +1341,10 @@ dx_final_kernel(int64_t H, int64_t V, int64_t R, int64_t c0, int nht, int ksplit
 }
 
 // ------------------------------------------------------------------------------- dW
-// C[h][v] = sum_r Xg[r][h] T[r][v] over the chunk's rows; dW[v][h] = 2^-k C (+ dW[v][h]),
-// 2^k the chunk's scale of Xg (xg_scale).  Both operands are natural-layout tiles read in
-// place: Xg [R][H] (gather_rows_kernel) and the chunk's T [R][Vpad].
+// C[h][v] = sum_r XgT[h][r] T[r][v] over the chunk's rows; dW[v][h] = 2^-k C (+ dW[v][h]),
+// 2^k the chunk's scale of the operand (xg_scale).  A is XgT [H][R] (gather_cols_kernel),
+// rows contiguous, staged like the forward's operands; B is a natural-layout tile of the
+// chunk's T [R][Vpad] read in place.
 //
 // Persistent over the (vocabulary tile, H tile) items, H tile fastest, numbered so that
 // workgroup b (on XCD b % 8) takes item 256 r + 32 (b % 8) + b / 8 in round r: the items
@@ -1353,7 +1356,7 @@ dx_final_kernel(int64_t H, int64_t V, int64_t R, int64_t c0, int nht, int ksplit
 template <class E>
 __global__ void __launch_bounds__(kThreads, 1)
 dw_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int nht, int accumulate,
-          const int32_t* __restrict__ ntok_p, const char* __restrict__ Xg,
+          const int32_t* __restrict__ ntok_p, const char* __restrict__ XgT,
           const char* __restrict__ T, float* __restrict__ dW, int32_t* __restrict__ found_inf,
           const float* __restrict__ xg_scale) {
   const int tid = threadIdx.x;
@@ -1364,18 +1367,22 @@ dw_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int nht, in
   if (nrows <= 0 && accumulate) return;
   if (nrows < 0) nrows = 0;
   // rows padded to a multiple of 128 (an even number of k-steps); the padding rows of
-  // T and Xg are zero
+  // T and XgT are zero
   const int nk = (int)(2 * ((nrows + 127) / 128));
-  const int64_t ldx = H * 2, ldt = Vpad * 2;
+  const int64_t ldx = R * 2, ldt = Vpad * 2;   // bytes per row of XgT and of T
   const int64_t n_items = (int64_t)nht * (Vpad / 256);
   const int nwg = gridDim.x;  // a multiple of 8
   const int64_t first = (int64_t)(blockIdx.x % kXcds) * (nwg / kXcds) + blockIdx.x / kXcds;
   Offs ao, bo;
-  nat_offsets(ldx, ao);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int sr = stage_row(i);
+    ao[i] = (uint32_t)(sr * ldx) + stage_chunk_bytes(sr);
+  }
   nat_offsets(ldt, bo);
   auto opA = [&](int64_t it) {
     const int64_t h0 = (it % nht) * 256;
-    return Op<true>{Xg + h0 * 2, R * ldx - h0 * 2, 64 * ldx};
+    return Op<false>{make_src(XgT + h0 * ldx, XgT + H * ldx)};
   };
   auto opB = [&](int64_t it) {
     const int64_t v0 = (it / nht) * 256;
@@ -1387,7 +1394,7 @@ dw_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int nht, in
   for (int64_t it = first; it < n_items; it += nwg) {
     Acc acc;
     zero_acc(acc);
-    if (nk > 0) gemm_main_op<E, true, true>(opA(it), opB(it), ao, bo, nk, acc);
+    if (nk > 0) gemm_main_op<E, false, true>(opA(it), opB(it), ao, bo, nk, acc);
     const int64_t next = it + nwg;
     if (next < n_items && nk > 0) gemm_pre_op(opA(next), opB(next), ao, bo);
     const int lq = tid_opaque() & 63;
@@ -1477,41 +1484,56 @@ xg_scale_kernel(int64_t R, int64_t c0, const int32_t* __restrict__ ntok_p,
   }
 }
 
-// Xg[rl][h] = 2^k c g_r s_r X_q[idx[c0 + rl]][h] in the storage type for the chunk's loss
-// rows rl < nrows (2^k = xg_scale[0]), and 0 for the rows from nrows up to the next
-// multiple of 128 (the k range of dw_kernel).  One row per block, 8 entries (16 bytes)
-// per thread and step.
+// XgT[h][rl] = 2^k c g_r s_r X_q[idx[c0 + rl]][h] in the storage type (2^k = xg_scale[0])
+// for the chunk's loss rows rl < nrows, and 0 for rl from nrows up to the next multiple of
+// 128 (the k range of dw_kernel): the dW operand with the chunk's rows, the reduction index,
+// contiguous (R entries per h), so dw_kernel stages it like the forward's operands.  One
+// 64-row x 64-column tile per workgroup, transposed through LDS: a thread reads 16
+// consecutive h of one row (two 16-byte loads) and writes 16 consecutive rows of one h
+// (two 16-byte stores).
 template <class E>
 __global__ void __launch_bounds__(256)
-gather_rows_kernel(const typename E::T* __restrict__ X, int64_t H, int64_t R, int64_t c0,
+gather_cols_kernel(const typename E::T* __restrict__ X, int64_t H, int64_t R, int64_t c0,
                    const int32_t* __restrict__ ntok_p, const int32_t* __restrict__ idx,
                    const float* __restrict__ saved, const float* __restrict__ grad_loss,
-                   float loss_scale, typename E::T* __restrict__ Xg,
+                   float loss_scale, typename E::T* __restrict__ XgT,
                    const int32_t* __restrict__ redo, const float* __restrict__ mr,
                    const float* __restrict__ xg_scale) {
-  const int64_t rl = blockIdx.x;
+  typedef typename E::T T;
+  __shared__ __attribute__((aligned(16))) T tile[64][72];  // [h][row], 144-byte rows
   int64_t nrows = (int64_t)(*ntok_p) - c0;
   if (nrows > R) nrows = R;
-  if (nrows <= 0 || rl >= (nrows + 127) / 128 * 128) return;
-  uint4* dst = reinterpret_cast<uint4*>(Xg + rl * H);
-  if (rl >= nrows) {
-    for (int64_t h8 = threadIdx.x; h8 < H / 8; h8 += 256) dst[h8] = uint4{0u, 0u, 0u, 0u};
-    return;
-  }
-  const int64_t t = idx[c0 + rl];
-  const float sc = xg_row_factor(rl, t, saved, (grad_loss ? *grad_loss : 1.f) / loss_scale,
-                                 redo && *redo == 0, mr) * xg_scale[0];
-  const uint4* src = reinterpret_cast<const uint4*>(X + t * H);
-  for (int64_t h8 = threadIdx.x; h8 < H / 8; h8 += 256) {
-    const uint4 q = src[h8];
-    const uint32_t in[4] = {q.x, q.y, q.z, q.w};
-    uint32_t out[4];
+  const int64_t r0 = (int64_t)blockIdx.x * 64, h0 = (int64_t)blockIdx.y * 64;
+  if (nrows <= 0 || r0 >= (nrows + 127) / 128 * 128) return;
+  const int tid = threadIdx.x;
+  {
+    const int rr = tid >> 2, hs = (tid & 3) * 16;
+    const int64_t rl = r0 + rr;
+    uint32_t out[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    if (rl < nrows) {
+      const int64_t t = idx[c0 + rl];
+      const float sc = xg_row_factor(rl, t, saved, (grad_loss ? *grad_loss : 1.f) / loss_scale,
+                                     redo && *redo == 0, mr) * xg_scale[0];
+      const uint4* src = reinterpret_cast<const uint4*>(X + t * H + h0 + hs);
+      const uint4 q0 = src[0], q1 = src[1];
+      const uint32_t in[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      out[k] = E::pack2(sc * E::to_f32((typename E::T)(in[k] & 0xffffu)),
-                        sc * E::to_f32((typename E::T)(in[k] >> 16)));
-    dst[h8] = uint4{out[0], out[1], out[2], out[3]};
+      for (int k = 0; k < 8; ++k)
+        out[k] = E::pack2(sc * E::to_f32((T)(in[k] & 0xffffu)), sc * E::to_f32((T)(in[k] >> 16)));
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      tile[hs + 2 * k][rr] = (T)(out[k] & 0xffffu);
+      tile[hs + 2 * k + 1][rr] = (T)(out[k] >> 16);
+    }
   }
+  __syncthreads();
+  const int hh = tid >> 2, rs = (tid & 3) * 16;
+  const uint4 v0 = *reinterpret_cast<const uint4*>(&tile[hh][rs]);
+  const uint4 v1 = *reinterpret_cast<const uint4*>(&tile[hh][rs + 8]);
+  uint4* dst = reinterpret_cast<uint4*>(XgT + (h0 + hh) * R + r0 + rs);
+  dst[0] = v0;
+  dst[1] = v1;
 }
 
 __global__ void __launch_bounds__(256) fill_i32_kernel(int32_t* __restrict__ p, int n, int v) {
@@ -1603,15 +1625,16 @@ hipError_t chunk_grads(const Plan& p, void* ws, int64_t c0, const void* Xq, cons
   trace_begin(p, GRPO_TRACE_DX, st);
   hipLaunchKernelGGL(dx_kernel<E>, dim3(kNumWG), dim3(kThreads), 0, st,
                      p.H, p.V, p.Vpad, p.Vpad, (int64_t)0, p.R, c0, nht, p.ksplit, 0, ntok, idx,
-                     (const char*)W, (const char*)Tb, saved, grad_loss, loss_scale, (T*)dX,
-                     ws_ptr<float>(ws, p.off_dxp), found_inf, redo, mr,
-                     (const int32_t*)nullptr);
+                     (const char*)W, (const char*)Tb, saved, grad_loss, loss_scale,
+                     (T*)dx_out(p, dX, c0), stage_row0(p, c0), ws_ptr<float>(ws, p.off_dxp),
+                     found_inf, redo, mr, (const int32_t*)nullptr);
   trace_end(p, GRPO_TRACE_DX, st);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.ksplit > 1) {
     hipLaunchKernelGGL(dx_reduce_kernel<E>, dim3((unsigned)p.R), dim3(256), 0, st, p.H, p.R, c0,
                        p.ksplit, ntok, idx, (const float*)ws_ptr<float>(ws, p.off_dxp), saved,
-                       grad_loss, loss_scale, (T*)dX, found_inf, redo, mr);
+                       grad_loss, loss_scale, (T*)dx_out(p, dX, c0), stage_row0(p, c0),
+                       found_inf, redo, mr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (dW) {
@@ -1620,9 +1643,9 @@ hipError_t chunk_grads(const Plan& p, void* ws, int64_t c0, const void* Xq, cons
     hipLaunchKernelGGL(xg_scale_kernel, dim3(1), dim3(256), 0, st, p.R, c0, ntok, idx, saved,
                        grad_loss, loss_scale, redo, mr, xs);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(gather_rows_kernel<E>, dim3((unsigned)p.R), dim3(256), 0, st,
-                       (const T*)Xq, p.H, p.R, c0, ntok, idx, saved, grad_loss, loss_scale, Xg,
-                       redo, mr, (const float*)xs);
+    hipLaunchKernelGGL(gather_cols_kernel<E>, dim3((unsigned)(p.R / 64), (unsigned)(p.H / 64)),
+                       dim3(256), 0, st, (const T*)Xq, p.H, p.R, c0, ntok, idx, saved, grad_loss,
+                       loss_scale, Xg, redo, mr, (const float*)xs);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     trace_begin(p, GRPO_TRACE_DW, st);
     hipLaunchKernelGGL(dw_kernel<E>, dim3(kNumWG), dim3(kThreads), 0, st, p.H,
@@ -1729,9 +1752,11 @@ hipError_t fused_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, c
                        dim3(256), 0, st, p.Vpad, nvt, c0, p.R, ntok, idx, targets, saved,
                        (const float*)pm, Tb, (const int32_t*)rd);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (p.ring && (e = p.ring->acquire(c0)) != hipSuccess) return e;
     e = chunk_grads<E>(p, ws, c0, Xq, W, saved, grad_loss, loss_scale, dX, dW, accumulate_dW,
                        found_inf, st, rd, pm);
     if (e != hipSuccess) return e;
+    if (p.ring && (e = p.ring->transfer(c0)) != hipSuccess) return e;
   }
   return launch_loss_final(p, ws, 1, status, loss, st);
 }
@@ -1752,7 +1777,8 @@ hipError_t piece_dx(const Plan& p, void* ws, int64_t c0, int piece, const void* 
                      piece == 0 ? 1 : 2, ws_ptr<int32_t>(ws, p.off_ntok),
                      ws_ptr<int32_t>(ws, p.off_idx), (const char*)W,
                      (const char*)ws_ptr<T>(ws, p.off_T), (const float*)nullptr,
-                     (const float*)nullptr, 1.f, (T*)nullptr, ws_ptr<float>(ws, p.off_dxp),
+                     (const float*)nullptr, 1.f, (T*)nullptr, (int64_t)-1,
+                     ws_ptr<float>(ws, p.off_dxp),
                      found_inf, (const int32_t*)nullptr, (const float*)nullptr, gate);
   if (traced) trace_end(p, GRPO_TRACE_DX, st);
   return hipGetLastError();
@@ -1770,7 +1796,7 @@ hipError_t split_dx_final(const Plan& p, void* ws, int64_t c0, const void* W,
                      st, p.H, p.V, p.R, c0, nht, p.ksplit, ws_ptr<int32_t>(ws, p.off_ntok),
                      ws_ptr<int32_t>(ws, p.off_idx), targets,
                      (const float*)ws_ptr<float>(ws, p.off_dxp), saved, grad_loss, loss_scale, pm,
-                     (const T*)W, (T*)dX, found_inf);
+                     (const T*)W, (T*)dx_out(p, dX, c0), stage_row0(p, c0), found_inf);
   return hipGetLastError();
 }
 
@@ -1894,9 +1920,11 @@ hipError_t fused_split_impl(const Plan& p, void* ws, const void* Xq, const void*
       if ((e = hipGetLastError()) != hipSuccess) return e;
       if ((e = piece_dx<E>(p, ws, c0, j, W, found_inf, st, rd, false)) != hipSuccess) return e;
     }
+    if (p.ring && (e = p.ring->acquire(c0)) != hipSuccess) return e;
     e = split_dx_final<E>(p, ws, c0, W, targets, saved, grad_loss, loss_scale, pm, dX,
                           found_inf, st);
     if (e != hipSuccess) return e;
+    if (p.ring && (e = p.ring->transfer(c0)) != hipSuccess) return e;
   }
   return launch_loss_final(p, ws, 1, status, loss, st);
 }

@@ -30,7 +30,8 @@ __device__ inline void fma_tile(const float (*As)[kPadLds], const float (*Bs)[kP
   }
 }
 
-// z = X[idx[r]] . W[v] for a 64-token x 64-vocabulary tile, K = H.
+// z = X[idx[r]] . W[v] for a 64-token x 64-vocabulary tile, K = H (any multiple of 8: the
+// last reduction step's entries past H load as 0).
 template <class E>
 __device__ inline void logits_tile(const typename E::T* __restrict__ xrow,
                                    const typename E::T* __restrict__ wrow, bool vok, int64_t H,
@@ -41,10 +42,11 @@ __device__ inline void logits_tile(const typename E::T* __restrict__ xrow,
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
   for (int64_t k0 = 0; k0 < H; k0 += kBK) {
+    const bool kok = k0 + lk < H;  // H % 4 == 0: a thread's 4 entries are all in or all out
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      As[lk + j][lrow] = E::to_f32(xrow[k0 + lk + j]);
-      Bs[lk + j][lrow] = vok ? E::to_f32(wrow[k0 + lk + j]) : 0.0f;
+      As[lk + j][lrow] = kok ? E::to_f32(xrow[k0 + lk + j]) : 0.0f;
+      Bs[lk + j][lrow] = vok && kok ? E::to_f32(wrow[k0 + lk + j]) : 0.0f;
     }
     __syncthreads();
     fma_tile(As, Bs, ty, tx, acc);
@@ -171,14 +173,16 @@ simple_recompute_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t c0, float sc
   }
 }
 
-// dX[idx[r]] = c * g_r * sum_v T[r][v] W[v]   (c = grad_loss / loss_scale)
+// dX[idx[r]] = c * g_r * sum_v T[r][v] W[v]   (c = grad_loss / loss_scale; row r - srow0
+// instead of idx[r] when srow0 >= 0: a staging slot of the gradient offload)
 template <class E>
 __global__ void __launch_bounds__(256)
 simple_dx_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t c0,
                  const int32_t* __restrict__ ntok_p, const int32_t* __restrict__ idx,
                  const typename E::T* __restrict__ T, const typename E::T* __restrict__ W,
                  const float* __restrict__ saved, const float* __restrict__ grad_loss,
-                 float loss_scale, typename E::T* __restrict__ dX, int32_t* __restrict__ found_inf) {
+                 float loss_scale, typename E::T* __restrict__ dX, int64_t srow0,
+                 int32_t* __restrict__ found_inf) {
   __shared__ float As[kBK][kPadLds];
   __shared__ float Bs[kBK][kPadLds];
   const int ntok = *ntok_p;
@@ -199,7 +203,7 @@ simple_dx_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t c0,
     for (int j = 0; j < 4; ++j) {
       As[lk + j][lrow] = E::to_f32(trow[v0 + lk + j]);
       const int64_t v = v0 + kr;
-      Bs[kr][hc + j] = v < V ? E::to_f32(W[v * H + h0 + hc + j]) : 0.0f;
+      Bs[kr][hc + j] = v < V && h0 + hc < H ? E::to_f32(W[v * H + h0 + hc + j]) : 0.0f;
     }
     __syncthreads();
     fma_tile(As, Bs, ty, tx, acc);
@@ -213,12 +217,13 @@ simple_dx_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t c0,
     if (r >= ntok) continue;
     const int64_t t = idx[r];
     const float gs = saved[t * 4 + 3] * c;
+    if (h0 + tx * 4 >= H) continue;  // the last H tile's columns past H (H % 4 == 0)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float val = acc[i][j] * gs;
       const typename E::T o = E::from_f32(val);
       bad |= !isfinite(E::to_f32(o));
-      dX[t * H + h0 + tx * 4 + j] = o;
+      dX[(srow0 < 0 ? t : r - srow0) * H + h0 + tx * 4 + j] = o;
     }
   }
   if (bad) atomicOr(found_inf, 1);
@@ -256,7 +261,7 @@ simple_dw_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       As[kr][cc + j] = ok ? E::to_f32(T[r * Vpad + v0 + cc + j]) : 0.0f;
-      Bs[kr][cc + j] = ok ? gs * E::to_f32(Xq[t * H + h0 + cc + j]) : 0.0f;
+      Bs[kr][cc + j] = ok && h0 + cc < H ? gs * E::to_f32(Xq[t * H + h0 + cc + j]) : 0.0f;
     }
     __syncthreads();
     fma_tile(As, Bs, ty, tx, acc);
@@ -266,7 +271,7 @@ simple_dw_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int 
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t v = v0 + ty * 4 + i;
-    if (v >= V) continue;
+    if (v >= V || h0 + tx * 4 >= H) continue;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float* o = dW + v * H + h0 + tx * 4 + j;
@@ -305,13 +310,17 @@ hipError_t simple_bwd(const Plan& p, void* ws, const void* Xq, const void* W,
                        (const T*)W, targets, saved, Tbuf);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(simple_dx_kernel<E>, dim3((unsigned)(p.R / kT), (unsigned)(p.H / kT)),
+    if (p.ring && (e = p.ring->acquire(c0)) != hipSuccess) return e;
+    const unsigned htiles = (unsigned)((p.H + kT - 1) / kT);
+    hipLaunchKernelGGL(simple_dx_kernel<E>, dim3((unsigned)(p.R / kT), htiles),
                        dim3(256), 0, st, p.H, p.V, p.Vpad, c0, ntok, idx, (const T*)Tbuf,
-                       (const T*)W, saved, grad_loss, loss_scale, (T*)dX, found_inf);
+                       (const T*)W, saved, grad_loss, loss_scale, (T*)dx_out(p, dX, c0),
+                       stage_row0(p, c0), found_inf);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (p.ring && (e = p.ring->transfer(c0)) != hipSuccess) return e;
     if (dW) {
-      hipLaunchKernelGGL(simple_dw_kernel<E>, dim3((unsigned)(p.Vpad / kT), (unsigned)(p.H / kT)),
+      hipLaunchKernelGGL(simple_dw_kernel<E>, dim3((unsigned)(p.Vpad / kT), htiles),
                          dim3(256), 0, st, p.H, p.V, p.Vpad, p.R, c0,
                          c0 == 0 ? accumulate_dW : 1, ntok, idx, (const T*)Tbuf, (const T*)Xq,
                          saved, grad_loss, loss_scale, dW, found_inf);

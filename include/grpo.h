@@ -29,8 +29,10 @@
  *     and never aborts.  All work is enqueued on `stream` (a hipStream_t; NULL = the
  *     default stream) in order, and may still be running when the call returns.
  *   - Matrices are row-major and dense: X_q, X_p, dX_q are [S*L, H] with row t = position
- *     t % L of sequence t / L; W is [V, H].  H must be a positive multiple of 64; V is
- *     arbitrary (ragged vocabulary tails are handled).  S * L must fit in int32.
+ *     t % L of sequence t / L; W is [V, H].  H must be a positive multiple of 8 (16-byte
+ *     rows of 16-bit data); 16-bit inputs with H a multiple of 256 run on the MFMA
+ *     kernels, everything else on fp32-accumulating FMA kernels.  V is arbitrary (ragged
+ *     vocabulary tails are handled).  S * L must fit in int32.
  *   - `targets[t]` is the token that row t's hidden state predicts (the caller has already
  *     shifted ids by one position).  Rows with mask 0 are never read and their outputs are 0;
  *     a NaN in a masked-out row therefore sets no flag.
@@ -60,7 +62,7 @@ typedef enum grpo_dtype {
 typedef enum grpo_status {
   GRPO_OK = 0,
   GRPO_ERR_NULL = -1,      /* a required pointer is NULL                                  */
-  GRPO_ERR_SHAPE = -2,     /* a size is out of range (G < 2, H not a multiple of 64, ...) */
+  GRPO_ERR_SHAPE = -2,     /* a size is out of range (G < 2, H not a multiple of 8, ...)  */
   GRPO_ERR_DTYPE = -3,     /* unknown grpo_dtype                                          */
   GRPO_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned                            */
   GRPO_ERR_WORKSPACE = -5, /* workspace smaller than grpo_workspace_bytes()               */
@@ -130,6 +132,24 @@ typedef struct grpo_options {
   int trace_capacity;
   void* const* trace_events;
   int* trace_count;
+  /* Gradient offload of grpo_loss_fwd_bwd to host memory: what a training step holds
+   * between its forward and its backward goes to system RAM asynchronously, at a small
+   * cost in step time [Long-context GRPO (note.com), §2, the offloaded activations].
+   * dx_host: NULL, or pinned host memory (hipHostMalloc) of S*L rows x H in `dtype`, 16-byte
+   * aligned.  When set, dXq must be NULL and no device dX is written: each chunk's dX rows
+   * go to one of two staging slots in the workspace and are copied from there to dx_host on
+   * copy_stream while the next chunks compute.  Row r of dx_host then holds the gradient of
+   * the r-th loss row (mask = 1 rows in order); the rows past the loss-row count are
+   * undefined.  dw_host: NULL, or pinned host memory of V x H fp32, which receives dW (still
+   * accumulated in the dW given to the call) after the last chunk.  copy_stream: required
+   * when either is set, not the call's stream; a stream of the same device, created with
+   * the default priority.  Before the call returns, `stream` is made to wait for the
+   * copies, so that work enqueued on it afterwards (grpo_grad_restore, an event) finds the
+   * host buffers complete.  grpo_grad_restore brings the gradients back.  The workspace
+   * grows by two chunks of rows x H (grpo_workspace_bytes_opts).                           */
+  void* dx_host;
+  void* dw_host;
+  grpo_stream_t copy_stream;
 } grpo_options;
 
 /* Bits of the forward's status word. */
@@ -261,6 +281,7 @@ int grpo_loss_bwd(const void* Xq, const void* W, grpo_dtype dtype, const int64_t
  *   autograd caller passes NULL and 1, keeps dXq (and dW), and applies its upstream
  *   gradient later with grpo_scale_grad.
  *   workspace: at least grpo_workspace_bytes(..., need_dW = (dW != NULL)).
+ *   dXq may be NULL when opts->dx_host is set (the gradient offload, see grpo_options).
  * Results equal grpo_loss_fwd followed by grpo_loss_bwd up to rounding: the kept softmax
  * terms are rounded to the storage type once more than the recomputed ones.  fp32, and H
  * not a multiple of 256, run the two passes back to back inside this call. */
@@ -280,6 +301,33 @@ int grpo_loss_fwd_bwd(const void* Xq, const void* Xp, const void* W, grpo_dtype 
 int grpo_scale_grad(void* dXq, grpo_dtype dtype, int64_t rows, int64_t H, float* dW, int64_t V,
                     const float* grad_loss, float loss_scale, int32_t* found_inf,
                     grpo_stream_t stream);
+
+/* Workspace of grpo_grad_restore: the loss-row list of S*L rows and two staging slots of
+ * chunk rows x H (chunk_rows of opts, or 4096). */
+size_t grpo_restore_workspace_bytes(int64_t S, int64_t L, int64_t H, grpo_dtype dtype,
+                                    const grpo_options* opts);
+
+/* The way back of the gradient offload (grpo_options.dx_host / dw_host of
+ * grpo_loss_fwd_bwd), with the upstream gradient applied as grpo_scale_grad applies it:
+ *   dXq[t] = dx_host[k] * grad_loss / loss_scale for the k-th loss row t (mask[t] = 1),
+ *            0 for the other rows;
+ *   dW     = dw_host * grad_loss / loss_scale;
+ * the product is skipped when the factor is exactly 1, so the results equal those of a
+ * device-held gradient scaled by grpo_scale_grad, bit for bit.  grad_loss: fp32 [1] device,
+ * or NULL for 1.0.  dx_host, dXq: both set or both NULL (dtype, S*L rows x H); dw_host, dW:
+ * both set or both NULL (fp32 V x H); at least one pair.  found_inf: int32 [1] device, set to
+ * 1 on a non-finite product (never cleared).  The host-to-device copies run on
+ * opts->copy_stream (required, not `stream`, default priority) after the work already
+ * enqueued on `stream`, each chunk of rows into one of two staging slots of the workspace
+ * and scattered on `stream` as it lands; `stream` waits for every copy, so the outputs are
+ * complete for work enqueued on it afterwards.  The host buffers must stay allocated until
+ * then.  workspace: at least grpo_restore_workspace_bytes(S, L, H, dtype, opts).  dXq, dW
+ * and the host buffers 16-byte aligned; H a multiple of 8. */
+int grpo_grad_restore(const void* dx_host, const float* dw_host, grpo_dtype dtype,
+                      const uint8_t* mask, int64_t S, int64_t L, int64_t H, int64_t V,
+                      const float* grad_loss, float loss_scale, void* dXq, float* dW,
+                      int32_t* found_inf, const grpo_options* opts, void* workspace,
+                      size_t workspace_bytes, grpo_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -44,7 +44,8 @@ def test_workspace_bytes(lib):
     assert f(8, 20480, 4096, 128256, 1, 0) > 0
     assert f(8, 20480, 4096, 128256, 1, 0) == f(8, 20480, 4096, 128256, 1, 0)
     assert f(0, 10, 64, 10, 1, 0) == 0          # S < 1
-    assert f(2, 10, 100, 10, 1, 0) == 0         # H not a multiple of 64
+    assert f(2, 10, 100, 10, 1, 0) == 0         # H not a multiple of 8
+    assert f(2, 10, 72, 10, 1, 0) > 0           # H a multiple of 8 (FMA kernels)
     assert f(2, 10, 64, 10, 7, 0) == 0          # bad dtype
     # O(chunk): doubling L adds only per-row bookkeeping (indices, partials: about 1 KB a
     # row), against 2 * 2 * V bytes a row for materialised policy and reference logits
@@ -89,7 +90,7 @@ def test_bad_arguments_rejected_before_launch(lib):
     rc = lib.grpo_loss_fwd(p, p, p, 9, p, p, p, 2, 3, 64, 5, ctypes.c_float(0.04), p, p,
                            nul, nul, nul, p, nul, p, ctypes.c_size_t(1 << 40), nul)
     assert rc == -3
-    rc = lib.grpo_loss_fwd(p, p, p, 1, p, p, p, 2, 3, 96, 5, ctypes.c_float(0.04), p, p,
+    rc = lib.grpo_loss_fwd(p, p, p, 1, p, p, p, 2, 3, 100, 5, ctypes.c_float(0.04), p, p,
                            nul, nul, nul, p, nul, p, ctypes.c_size_t(1 << 40), nul)
     assert rc == -2
     odd = ctypes.c_void_p(18)
@@ -224,8 +225,60 @@ def test_noalloc_rejects_before_launch(lib):
     f = ctypes.c_float(0.04)
     assert lib.grpo_loss_fwd_noalloc(nul, p, p, 1, p, p, p, 2, 3, 64, 5, f, p, p, nul, nul,
                                      nul, p, nul, nul) == -1
-    assert lib.grpo_loss_fwd_noalloc(p, p, p, 1, p, p, p, 2, 3, 96, 5, f, p, p, nul, nul, nul,
+    assert lib.grpo_loss_fwd_noalloc(p, p, p, 1, p, p, p, 2, 3, 100, 5, f, p, p, nul, nul, nul,
                                      p, nul, nul) == -2
     # the long-context forward: 118 MB of partials, past the 64 MiB array
     assert lib.grpo_loss_fwd_noalloc(p, p, p, 1, p, p, p, 8, 20480, 4096, 128256, f, p, p,
                                      nul, nul, nul, p, nul, nul) == -9
+
+
+def test_offload_options_validated(lib):
+    """Gradient offload: host buffers need a copy stream other than the call's stream, the
+    offload takes dXq NULL (and dW for dw_host), the workspace grows by two staging slots
+    of a chunk's rows, and grpo_grad_restore checks its arguments, all before any launch."""
+    import grpo_loss_amd as g
+    p = ctypes.c_void_p(256)
+    cs = ctypes.c_void_p(4096)
+    nul = None
+    f = ctypes.c_float
+    S, L, H, V = 8, 20480, 4096, 128256
+    base = lib.grpo_workspace_bytes_opts(S, L, H, V, 1, 0, None)
+    o = g.options()
+    o.dx_host = 512
+    assert lib.grpo_workspace_bytes_opts(S, L, H, V, 1, 0, ctypes.byref(o)) == 0  # no stream
+    o.copy_stream = cs.value
+    grown = lib.grpo_workspace_bytes_opts(S, L, H, V, 1, 0, ctypes.byref(o))
+    assert grown - base == 2 * 4096 * H * 2
+    o.dx_host = 520                                    # not 16-byte aligned
+    assert lib.grpo_workspace_bytes_opts(S, L, H, V, 1, 0, ctypes.byref(o)) == 0
+    o.dx_host = 512
+
+    def fb(dXq, dW, opts, stream, ws=1 << 40):
+        return lib.grpo_loss_fwd_bwd(p, p, p, 1, p, p, p, 2, 3, 256, 5, f(0.04), nul, f(1.0), p,
+                                     p, nul, nul, nul, p, dXq, dW, 0, p, opts, p,
+                                     ctypes.c_size_t(ws), stream)
+    assert fb(p, nul, ctypes.byref(o), nul) == -8      # dXq given with dx_host
+    assert fb(nul, nul, ctypes.byref(o), cs) == -8     # copy stream == call stream
+    o2 = g.options()
+    o2.dw_host, o2.copy_stream = 512, cs.value
+    assert fb(p, nul, ctypes.byref(o2), nul) == -8     # dw_host without a device dW
+    assert fb(nul, nul, None, nul) == -1               # no dXq, no offload
+    # valid arguments get as far as the device check (no GPU here)
+    assert fb(nul, nul, ctypes.byref(o), nul) == -7
+    # restore
+    rb = lib.grpo_restore_workspace_bytes(1, 1000, 256, 1, None)
+    assert rb >= 2 * 1000 * 4 + 2 * 1000 * 256 * 2
+    assert lib.grpo_restore_workspace_bytes(1, 1000, 100, 1, None) == 0
+
+    def rs(dxh, dwh, dX, dW, opts, ws=1 << 40, stream=nul, H=256):
+        return lib.grpo_grad_restore(dxh, dwh, 1, p, 1, 1000, H, 50, nul, f(1.0), dX, dW, p,
+                                     opts, p, ctypes.c_size_t(ws), stream)
+    oc = g.options()
+    oc.copy_stream = cs.value
+    assert rs(p, nul, p, nul, None) == -1              # no copy stream
+    assert rs(p, nul, nul, nul, ctypes.byref(oc)) == -1  # dx_host without dXq
+    assert rs(nul, nul, nul, nul, ctypes.byref(oc)) == -1  # nothing to restore
+    assert rs(p, nul, p, nul, ctypes.byref(oc), H=100) == -2
+    assert rs(p, nul, p, nul, ctypes.byref(oc), stream=cs) == -8
+    assert rs(p, nul, p, nul, ctypes.byref(oc), ws=8) == -5
+    assert rs(p, p, p, p, ctypes.byref(oc)) == -7

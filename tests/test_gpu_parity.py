@@ -947,3 +947,152 @@ def test_kernel_trace_brackets_launches(kernel):
     assert tr.count.value == expect and len(ms) == expect and all(t > 0 for t in ms)
     for k in ("loss", "dXq", "dW", "saved"):
         assert torch.equal(ref[k], got[k]), k
+
+
+# ------------------------------------------------------------------ gradient offload
+
+def _bits(t):
+    return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
+
+
+OFFLOAD_CASES = {
+    # vocabulary-split single pass (no dW), 5 chunks of 256 rows: both staging slots reused
+    "bf16-split": ("qwen2.5-1.5b-bf16", dict(G=8, L=160, prefix=16, comp_min=8, comp_max=144),
+                   False, 256),
+    # single pass with dW (whole-vocabulary chunks), 2 chunks, ragged last one
+    "bf16-dW": ("llama3.1-8b-train-bf16", SMALL["llama3.1-8b-train-bf16"], True, 256),
+    "f16-split": ("phi4-f16", SMALL["phi4-f16"], False, 0),
+    # fp32: the FMA kernels
+    "f32-dW": ("tiny-f32", SMALL["tiny-f32"], True, 0),
+}
+
+
+@pytest.mark.parametrize("case", list(OFFLOAD_CASES))
+def test_offload_roundtrip_bit_identical(case):
+    """grpo_loss_fwd_bwd with dx_host / dw_host, then grpo_grad_restore: the gradients are
+    the bits of the device-held ones scaled by grpo_scale_grad, for an upstream gradient of
+    1 (no product) and of 0.7; the host rows are the loss rows in order; loss and saved
+    terms are unchanged by the offload."""
+    g = _lib()
+    name, small, need_dW, chunk_rows = OFFLOAD_CASES[case]
+    wl = dataclasses.replace(workload_by_name(name), **small)
+    _say(f"[offload] {case}: N={wl.N} H={wl.H} V={wl.V} chunk_rows={chunk_rows}")
+    d = to_device(generate(wl))
+    opts = g.options(chunk_rows=chunk_rows) if chunk_rows else None
+    adv = g.grpo_advantages(d["rewards"], wl.eps)
+    args = (d["xq"], d["xp"], d["W"], d["targets"], d["mask"], adv, wl.beta, wl.L, None, 1.0)
+    ref = g.grpo_loss_fwd_bwd(*args, need_dW=need_dW, opts=opts)
+    dx_host = torch.empty(wl.N, wl.H, dtype=d["xq"].dtype, pin_memory=True)
+    dw_host = (torch.empty(wl.V, wl.H, dtype=torch.float32, pin_memory=True) if need_dW
+               else None)
+    off = g.grpo_loss_fwd_bwd(*args, need_dW=need_dW, opts=opts, dx_host=dx_host,
+                              dw_host=dw_host)
+    assert off["dXq"] is None
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(off["loss"]), _bits(ref["loss"]))
+    assert torch.equal(_bits(off["saved"]), _bits(ref["saved"]))
+    assert int(off["found_inf"].item()) == 0 and int(off["status"].item()) == 0
+    rows = torch.nonzero(d["mask"].bool()).flatten()
+    assert torch.equal(_bits(dx_host[:rows.numel()]), _bits(ref["dXq"][rows].cpu()))
+    if need_dW:
+        assert torch.equal(_bits(dw_host), _bits(ref["dW"].cpu()))
+    for grad in (1.0, 0.7):
+        gl = torch.full((1,), grad, dtype=torch.float32, device="cuda")
+        dX = ref["dXq"].clone()
+        dW = ref["dW"].clone() if need_dW else None
+        g.grpo_scale_grad(dX, gl, 1.0, dW=dW)
+        r = g.grpo_grad_restore(d["mask"], dx_host, dw_host, gl, 1.0)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(r["dXq"]), _bits(dX)), grad
+        if need_dW:
+            assert torch.equal(_bits(r["dW"]), _bits(dW)), grad
+        assert int(r["found_inf"].item()) == 0
+
+
+@pytest.mark.parametrize("need_dW", [False, True], ids=["dX", "dX+dW"])
+def test_autograd_offload_bit_identical(need_dW):
+    """grpo_loss(single_pass=True, offload=True) returns the bits of the device-held single
+    pass, over two steps (the pinned buffers are reused), for an upstream gradient of 3."""
+    g = _lib()
+    wl = dataclasses.replace(workload_by_name("llama3.1-8b-train-bf16"),
+                             **SMALL["llama3.1-8b-train-bf16"])
+    d = to_device(generate(wl))
+
+    def step(offload):
+        xq = d["xq"].view(wl.S, wl.L, wl.H).clone().requires_grad_(True)
+        W = d["W"].clone().requires_grad_(need_dW)
+        loss, _ = g.grpo_loss(xq, d["xp"].view(wl.S, wl.L, wl.H), W, d["targets"], d["mask"],
+                              d["rewards"], beta=wl.beta, eps=wl.eps, need_dW=need_dW,
+                              single_pass=True, offload=offload)
+        (3.0 * loss).backward()
+        torch.cuda.synchronize()
+        return loss.detach(), xq.grad, (W.grad if need_dW else None)
+
+    base = step(False)
+    for _ in range(2):
+        got = step(True)
+        assert torch.equal(_bits(got[0]), _bits(base[0]))
+        assert torch.equal(_bits(got[1]), _bits(base[1]))
+        if need_dW:
+            assert torch.equal(_bits(got[2]), _bits(base[2]))
+
+
+def test_autograd_grad_hint_applied_before_narrowing():
+    """With grad_hint equal to the actual upstream gradient, the single pass's dX is the
+    bits of grpo_loss_fwd_bwd called with that gradient (one rounding to bf16), not a
+    rounded gradient rounded again."""
+    g = _lib()
+    wl = dataclasses.replace(workload_by_name("qwen2.5-1.5b-bf16"), **SMALL["qwen2.5-1.5b-bf16"])
+    d = to_device(generate(wl))
+    gr = 0.3
+    xq = d["xq"].view(wl.S, wl.L, wl.H).clone().requires_grad_(True)
+    loss, _ = g.grpo_loss(xq, d["xp"].view(wl.S, wl.L, wl.H), d["W"], d["targets"], d["mask"],
+                          d["rewards"], beta=wl.beta, eps=wl.eps, single_pass=True,
+                          grad_hint=gr)
+    (gr * loss).backward()
+    adv = g.grpo_advantages(d["rewards"], wl.eps)
+    gl = torch.full((1,), gr, dtype=torch.float32, device="cuda")
+    ref = g.grpo_loss_fwd_bwd(d["xq"], d["xp"], d["W"], d["targets"], d["mask"], adv, wl.beta,
+                              wl.L, gl, 1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(xq.grad.reshape(wl.N, wl.H)), _bits(ref["dXq"]))
+
+
+# H a multiple of 8 but not of 256: the FMA kernels, with a partial last reduction step
+# over H and a partial last H tile of dX and dW
+H8_CASES = {
+    "f32-H72": ("tiny-f32", dict(H=72), True),
+    "bf16-H200": ("qwen2.5-1.5b-bf16", dict(SMALL["qwen2.5-1.5b-bf16"], H=200, V=5003), True),
+    "f16-H328": ("phi4-f16", dict(SMALL["phi4-f16"], H=328, V=3001), False),
+}
+
+
+@pytest.mark.parametrize("single_pass", [False, True], ids=["two-pass", "single-pass"])
+@pytest.mark.parametrize("case", list(H8_CASES))
+def test_hidden_size_multiple_of_8(case, single_pass):
+    name, repl, need_dW = H8_CASES[case]
+    wl = dataclasses.replace(workload_by_name(name), need_dW=need_dW, **repl)
+    _say(f"[H%8] {case} single_pass={single_pass}: N={wl.N} H={wl.H} V={wl.V}")
+    check_small(wl, generate(wl), single_pass=single_pass)
+
+
+def test_restore_scatter_matches_mask_order():
+    """grpo_grad_restore over 5,000,003 rows with a random mask: row t of dXq is host row k
+    for the k-th mask-1 row and 0 for the others.  This checks the row compaction exactly
+    (1,221 blocks of 4,096 rows, so its block scan takes two rounds, and a ragged last
+    block) and the staging of many chunks."""
+    g = _lib()
+    N, H = 5_000_003, 8
+    rng = np.random.default_rng(11)
+    mask_h = (rng.random(N) < 0.5).astype(np.uint8)
+    n_tok = int(mask_h.sum())
+    host = torch.arange(N, dtype=torch.float32).unsqueeze(1).repeat(1, H).contiguous()
+    host = host.pin_memory()
+    mask = torch.from_numpy(mask_h).cuda()
+    r = g.grpo_grad_restore(mask, dx_host=host)
+    got = r["dXq"].cpu().numpy()
+    want = np.zeros((N, H), np.float32)
+    rows = np.nonzero(mask_h)[0]
+    want[rows] = np.arange(n_tok, dtype=np.float32)[:, None]
+    assert np.array_equal(got, want)
+    assert int(r["found_inf"].item()) == 0
