@@ -347,9 +347,10 @@ def main():
         opts["v"] = None
     if not args.no_offload and args.path == "single":
         # the single pass with its gradients kept in pinned host memory between forward and
-        # backward: each chunk's dX rows are copied out on a second stream while the next
-        # chunks compute, and grpo_grad_restore brings them back (a host-to-device copy the
-        # step waits for).  Reported beside the default, never as `value`.
+        # backward: each chunk's dX rows are copied out by the copy engines while the next
+        # chunks compute, and grpo_grad_restore brings them back (kernels reading host
+        # memory over PCIe, which the step waits for).  Reported beside the default, never
+        # as `value`.
         del ws
         torch.cuda.empty_cache()
         cs = g.offload_stream()
@@ -360,7 +361,7 @@ def main():
         oo.dx_host, oo.copy_stream = dx_host.data_ptr(), cs.cuda_stream
         wso_bytes = g.grpo_workspace_bytes(wl.S, wl.L, wl.H, wl.V, dt, need_dW, oo)
         ws = torch.empty(wso_bytes, dtype=torch.uint8, device="cuda")
-        rws = torch.empty(g.grpo_restore_workspace_bytes(wl.N, wl.H, dt), dtype=torch.uint8,
+        rws = torch.empty(g.grpo_restore_workspace_bytes(wl.N), dtype=torch.uint8,
                           device="cuda")
 
         def step_offload_fwd(step_no):
@@ -373,7 +374,7 @@ def main():
         def step_offload(step_no):
             f = step_offload_fwd(step_no)
             g.grpo_grad_restore(d["mask"], dx_host, dw_host, None, 1.0, dXq=dX, dW=dW,
-                                found_inf=found, copy_stream=cs, workspace=rws)
+                                found_inf=found, workspace=rws)
             return f
 
         ms_fwd, f = timed(step_offload_fwd)

@@ -168,11 +168,11 @@ def load_library():
     lib.grpo_scale_grad.argtypes = [_c_p, ctypes.c_int, _c_i64, _c_i64, _c_p, _c_i64, _c_p,
                                     ctypes.c_float, _c_p, _c_p]
     lib.grpo_restore_workspace_bytes.restype = ctypes.c_size_t
-    lib.grpo_restore_workspace_bytes.argtypes = [_c_i64, _c_i64, _c_i64, ctypes.c_int, opt_p]
+    lib.grpo_restore_workspace_bytes.argtypes = [_c_i64, _c_i64]
     lib.grpo_grad_restore.restype = ctypes.c_int
     lib.grpo_grad_restore.argtypes = [_c_p, _c_p, ctypes.c_int, _c_p, _c_i64, _c_i64, _c_i64,
-                                      _c_i64, _c_p, ctypes.c_float, _c_p, _c_p, _c_p, opt_p,
-                                      _c_p, ctypes.c_size_t, _c_p]
+                                      _c_i64, _c_p, ctypes.c_float, _c_p, _c_p, _c_p, _c_p,
+                                      ctypes.c_size_t, _c_p]
     _LIB = lib
     return lib
 
@@ -422,26 +422,22 @@ def grpo_loss_fwd_bwd(xq, xp, W, targets, mask, adv, beta: float = 0.04, L: int 
             "found_inf": found_inf, "workspace": workspace}
 
 
-def grpo_restore_workspace_bytes(N: int, H: int, dtype: torch.dtype, opts=None) -> int:
-    return int(_LIB.grpo_restore_workspace_bytes(1, N, H, _DTYPE[dtype], _opts(opts)))
+def grpo_restore_workspace_bytes(N: int) -> int:
+    return int(_LIB.grpo_restore_workspace_bytes(1, N))
 
 
 def grpo_grad_restore(mask, dx_host=None, dw_host=None, grad_loss=None, loss_scale: float = 1.0,
-                      dXq=None, dW=None, found_inf=None, copy_stream=None, workspace=None,
-                      stream=None, opts=None):
+                      dXq=None, dW=None, found_inf=None, workspace=None, stream=None):
     """The way back of the gradient offload: dXq [S*L, H] (device, X's dtype; masked rows
     0) from dx_host, and dW [V, H] fp32 from dw_host, both times grad_loss / loss_scale as
-    grpo_scale_grad applies it.  Returns dict(dXq, dW, found_inf).  The host tensors must
-    outlive the copies: they are ordered before any work enqueued on `stream` after this
-    call."""
-    _need(mask, "mask")
+    grpo_scale_grad applies it; the kernels read the pinned host tensors directly.
+    Returns dict(dXq, dW, found_inf).  The host tensors must stay alive until the kernels
+    enqueued on `stream` have run."""
     if dx_host is None and dw_host is None:
         raise ValueError("nothing to restore")
+    _need(mask, "mask")
     N = mask.numel()
     dev = mask.device
-    o = _copy_options(opts)
-    cs = offload_stream(dev) if copy_stream is None else copy_stream
-    o.copy_stream = cs.cuda_stream
     H = (dx_host if dx_host is not None else dw_host).shape[1]
     V = dw_host.shape[0] if dw_host is not None else 0
     if dx_host is not None:
@@ -459,15 +455,14 @@ def grpo_grad_restore(mask, dx_host=None, dw_host=None, grad_loss=None, loss_sca
         found_inf = torch.zeros(1, dtype=torch.int32, device=dev)
     if grad_loss is not None:
         _need(grad_loss, "grad_loss")
-    need = int(_LIB.grpo_restore_workspace_bytes(1, N, H, _DTYPE[dtype], ctypes.byref(o)))
+    need = grpo_restore_workspace_bytes(N)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     _check(_LIB.grpo_grad_restore(_ptr(dx_host), _ptr(dw_host), _DTYPE[dtype], _ptr(mask), 1, N,
                                   H, V, _ptr(grad_loss), float(loss_scale),
                                   _ptr(dXq) if dx_host is not None else None,
                                   _ptr(dW) if dw_host is not None else None, _ptr(found_inf),
-                                  ctypes.byref(o), _ptr(workspace), workspace.numel(),
-                                  _stream(stream)))
+                                  _ptr(workspace), workspace.numel(), _stream(stream)))
     return {"dXq": dXq if dx_host is not None else None,
             "dW": dW if dw_host is not None else None, "found_inf": found_inf}
 

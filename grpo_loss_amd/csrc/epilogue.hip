@@ -427,29 +427,29 @@ scale_kernel(typename E::T* __restrict__ x, int64_t n, const float* __restrict__
   if (bad) atomicOr(found_inf, 1);
 }
 
-// Gradient offload, the way back: dX[idx[r]] = rows[r - r0] * grad_loss / loss_scale for
-// the loss rows r in [r0, r0 + n) of a staging slot, with the arithmetic of scale_kernel
+// Gradient offload, the way back: dst[idx[r]] = src[r] * grad_loss / loss_scale for the
+// rows r < *ntok (idx, ntok null: all n rows, dst[r]), with the arithmetic of scale_kernel
 // (the product skipped when the factor is exactly 1), so the result equals a device-held
-// gradient scaled by grpo_scale_grad bit for bit.  One row per block, 16 bytes per thread
-// and step.
+// gradient scaled by grpo_scale_grad bit for bit.  src is pinned host memory, read over
+// PCIe: no staging copy, and nothing else to overlap with in a backward.  One row per
+// block, 16 bytes per thread and step.
 template <class E>
 __global__ void __launch_bounds__(256)
-restore_rows_kernel(const typename E::T* __restrict__ rows, int64_t r0, int64_t n, int64_t H,
+restore_rows_kernel(const typename E::T* __restrict__ src, int64_t n, int64_t H,
                     const int32_t* __restrict__ ntok_p, const int32_t* __restrict__ idx,
                     const float* __restrict__ grad_loss, float loss_scale,
-                    typename E::T* __restrict__ dX, int32_t* __restrict__ found_inf) {
+                    typename E::T* __restrict__ dst, int32_t* __restrict__ found_inf) {
   typedef typename E::T T;
   constexpr int kPer = 16 / sizeof(T);
-  const int64_t rl = blockIdx.x;
-  const int64_t r = r0 + rl;
-  if (rl >= n || r >= *ntok_p) return;
+  const int64_t r = blockIdx.x;
+  if (r >= n || (ntok_p && r >= *ntok_p)) return;
   const float c = (grad_loss ? *grad_loss : 1.0f) / loss_scale;
-  const T* src = rows + rl * H;
-  T* dst = dX + (int64_t)idx[r] * H;
+  const T* in = src + r * H;
+  T* out = dst + (idx ? (int64_t)idx[r] : r) * H;
   bool bad = false;
   for (int64_t h = (int64_t)threadIdx.x * kPer; h < H; h += 256 * kPer) {
     T v[kPer];
-    __builtin_memcpy(v, src + h, 16);
+    __builtin_memcpy(v, in + h, 16);
     if (c != 1.0f) {
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
@@ -457,7 +457,7 @@ restore_rows_kernel(const typename E::T* __restrict__ rows, int64_t r0, int64_t 
         bad |= !isfinite(E::to_f32(v[j]));
       }
     }
-    __builtin_memcpy(dst + h, v, 16);
+    __builtin_memcpy(out + h, v, 16);
   }
   if (bad) atomicOr(found_inf, 1);
 }
@@ -488,23 +488,23 @@ hipError_t launch_scale_grad(void* dX, int dtype, int64_t nX, float* dW, int64_t
   return scale_one<F32T>(dW, nW, grad_loss, loss_scale, found_inf, st);
 }
 
-hipError_t launch_restore_rows(int dtype, const void* rows, int64_t r0, int64_t n, int64_t H,
+hipError_t launch_restore_rows(int dtype, const void* src, int64_t n, int64_t H,
                                const int32_t* ntok, const int32_t* idx, const float* grad_loss,
-                               float loss_scale, void* dX, int32_t* found_inf, hipStream_t st) {
+                               float loss_scale, void* dst, int32_t* found_inf, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   const dim3 grid((unsigned)n), block(256);
   switch (dtype) {
     case GRPO_F32:
-      hipLaunchKernelGGL(restore_rows_kernel<F32T>, grid, block, 0, st, (const float*)rows, r0,
-                         n, H, ntok, idx, grad_loss, loss_scale, (float*)dX, found_inf);
+      hipLaunchKernelGGL(restore_rows_kernel<F32T>, grid, block, 0, st, (const float*)src, n, H,
+                         ntok, idx, grad_loss, loss_scale, (float*)dst, found_inf);
       break;
     case GRPO_BF16:
-      hipLaunchKernelGGL(restore_rows_kernel<BF16T>, grid, block, 0, st, (const u16*)rows, r0,
-                         n, H, ntok, idx, grad_loss, loss_scale, (u16*)dX, found_inf);
+      hipLaunchKernelGGL(restore_rows_kernel<BF16T>, grid, block, 0, st, (const u16*)src, n, H,
+                         ntok, idx, grad_loss, loss_scale, (u16*)dst, found_inf);
       break;
     default:
-      hipLaunchKernelGGL(restore_rows_kernel<F16T>, grid, block, 0, st, (const u16*)rows, r0,
-                         n, H, ntok, idx, grad_loss, loss_scale, (u16*)dX, found_inf);
+      hipLaunchKernelGGL(restore_rows_kernel<F16T>, grid, block, 0, st, (const u16*)src, n, H,
+                         ntok, idx, grad_loss, loss_scale, (u16*)dst, found_inf);
       break;
   }
   return hipGetLastError();

@@ -289,16 +289,13 @@ hipError_t stream_after(hipStream_t to, hipStream_t from, hipEvent_t ev) {
   return e != hipSuccess ? e : hipStreamWaitEvent(to, ev, 0);
 }
 
-// Workspace of grpo_grad_restore: the loss-row list, then two staging slots of R rows.
+// Workspace of grpo_grad_restore: the loss-row list of S*L rows.
 struct RestorePlan {
-  int64_t R;
-  size_t off_ntok, off_idx, off_rank, off_ring, total;
+  size_t off_ntok, off_idx, off_rank, total;
 };
-RestorePlan restore_plan(int64_t S, int64_t L, int64_t H, int dtype, const grpo_options* opts) {
+RestorePlan restore_plan(int64_t S, int64_t L) {
   RestorePlan r;
   const int64_t N = S * L;
-  const int64_t chunk = opts && opts->chunk_rows > 0 ? opts->chunk_rows : kChunkRows;
-  r.R = N < chunk ? N : chunk;
   size_t o = 0;
   r.off_ntok = o;
   o = align_up(o + compact_bytes(N));
@@ -306,10 +303,29 @@ RestorePlan restore_plan(int64_t S, int64_t L, int64_t H, int dtype, const grpo_
   o = align_up(o + (size_t)N * 4);
   r.off_rank = o;
   o = align_up(o + (size_t)N * 4);
-  r.off_ring = o;
-  o = align_up(o + (size_t)2 * r.R * H * (dtype == GRPO_F32 ? 4 : 2));
   r.total = o;
   return r;
+}
+
+// [p, p + bytes) lies inside one allocation of pinned host memory (hipHostMalloc), which
+// kernels and the copy engines reach over PCIe.  Pageable memory, or a range that runs past
+// its allocation, would fault a kernel that reads it.
+bool pinned_host(const void* p, size_t bytes) {
+  if (!p || bytes == 0) return false;
+  hipPointerAttribute_t a;
+  void* start = nullptr;
+  size_t size = 0;
+  hipDeviceptr_t dp = const_cast<void*>(p);
+  const bool ok =
+      hipPointerGetAttributes(&a, p) == hipSuccess && a.type == hipMemoryTypeHost &&
+      hipPointerGetAttribute(&start, HIP_POINTER_ATTRIBUTE_RANGE_START_ADDR, dp) == hipSuccess &&
+      hipPointerGetAttribute(&size, HIP_POINTER_ATTRIBUTE_RANGE_SIZE, dp) == hipSuccess;
+  if (!ok) {
+    (void)hipGetLastError();  // leave no error behind for the launches' checks
+    return false;
+  }
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(start), q = reinterpret_cast<uintptr_t>(p);
+  return q >= s0 && q - s0 <= size && bytes <= size - (q - s0);
 }
 
 }  // namespace grpo
@@ -330,6 +346,7 @@ const char* grpo_status_string(int status) {
     case GRPO_ERR_DEVICE: return "current device is not gfx950";
     case GRPO_ERR_OPTIONS: return "a loss option is out of range";
     case GRPO_ERR_SCRATCH: return "the forward needs more than the fixed scratch array holds";
+    case GRPO_ERR_HOST: return "a host buffer is not pinned host memory";
     default: return "unknown status";
   }
 }
@@ -524,6 +541,9 @@ int grpo_loss_fwd_bwd(const void* Xq, const void* Xp, const void* W, grpo_dtype 
   if (!(ls_eff > 0.0f) || !isfinite(ls_eff)) return GRPO_ERR_SHAPE;
   if (workspace_bytes < p.total) return GRPO_ERR_WORKSPACE;
   if (!device_ok()) return GRPO_ERR_DEVICE;
+  if ((offload && !pinned_host(opts->dx_host, (size_t)p.N * H * p.esize)) ||
+      (opts && opts->dw_host && !pinned_host(opts->dw_host, (size_t)V * H * 4)))
+    return GRPO_ERR_HOST;
   hipStream_t st = (hipStream_t)stream;
   int launches = 0;  // launches of the traced kernel
   p.trace_n = &launches;
@@ -543,7 +563,6 @@ int grpo_loss_fwd_bwd(const void* Xq, const void* Xp, const void* W, grpo_dtype 
       ring.total = p.N;
       ring.st = st;
       ring.cs = cs;
-      ring.to_host = 1;
       p.ring = &ring;
     }
   }
@@ -572,8 +591,7 @@ int grpo_loss_fwd_bwd(const void* Xq, const void* Xp, const void* W, grpo_dtype 
   if (host_copies) {
     if (opts->dw_host) {
       if (stream_after(cs, st, evs.ev[4]) != hipSuccess ||
-          hipMemcpyAsync(opts->dw_host, dW, (size_t)V * H * 4, hipMemcpyDeviceToHost, cs) !=
-              hipSuccess)
+          copy_to_host(opts->dw_host, dW, (size_t)H * 4, (size_t)V, cs) != hipSuccess)
         return GRPO_ERR_HIP;
     }
     if (stream_after(st, cs, evs.ev[5]) != hipSuccess) return GRPO_ERR_HIP;
@@ -597,19 +615,18 @@ int grpo_scale_grad(void* dXq, grpo_dtype dtype, int64_t rows, int64_t H, float*
   return GRPO_OK;
 }
 
-size_t grpo_restore_workspace_bytes(int64_t S, int64_t L, int64_t H, grpo_dtype dtype,
-                                    const grpo_options* opts) {
-  if (!valid_dtype(dtype) || !sizes_ok(S, L, H, 1) || !options_ok(opts)) return 0;
-  return restore_plan(S, L, H, dtype, opts).total;
+size_t grpo_restore_workspace_bytes(int64_t S, int64_t L) {
+  if (S < 1 || L < 1 || S > INT32_MAX / L) return 0;
+  return restore_plan(S, L).total;
 }
 
 int grpo_grad_restore(const void* dx_host, const float* dw_host, grpo_dtype dtype,
                       const uint8_t* mask, int64_t S, int64_t L, int64_t H, int64_t V,
                       const float* grad_loss, float loss_scale, void* dXq, float* dW,
-                      int32_t* found_inf, const grpo_options* opts, void* workspace,
-                      size_t workspace_bytes, grpo_stream_t stream) {
-  if (!mask || !found_inf || !workspace || !opts || !opts->copy_stream ||
-      (!dx_host != !dXq) || (!dw_host != !dW) || (!dx_host && !dw_host))
+                      int32_t* found_inf, void* workspace, size_t workspace_bytes,
+                      grpo_stream_t stream) {
+  if (!found_inf || (!dx_host != !dXq) || (!dw_host != !dW) || (!dx_host && !dw_host) ||
+      (dx_host && (!mask || !workspace)))
     return GRPO_ERR_NULL;
   if (!valid_dtype(dtype)) return GRPO_ERR_DTYPE;
   if (!sizes_ok(S, L, H, dW ? V : 1) || !(loss_scale > 0.0f) || !isfinite(loss_scale))
@@ -617,53 +634,33 @@ int grpo_grad_restore(const void* dx_host, const float* dw_host, grpo_dtype dtyp
   if (!aligned16(dx_host) || !aligned16(dw_host) || !aligned16(dXq) || !aligned16(dW) ||
       !aligned16(workspace))
     return GRPO_ERR_ALIGN;
-  if (!options_ok(opts) || opts->copy_stream == stream) return GRPO_ERR_OPTIONS;
-  const RestorePlan rp = restore_plan(S, L, H, dtype, opts);
-  if (workspace_bytes < rp.total) return GRPO_ERR_WORKSPACE;
+  const RestorePlan rp = restore_plan(S, L);
+  if (dx_host && workspace_bytes < rp.total) return GRPO_ERR_WORKSPACE;
   if (!device_ok()) return GRPO_ERR_DEVICE;
-  hipStream_t st = (hipStream_t)stream, cs = (hipStream_t)opts->copy_stream;
-  CopyRing ring;
-  RingEvents evs;
-  if (evs.create(&ring) != hipSuccess) return GRPO_ERR_HIP;
-  // the copies start after the work already on `stream` (the forward's own copies)
-  if (stream_after(cs, st, evs.ev[4]) != hipSuccess) return GRPO_ERR_HIP;
+  const int64_t N = S * L;
+  const size_t esize = dtype == GRPO_F32 ? 4 : 2;
+  if ((dx_host && !pinned_host(dx_host, (size_t)N * H * esize)) ||
+      (dw_host && !pinned_host(dw_host, (size_t)V * H * 4)))
+    return GRPO_ERR_HOST;
+  hipStream_t st = (hipStream_t)stream;
   if (dx_host) {
-    const int64_t N = S * L;
     int32_t* ntok = ws_ptr<int32_t>(workspace, rp.off_ntok);
     int32_t* idx = ws_ptr<int32_t>(workspace, rp.off_idx);
     Plan p;
     memset(&p, 0, sizeof(p));
     p.N = N;
     p.H = H;
-    p.esize = dtype == GRPO_F32 ? 4 : 2;
+    p.esize = (int)esize;
     if (launch_compact(mask, N, ntok, idx, ws_ptr<int32_t>(workspace, rp.off_rank), st) !=
             hipSuccess ||
-        launch_zero_masked_rows(p, mask, dXq, st) != hipSuccess)
-      return GRPO_ERR_HIP;
-    ring.slots = ws_ptr<char>(workspace, rp.off_ring);
-    ring.host = reinterpret_cast<char*>(const_cast<void*>(dx_host));
-    ring.row_bytes = (size_t)H * p.esize;
-    ring.rows = rp.R;
-    ring.total = N;
-    ring.st = st;
-    ring.cs = cs;
-    ring.to_host = 0;
-    for (int64_t r0 = 0; r0 < N; r0 += rp.R) {
-      const int64_t n = N - r0 < rp.R ? N - r0 : rp.R;
-      if (ring.acquire(r0) != hipSuccess || ring.transfer(r0) != hipSuccess ||
-          launch_restore_rows(dtype, ring.slot(r0), r0, n, H, ntok, idx, grad_loss, loss_scale,
-                              dXq, found_inf, st) != hipSuccess ||
-          ring.release(r0) != hipSuccess)
-        return GRPO_ERR_HIP;
-    }
-  }
-  if (dw_host) {
-    if (hipMemcpyAsync(dW, dw_host, (size_t)V * H * 4, hipMemcpyHostToDevice, cs) != hipSuccess ||
-        stream_after(st, cs, evs.ev[5]) != hipSuccess ||
-        launch_scale_grad(nullptr, GRPO_F32, 0, dW, V * H, grad_loss, loss_scale, found_inf,
-                          st) != hipSuccess)
+        launch_zero_masked_rows(p, mask, dXq, st) != hipSuccess ||
+        launch_restore_rows(dtype, dx_host, N, H, ntok, idx, grad_loss, loss_scale, dXq,
+                            found_inf, st) != hipSuccess)
       return GRPO_ERR_HIP;
   }
+  if (dw_host && launch_restore_rows(GRPO_F32, dw_host, V, H, nullptr, nullptr, grad_loss,
+                                     loss_scale, dW, found_inf, st) != hipSuccess)
+    return GRPO_ERR_HIP;
   return GRPO_OK;
 }
 

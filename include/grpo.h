@@ -70,8 +70,10 @@ typedef enum grpo_status {
   GRPO_ERR_DEVICE = -7,    /* the current device is not a gfx950 GPU                      */
   GRPO_ERR_OPTIONS = -8,   /* a grpo_options field is out of range, or not supported for  */
                            /* these inputs (fp8_logits with fp32 data)                     */
-  GRPO_ERR_SCRATCH = -9    /* grpo_loss_fwd_noalloc: the forward of these sizes needs more */
+  GRPO_ERR_SCRATCH = -9,   /* grpo_loss_fwd_noalloc: the forward of these sizes needs more */
                            /* than GRPO_NOALLOC_SCRATCH_BYTES                              */
+  GRPO_ERR_HOST = -10      /* a host buffer of the gradient offload is not pinned host     */
+                           /* memory (hipHostMalloc) over its whole extent                 */
 } grpo_status;
 
 /* Loss variants: the four experiments of [Long-context GRPO, §4] and two readings the
@@ -143,10 +145,12 @@ typedef struct grpo_options {
    * undefined.  dw_host: NULL, or pinned host memory of V x H fp32, which receives dW (still
    * accumulated in the dW given to the call) after the last chunk.  copy_stream: required
    * when either is set, not the call's stream; a stream of the same device, created with
-   * the default priority.  Before the call returns, `stream` is made to wait for the
-   * copies, so that work enqueued on it afterwards (grpo_grad_restore, an event) finds the
-   * host buffers complete.  grpo_grad_restore brings the gradients back.  The workspace
-   * grows by two chunks of rows x H (grpo_workspace_bytes_opts).                           */
+   * the default priority.  The copies run on the SDMA engines, beside the kernels.  Before
+   * the call returns, `stream` is made to wait for them, so that work enqueued on it
+   * afterwards (grpo_grad_restore, an event) finds the host buffers complete; a host
+   * buffer that is not pinned memory over its extent is rejected with GRPO_ERR_HOST.
+   * grpo_grad_restore brings the gradients back.  The workspace grows by two chunks of
+   * rows x H (grpo_workspace_bytes_opts).                                                  */
   void* dx_host;
   void* dw_host;
   grpo_stream_t copy_stream;
@@ -302,10 +306,8 @@ int grpo_scale_grad(void* dXq, grpo_dtype dtype, int64_t rows, int64_t H, float*
                     const float* grad_loss, float loss_scale, int32_t* found_inf,
                     grpo_stream_t stream);
 
-/* Workspace of grpo_grad_restore: the loss-row list of S*L rows and two staging slots of
- * chunk rows x H (chunk_rows of opts, or 4096). */
-size_t grpo_restore_workspace_bytes(int64_t S, int64_t L, int64_t H, grpo_dtype dtype,
-                                    const grpo_options* opts);
+/* Workspace of grpo_grad_restore: the loss-row list of S*L rows (0 for invalid sizes). */
+size_t grpo_restore_workspace_bytes(int64_t S, int64_t L);
 
 /* The way back of the gradient offload (grpo_options.dx_host / dw_host of
  * grpo_loss_fwd_bwd), with the upstream gradient applied as grpo_scale_grad applies it:
@@ -313,21 +315,23 @@ size_t grpo_restore_workspace_bytes(int64_t S, int64_t L, int64_t H, grpo_dtype 
  *            0 for the other rows;
  *   dW     = dw_host * grad_loss / loss_scale;
  * the product is skipped when the factor is exactly 1, so the results equal those of a
- * device-held gradient scaled by grpo_scale_grad, bit for bit.  grad_loss: fp32 [1] device,
- * or NULL for 1.0.  dx_host, dXq: both set or both NULL (dtype, S*L rows x H); dw_host, dW:
- * both set or both NULL (fp32 V x H); at least one pair.  found_inf: int32 [1] device, set to
- * 1 on a non-finite product (never cleared).  The host-to-device copies run on
- * opts->copy_stream (required, not `stream`, default priority) after the work already
- * enqueued on `stream`, each chunk of rows into one of two staging slots of the workspace
- * and scattered on `stream` as it lands; `stream` waits for every copy, so the outputs are
- * complete for work enqueued on it afterwards.  The host buffers must stay allocated until
- * then.  workspace: at least grpo_restore_workspace_bytes(S, L, H, dtype, opts).  dXq, dW
- * and the host buffers 16-byte aligned; H a multiple of 8. */
+ * device-held gradient scaled by grpo_scale_grad, bit for bit.  The kernels read the pinned
+ * host buffers directly over PCIe (no staging copy: in a backward there is no computation
+ * of this op to overlap it with), enqueued on `stream` after the work already there.
+ *   dx_host, dXq: both set or both NULL (dtype, S*L rows x H); dw_host, dW: both set or
+ *   both NULL (fp32 V x H); at least one pair.  Host buffers must be pinned host memory
+ *   over their whole extent (else GRPO_ERR_HOST, before anything is enqueued) and stay
+ *   allocated until the kernels have run.
+ *   mask      the forward's mask (loss rows are found again from it); needed with dx_host.
+ *   grad_loss fp32 [1] device, or NULL for 1.0.
+ *   found_inf int32 [1] device, set to 1 on a non-finite product (never cleared).
+ *   workspace at least grpo_restore_workspace_bytes(S, L) (needed with dx_host).
+ * dXq, dW and the host buffers 16-byte aligned; H a multiple of 8. */
 int grpo_grad_restore(const void* dx_host, const float* dw_host, grpo_dtype dtype,
                       const uint8_t* mask, int64_t S, int64_t L, int64_t H, int64_t V,
                       const float* grad_loss, float loss_scale, void* dXq, float* dW,
-                      int32_t* found_inf, const grpo_options* opts, void* workspace,
-                      size_t workspace_bytes, grpo_stream_t stream);
+                      int32_t* found_inf, void* workspace, size_t workspace_bytes,
+                      grpo_stream_t stream);
 
 #ifdef __cplusplus
 }

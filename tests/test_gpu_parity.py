@@ -1080,7 +1080,7 @@ def test_restore_scatter_matches_mask_order():
     """grpo_grad_restore over 5,000,003 rows with a random mask: row t of dXq is host row k
     for the k-th mask-1 row and 0 for the others.  This checks the row compaction exactly
     (1,221 blocks of 4,096 rows, so its block scan takes two rounds, and a ragged last
-    block) and the staging of many chunks."""
+    block) and the scatter from pinned host memory."""
     g = _lib()
     N, H = 5_000_003, 8
     rng = np.random.default_rng(11)
@@ -1096,3 +1096,32 @@ def test_restore_scatter_matches_mask_order():
     want[rows] = np.arange(n_tok, dtype=np.float32)[:, None]
     assert np.array_equal(got, want)
     assert int(r["found_inf"].item()) == 0
+
+
+def test_offload_rejects_pageable_host_memory():
+    """Host buffers of the offload must be pinned: a pageable buffer (or one that ends past
+    its pinned allocation) is rejected with GRPO_ERR_HOST before anything is enqueued,
+    since a kernel reading it would fault."""
+    import ctypes
+    g = _lib()
+    lib = g.load_library()
+    N, H = 512, 64
+    mask = torch.ones(N, dtype=torch.uint8, device="cuda")
+    dX = torch.empty(N, H, dtype=torch.bfloat16, device="cuda")
+    found = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(g.grpo_restore_workspace_bytes(N), dtype=torch.uint8, device="cuda")
+    pageable = torch.zeros(N, H, dtype=torch.bfloat16)
+    short = torch.zeros(N // 2, H, dtype=torch.bfloat16, pin_memory=True)
+    for host in (pageable, short):
+        rc = lib.grpo_grad_restore(ctypes.c_void_p(host.data_ptr()), None, 1,
+                                   ctypes.c_void_p(mask.data_ptr()), 1, N, H, 0, None,
+                                   ctypes.c_float(1.0), ctypes.c_void_p(dX.data_ptr()), None,
+                                   ctypes.c_void_p(found.data_ptr()),
+                                   ctypes.c_void_p(ws.data_ptr()), ws.numel(), None)
+        assert rc == -10
+    torch.cuda.synchronize()
+    # a later call still works (no error left behind by the check)
+    ok = torch.zeros(N, H, dtype=torch.bfloat16, pin_memory=True)
+    r = g.grpo_grad_restore(mask, dx_host=ok, dXq=dX, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(r["found_inf"].item()) == 0 and bool((dX == 0).all())
