@@ -131,13 +131,20 @@ def cpu_baseline(wl, inp, adv_host, rows_per_seq):
 
 
 def _cpu_model():
+    """The host CPU's model name, with its family and model numbers (a virtual machine may
+    report only the vendor's brand)."""
+    f = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = line.split(":", 1)
+                f.setdefault(k.strip(), v.strip())
+            if not line.strip() and f:
+                break
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    return (f"{f.get('model name', 'unknown')} (family {f.get('cpu family', '?')}, "
+            f"model {f.get('model', '?')}, {f.get('vendor_id', '?')})")
 
 
 def main():
@@ -283,9 +290,13 @@ def main():
         k = names[kid]
         n = len(steps[0])
         tot = float(np.mean([np.sum(x) for x in steps]))       # ms per step
+        # launches that did work: a chunk past the loss-row count is launched too (the host
+        # never reads the count) and exits within microseconds
+        nw = float(np.mean([sum(1 for t in x if t > 0.05) for x in steps]))
         kernels[k] = {"kernel": kernel_names[k][args.path], "launches_per_step": n,
-                      "ms_per_step": tot, "launch_ms": tot / n,
-                      "flop_per_launch": flops_kind[(args.path, k)] / n,
+                      "working_launches_per_step": nw,
+                      "ms_per_step": tot, "launch_ms": tot / nw,
+                      "flop_per_launch": flops_kind[(args.path, k)] / nw,
                       "tflops": flops_kind[(args.path, k)] / (tot * 1e-3) / 1e12,
                       "steps_traced": len(steps)}
         kernels[k]["frac"] = kernels[k]["tflops"] / peak
@@ -320,7 +331,8 @@ def main():
                            "peak": peak, "unit": "TFLOP/s", "frac": kd["frac"],
                            "traffic": measured_traffic(wl.name, dom),
                            "launch_ms": kd["launch_ms"], "flop_per_launch": kd["flop_per_launch"],
-                           "launches_per_step": kd["launches_per_step"]}
+                           "launches_per_step": kd["launches_per_step"],
+                           "working_launches_per_step": kd["working_launches_per_step"]}
         out["kernels"] = kernels
     other = [p for p in legs if p != args.path]
     if other:

@@ -96,9 +96,13 @@ compact_scatter_kernel(const uint8_t* __restrict__ mask, int64_t N,
 // exp2(logit*log2e - max).
 __device__ inline void merge_side(const float* __restrict__ part, const PartLayout& l, int sd,
                                   int64_t r, float* lse, float* zt) {
+  // (unrolled so that a wave has several phases' loads in flight: the single pass's chunk
+  // merge reads 64 phases per row on only R / 256 workgroups; the sums keep their order)
   float M = -INFINITY;
+#pragma unroll 8
   for (int p = 0; p < l.P; ++p) M = fmaxf(M, part[l.at(0, sd, p, r)]);
   float s = 0.0f, z = 0.0f;
+#pragma unroll 8
   for (int p = 0; p < l.P; ++p) {
     const float sp = part[l.at(1, sd, p, r)];
     if (sp != 0.0f) s += sp * exp2f(part[l.at(0, sd, p, r)] - M);
@@ -375,15 +379,19 @@ loss_final_kernel(const double* __restrict__ lsum, int64_t nblocks, int compact,
   }
 }
 
-// dX rows of masked positions are zero.  One block per 4 rows, 16-byte stores.
+// dX rows of masked positions are zero.  A wave per row, grid-stride over the rows (a
+// launch of one block per 4 rows spent 0.25 ms scheduling 41k blocks for 2k masked rows),
+// 16-byte stores.
 __global__ void __launch_bounds__(256)
 zero_rows_kernel(const uint8_t* __restrict__ mask, int64_t N, int64_t row_bytes,
                  char* __restrict__ dX) {
-  const int64_t t = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;
-  if (t >= N || mask[t]) return;
-  uint4* row = reinterpret_cast<uint4*>(dX + t * row_bytes);
+  const int64_t waves = (int64_t)gridDim.x * 4;
   const int64_t n16 = row_bytes / 16;
-  for (int64_t i = threadIdx.x % 64; i < n16; i += 64) row[i] = make_uint4(0, 0, 0, 0);
+  for (int64_t t = (int64_t)blockIdx.x * 4 + threadIdx.x / 64; t < N; t += waves) {
+    if (mask[t]) continue;
+    uint4* row = reinterpret_cast<uint4*>(dX + t * row_bytes);
+    for (int64_t i = threadIdx.x % 64; i < n16; i += 64) row[i] = make_uint4(0, 0, 0, 0);
+  }
 }
 
 // x * c rounded to fp32, then to the storage type.  The product is pinned in a register
@@ -659,7 +667,7 @@ hipError_t launch_seq_counts(const Plan& p, const uint8_t* mask, void* ws, hipSt
 
 hipError_t launch_zero_masked_rows(const Plan& p, const uint8_t* mask, void* dX,
                                    hipStream_t st) {
-  const int64_t blocks = (p.N + 3) / 4;
+  const int64_t blocks = (p.N + 3) / 4 < 1024 ? (p.N + 3) / 4 : 1024;
   hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, st, mask, p.N,
                      p.H * p.esize, reinterpret_cast<char*>(dX));
   return hipGetLastError();

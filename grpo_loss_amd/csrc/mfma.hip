@@ -1874,7 +1874,12 @@ hipError_t fused_split_impl(const Plan& p, void* ws, const void* Xq, const void*
   hipLaunchKernelGGL((fwd_kernel<E, G, 1>), dim3(kNumWG), dim3(kThreads), 0, st, a);
   trace_end(p, GRPO_TRACE_FWD_ALL, st);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  for (int64_t c0 = 0, ci = 0; c0 < p.N; c0 += p.R, ++ci) {
+  // chunks last to first: they are independent here (no dW to accumulate), and the
+  // chunks past the loss-row count, which exit at once, then come first, so that the
+  // gradient offload's copies of their (unused) rows run beside real work instead of
+  // after it
+  for (int64_t ci = nchunks - 1; ci >= 0; --ci) {
+    const int64_t c0 = ci * p.R;
     int32_t* rd = redo + ci;
     FwdArgs c = a;
     c.row_lo = c0;
