@@ -186,6 +186,7 @@ inline int64_t stage_row0(const Plan& p, int64_t c0) { return p.ring ? c0 : -1; 
 constexpr int kTokTile = 256;    // rows per token tile of the MFMA kernels
 constexpr int kVocTile = 256;    // vocabulary entries per tile
 constexpr int kMergeBlock = 256; // rows per block of the merge kernel
+constexpr int kMergeLanes = 4;   // lanes per row merging a chunk's policy partials
 constexpr int kMaxPhases = 32;   // most vocabulary phases of one forward launch
 constexpr int kPieceTiles = 128; // vocabulary tiles per piece of the split backward (32768)
 constexpr int kCompactRows = 4096; // rows per workgroup of the row compaction

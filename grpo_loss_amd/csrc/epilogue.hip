@@ -182,10 +182,11 @@ struct MergeArgs {
 // row's sequence, S' sequences with any) [Long-context GRPO, §4].  pr: where the row's
 // partials are (r: its compact index).  Returns the row's contribution to the loss sum
 // (l, or l / n_s for the sequence mean) and ORs status bits into *flags.
-__device__ inline double merge_row(const MergeArgs& a, int64_t t, int64_t r, const PartRefs& pr,
-                                   int32_t ntok, int* flags) {
-  float lse_q, zq, lse_p, zp;
-  merge_side(pr.q, pr.lq, pr.sdq, pr.rq, &lse_q, &zq);
+// (merge_row_q: the same with the policy side's lse_q and target logit zq merged already.)
+__device__ inline double merge_row_q(const MergeArgs& a, int64_t t, int64_t r,
+                                     const PartRefs& pr, int32_t ntok, int* flags, float lse_q,
+                                     float zq) {
+  float lse_p, zp;
   merge_side(pr.p, pr.lp, pr.sdp, pr.rp, &lse_p, &zp);
   bool quiet = false;
   float l2s = 0.f;
@@ -243,6 +244,37 @@ __device__ inline double merge_row(const MergeArgs& a, int64_t t, int64_t r, con
   return ell_d;
 }
 
+__device__ inline double merge_row(const MergeArgs& a, int64_t t, int64_t r, const PartRefs& pr,
+                                   int32_t ntok, int* flags) {
+  float lse_q, zq;
+  merge_side(pr.q, pr.lq, pr.sdq, pr.rq, &lse_q, &zq);
+  return merge_row_q(a, t, r, pr, ntok, flags, lse_q, zq);
+}
+
+// merge_side by a group of kMergeLanes consecutive lanes, lane q taking the phases
+// p = q (mod kMergeLanes) and the group combining them with shuffles; every lane of the
+// group returns the row's results.  The whole group must be active.
+__device__ inline void merge_side_group(const float* __restrict__ part, const PartLayout& l,
+                                        int sd, int64_t r, int q, float* lse, float* zt) {
+  float M = -INFINITY;
+  for (int p = q; p < l.P; p += kMergeLanes) M = fmaxf(M, part[l.at(0, sd, p, r)]);
+#pragma unroll
+  for (int off = 1; off < kMergeLanes; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, kMergeLanes));
+  float s = 0.0f, z = 0.0f;
+  for (int p = q; p < l.P; p += kMergeLanes) {
+    const float sp = part[l.at(1, sd, p, r)];
+    if (sp != 0.0f) s += sp * exp2f(part[l.at(0, sd, p, r)] - M);
+    z += part[l.at(2, sd, p, r)];
+  }
+#pragma unroll
+  for (int off = 1; off < kMergeLanes; off <<= 1) {
+    s += __shfl_xor(s, off, kMergeLanes);
+    z += __shfl_xor(z, off, kMergeLanes);
+  }
+  *lse = (M + log2f(s)) * kLn2;
+  *zt = z;
+}
+
 __device__ inline void block_sum_store(double v, double* out) {
   __shared__ double red[kMergeBlock];
   red[threadIdx.x] = v;
@@ -293,10 +325,15 @@ __global__ void __launch_bounds__(kMergeBlock) merge_kernel(MergeArgs a) {
 // partials; the reference partials come from one launch over all rows.  Blocks are
 // aligned to 256 compact rows, so lsum[r / 256] sums the same rows in the same order
 // whatever the chunking.
-__global__ void __launch_bounds__(kMergeBlock) merge_rows_kernel(MergeArgs a) {
+// kMergeLanes lanes per row: the chunk's policy partials (pieces x phases of them) are
+// merged by the row's group of lanes, the rest of the row by its first lane; the block's
+// loss sum is the same 256-row tree as merge_kernel's.
+__global__ void __launch_bounds__(kMergeBlock * kMergeLanes) merge_rows_kernel(MergeArgs a) {
+  __shared__ double red[kMergeBlock];
   if (a.gate && *a.gate == 0) return;
   const int32_t ntok = *a.ntok;
-  const int64_t r = a.c0 + (int64_t)blockIdx.x * kMergeBlock + threadIdx.x;
+  const int row = threadIdx.x / kMergeLanes, q = threadIdx.x % kMergeLanes;
+  const int64_t r = a.c0 + (int64_t)blockIdx.x * kMergeBlock + row;
   const int64_t blk0 = a.c0 / kMergeBlock + blockIdx.x;
   if ((int64_t)blk0 * kMergeBlock >= ntok) return;   // whole block past the last row
   const int64_t nvt = (a.V + 255) / 256;
@@ -306,9 +343,19 @@ __global__ void __launch_bounds__(kMergeBlock) merge_rows_kernel(MergeArgs a) {
                     a.part, part_layout(ntok, 1, nvt), 0, r};
   double ell_d = 0.0;
   int flags = 0;
-  if (r < ntok && r < a.c0 + a.R) ell_d = merge_row(a, a.idx[r], r, pr, ntok, &flags);
+  if (r < ntok && r < a.c0 + a.R) {   // the same for the row's whole group
+    float lse_q, zq;
+    merge_side_group(pr.q, pr.lq, pr.sdq, pr.rq, q, &lse_q, &zq);
+    if (q == 0) ell_d = merge_row_q(a, a.idx[r], r, pr, ntok, &flags, lse_q, zq);
+  }
   if (flags) atomicOr(a.status, flags);
-  block_sum_store(ell_d, a.lsum + blk0);
+  if (q == 0) red[row] = ell_d;
+  __syncthreads();
+  for (int off = kMergeBlock / 2; off > 0; off >>= 1) {
+    if (threadIdx.x < (unsigned)off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) a.lsum[blk0] = red[0];
 }
 
 // Outputs of masked rows for the single-pass forward (its merge visits loss rows only).
@@ -643,7 +690,8 @@ hipError_t launch_merge_rows(const Plan& p, const void* ws, int64_t c0, const in
   a.patch_ld = p.Vpad;
   a.patch_dtype = p.dtype;
   a.gate = gate;
-  hipLaunchKernelGGL(merge_rows_kernel, dim3((unsigned)(p.R / kMergeBlock)), dim3(kMergeBlock),
+  hipLaunchKernelGGL(merge_rows_kernel, dim3((unsigned)(p.R / kMergeBlock)),
+                     dim3(kMergeBlock * kMergeLanes),
                      0, st, a);
   return hipGetLastError();
 }

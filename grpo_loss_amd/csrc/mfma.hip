@@ -1099,7 +1099,10 @@ __host__ __device__ inline int64_t dx_sum_offset(int64_t tile, int w, int nb, in
 // acc_mode 0, ksplit > 1: fp32 partials of C to dxp[ks][r - c0][h], reduced by
 // dx_reduce_kernel, which scales the same.  acc_mode 1: fp32 partials for every ksplit
 // (the first piece of a vocabulary-split chunk); acc_mode 2: added to them (the later
-// pieces: the k loop starts from the stored sums), scaled by dx_final_kernel.
+// pieces: the k loop starts from the stored sums), scaled by dx_final_kernel.  acc_mode 3
+// (ksplit == 1, the last piece once the chunk's merge has run): starts from the sums like
+// 2 (from 0 when it is also the first piece) and writes dX itself with dx_final_kernel's arithmetic (targets; mr the per-row
+// reference, pm there), or nothing when the chunk's flag (redo) sends it to the fallback.
 // s_r = 1 where the chunk buffer holds T = onehot - softmax (two-pass, single-pass mode 2,
 // or a mode-3 chunk whose fallback ran: redo null or *redo != 0).  Otherwise it holds the
 // mode-3 row E = -T / f_r: the kept terms e_v = p_v / f_r, f_r = exp2(mr_r - lse2_r) (mr:
@@ -1121,7 +1124,8 @@ dx_kernel(int64_t H, int64_t V, int64_t ld, int64_t kcols, int64_t v_base, int64
           const float* __restrict__ grad_loss, float loss_scale,
           typename E::T* __restrict__ dX, int64_t srow0, float* __restrict__ dxp,
           int32_t* __restrict__ found_inf, const int32_t* __restrict__ redo,
-          const float* __restrict__ mr, const int32_t* __restrict__ gate) {
+          const float* __restrict__ mr, const int32_t* __restrict__ gate,
+          const int64_t* __restrict__ targets) {
   if (gate && *gate == 0) return;   // the vocabulary split's fallback
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w / kWN, wn = w % kWN;
@@ -1148,7 +1152,9 @@ dx_kernel(int64_t H, int64_t V, int64_t ld, int64_t kcols, int64_t v_base, int64
   }
   const float c = (grad_loss ? *grad_loss : 1.f) / loss_scale;
   const bool fixed = redo && *redo == 0;
-  const bool to_slots = acc_mode != 0 || ksplit > 1;
+  const bool final_dx = acc_mode == 3;
+  const bool skip = final_dx && redo && *redo != 0;   // the fallback writes this chunk
+  const bool to_slots = acc_mode == 1 || acc_mode == 2 || (acc_mode == 0 && ksplit > 1);
   bool bad = false;
   // item -> (token tile, H tile, k range) and its two operands
   struct Item {
@@ -1184,8 +1190,10 @@ dx_kernel(int64_t H, int64_t V, int64_t ld, int64_t kcols, int64_t v_base, int64
     const int hb = (int)d.h0 + wm * 128 + 4 * (lq >> 4);
     return reinterpret_cast<f32x4*>(dxp + (d.ks * R + rl) * H + hb + mb * 16);
   };
+  // the sums of the pieces before this one (acc_mode 3 on the first piece: none)
+  const bool from_sums = acc_mode == 2 || (acc_mode == 3 && v_base > 0);
   auto init_acc = [&](Acc& acc, const Item& d) {
-    if (acc_mode != 2) {
+    if (!from_sums) {
       zero_acc(acc);
       return;
     }
@@ -1209,7 +1217,42 @@ dx_kernel(int64_t H, int64_t V, int64_t ld, int64_t kcols, int64_t v_base, int64
       const Item dn = decode(item + nwg);
       if (dn.kend > dn.kbeg) gemm_pre_op(opA(dn), opB(dn), ao, bo);
     }
-    if (!to_slots) {
+    if (final_dx) {
+      if (!skip) {
+        // dX = c g_r ((1 - p_y) W[y_r] - f_r C), as dx_final_kernel
+        const int lq = tid_opaque() & 63;
+        const int hb = (int)d.h0 + wm * 128 + 4 * (lq >> 4);
+        const typename E::T* Wt = reinterpret_cast<const typename E::T*>(W);
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) {
+          const int r = (int)tok0 + wn * kWaveN + nb * 16 + (lq & 15);
+          if (r >= ntok) continue;
+          const int64_t t = idx[r];
+          const int64_t y = targets[t];
+          const float lse2 = saved[t * 4] * kLog2e;
+          const float gs = saved[t * 4 + 3] * c;
+          const float f = mr ? exp2f(mr[r - c0] - lse2) : 1.f;
+          const bool yok = y >= 0 && y < V;
+          const float ty = yok ? -expm1f(saved[t * 4 + 1]) : 0.f;
+          const typename E::T* wy = Wt + (yok ? y : 0) * H + hb;
+          typename E::T* drow = dX + (srow0 < 0 ? t : r - srow0) * H + hb;
+#pragma unroll
+          for (int mb = 0; mb < kMB; ++mb) {
+            const f32x4 sm = acc[mb][nb];
+            const uint2 wv = *reinterpret_cast<const uint2*>(wy + mb * 16);
+            const float w0 = E::to_f32((typename E::T)(wv.x & 0xffffu));
+            const float w1 = E::to_f32((typename E::T)(wv.x >> 16));
+            const float w2 = E::to_f32((typename E::T)(wv.y & 0xffffu));
+            const float w3 = E::to_f32((typename E::T)(wv.y >> 16));
+            uint2 pk;
+            pk.x = E::pack2(gs * (ty * w0 - f * sm[0]), gs * (ty * w1 - f * sm[1]));
+            pk.y = E::pack2(gs * (ty * w2 - f * sm[2]), gs * (ty * w3 - f * sm[3]));
+            bad |= E::nonfinite2(pk.x) || E::nonfinite2(pk.y);
+            *reinterpret_cast<uint2*>(drow + mb * 16) = pk;
+          }
+        }
+      }
+    } else if (!to_slots) {
       // lane-derived indices recomputed here (32-bit: rows and H fit), not held across
       // the k loop
       const int lq = tid_opaque() & 63;
@@ -1295,7 +1338,8 @@ dx_final_kernel(int64_t H, int64_t V, int64_t R, int64_t c0, int nht, int ksplit
                 const float* __restrict__ saved, const float* __restrict__ grad_loss,
                 float loss_scale, const float* __restrict__ pm,
                 const typename E::T* __restrict__ W, typename E::T* __restrict__ dX,
-                int64_t srow0, int32_t* __restrict__ found_inf) {
+                int64_t srow0, int32_t* __restrict__ found_inf, const int32_t* __restrict__ gate) {
+  if (gate && *gate == 0) return;   // the fallback's final dX, when the last piece did not write it
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w / kWN, wn = w % kWN;
   const int64_t tt = blockIdx.x / nht, ht = blockIdx.x % nht;
@@ -1627,7 +1671,7 @@ hipError_t chunk_grads(const Plan& p, void* ws, int64_t c0, const void* Xq, cons
                      p.H, p.V, p.Vpad, p.Vpad, (int64_t)0, p.R, c0, nht, p.ksplit, 0, ntok, idx,
                      (const char*)W, (const char*)Tb, saved, grad_loss, loss_scale,
                      (T*)dx_out(p, dX, c0), stage_row0(p, c0), ws_ptr<float>(ws, p.off_dxp),
-                     found_inf, redo, mr, (const int32_t*)nullptr);
+                     found_inf, redo, mr, (const int32_t*)nullptr, (const int64_t*)nullptr);
   trace_end(p, GRPO_TRACE_DX, st);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.ksplit > 1) {
@@ -1763,23 +1807,40 @@ hipError_t fused_impl(const Plan& p, void* ws, const void* Xq, const void* Xp, c
 
 // Vocabulary split: dX of chunk c0 from one piece of its buffer (columns 0 .. pt_ld - 1
 // hold vocabulary rows piece ptiles 256 ..), into the chunk's fp32 sums: the first piece
-// writes them, the later ones add to them.  gate: the fallback's launches.
+// writes them, the later ones add to them.  gate: the fallback's launches.  fin (non-null,
+// ksplit == 1, the last piece after the chunk's merge): dX itself (dx_kernel's acc_mode 3)
+// with the row factors of the merged chunk, skipped when the chunk's flag fin->redo is set.
+struct FinalDx {
+  const int64_t* targets;
+  const float* saved;
+  const float* grad_loss;
+  float loss_scale;
+  void* dX;
+  const int32_t* redo;
+  const float* pm;
+};
 template <class E>
 hipError_t piece_dx(const Plan& p, void* ws, int64_t c0, int piece, const void* W,
-                    int32_t* found_inf, hipStream_t st, const int32_t* gate, bool traced) {
+                    int32_t* found_inf, hipStream_t st, const int32_t* gate, bool traced,
+                    const FinalDx* fin = nullptr) {
   typedef typename E::T T;
   const int nht = (int)(p.H / 256);
   const int64_t nvt = p.Vpad / kVocTile, vt0 = (int64_t)piece * p.ptiles;
   const int64_t tiles = nvt - vt0 < p.ptiles ? nvt - vt0 : p.ptiles;
+  const int mode = fin ? 3 : (piece == 0 ? 1 : 2);
   if (traced) trace_begin(p, GRPO_TRACE_DX, st);
   hipLaunchKernelGGL(dx_kernel<E>, dim3(kNumWG), dim3(kThreads), 0, st, p.H, p.V, p.pt_ld,
-                     tiles * kVocTile, vt0 * kVocTile, p.R, c0, nht, p.ksplit,
-                     piece == 0 ? 1 : 2, ws_ptr<int32_t>(ws, p.off_ntok),
-                     ws_ptr<int32_t>(ws, p.off_idx), (const char*)W,
-                     (const char*)ws_ptr<T>(ws, p.off_T), (const float*)nullptr,
-                     (const float*)nullptr, 1.f, (T*)nullptr, (int64_t)-1,
-                     ws_ptr<float>(ws, p.off_dxp),
-                     found_inf, (const int32_t*)nullptr, (const float*)nullptr, gate);
+                     tiles * kVocTile, vt0 * kVocTile, p.R, c0, nht, p.ksplit, mode,
+                     ws_ptr<int32_t>(ws, p.off_ntok), ws_ptr<int32_t>(ws, p.off_idx),
+                     (const char*)W, (const char*)ws_ptr<T>(ws, p.off_T),
+                     fin ? fin->saved : (const float*)nullptr,
+                     fin ? fin->grad_loss : (const float*)nullptr,
+                     fin ? fin->loss_scale : 1.f,
+                     fin ? (T*)dx_out(p, fin->dX, c0) : (T*)nullptr,
+                     fin ? stage_row0(p, c0) : (int64_t)-1, ws_ptr<float>(ws, p.off_dxp),
+                     found_inf, fin ? fin->redo : (const int32_t*)nullptr,
+                     fin ? fin->pm : (const float*)nullptr, gate,
+                     fin ? fin->targets : (const int64_t*)nullptr);
   if (traced) trace_end(p, GRPO_TRACE_DX, st);
   return hipGetLastError();
 }
@@ -1789,14 +1850,14 @@ template <class E>
 hipError_t split_dx_final(const Plan& p, void* ws, int64_t c0, const void* W,
                           const int64_t* targets, const float* saved, const float* grad_loss,
                           float loss_scale, const float* pm, void* dX, int32_t* found_inf,
-                          hipStream_t st) {
+                          hipStream_t st, const int32_t* gate = nullptr) {
   typedef typename E::T T;
   const int nht = (int)(p.H / 256);
   hipLaunchKernelGGL(dx_final_kernel<E>, dim3((unsigned)(p.R / 256 * nht)), dim3(kThreads), 0,
                      st, p.H, p.V, p.R, c0, nht, p.ksplit, ws_ptr<int32_t>(ws, p.off_ntok),
                      ws_ptr<int32_t>(ws, p.off_idx), targets,
                      (const float*)ws_ptr<float>(ws, p.off_dxp), saved, grad_loss, loss_scale, pm,
-                     (const T*)W, (T*)dx_out(p, dX, c0), stage_row0(p, c0), found_inf);
+                     (const T*)W, (T*)dx_out(p, dX, c0), stage_row0(p, c0), found_inf, gate);
   return hipGetLastError();
 }
 
@@ -1830,12 +1891,19 @@ hipError_t bwd_split_impl(const Plan& p, void* ws, const void* Xq, const void* W
                          (const float*)ws_ptr<float>(ws, p.off_sxq));
       trace_end(p, GRPO_TRACE_RECOMPUTE, st);
       if ((e = hipGetLastError()) != hipSuccess) return e;
-      if ((e = piece_dx<E>(p, ws, c0, j, W, found_inf, st, nullptr, true)) != hipSuccess)
+      // the last piece writes dX itself when the reduction is not split (the row
+      // factors are the forward's, already in `saved`)
+      const bool last = j == p.npieces - 1 && p.ksplit == 1;
+      const FinalDx fin{targets, saved, grad_loss, loss_scale, dX, nullptr, nullptr};
+      if ((e = piece_dx<E>(p, ws, c0, j, W, found_inf, st, nullptr, true,
+                           last ? &fin : nullptr)) != hipSuccess)
         return e;
     }
-    e = split_dx_final<E>(p, ws, c0, W, targets, saved, grad_loss, loss_scale, nullptr, dX,
-                          found_inf, st);
-    if (e != hipSuccess) return e;
+    if (p.ksplit > 1) {
+      e = split_dx_final<E>(p, ws, c0, W, targets, saved, grad_loss, loss_scale, nullptr, dX,
+                            found_inf, st);
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }
@@ -1891,18 +1959,29 @@ hipError_t fused_split_impl(const Plan& p, void* ws, const void* Xq, const void*
     c.npieces = p.npieces;
     c.ptiles = p.ptiles;
     c.zero_target = 1;
+    // With the reduction not split, the last piece's dX waits for the chunk's merge and
+    // writes dX itself (no fp32 sums round trip, no final launch), unless the merge sends
+    // the chunk to the fallback, which then ends with dx_final_kernel.
+    const bool fuse = p.ksplit == 1;
     for (int j = 0; j < p.npieces; ++j) {
       c.piece = j;
       trace_begin(p, GRPO_TRACE_FWD_CHUNK, st);
       hipLaunchKernelGGL((fwd_kernel<E, G, 3>), dim3(kNumWG), dim3(kThreads), 0, st, c);
       trace_end(p, GRPO_TRACE_FWD_CHUNK, st);
       if ((e = hipGetLastError()) != hipSuccess) return e;
+      if (fuse && j == p.npieces - 1) break;
       if ((e = piece_dx<E>(p, ws, c0, j, W, found_inf, st, nullptr, true)) != hipSuccess)
         return e;
     }
     e = launch_merge_rows(p, ws, c0, targets, mask, adv, beta, saved, logp, ref_logp, kl,
                           status, st, rd, nullptr, nullptr, p.ptiles, p.npieces);
     if (e != hipSuccess) return e;
+    if (p.ring && (e = p.ring->acquire(c0)) != hipSuccess) return e;
+    if (fuse) {
+      const FinalDx fin{targets, saved, grad_loss, loss_scale, dX, rd, pm};
+      e = piece_dx<E>(p, ws, c0, p.npieces - 1, W, found_inf, st, nullptr, true, &fin);
+      if (e != hipSuccess) return e;
+    }
     // fallback, gated on the chunk's flag: a robust policy sweep, its merge, the pieces
     FwdArgs f = c;
     f.gate = rd;
@@ -1925,9 +2004,8 @@ hipError_t fused_split_impl(const Plan& p, void* ws, const void* Xq, const void*
       if ((e = hipGetLastError()) != hipSuccess) return e;
       if ((e = piece_dx<E>(p, ws, c0, j, W, found_inf, st, rd, false)) != hipSuccess) return e;
     }
-    if (p.ring && (e = p.ring->acquire(c0)) != hipSuccess) return e;
     e = split_dx_final<E>(p, ws, c0, W, targets, saved, grad_loss, loss_scale, pm, dX,
-                          found_inf, st);
+                          found_inf, st, fuse ? rd : nullptr);
     if (e != hipSuccess) return e;
     if (p.ring && (e = p.ring->transfer(c0)) != hipSuccess) return e;
   }

@@ -1125,3 +1125,27 @@ def test_offload_rejects_pageable_host_memory():
     r = g.grpo_grad_restore(mask, dx_host=ok, dXq=dX, workspace=ws)
     torch.cuda.synchronize()
     assert int(r["found_inf"].item()) == 0 and bool((dX == 0).all())
+
+
+# The last vocabulary piece writes dX itself when the dX reduction is not split (ksplit 1:
+# H x chunk rows fills 256 tiles, so a full 4096-row chunk at H = 4096): one piece (it is
+# also the first, so it starts from zero), several pieces, and chunks whose flag sends them
+# to the fallback (reference hidden states scaled by 32), two-pass and single pass.
+FUSED_CASES = [  # (vocab_piece, far reference, single pass); the two-pass has no fallback
+    (0, False, False), (0, False, True), (768, False, False), (768, False, True),
+    (768, True, True)]
+
+
+@pytest.mark.parametrize("piece,far,single_pass", FUSED_CASES,
+                         ids=["one-piece-two-pass", "one-piece-single-pass",
+                              "seven-pieces-two-pass", "seven-pieces-single-pass",
+                              "fallback-single-pass"])
+def test_final_piece_writes_dx(piece, far, single_pass):
+    wl = dataclasses.replace(workload_by_name("llama3.1-8b-long-bf16"), G=2, L=2304, V=5003,
+                             prefix=16, comp_min=2288, comp_max=2288)
+    _say(f"[final piece] piece={piece} far={far} single_pass={single_pass}: N={wl.N} H={wl.H} "
+         f"V={wl.V}")
+    inp = generate(wl)
+    if far:   # the reference far below the policy: reverse KL exp(ref - q) stays finite
+        inp = dataclasses.replace(inp, xp=inp.xp * 32)
+    check_small(wl, inp, single_pass=single_pass, vocab_piece=piece)
