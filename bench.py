@@ -167,14 +167,34 @@ def main():
     del inp.xq, inp.xp  # host copies no longer needed
     dt = d["xq"].dtype
     need_dW = wl.need_dW
+    # Kernel timing inside the timed steps: each timed step of the leg reported as `value`
+    # has the library bracket every launch of one GEMM kernel with a pair of HIP events of
+    # its own, recorded on the stream the kernel runs on; the steps take the kernels in
+    # turn, and all events are read after the timed region.
+    kinds = {"single": ["fwd_all", "fwd_chunk", "dx"] + (["dw"] if need_dW else []),
+             "two": ["fwd_all", "recompute", "dx"] + (["dw"] if need_dW else [])}
+    max_launches = -(-wl.N // 256) + 1        # chunks of at least 256 rows
+    step_traces = []
+    if not args.no_trace:
+        for i in range(args.steps):
+            k = kinds[args.path][i % len(kinds[args.path])]
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * max_launches)]
+            for e in evs:
+                e.record()   # creates the HIP event
+            step_traces.append(g.KernelTrace(k, evs))
+        torch.cuda.synchronize()
+
     # inputs and outputs first: everything allocated after this point is extra memory
     dX = torch.empty_like(d["xq"])
     dW = torch.empty(wl.V, wl.H, dtype=torch.float32, device="cuda") if need_dW else None
     found = torch.zeros(1, dtype=torch.int32, device="cuda")
     grad = torch.full((1,), wl.loss_scale, dtype=torch.float32, device="cuda")
     adv = torch.empty(wl.S, dtype=torch.float32, device="cuda")
+    g.grpo_advantages(d["rewards"], wl.eps, out=adv)  # the library's code object loaded
     torch.cuda.synchronize()
     base_mem = torch.cuda.memory_allocated()
+    base_reserved = torch.cuda.memory_reserved()
+    base_free = torch.cuda.mem_get_info()[0]   # hipMemGetInfo: the device's own count
     torch.cuda.reset_peak_memory_stats()
     ws_bytes = g.grpo_workspace_bytes(wl.S, wl.L, wl.H, wl.V, dt, need_dW)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
@@ -192,23 +212,6 @@ def main():
         del src, dst, flush
         torch.cuda.empty_cache()
         torch.cuda.reset_peak_memory_stats()
-
-    # Kernel timing inside the timed steps: each timed step of the leg reported as `value`
-    # has the library bracket every launch of one GEMM kernel with a pair of HIP events of
-    # its own, recorded on the stream the kernel runs on; the steps take the kernels in
-    # turn, and all events are read after the timed region.
-    kinds = {"single": ["fwd_all", "fwd_chunk", "dx"] + (["dw"] if need_dW else []),
-             "two": ["fwd_all", "recompute", "dx"] + (["dw"] if need_dW else [])}
-    max_launches = -(-wl.N // 256) + 1        # chunks of at least 256 rows
-    step_traces = []
-    if not args.no_trace:
-        for i in range(args.steps):
-            k = kinds[args.path][i % len(kinds[args.path])]
-            evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * max_launches)]
-            for e in evs:
-                e.record()   # creates the HIP event
-            step_traces.append(g.KernelTrace(k, evs))
-        torch.cuda.synchronize()
 
     opts = {"v": None}
 
@@ -301,6 +304,12 @@ def main():
                       "steps_traced": len(steps)}
         kernels[k]["frac"] = kernels[k]["tflops"] / peak
     peak_extra = torch.cuda.max_memory_allocated() - base_mem
+    # cross-check against the device: the free memory it lost over the timed legs, and how
+    # much of that torch's caching allocator does not account for (anything the library or
+    # the runtime took outside torch)
+    torch.cuda.synchronize()
+    dev_delta = base_free - torch.cuda.mem_get_info()[0]
+    untracked = dev_delta - (torch.cuda.memory_reserved() - base_reserved)
     main_leg = legs[args.path]
     out = {
         "metric": METRIC,
@@ -321,6 +330,8 @@ def main():
         "mfma_peak_frac": main_leg["mfma_peak_frac"],
         "recompute_equiv_frac": main_leg["recompute_equiv_frac"],
         "extra_gib": peak_extra / 2 ** 30,
+        "device_free_drop_gib": dev_delta / 2 ** 30,
+        "untracked_by_torch_gib": untracked / 2 ** 30,
         "workspace_gib": ws_bytes / 2 ** 30,
         "materialized_logits_gib": 2 * 2 * wl.S * wl.L * wl.V / 2 ** 30,
     }

@@ -526,6 +526,59 @@ def test_repeat_is_bit_identical():
     assert np.array_equal(a["dX"], b["dX"]) and np.array_equal(a["saved"], b["saved"])
 
 
+def test_calls_take_no_device_memory():
+    """The library allocates no device memory: with the workspace and the outputs reused,
+    repeated calls of every entry point (the gradient offload and restore included) leave
+    the device's free-memory count (hipMemGetInfo) and torch's reserve unchanged.  A warm
+    round first loads the code objects and fills torch's cache with the outputs' sizes."""
+    g = _lib()
+    wl = dataclasses.replace(workload_by_name("qwen2.5-1.5b-bf16"), **SMALL["qwen2.5-1.5b-bf16"])
+    inp = generate(wl)
+    d = to_device(inp)
+    N, H, V = wl.S * wl.L, wl.H, wl.V
+    grad = torch.full((1,), wl.loss_scale, dtype=torch.float32, device="cuda")
+    dX = torch.empty_like(d["xq"])
+    dW = torch.empty(V, H, dtype=torch.float32, device="cuda")
+    found = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(g.grpo_workspace_bytes(wl.S, wl.L, H, V, d["xq"].dtype, True),
+                     dtype=torch.uint8, device="cuda")
+    cs = g.offload_stream()
+    dx_host = torch.empty(N, H, dtype=d["xq"].dtype, pin_memory=True)
+    dw_host = torch.empty(V, H, dtype=torch.float32, pin_memory=True)
+    oo = g.options()
+    oo.dx_host, oo.dw_host, oo.copy_stream = (dx_host.data_ptr(), dw_host.data_ptr(),
+                                              cs.cuda_stream)
+    wso = torch.empty(g.grpo_workspace_bytes(wl.S, wl.L, H, V, d["xq"].dtype, True, oo),
+                      dtype=torch.uint8, device="cuda")
+    rws = torch.empty(g.grpo_restore_workspace_bytes(N), dtype=torch.uint8, device="cuda")
+    args = (d["xq"], d["xp"], d["W"], d["targets"], d["mask"])
+
+    def one_round():
+        adv = g.grpo_advantages(d["rewards"], wl.eps)
+        f = g.grpo_loss_fwd(*args, adv, wl.beta, wl.L, workspace=ws)
+        g.grpo_loss_bwd(d["xq"], d["W"], d["targets"], d["mask"], f["saved"], wl.L, grad,
+                        wl.loss_scale, dW=dW, found_inf=found, workspace=ws, dXq=dX)
+        g.grpo_loss_fwd_bwd(*args, adv, wl.beta, wl.L, grad, wl.loss_scale, dW=dW,
+                            found_inf=found, workspace=ws, dXq=dX)
+        g.grpo_loss_fwd_noalloc(*args, adv, wl.beta, wl.L)
+        g.grpo_scale_grad(dX, grad, wl.loss_scale, dW=dW, found_inf=found)
+        g.grpo_loss_fwd_bwd(*args, adv, wl.beta, wl.L, grad, wl.loss_scale,
+                            found_inf=found, workspace=wso, dx_host=dx_host, dw_host=dw_host,
+                            copy_stream=cs)
+        g.grpo_grad_restore(d["mask"], dx_host, dw_host, None, 1.0, dXq=dX, dW=dW,
+                            found_inf=found, workspace=rws)
+        torch.cuda.synchronize()
+
+    one_round()
+    free0, res0 = torch.cuda.mem_get_info()[0], torch.cuda.memory_reserved()
+    for i in range(3):
+        one_round()
+        free, res = torch.cuda.mem_get_info()[0], torch.cuda.memory_reserved()
+        _say(f"round {i}: free drop {free0 - free} B, reserve growth {res - res0} B")
+        assert res == res0
+        assert free == free0
+
+
 # ------------------------------------------------------------------ full sizes, sampled rows
 
 FULL = ["qwen2.5-1.5b-bf16", "llama3.1-8b-train-bf16", "llama3.1-8b-long-bf16", "phi4-f16"]
