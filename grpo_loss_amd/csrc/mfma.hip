@@ -39,6 +39,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <class E>
 struct Mma;
@@ -533,14 +534,19 @@ __device__ inline FwdRange fwd_range(const FwdArgs& a, int ntok) {
   return f;
 }
 
-// Staging offsets of vocabulary tile v0 (rows past V clamped to the last one).
+// Staging offsets of vocabulary tile v0 < V (rows from V on clamped to V - 1), in 32-bit
+// row arithmetic on a lane index recomputed here: 64-bit rows derived from threadIdx.x
+// are hoisted out of a persistent tile loop and spilled, and each reload then waits for
+// every vector memory operation in flight.
 __device__ inline void w_offsets(int64_t v0, int64_t V, int64_t rowb, Offs& ao) {
+  const int64_t left = V - 1 - v0;
+  const int lim = left < 255 ? (int)left : 255;
+  const int t = tid_opaque();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int sr = stage_row(i);
-    int64_t v = v0 + sr;
-    if (v >= V) v = V - 1;
-    ao[i] = (uint32_t)((v - v0) * rowb) + stage_chunk_bytes(sr);
+    const int sr = 32 * (t >> 6) + 8 * i + ((t & 63) >> 3);
+    const int d = sr < lim ? sr : lim;
+    ao[i] = (uint32_t)d * (uint32_t)rowb + (uint32_t)(((t & 7) ^ swz_f(sr)) << 4);
   }
 }
 
@@ -878,9 +884,6 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
       const int64_t v0 = vt * 256;
       Acc acc;
       zero_acc(acc);
-      // the previous tile's fold stored kMB x kNB packed terms per thread after this tile's
-      // first loads: the k loop starts without waiting for them (16-bit kept terms only;
-      // the fp8 core's stage loop waits for everything)
       gemm_main<G>(
           make_src(Wop + v0 * rowb, wend), make_src(X, X + xbytes), ao, bo, nk, acc);
       // enqueue the next tile: the next vocabulary tile of this block, else the first
@@ -1444,6 +1447,11 @@ dw_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int nht, in
     const int lq = tid_opaque() & 63;
     const int hb = (int)((it % nht) * 256) + wm * 128 + 4 * (lq >> 4);
     const int64_t v0 = (it / nht) * 256;
+    // the tile's rows below V as a buffer resource: rows from V on read 0 and their stores
+    // are dropped by the resource's extent, with no per-lane branch
+    const int64_t vrows = V - v0 < 256 ? V - v0 : 256;
+    const Src dws = make_src(reinterpret_cast<const char*>(dW + v0 * H),
+                             reinterpret_cast<const char*>(dW + (v0 + vrows) * H));
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
@@ -1454,10 +1462,11 @@ dw_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int nht, in
       f32x4 old[kNB][kMB];
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) {
-        const int64_t v = v0 + wn * kWaveN + nb * 16 + (lq & 15);
-        const f32x4* p = reinterpret_cast<const f32x4*>(dW + (v < V ? v : 0) * H + hb);
+        const uint32_t o = (uint32_t)((wn * kWaveN + nb * 16 + (lq & 15)) * H + hb) * 4u;
 #pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) old[nb][mb] = p[mb * 4];
+        for (int mb = 0; mb < kMB; ++mb)
+          old[nb][mb] = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(dws, o + mb * 64, 0, 0));
       }
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb)
@@ -1466,15 +1475,16 @@ dw_kernel(int64_t H, int64_t V, int64_t Vpad, int64_t R, int64_t c0, int nht, in
     }
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
-      const int64_t v = v0 + wn * kWaveN + nb * 16 + (lq & 15);
-      if (v >= V) continue;
-      f32x4* p = reinterpret_cast<f32x4*>(dW + v * H + hb);
+      const int vr = wn * kWaveN + nb * 16 + (lq & 15);
+      const uint32_t o = (uint32_t)(vr * H + hb) * 4u;
+      const bool ok = vr < vrows;
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb) {
         const f32x4 val = acc[mb][nb];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bad |= !isfinite(val[j]);
-        p[mb * 4] = val;
+        for (int j = 0; j < 4; ++j) bad |= ok && !isfinite(val[j]);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, val), dws,
+                                               o + mb * 64, 0, 0);
       }
     }
   }
