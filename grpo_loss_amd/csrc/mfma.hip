@@ -290,14 +290,16 @@ __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 // First half of the k-loop prologue: enqueue k-step 0 into stage 0.  Stage 0 is free
 // once the previous gemm_main on this workgroup has returned, so a persistent kernel
 // issues its next tile's loads before working on the previous tile's accumulators.
+// rot: the k loop visits k-steps rot, rot + 1, .., nk - 1, 0, .., rot - 1 (0 <= rot < nk),
+// the same rot given to gemm_main for the tile.
 template <bool kNatA = false, bool kNatB = false>
 __device__ inline void gemm_pre_op(const Op<kNatA>& A, const Op<kNatB>& B, const Offs& ao,
-                                   const Offs& bo) {
+                                   const Offs& bo, int rot = 0) {
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  stage_tiles<0>(A, B, ao, bo, 0, w);
+  stage_tiles<0>(A, B, ao, bo, rot, w);
 }
-__device__ inline void gemm_pre(Src ra, Src rb, const Offs& ao, const Offs& bo) {
-  gemm_pre_op(Op<false>{ra}, Op<false>{rb}, ao, bo);
+__device__ inline void gemm_pre(Src ra, Src rb, const Offs& ao, const Offs& bo, int rot = 0) {
+  gemm_pre_op(Op<false>{ra}, Op<false>{rb}, ao, bo, rot);
 }
 
 // Fragment reads of one k-step for the pipelined core below.  A fragment (A row block mb,
@@ -329,8 +331,8 @@ __device__ inline uint4 frag_b(const FragBase& q, int nb, int hf) {
 // the current group's and the next one's, 48 at a k-half boundary.
 template <class G, int S, bool kNatA, bool kNatB>
 __device__ inline void kstep_pipe(const Op<kNatA>& A, const Op<kNatB>& B, const Offs& ao,
-                                  const Offs& bo, int kt, int nk, int w, FragBase q, Acc& acc,
-                                  uint4 (&a)[2], uint4 (&b)[kNB]) {
+                                  const Offs& bo, int kt, int nk, int rot, int w, FragBase q,
+                                  Acc& acc, uint4 (&a)[2], uint4 (&b)[kNB]) {
   // keep the natural-layout fragment addresses from being hoisted out of the k loop and
   // held in registers (they are one v_xad each at the read)
   if constexpr (kNatA || kNatB) asm("" : "+v"(q.F) : "s"(kt));
@@ -375,7 +377,10 @@ __device__ inline void kstep_pipe(const Op<kNatA>& A, const Op<kNatB>& B, const 
         // MFMAs, so the matrix unit restarts right after the barrier
         if (last && i == 0) {
           __builtin_amdgcn_sched_barrier(0);
-          if (kt + 2 < nk) stage_tiles<S>(A, B, ao, bo, kt + 2, w);
+          if (kt + 2 < nk) {
+            const int k = kt + 2 + rot;
+            stage_tiles<S>(A, B, ao, bo, k < nk ? k : k - nk, w);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -409,7 +414,7 @@ __device__ inline int tid_opaque() {
 
 template <class E, bool kNatA = false, bool kNatB = false>
 __device__ inline void gemm_main_op(const Op<kNatA>& A, const Op<kNatB>& B, const Offs& ao,
-                                    const Offs& bo, int nk, Acc& acc) {
+                                    const Offs& bo, int nk, Acc& acc, int rot = 0) {
   const int lane = tid_opaque() & 63;
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int wm = w / kWN, wn = w % kWN;
@@ -426,11 +431,12 @@ __device__ inline void gemm_main_op(const Op<kNatA>& A, const Op<kNatB>& B, cons
     for (int kt = 0; kt < nk; kt += 2) {
       wait_vmem();
       __syncthreads();  // stage 0 holds k-step kt; every wave is done reading stage 1
-      stage_tiles<1>(A, B, ao, bo, kt + 1, w);
+      const int k1 = kt + 1 + rot, k2 = kt + 2 + rot;
+      stage_tiles<1>(A, B, ao, bo, k1 < nk ? k1 : k1 - nk, w);
       mma_stage_fp8<0>(acc, fa, fb, fs, lane);
       wait_vmem();
       __syncthreads();  // stage 1 holds k-step kt + 1; every wave is done reading stage 0
-      if (kt + 2 < nk) stage_tiles<0>(A, B, ao, bo, kt + 2, w);
+      if (kt + 2 < nk) stage_tiles<0>(A, B, ao, bo, k2 < nk ? k2 : k2 - nk, w);
       mma_stage_fp8<1>(acc, fa, fb, fs, lane);
     }
   } else {
@@ -438,21 +444,21 @@ __device__ inline void gemm_main_op(const Op<kNatA>& A, const Op<kNatB>& B, cons
     uint4 a[2], b[kNB];
     wait_vmem();
     __syncthreads();  // stage 0 holds k-step 0; every wave is done reading stage 1
-    stage_tiles<1>(A, B, ao, bo, 1, w);
+    stage_tiles<1>(A, B, ao, bo, rot + 1 < nk ? rot + 1 : rot + 1 - nk, w);
 #pragma unroll
     for (int i = 0; i < 2; ++i) a[i] = frag_a<0, kNatA>(q, i, 0);
 #pragma unroll
     for (int j = 0; j < kNB; ++j) b[j] = frag_b<0, kNatB>(q, j, 0);
     for (int kt = 0; kt < nk; kt += 2) {
-      kstep_pipe<E, 0>(A, B, ao, bo, kt, nk, w, q, acc, a, b);
-      kstep_pipe<E, 1>(A, B, ao, bo, kt + 1, nk, w, q, acc, a, b);
+      kstep_pipe<E, 0>(A, B, ao, bo, kt, nk, rot, w, q, acc, a, b);
+      kstep_pipe<E, 1>(A, B, ao, bo, kt + 1, nk, rot, w, q, acc, a, b);
     }
   }
 }
 template <class E>
 __device__ inline void gemm_main(Src ra, Src rb, const Offs& ao, const Offs& bo, int nk,
-                                 Acc& acc) {
-  gemm_main_op<E, false, false>(Op<false>{ra}, Op<false>{rb}, ao, bo, nk, acc);
+                                 Acc& acc, int rot = 0) {
+  gemm_main_op<E, false, false>(Op<false>{ra}, Op<false>{rb}, ao, bo, nk, acc, rot);
 }
 
 template <class E, bool kNatA = false, bool kNatB = false>
@@ -468,6 +474,16 @@ __device__ inline void gemm_core(Src ra, Src rb, const Offs& ao, const Offs& bo,
 }
 
 // ------------------------------------------------------------------------------ forward
+// First k-step of a tile of rows tok0 .. tok0 + 255 in the forward that keeps softmax
+// terms: the workgroups that share a W tile (one per token block of the chunk) start one
+// k-step apart instead of all reading the same k-slab of it at once (measured: 2.4% of
+// the chunk forward; the same rotation made the other forward modes no faster and dX
+// slower).  A function of the row block alone, so a logit's k-steps are summed in the
+// same order whichever workgroup computes it.
+__device__ inline int tile_rot(int64_t tok0, int nk) {
+  return (int)((uint32_t)(int)(tok0 >> 8) % (uint32_t)nk);
+}
+
 struct FwdArgs {
   int64_t N, H, V;
   const int32_t* ntok;
@@ -816,7 +832,8 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
     const int64_t f0 = (vt_lo + phase) * 256;
     w_offsets(f0, a.V, rowb, ao);
     const char* X0 = xop(a.side0 + sd);
-    gemm_pre(make_src(Wop + f0 * rowb, wend), make_src(X0, X0 + xbytes), ao, bo);
+    gemm_pre(make_src(Wop + f0 * rowb, wend), make_src(X0, X0 + xbytes), ao, bo,
+             kStore ? tile_rot(a.row_lo + (tb - sd * fr.ntbs) * 256, nk) : 0);
   }
   for (; tb < TB; tb += tbg) {
     const int sd = (int)(tb / fr.ntbs);
@@ -884,8 +901,8 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
       const int64_t v0 = vt * 256;
       Acc acc;
       zero_acc(acc);
-      gemm_main<G>(
-          make_src(Wop + v0 * rowb, wend), make_src(X, X + xbytes), ao, bo, nk, acc);
+      gemm_main<G>(make_src(Wop + v0 * rowb, wend), make_src(X, X + xbytes), ao, bo, nk, acc,
+                   kStore ? tile_rot(tok0, nk) : 0);
       // enqueue the next tile: the next vocabulary tile of this block, else the first
       // tile of this workgroup's next token block
       {
@@ -897,10 +914,12 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
         }
         if (ntb < TB) {
           const int nsd = (int)(ntb / fr.ntbs);
-          if (ntb != tb) xoffs(a.row_lo + (ntb - nsd * fr.ntbs) * 256, bo);
+          const int64_t ntok0 = a.row_lo + (ntb - nsd * fr.ntbs) * 256;
+          if (ntb != tb) xoffs(ntok0, bo);
           w_offsets(nv * 256, a.V, rowb, ao);
           const char* Xn = xop(a.side0 + nsd);
-          gemm_pre(make_src(Wop + nv * 256 * rowb, wend), make_src(Xn, Xn + xbytes), ao, bo);
+          gemm_pre(make_src(Wop + nv * 256 * rowb, wend), make_src(Xn, Xn + xbytes), ao, bo,
+                   kStore ? tile_rot(ntok0, nk) : 0);
         }
       }
       // vocab of acc[mb][.][j] = vb + 16 mb + j (the lane part recomputed here, not held
