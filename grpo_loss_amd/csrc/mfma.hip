@@ -474,14 +474,20 @@ __device__ inline void gemm_core(Src ra, Src rb, const Offs& ao, const Offs& bo,
 }
 
 // ------------------------------------------------------------------------------ forward
-// First k-step of a tile of rows tok0 .. tok0 + 255 in the forward that keeps softmax
-// terms: the workgroups that share a W tile (one per token block of the chunk) start one
-// k-step apart instead of all reading the same k-slab of it at once (measured: 2.4% of
-// the chunk forward; the same rotation made the other forward modes no faster and dX
-// slower).  A function of the row block alone, so a logit's k-steps are summed in the
-// same order whichever workgroup computes it.
-__device__ inline int tile_rot(int64_t tok0, int nk) {
-  return (int)((uint32_t)(int)(tok0 >> 8) % (uint32_t)nk);
+// First k-step of a tile of rows tok0 .. tok0 + 255 (the k loop wraps around).  With all
+// workgroups starting at k-step 0, the concurrent loads of a k-step fall at one offset of
+// rows rowb bytes apart, and where rowb is a multiple of 4 KB that offset is a hot spot.
+// The forward that keeps softmax terms (an XCD holds 2 token blocks x 16 vocabulary
+// phases of a chunk) starts each token block one k-step further on (2.4% of that kernel
+// measured, on any row size); the forwards over all rows (8 token blocks x 4 phases per
+// XCD) start every second token block half of K further on when rowb is a multiple of
+// 4 KB (1.5-5% measured; one k-step apart gained nothing, and with 10 KB rows half of K
+// lost 1.5%).  A function of the row block alone, so each logit's k-steps are summed in
+// the same order whichever workgroup computes it.
+__device__ inline int tile_rot(int64_t tok0, int nk, bool keep_terms, int64_t rowb) {
+  if (keep_terms) return (int)((uint32_t)(int)(tok0 >> 8) % (uint32_t)nk);
+  if (rowb % 4096 == 0) return (int)((tok0 >> 8) & 1) * (nk >> 1);
+  return 0;
 }
 
 struct FwdArgs {
@@ -833,7 +839,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
     w_offsets(f0, a.V, rowb, ao);
     const char* X0 = xop(a.side0 + sd);
     gemm_pre(make_src(Wop + f0 * rowb, wend), make_src(X0, X0 + xbytes), ao, bo,
-             kStore ? tile_rot(a.row_lo + (tb - sd * fr.ntbs) * 256, nk) : 0);
+             tile_rot(a.row_lo + (tb - sd * fr.ntbs) * 256, nk, kStore, rowb));
   }
   for (; tb < TB; tb += tbg) {
     const int sd = (int)(tb / fr.ntbs);
@@ -902,7 +908,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
       Acc acc;
       zero_acc(acc);
       gemm_main<G>(make_src(Wop + v0 * rowb, wend), make_src(X, X + xbytes), ao, bo, nk, acc,
-                   kStore ? tile_rot(tok0, nk) : 0);
+                   tile_rot(tok0, nk, kStore, rowb));
       // enqueue the next tile: the next vocabulary tile of this block, else the first
       // tile of this workgroup's next token block
       {
@@ -919,7 +925,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
           w_offsets(nv * 256, a.V, rowb, ao);
           const char* Xn = xop(a.side0 + nsd);
           gemm_pre(make_src(Wop + nv * 256 * rowb, wend), make_src(Xn, Xn + xbytes), ao, bo,
-                   kStore ? tile_rot(ntok0, nk) : 0);
+                   tile_rot(ntok0, nk, kStore, rowb));
         }
       }
       // vocab of acc[mb][.][j] = vb + 16 mb + j (the lane part recomputed here, not held
