@@ -187,7 +187,8 @@ constexpr int kTokTile = 256;    // rows per token tile of the MFMA kernels
 constexpr int kVocTile = 256;    // vocabulary entries per tile
 constexpr int kMergeBlock = 256; // rows per block of the merge kernel
 constexpr int kMergeLanes = 4;   // lanes per row merging a chunk's policy partials
-constexpr int kMaxPhases = 32;   // most vocabulary phases of one forward launch
+constexpr int kMaxPhases = 32;   // vocabulary phases of the FMA forward
+constexpr int kMaxFwdPhases = 256; // most vocabulary phases of one MFMA forward launch
 constexpr int kPieceTiles = 128; // vocabulary tiles per piece of the split backward (32768)
 constexpr int kCompactRows = 4096; // rows per workgroup of the row compaction
 
@@ -198,15 +199,20 @@ inline size_t compact_bytes(int64_t N) {
 }
 
 // Vocabulary phases of the MFMA forward.  Its persistent grid (8 XCDs x 32 workgroups)
-// covers 32 / P token blocks per XCD x P phases per round; pick P in {4, 8, 16, 32} that
-// minimises the tiles per workgroup, ceil(blocks / (8 * 32 / P)) * ceil(tiles / P),
+// covers 256 / P token blocks x P phases per round (32 / P per XCD for P <= 32; a token
+// block's phases spread over P / 32 XCDs above that); pick P in {4, .., 256} that
+// minimises the tiles per workgroup, ceil(blocks / (256 / P)) * ceil(tiles / P),
 // preferring fewer phases (each W tile then feeds more workgroups of an XCD; W tiles are
-// also shared across XCDs, X blocks are not).
+// also shared across XCDs, X blocks are not).  Phases past 32 serve only launches of
+// fewer than 8 token blocks, which 32 phases would leave on fewer than 8 XCDs (a last
+// chunk of 3 token blocks: P = 64, all 8 XCDs, instead of 3); elsewhere their rounding
+// gain is marginal and the partials, P per row, would grow.
 __host__ __device__ inline int fwd_phases(int64_t token_blocks, int64_t vocab_tiles) {
   int best = 4;
   int64_t best_cost = -1;
-  for (int P = 4; P <= kMaxPhases; P *= 2) {
-    const int64_t per_round = 8 * (32 / P);
+  const int max_p = token_blocks < 8 ? kMaxFwdPhases : 32;
+  for (int P = 4; P <= max_p; P *= 2) {
+    const int64_t per_round = 256 / P;
     const int64_t cost = ((token_blocks + per_round - 1) / per_round) * ((vocab_tiles + P - 1) / P);
     if (best_cost < 0 || cost < best_cost) {
       best_cost = cost;

@@ -102,7 +102,7 @@ bool options_ok(const grpo_options* o) {
 // Pieces of the vocabulary split when the caller names no size: at least enough that no
 // piece has more than kPieceTiles tiles (the workspace bound), at most twice that, chosen
 // for the fewest rounds of the chunk forward's persistent grid on a full chunk (ntb token
-// blocks): a piece of pt tiles takes ceil(ntb / (8 (32 / P))) ceil(pt / P) rounds with P
+// blocks): a piece of pt tiles takes ceil(ntb / (256 / P)) ceil(pt / P) rounds with P
 // phases (fwd_phases), plus about one round's worth per piece for its launches and the dX
 // sums it writes and reads (measured at the 20K-context shape: 87 us per extra piece
 // against 112 us per round).  Phi-4's 392 tiles: 5 pieces of 79 tiles, 25 rounds, instead
@@ -113,7 +113,7 @@ int default_pieces(int64_t nvt, int64_t ntb) {
   for (int64_t np = lo; np <= 2 * lo; ++np) {
     const int64_t pt = (nvt + np - 1) / np;
     const int P = fwd_phases(ntb, pt);
-    const int64_t per_round = (int64_t)kXcdsHost * (32 / P);
+    const int64_t per_round = (int64_t)kXcdsHost * 32 / P;   // P <= 256
     const int64_t rounds = ((ntb + per_round - 1) / per_round) * ((pt + P - 1) / P);
     const int64_t cost = np * (rounds + 1);
     if (best_cost < 0 || cost < best_cost) {
@@ -257,8 +257,8 @@ static int traced(const grpo_options* opts, int launches) {
 
 size_t part_floats_max(int64_t max_rows, int nsides, int64_t tiles, int npieces) {
   // the phase count depends on the token blocks through a ceiling, so the product is not
-  // monotone in the rows: take the maximum over every block count (P <= kMaxPhases bounds
-  // the blocks past a million, which no workload reaches)
+  // monotone in the rows: take the maximum over every block count (P <= kMaxFwdPhases
+  // bounds the blocks past a million, which no workload reaches)
   const int64_t nb = (max_rows + 255) / 256;
   const int64_t lim = nb < ((int64_t)1 << 20) ? nb : ((int64_t)1 << 20);
   size_t best = 0;
@@ -266,7 +266,7 @@ size_t part_floats_max(int64_t max_rows, int nsides, int64_t tiles, int npieces)
     const size_t f = (size_t)3 * nsides * npieces * fwd_phases(nsides * b, tiles) * b * 256;
     best = std::max(best, f);
   }
-  if (nb > lim) best = std::max(best, (size_t)3 * nsides * npieces * kMaxPhases * nb * 256);
+  if (nb > lim) best = std::max(best, (size_t)3 * nsides * npieces * kMaxFwdPhases * nb * 256);
   return best;
 }
 

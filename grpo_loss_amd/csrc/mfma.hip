@@ -769,7 +769,9 @@ __device__ inline void fwd_fold_fixed(const Acc& acc, float s2, int vlim, int vb
 // the current round and a vocabulary phase: the 32 workgroups of one XCD cover 32 / P
 // token blocks x P phases (P = fwd_phases(...), 4 for the long-context shape), so each W
 // tile in flight on an XCD is shared by 32 / P workgroups and each X block by P, and all
-// XCDs sweep the same W tiles together.  A workgroup keeps its token block for a whole
+// XCDs sweep the same W tiles together.  With few token blocks (a short last chunk) P
+// can exceed 32: the phases of one token block then span P / 32 XCDs, and the round
+// holds 256 / P token blocks.  A workgroup keeps its token block for a whole
 // round and walks the vocabulary tiles of its phase (vt = phase, phase + P, ...), folding
 // each 256 x 256 logit tile into per-lane running (max, sum of exp2, target logit)
 // without storing it (or, in single-pass mode, storing its softmax terms).  The loads of
@@ -809,9 +811,12 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
   pl.P = a.npieces * P;
   pl.nsides = a.nsides;
   pl.stride = (int64_t)fr.ntbs * 256;
-  const int tb_per_xcd = slots / P;
-  const int phase = slot % P;
-  const int tbg = kXcds * tb_per_xcd;            // token blocks per round
+  // P <= 32: each XCD holds 32 / P token blocks x P phases; P > 32 (fewer token blocks
+  // than XCDs x 32 / P... in the rounds): a token block's phases span P / 32 XCDs
+  const int xpb = P > slots ? P / slots : 1;     // XCDs per token block
+  const int tb_per_xcd = P > slots ? 0 : slots / P;
+  const int phase = P > slots ? (xcd % xpb) * slots + slot : slot % P;
+  const int tbg = P > slots ? kXcds / xpb : kXcds * tb_per_xcd;  // token blocks per round
   const int64_t rowb = a.H * G::kBytes;          // bytes per row
   const int nk = (int)(rowb / 128);              // k-steps of 128 bytes
   const float s2 = a.scale2;
@@ -827,7 +832,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
   };
 
   const int slot_ph = a.piece * P + phase;      // this phase's partial slot
-  int tb = xcd * tb_per_xcd + slot / P;
+  int tb = P > slots ? xcd / xpb : xcd * tb_per_xcd + slot / P;
   if (tb >= TB) return;
   // loads of the first tile.  A phase with no vocabulary tile (the piece has fewer than P
   // tiles) still writes its empty partials (max -inf, sum 0) for every token block.

@@ -81,6 +81,21 @@ def test_workspace_follows_chunk_rows(lib):
     assert f(*shape, ctypes.byref(g.options(vocab_piece=100))) == 0
 
 
+def test_workspace_for_few_token_blocks(lib):
+    """MFMA shapes with 1 to 40 token blocks: the plan (vocabulary pieces, phase counts,
+    partial buffers) is well defined wherever fewer than 8 token blocks let the forward's
+    phases span several XCDs, and the workspace grows with the rows."""
+    f = lib.grpo_workspace_bytes
+    for V in (300, 5003, 151936):
+        for need_dw in (0, 1):
+            prev = 0
+            for rows in (1, 200, 256, 700, 1000, 1800, 2047, 4096, 10000):
+                b = f(1, rows, 256, V, 1, need_dw)
+                assert b > 0, (V, need_dw, rows)
+                assert b >= prev, (V, need_dw, rows)
+                prev = b
+
+
 def test_bad_arguments_rejected_before_launch(lib):
     p = ctypes.c_void_p(16)   # never dereferenced: validation fails first
     nul = None
