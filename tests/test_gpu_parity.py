@@ -819,6 +819,22 @@ def test_vocab_boundary_targets():
     assert abs(gpu["loss"] - f["loss"]) <= 1e-3 * abs(f["loss"])
 
 
+@pytest.mark.parametrize("last_blocks", [1, 3, 7])
+def test_short_last_chunk(last_blocks):
+    """A single-pass step whose last 4096-row chunk holds only 1, 3 or 7 token blocks (the
+    last one ragged): that chunk's forward runs more than 32 vocabulary phases per token
+    block, spread over several XCDs, and the step still matches the oracle."""
+    loss_rows = 4096 + 256 * last_blocks - 100
+    comp = loss_rows // 2
+    wl = dataclasses.replace(workload_by_name("qwen2.5-1.5b-bf16"), G=2, L=comp + 16, H=256,
+                             V=5003, prefix=16, comp_min=comp, comp_max=comp)
+    inp = generate(wl)
+    n = int(inp.mask.sum())
+    _say(f"[short last chunk] {n} loss rows, last chunk {n - 4096} rows")
+    assert 0 < n - 4096 <= 256 * last_blocks
+    check_small(wl, inp, single_pass=True)
+
+
 @pytest.mark.parametrize("single_pass", [False, True], ids=["two-pass", "single-pass"])
 @pytest.mark.parametrize("need_dW", [False, True], ids=["dX", "dX+dW"])
 @pytest.mark.parametrize("V", [100, 5003])
