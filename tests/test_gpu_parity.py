@@ -330,14 +330,24 @@ def test_chunk_rows_agree():
         assert np.all(o["dX"][~m] == 0.0)
 
 
-def test_single_pass_graph_replay():
+GRAPH_SHAPES = {
+    "one-chunk": ("qwen2.5-1.5b-bf16", SMALL["qwen2.5-1.5b-bf16"]),
+    # about 9000 loss rows: three chunks, the last ragged, each in four vocabulary pieces
+    "three-chunks": ("llama3.1-8b-train-bf16",
+                     dict(G=4, L=2600, H=1024, prefix=100, comp_min=2000, comp_max=2500,
+                          need_dW=False)),
+}
+
+
+@pytest.mark.parametrize("shape", list(GRAPH_SHAPES))
+def test_single_pass_graph_replay(shape):
     """The single-pass call captured in a HIP graph and replayed three times, with eager work
     and synchronisations between the replays (outputs overwritten with NaN, another eager
     call of the library on other buffers): every replay reproduces the eager result bit for
     bit.  A replay after the inputs were changed in place matches an eager call on them."""
     g = _lib()
-    name = "qwen2.5-1.5b-bf16"
-    wl = dataclasses.replace(workload_by_name(name), **SMALL[name])
+    name, kw = GRAPH_SHAPES[shape]
+    wl = dataclasses.replace(workload_by_name(name), **kw)
     inp = generate(wl)
     d = to_device(inp)
     adv = g.grpo_advantages(d["rewards"], wl.eps)
