@@ -203,15 +203,17 @@ inline size_t compact_bytes(int64_t N) {
 // block's phases spread over P / 32 XCDs above that); pick P in {4, .., 256} that
 // minimises the tiles per workgroup, ceil(blocks / (256 / P)) * ceil(tiles / P),
 // preferring fewer phases (each W tile then feeds more workgroups of an XCD; W tiles are
-// also shared across XCDs, X blocks are not).  Phases past 32 serve only launches of
-// fewer than 8 token blocks, which 32 phases would leave on fewer than 8 XCDs (a last
-// chunk of 3 token blocks: P = 64, all 8 XCDs, instead of 3); elsewhere their rounding
-// gain is marginal and the partials, P per row, would grow.
+// also shared across XCDs, X blocks are not).  Phases past 32 serve short launches, whose
+// last round 32 phases would leave on few XCDs (a last chunk of 3 token blocks: P = 64,
+// all 8 XCDs, instead of 3; 19 token blocks: rounds of 4 instead of 8, 8 and 3); they are
+// considered only while P x blocks <= kWidePhaseBlocks, which bounds the partials (P per
+// row) of the launches that pick them below those of the largest launches.
+constexpr int64_t kWidePhaseBlocks = 2048;
 __host__ __device__ inline int fwd_phases(int64_t token_blocks, int64_t vocab_tiles) {
   int best = 4;
   int64_t best_cost = -1;
-  const int max_p = token_blocks < 8 ? kMaxFwdPhases : 32;
-  for (int P = 4; P <= max_p; P *= 2) {
+  for (int P = 4; P <= kMaxFwdPhases; P *= 2) {
+    if (P > 32 && P * token_blocks > kWidePhaseBlocks) break;
     const int64_t per_round = 256 / P;
     const int64_t cost = ((token_blocks + per_round - 1) / per_round) * ((vocab_tiles + P - 1) / P);
     if (best_cost < 0 || cost < best_cost) {

@@ -780,9 +780,11 @@ __device__ inline void fwd_fold_fixed(const Acc& acc, float s2, int vlim, int vb
 // kMode 0: both sides over all rows (two-pass forward); 1: one side over all rows
 // (single-pass reference); 2: policy rows of one chunk, softmax terms kept relative to a
 // running maximum (single-pass); 3: as 2 with the reference side's log-sum-exp of each
-// row as the fixed reference of its terms, which mode 1 must have produced: its partials
-// are merged per row at the start of each token block, and workgroups of phase 0 store
-// the result at pm[r - row_lo].  The partials of mode 3 carry that reference as their
+// row as the fixed reference of its terms, which mode 1 must have produced: the first
+// piece's launch merges its partials per row at the start of each token block, and its
+// workgroups of phase 0 store the result at pm[r - row_lo], which the later pieces read
+// back (the merge costs the reference launch's phase count in loads per row and
+// workgroup).  The partials of mode 3 carry that reference as their
 // maximum.  Modes 0 and 1 run the same code; distinct instances keep their profiles apart.
 template <class E, class G, int kMode>
 __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
@@ -868,6 +870,10 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
         if (r < fr.rhi) {
           if (a.ref_from_saved) {
             mr = a.saved[(int64_t)a.idx[r] * 4] * kLog2e;
+          } else if (a.piece > 0) {
+            // the chunk's first piece stored it (below); nothing writes pm between the
+            // pieces' forward launches
+            mr = a.pm[r - a.row_lo];
           } else {
             const PartLayout rl = part_layout(ntok, 1, nvt_all);
             float M = -INFINITY;
@@ -879,7 +885,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
             }
             mr = M + log2f(sm);
           }
-          if (phase == 0) a.pm[r - a.row_lo] = mr;
+          if (phase == 0 && (a.piece == 0 || a.ref_from_saved)) a.pm[r - a.row_lo] = mr;
         }
         s_mr[tid] = mr;
       }
