@@ -637,6 +637,33 @@ struct FoldOut {
   int nvalid;        // token columns of this block that are loss rows
 };
 
+// Kept terms of two vocabulary blocks (mb, mb + 1) of one token column, packed (4 terms
+// per lane and block: p for mb, q for mb + 1), written with one 16-byte store per lane
+// instead of two 8-byte ones.  A lane of an even 16-lane row (lane group g = 0, 2) holds
+// entries 4g .. 4g + 3 of each block and its partner lane ^ 16 in the odd row the next
+// four: the even lane trades its q for the odd lane's p (ds_swizzle, xor 16), so the even
+// lane stores entries 4g .. 4g + 7 of block mb and the odd lane entries 4(g - 1) .. 4g + 3
+// of block mb + 1, 24 bytes past its own 8-byte slot (term_lane_off).  Same bytes, same
+// addresses, half the store instructions.  Every lane of the wave must be active.
+__device__ inline uint32_t term_lane_off(int lane) { return ((lane >> 4) & 1) ? 24u : 0u; }
+__device__ inline uint32_t from_lane_xor16(uint32_t v) {
+  // ds_swizzle bit mode: and mask 0x1f, or mask 0, xor mask 0x10
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+}
+__device__ inline void store_term_pair(u32x2 p, u32x2 q, bool odd, Src pt, uint32_t lane_off,
+                                       uint32_t off) {
+  const uint32_t r0 = from_lane_xor16(odd ? p[0] : q[0]);
+  const uint32_t r1 = from_lane_xor16(odd ? p[1] : q[1]);
+  const u32x4 v = odd ? u32x4{r0, r1, q[0], q[1]} : u32x4{p[0], p[1], r0, r1};
+  __builtin_amdgcn_raw_buffer_store_b128(v, pt, lane_off, off, 0);
+  // A vector store of more than 8 bytes still reads its data registers after it issues:
+  // a VALU write of them in the next instruction slot changed what some lanes stored
+  // (the terms of the next block's fma), and the compiler puts no gap there by itself.
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 1");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Fold one 256 x 256 logit tile into this lane's running (max, sum of exp2) per token
 // column, kept in LDS, and catch the target logit.  kFull: every vocabulary row of the
 // tile is below V, so no row masks are evaluated.  kStore: single-pass mode; the running
@@ -685,16 +712,23 @@ __device__ inline void fwd_fold(const Acc& acc, float s2, int vlim, int vb, int 
       // stored as 0 (its sum is never read)
       const float ns = ok ? nm : INFINITY;
       const uint32_t so = (uint32_t)nb * fo.col16_t + fo.v0_t;
+      const bool odd = (lane >> 4) & 1;
+      const uint32_t lt = fo.lane_t + term_lane_off(lane);
 #pragma unroll
-      for (int mb = 0; mb < kMB; ++mb) {
-        float e[4];
+      for (int mb = 0; mb < kMB; mb += 2) {
+        u32x2 pk[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          e[j] = (kFull || mb * 16 + j < vlim) ? exp2_fast(fmaf(acc[mb][nb][j], s2, -ns)) : 0.f;
-          sum += e[j];
+        for (int h = 0; h < 2; ++h) {
+          float e[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            e[j] = (kFull || (mb + h) * 16 + j < vlim)
+                       ? exp2_fast(fmaf(acc[mb + h][nb][j], s2, -ns)) : 0.f;
+            sum += e[j];
+          }
+          pk[h] = u32x2{E::pack2(e[0], e[1]), E::pack2(e[2], e[3])};
         }
-        const u32x2 pk = {E::pack2(e[0], e[1]), E::pack2(e[2], e[3])};
-        __builtin_amdgcn_raw_buffer_store_b64(pk, fo.pt, fo.lane_t, so + mb * 32, 0);
+        store_term_pair(pk[0], pk[1], odd, fo.pt, lt, so + mb * 32);
       }
       if (wm == 0 && lane < 16 && ok)
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(nm), fo.pm, fo.lane_m,
@@ -735,19 +769,36 @@ __device__ inline void fwd_fold_fixed(const Acc& acc, float s2, int vlim, int vb
     const float mr = s_mr[n];
     float sum = s_run[1][nb][tid];
     const uint32_t so = (uint32_t)nb * fo.col16_t + fo.v0_t;
+    const bool odd = (lane >> 4) & 1;
+    const uint32_t lt = fo.lane_t + term_lane_off(lane);
 #pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) {
-      float e[4];
+    for (int mb = 0; mb < kMB; mb += 2) {
+      u32x2 pk[2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        e[j] = (kFull || mb * 16 + j < vlim) ? exp2_fast(fmaf(acc[mb][nb][j], s2, -mr)) : 0.f;
-        sum += e[j];
+      for (int h = 0; h < 2; ++h) {
+        float e[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          e[j] = (kFull || (mb + h) * 16 + j < vlim)
+                     ? exp2_fast(fmaf(acc[mb + h][nb][j], s2, -mr)) : 0.f;
+          sum += e[j];
+        }
+        pk[h] = u32x2{E::pack2(e[0], e[1]), E::pack2(e[2], e[3])};
       }
-      const u32x2 pk = {E::pack2(e[0], e[1]), E::pack2(e[2], e[3])};
-      __builtin_amdgcn_raw_buffer_store_b64(pk, fo.pt, fo.lane_t, so + mb * 32, 0);
+      store_term_pair(pk[0], pk[1], odd, fo.pt, lt, so + mb * 32);
     }
     s_run[1][nb][tid] = sum;
     const int loc = s_y[n] - vb;
+    if (zero_target) {
+      // The kept term of the target is replaced by 0 (its term is still in the row's sum)
+      // by the lane whose 16-byte store above wrote it, at the same address and after
+      // it, so it lands last.  That store's 8 entries start at vocabulary vb + 16 mb (even
+      // lane group) or vb + 16 mb + 12 (odd), mb = 0, 2, 4, 6.
+      const int d = loc - (odd ? 12 : 0);
+      if ((unsigned)d < 128u && (d & 31) < 8)
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, fo.pt,
+                                              lt + (d >> 5) * 64 + (d & 31) * 2, so, 0);
+    }
     if ((unsigned)loc < 128u && (loc & 12) == 0) {  // this lane holds the target logit
       float z = 0.f;
 #pragma unroll
@@ -755,12 +806,6 @@ __device__ inline void fwd_fold_fixed(const Acc& acc, float s2, int vlim, int vb
 #pragma unroll
         for (int j = 0; j < 4; ++j) z = (loc == mb * 16 + j) ? acc[mb][nb][j] : z;
       s_zt[n] = z;
-      // the kept term of the target is replaced by 0 (after the packed store above, same
-      // lane and address, so it lands last); its term is still in the row's sum
-      if (zero_target)
-        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, fo.pt,
-                                              fo.lane_t + (loc >> 4) * 32 + (loc & 3) * 2, so,
-                                              0);
     }
   }
 }
