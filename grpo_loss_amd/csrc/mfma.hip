@@ -1173,6 +1173,21 @@ __host__ __device__ inline int64_t dx_sum_offset(int64_t tile, int w, int nb, in
   return tile * 65536 + w * 8192 + (nb * 8 + mb) * 256 + lane * 4;
 }
 
+// dX with its reduction split ksplit ways over the vocabulary: a launch's n_items (output
+// tile, split) parts go out as runs when they divide evenly over its nwg workgroups, q =
+// n_items / nwg >= 2 each: workgroup L takes parts L q .. L q + q - 1 of the tile-major
+// order (part = tile ksplit + ks, tile = token tile nht + H tile), the consecutive parts of
+// one tile as one k loop whose sum goes to the slot of the run's first part.  Slot ks of a
+// tile then holds a partial only where a run starts: ks == 0 or part % q == 0.  Otherwise
+// (a ragged last chunk, no split) every item is one part and every slot holds one.
+__host__ __device__ inline bool dx_runs(int64_t n_items, int ksplit, int nwg) {
+  return ksplit > 1 && n_items > nwg && n_items % nwg == 0;
+}
+__host__ __device__ inline bool dx_slot_used(bool runs, int64_t tile, int ks, int ksplit,
+                                             int64_t q) {
+  return !runs || ks == 0 || (tile * ksplit + ks) % q == 0;
+}
+
 // ------------------------------------------------------------------------------- dX
 // C[h][r] = sum_v W[v][h] T[r][v] over the chunk buffer's vocabulary columns (the padded
 // vocabulary, or one piece of it: columns 0 .. kcols - 1 of rows of ld entries hold
@@ -1195,7 +1210,9 @@ __host__ __device__ inline int64_t dx_sum_offset(int64_t tile, int w, int nb, in
 //
 // Persistent over a work list of (k split, token tile, H tile) items, H tile fastest,
 // holding only the token tiles of this chunk that have loss rows, so every workgroup gets
-// the same number of items up to one.  Workgroups are numbered XCD-major (workgroup b
+// the same number of items up to one; with the reduction split and items that divide
+// evenly over the workgroups, as runs of one tile's consecutive parts instead (dx_runs),
+// so that a workgroup stores about 2 partials rather than one per part.  Workgroups are numbered XCD-major (workgroup b
 // runs on XCD b % 8), so the items that share a T tile and k range run on one XCD.  Each
 // item's first k-step is enqueued before the previous item's epilogue, so its memory
 // latency overlaps the epilogue's instead of following it.
@@ -1286,21 +1303,48 @@ dx_kernel(int64_t H, int64_t V, int64_t ld, int64_t kcols, int64_t v_base, int64
 #pragma unroll
       for (int mb = 0; mb < kMB; ++mb) acc[mb][nb] = *slot_ptr(d, nb, mb);
   };
+  // this workgroup's work units: items first, first + nwg, .. or, with runs (dx_runs), the
+  // runs of one tile's consecutive parts within parts first q .. first q + q - 1
+  const bool runs = dx_runs(n_items, ksplit, nwg);
+  const int64_t q = n_items / nwg;
+  auto unit = [&](int64_t u, Item& d) -> bool {
+    if (!runs) {
+      const int64_t item = first + u * nwg;
+      if (item >= n_items) return false;
+      d = decode(item);
+      return true;
+    }
+    int64_t part = first * q;
+    const int64_t pend = part + q;
+    for (int64_t i = 0; part < pend; ++i) {
+      const int64_t tile = part / ksplit, ks0 = part % ksplit;
+      const int64_t len = ksplit - ks0 < pend - part ? ksplit - ks0 : pend - part;
+      if (i == u) {
+        d.tt = tile / nht;
+        d.h0 = (tile % nht) * 256;
+        d.ks = ks0;
+        d.kbeg = 2 * (npair * ks0 / ksplit);
+        d.kend = 2 * (npair * (ks0 + len) / ksplit);
+        return true;
+      }
+      part += len;
+    }
+    return false;
+  };
   Acc acc;
-  if (first < n_items) {
-    const Item d = decode(first);
+  Item d;
+  bool have = unit(0, d);
+  if (have) {
     if (d.kend > d.kbeg) gemm_pre_op(opA(d), opB(d), ao, bo);
     init_acc(acc, d);
   }
-  for (int64_t item = first; item < n_items; item += nwg) {
-    const Item d = decode(item);
+  for (int64_t u = 0; have; ++u) {
     const int64_t tok0 = c0 + d.tt * 256;
     if (d.kend > d.kbeg)
       gemm_main_op<E, true, false>(opA(d), opB(d), ao, bo, (int)(d.kend - d.kbeg), acc);
-    if (item + nwg < n_items) {
-      const Item dn = decode(item + nwg);
-      if (dn.kend > dn.kbeg) gemm_pre_op(opA(dn), opB(dn), ao, bo);
-    }
+    Item dn;
+    const bool more = unit(u + 1, dn);
+    if (more && dn.kend > dn.kbeg) gemm_pre_op(opA(dn), opB(dn), ao, bo);
     if (final_dx) {
       if (!skip) {
         // dX = c g_r ((1 - p_y) W[y_r] - f_r C), as dx_final_kernel
@@ -1365,7 +1409,9 @@ dx_kernel(int64_t H, int64_t V, int64_t ld, int64_t kcols, int64_t v_base, int64
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb) *slot_ptr(d, nb, mb) = acc[mb][nb];
     }
-    if (item + nwg < n_items) init_acc(acc, decode(item + nwg));
+    if (more) init_acc(acc, dn);
+    d = dn;
+    have = more;
   }
   if (bad) atomicOr(found_inf, 1);
 }
@@ -1387,10 +1433,18 @@ dx_reduce_kernel(int64_t H, int64_t R, int64_t c0, int ksplit, const int32_t* __
   const int64_t t = idx[r];
   float gs = saved[t * 4 + 3] * ((grad_loss ? *grad_loss : 1.f) / loss_scale);
   if (redo && *redo == 0) gs *= fixed_row_factor(rl, t, saved, mr);
+  // the slots dx_kernel wrote: with runs, only those where a run starts
+  const int64_t rows = ntok - c0 < R ? ntok - c0 : R;
+  const int64_t nht = H / 256, n_items = (rows + 255) / 256 * nht * ksplit;
+  const bool runs = dx_runs(n_items, ksplit, kNumWG);
+  const int64_t q = n_items / kNumWG;
   bool bad = false;
   for (int64_t h = threadIdx.x * 4; h < H; h += 256 * 4) {
+    const int64_t tile = rl / 256 * nht + h / 256;
     f32x4 s = *reinterpret_cast<const f32x4*>(dxp + rl * H + h);
-    for (int k = 1; k < ksplit; ++k) s += *reinterpret_cast<const f32x4*>(dxp + (k * R + rl) * H + h);
+    for (int k = 1; k < ksplit; ++k)
+      if (dx_slot_used(runs, tile, k, ksplit, q))
+        s += *reinterpret_cast<const f32x4*>(dxp + (k * R + rl) * H + h);
     uint16_t o[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -1432,6 +1486,11 @@ dx_final_kernel(int64_t H, int64_t V, int64_t R, int64_t c0, int nht, int ksplit
   if (tok0 >= ntok) return;
   const float c = (grad_loss ? *grad_loss : 1.f) / loss_scale;
   const int64_t hb = ht * 256 + wm * 128 + 4 * (lane >> 4);
+  // the slots dx_kernel wrote: with runs, only those where a run starts
+  const int64_t rows = ntok - c0 < R ? ntok - c0 : R;
+  const int64_t n_items = (rows + 255) / 256 * nht * ksplit;
+  const bool runs = dx_runs(n_items, ksplit, kNumWG);
+  const int64_t q = n_items / kNumWG, tile = tt * nht + ht;
   bool bad = false;
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
@@ -1451,8 +1510,9 @@ dx_final_kernel(int64_t H, int64_t V, int64_t R, int64_t c0, int nht, int ksplit
     for (int mb = 0; mb < kMB; ++mb) {
       f32x4 sm = *reinterpret_cast<const f32x4*>(dxp + dx_sum_offset(tt * nht + ht, w, nb, mb, lane));
       for (int k = 1; k < ksplit; ++k)
-        sm += *reinterpret_cast<const f32x4*>(
-            dxp + dx_sum_offset((k * (R / 256) + tt) * nht + ht, w, nb, mb, lane));
+        if (dx_slot_used(runs, tile, k, ksplit, q))
+          sm += *reinterpret_cast<const f32x4*>(
+              dxp + dx_sum_offset((k * (R / 256) + tt) * nht + ht, w, nb, mb, lane));
       const uint2 wv = *reinterpret_cast<const uint2*>(wy + mb * 16);
       const float w0 = E::to_f32((typename E::T)(wv.x & 0xffffu));
       const float w1 = E::to_f32((typename E::T)(wv.x >> 16));
