@@ -829,6 +829,28 @@ def test_vocab_boundary_targets():
     assert abs(gpu["loss"] - f["loss"]) <= 1e-3 * abs(f["loss"])
 
 
+@pytest.mark.parametrize("single_pass,need_dW", [(False, False), (True, False), (True, True)],
+                         ids=["two-pass", "single-pass", "single-pass-dW"])
+def test_split_dx_runs(single_pass, need_dW):
+    """dX with its reduction split over the vocabulary and handed out as runs of one output
+    tile's consecutive parts: H = 1536 (6 H tiles) and a full 4096-row chunk give 96 tiles,
+    split 8 ways (768 parts, runs of 3 per workgroup), then a ragged 1000-row chunk whose
+    parts do not divide evenly (one part per item). Reduced by dx_final_kernel (vocabulary
+    split) or, for the single pass with dW, by dx_reduce_kernel; against the oracle."""
+    comp = 2548
+    wl = dataclasses.replace(workload_by_name("qwen2.5-1.5b-bf16"), G=2, L=comp + 16, H=1536,
+                             V=5003, prefix=16, comp_min=comp, comp_max=comp, need_dW=need_dW)
+    inp = generate(wl)
+    n = int(inp.mask.sum())
+    # the library's split rule: k <= 8 minimising ceil(tiles k / 256) / k, smallest on ties
+    tiles = (wl.H // 256) * (4096 // 256)
+    ksplit = min(range(1, 9), key=lambda k: (-(-tiles * k // 256) / k, k))
+    parts_full, parts_last = tiles * ksplit, (wl.H // 256) * (-(-(n - 4096) // 256)) * ksplit
+    _say(f"[split dX runs] {n} loss rows, ksplit {ksplit}, parts {parts_full} and {parts_last}")
+    assert ksplit == 8 and parts_full % 256 == 0 and parts_full > 256 and parts_last % 256 != 0
+    check_small(wl, inp, single_pass=single_pass)
+
+
 @pytest.mark.parametrize("last_blocks", [1, 3, 7])
 def test_short_last_chunk(last_blocks):
     """A single-pass step whose last 4096-row chunk holds only 1, 3 or 7 token blocks (the
