@@ -40,6 +40,8 @@
  *     failures return GRPO_ERR_HIP.  Data-dependent problems (non-finite values, a target
  *     outside [0, V) on a loss row) are reported through device-side flag words.
  *   - Calls that share a workspace must not overlap in time (same stream, or synchronised).
+ *   - A workspace's contents on entry do not matter: every call writes what it reads, and
+ *     grpo_loss_bwd takes nothing from the workspace of the forward before it.
  */
 #ifndef GRPO_H_
 #define GRPO_H_

@@ -851,6 +851,50 @@ def test_split_dx_runs(single_pass, need_dW):
     check_small(wl, inp, single_pass=single_pass)
 
 
+@pytest.mark.parametrize("path", ["two-pass", "single-pass", "single-pass-dW"])
+def test_workspace_contents_do_not_matter(path):
+    """Nothing is read from the workspace before the same call wrote it: a workspace filled
+    with 0xff bytes (NaN as fp32, -1 as int32), also between the two-pass forward and
+    backward, gives results bit-identical to a zeroed one.
+    The shape is the split-dX one, whose reductions skip the partial slots no run wrote."""
+    g = _lib()
+    comp = 2548
+    need_dW = path == "single-pass-dW"
+    wl = dataclasses.replace(workload_by_name("qwen2.5-1.5b-bf16"), G=2, L=comp + 16, H=1536,
+                             V=5003, prefix=16, comp_min=comp, comp_max=comp)
+    inp = generate(wl)
+    d = to_device(inp)
+    adv = g.grpo_advantages(d["rewards"], wl.eps)
+    grad = torch.ones(1, dtype=torch.float32, device="cuda")
+    nbytes = g.grpo_workspace_bytes(wl.S, wl.L, wl.H, wl.V, d["xq"].dtype, need_dW)
+    outs = []
+    for fill in (0, 255):
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device="cuda")
+        _say(f"[workspace contents] {path}, workspace bytes all {fill:#04x}")
+        if path == "two-pass":
+            f = g.grpo_loss_fwd(d["xq"], d["xp"], d["W"], d["targets"], d["mask"], adv, wl.beta,
+                                wl.L, workspace=ws)
+            ws.fill_(fill)   # the backward takes nothing from the forward's workspace either
+            b = g.grpo_loss_bwd(d["xq"], d["W"], d["targets"], d["mask"], f["saved"], wl.L,
+                                grad, 1.0, workspace=ws)
+        else:
+            f = b = g.grpo_loss_fwd_bwd(d["xq"], d["xp"], d["W"], d["targets"], d["mask"], adv,
+                                        wl.beta, wl.L, grad, 1.0, need_dW=need_dW, workspace=ws)
+        torch.cuda.synchronize()
+        o = {"loss": f["loss"].cpu(), "logp": f["logp"].cpu(), "kl": f["kl"].cpu(),
+             "dX": b["dXq"].view(torch.int16).cpu(), "status": int(f["status"].item()),
+             "found_inf": int(b["found_inf"].item())}
+        if need_dW:
+            o["dW"] = b["dW"].cpu()
+        outs.append(o)
+    z, p = outs
+    assert z["status"] == 0 and z["found_inf"] == 0 and p["status"] == 0 and p["found_inf"] == 0
+    for k in z:
+        if isinstance(z[k], torch.Tensor):
+            assert torch.equal(z[k].view(torch.uint8) if z[k].dtype != torch.int16 else z[k],
+                               p[k].view(torch.uint8) if p[k].dtype != torch.int16 else p[k]), k
+
+
 @pytest.mark.parametrize("last_blocks", [1, 3, 7])
 def test_short_last_chunk(last_blocks):
     """A single-pass step whose last 4096-row chunk holds only 1, 3 or 7 token blocks (the
