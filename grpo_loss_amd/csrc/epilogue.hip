@@ -104,8 +104,12 @@ __device__ inline void merge_side(const float* __restrict__ part, const PartLayo
   float s = 0.0f, z = 0.0f;
 #pragma unroll 8
   for (int p = 0; p < l.P; ++p) {
-    const float sp = part[l.at(1, sd, p, r)];
-    if (sp != 0.0f) s += sp * exp2f(part[l.at(0, sd, p, r)] - M);
+    // all three loads unconditional and the empty partial's factor a select, so the
+    // unrolled loads are issued together (a branch around one of them kept them one at a
+    // time); the fused multiply-add rounds as the branch's contracted form did, and adds
+    // exactly 0 for an empty partial
+    const float sp = part[l.at(1, sd, p, r)], mp = part[l.at(0, sd, p, r)];
+    s = fmaf(sp, sp != 0.0f ? exp2f(mp - M) : 0.0f, s);
     z += part[l.at(2, sd, p, r)];
   }
   *lse = (M + log2f(s)) * kLn2;
@@ -256,14 +260,18 @@ __device__ inline double merge_row(const MergeArgs& a, int64_t t, int64_t r, con
 // group returns the row's results.  The whole group must be active.
 __device__ inline void merge_side_group(const float* __restrict__ part, const PartLayout& l,
                                         int sd, int64_t r, int q, float* lse, float* zt) {
+  // (unrolled like merge_side, so that each lane has several phases' loads in flight; the
+  // sums keep their order)
   float M = -INFINITY;
+#pragma unroll 8
   for (int p = q; p < l.P; p += kMergeLanes) M = fmaxf(M, part[l.at(0, sd, p, r)]);
 #pragma unroll
   for (int off = 1; off < kMergeLanes; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, kMergeLanes));
   float s = 0.0f, z = 0.0f;
+#pragma unroll 8
   for (int p = q; p < l.P; p += kMergeLanes) {
-    const float sp = part[l.at(1, sd, p, r)];
-    if (sp != 0.0f) s += sp * exp2f(part[l.at(0, sd, p, r)] - M);
+    const float sp = part[l.at(1, sd, p, r)], mp = part[l.at(0, sd, p, r)];
+    s = fmaf(sp, sp != 0.0f ? exp2f(mp - M) : 0.0f, s);   // as in merge_side
     z += part[l.at(2, sd, p, r)];
   }
 #pragma unroll
